@@ -1,0 +1,17 @@
+"""MI355X (gfx950) fused attention forward: dense, causal, forward-mode JVP and
+jagged multi-head variants, behind the C ABI declared in include/attn.h.
+
+The Python layer only marshals arguments: every step of the computation runs
+in the HIP kernels of libattn_mi355x.so.  torch supplies device memory and the
+current stream.
+"""
+
+from .binding import (  # noqa: F401
+    AttnError,
+    fwd,
+    fwd_jvp,
+    jagged_fwd,
+    jagged_workspace_bytes,
+    library_path,
+    load_library,
+)

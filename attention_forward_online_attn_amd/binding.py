@@ -1,0 +1,172 @@
+"""ctypes binding of libattn_mi355x.so (declarations in include/attn.h).
+
+Argument marshalling only: tensors become device pointers and element strides,
+outputs are allocated with torch.empty, the stream is torch's current HIP
+stream.  A missing library or a non-zero status raises AttnError; there is no
+fallback of any kind.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_NAME = "libattn_mi355x.so"
+_lib = None
+
+ATTN_BF16 = 0
+ATTN_FP32 = 1
+
+
+class AttnError(RuntimeError):
+    """A failed library call; ``status`` holds the C status code."""
+
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+class Strides4(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64),
+                ("n", ctypes.c_int64), ("d", ctypes.c_int64)]
+
+
+class Strides3(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_int64), ("t", ctypes.c_int64), ("d", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
+
+
+def load_library():
+    """Load libattn_mi355x.so and declare its entry points (once)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise AttnError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    S4, S3 = Strides4, Strides3
+    lib.attn_fwd.argtypes = [i32, vp, S4, vp, S4, vp, S4, vp, S4, vp,
+                             i64, i64, i64, i64, i64, f32, i32, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd_jvp.argtypes = [i32, vp, vp, vp, vp, vp, vp, S4, S4, S4, vp, vp, S4, vp,
+                                 i64, i64, i64, i64, i64, f32, i32, vp]
+    lib.attn_fwd_jvp.restype = i32
+    lib.jagged_attn_workspace_bytes.argtypes = [i64, i64]
+    lib.jagged_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.jagged_attn_fwd.argtypes = [i32, vp, S3, vp, S3, vp, S3, vp, S3, vp, vp,
+                                    i64, i64, i64, i64, i64, f32, i32, vp, ctypes.c_size_t, vp]
+    lib.jagged_attn_fwd.restype = i32
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != 0:
+        msg = load_library().attn_status_string(rc).decode()
+        raise AttnError(f"attention library call failed: {msg} (status {rc})", rc)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_FP32
+    raise AttnError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _s4(t):
+    return Strides4(*t.stride())
+
+
+def _s3(t):
+    return Strides3(*t.stride())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _same(ref, *ts):
+    for t in ts:
+        if t.dtype != ref.dtype or t.device != ref.device:
+            raise AttnError("all tensors must share dtype and device")
+        if not t.is_cuda:
+            raise AttnError("tensors must be on a HIP device")
+
+
+def fwd(q, k, v, causal=False, sm_scale=None):
+    """Dense forward.  q [B,H,Nq,D], k/v [B,H,Nkv,D] -> (o [B,H,Nq,D], lse fp32 [B,H,Nq])."""
+    lib = load_library()
+    _same(q, k, v)
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    o = torch.empty((B, H, Nq, D), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd(_dtype_code(q), _ptr(q), _s4(q), _ptr(k), _s4(k), _ptr(v), _s4(v),
+                        _ptr(o), _s4(o), _ptr(lse), B, H, Nq, Nkv, D,
+                        float(sm_scale), int(bool(causal)), _stream(q)))
+    return o, lse
+
+
+def fwd_jvp(q, k, v, tq, tk, tv, causal=False, sm_scale=None):
+    """Dense forward fused with the JVP -> (o, to, lse).  Tangents must have
+    the strides of their primals."""
+    lib = load_library()
+    _same(q, k, v, tq, tk, tv)
+    for t, p in ((tq, q), (tk, k), (tv, v)):
+        if t.shape != p.shape or t.stride() != p.stride():
+            raise AttnError("tangents must match their primals in shape and strides")
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    o = torch.empty((B, H, Nq, D), dtype=q.dtype, device=q.device)
+    to = torch.empty_like(o)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd_jvp(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                            _s4(q), _s4(k), _s4(v), _ptr(o), _ptr(to), _s4(o), _ptr(lse),
+                            B, H, Nq, Nkv, D, float(sm_scale), int(bool(causal)), _stream(q)))
+    return o, to, lse
+
+
+def jagged_workspace_bytes(num_seqs, total_len) -> int:
+    return int(load_library().jagged_attn_workspace_bytes(int(num_seqs), int(total_len)))
+
+
+def jagged_fwd(q, k, v, offsets, max_seq_len, causal=False, sm_scale=None, workspace=None):
+    """Jagged forward.  q/k/v [H, total_len, D], offsets int64 [num_seqs+1] on
+    the device -> (o [H, total_len, D], lse fp32 [H, total_len])."""
+    lib = load_library()
+    _same(q, k, v)
+    if offsets.dtype != torch.int64 or offsets.device != q.device or offsets.dim() != 1:
+        raise AttnError("offsets must be a 1-D int64 tensor on the same device")
+    offsets = offsets.contiguous()
+    H, T, D = q.shape
+    S = offsets.numel() - 1
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    need = jagged_workspace_bytes(S, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty((H, T, D), dtype=q.dtype, device=q.device)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check(lib.jagged_attn_fwd(_dtype_code(q), _ptr(q), _s3(q), _ptr(k), _s3(k), _ptr(v), _s3(v),
+                               _ptr(o), _s3(o), _ptr(lse), _ptr(offsets), S, H, T, D,
+                               int(max_seq_len), float(sm_scale), int(bool(causal)),
+                               _ptr(workspace), workspace.numel(), _stream(q)))
+    return o, lse

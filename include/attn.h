@@ -1,0 +1,152 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention forward library
+ * (libattn_mi355x.so).
+ *
+ * The operation is the FlashAttention-2 style forward pass that the four
+ * source pages share: for each query row i of a (batch, head),
+ *
+ *     S_ij   = sm_scale * <q_i, k_j>
+ *     O_i    = sum_j softmax_j(S_i.) v_j
+ *     LSE_i  = log sum_j exp(S_ij)                      (natural log, fp32)
+ *
+ * computed in one streaming pass over key/value tiles with an online softmax
+ * (Triton fused-attention tutorial with JVP, "_06_fused_attention_blockptr_jvp.py":
+ * _attn_fwd and _attn_fwd_inner; "Flash Attention v2 with JVP", flm/utils/jvp.py:
+ * _attn_fwd and its epilogue).  The LSE follows the JVP page, which stores the
+ * natural-log value in fp32.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
+ *   every buffer; the library never allocates or frees device memory.
+ * - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *   default stream).  Calls are asynchronous: nothing synchronises the host.
+ * - Strides are in ELEMENTS.  The innermost (head-dim) stride must be 1.
+ *   Base pointers must be 16-byte aligned and every other stride a multiple of
+ *   16 bytes (8 bf16 elements, 4 fp32 elements); contiguous torch tensors
+ *   satisfy this.  Anything else is ATTN_ERR_UNSUPPORTED.
+ * - Tangent tensors (JVP) share the strides of their primals, and tO shares
+ *   the strides of O (as the JVP page's wrapper requires).
+ * - Supported head dims: 64 and 128.  dtype ATTN_BF16 computes the products on
+ *   bf16 MFMA with fp32 accumulation and rounds O/tO to bf16 (RNE); ATTN_FP32
+ *   computes everything in fp32.  LSE is always fp32.
+ * - sm_scale must be finite and >= 0 (every page uses a positive scale,
+ *   by default D^-0.5).
+ * - A query row with no key to attend (Nkv == 0, or a jagged row beyond
+ *   max_seq_len inside its sequence) gets O = 0, tO = 0 and LSE = -inf.
+ * - All argument checks happen on the host before anything is enqueued; a
+ *   failed check enqueues nothing and returns a negative status.
+ * - The library keeps no mutable global state beyond a per-process cache of
+ *   kernel attributes, so concurrent calls on different streams are safe.
+ */
+#ifndef ATTN_MI355X_ATTN_H
+#define ATTN_MI355X_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (every entry point returns one). */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = -1,      /* null pointer with work to do, negative size, bad stride, bad scale */
+  ATTN_ERR_UNSUPPORTED = -2,  /* head dim not in {64,128}, unknown dtype, misaligned pointer/stride */
+  ATTN_ERR_CAUSAL_SHAPE = -3, /* causal with Nq != Nkv (the mask is top-left aligned) */
+  ATTN_ERR_WORKSPACE = -4,    /* jagged workspace missing or too small */
+  ATTN_ERR_HIP = -5           /* the HIP runtime reported an error while enqueuing */
+};
+
+typedef enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype;
+
+/* Element strides of a dense [B, H, N, D] view. */
+typedef struct attn_strides4 { int64_t b, h, n, d; } attn_strides4;
+
+/* Element strides of a jagged [H, total_len, D] view. */
+typedef struct attn_strides3 { int64_t h, t, d; } attn_strides3;
+
+/*
+ * Dense attention forward (tutorial page: _attn_fwd with ENABLE_JVP off;
+ * JVP page: _attn_fwd).
+ *   q  [B, H, Nq,  D]   k, v [B, H, Nkv, D]   (dtype)
+ *   o  [B, H, Nq,  D]   written (dtype)
+ *   lse [B, H, Nq] contiguous fp32, written (natural log)
+ *   causal != 0: query i attends key j only when j <= i (top-left mask,
+ *   the pages' on-band stage); requires Nq == Nkv.
+ * B*H*Nq == 0 is a no-op returning ATTN_OK.
+ */
+int attn_fwd(attn_dtype dtype,
+             const void* q, attn_strides4 q_strides,
+             const void* k, attn_strides4 k_strides,
+             const void* v, attn_strides4 v_strides,
+             void* o, attn_strides4 o_strides,
+             float* lse,
+             int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+             float sm_scale, int causal, void* stream);
+
+/*
+ * Dense attention forward fused with its forward-mode JVP (tutorial page:
+ * _attn_fwd_inner / _attn_fwd with ENABLE_JVP; JVP page: _attn_fwd_inner and
+ * the epilogue).  With tangents (tq, tk, tv) of the inputs, it writes the
+ * output tangent
+ *     tS = sm_scale (tq k^T + q tk^T),  tP = P * (tS - rowsum(P * tS)),
+ *     to = tP v + P tv
+ * alongside o and lse in the same pass.  Tangents use the primal strides;
+ * `to` uses o_strides.  Other arguments as attn_fwd.
+ */
+int attn_fwd_jvp(attn_dtype dtype,
+                 const void* q, const void* k, const void* v,
+                 const void* tq, const void* tk, const void* tv,
+                 attn_strides4 q_strides, attn_strides4 k_strides, attn_strides4 v_strides,
+                 void* o, void* to, attn_strides4 o_strides,
+                 float* lse,
+                 int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                 float sm_scale, int causal, void* stream);
+
+/*
+ * Bytes of device workspace jagged_attn_fwd needs (host function, no GPU
+ * access).  Returns 0 for invalid sizes.
+ */
+size_t jagged_attn_workspace_bytes(int64_t num_seqs, int64_t total_len);
+
+/*
+ * Jagged multi-head attention forward (FBGEMM SLL page,
+ * triton_multi_head_jagged_flash_attention.py:
+ * _multi_head_jagged_flash_attention_fwd_kernel and the public wrapper).
+ *   q, k, v, o  [H, total_len, D]  (dtype)
+ *   lse         [H, total_len] contiguous fp32, written
+ *   offsets     DEVICE int64 [num_seqs + 1]: offsets[0] = 0, non-decreasing,
+ *               offsets[num_seqs] = total_len.  Sequence s owns rows
+ *               [offsets[s], offsets[s+1]).  Not checked (reading them would
+ *               need a host sync); out-of-range values are clamped so that no
+ *               access leaves the buffers, with unspecified results.
+ *   Only the first min(len_s, max_seq_len) rows of a sequence take part, as
+ *   queries and as keys; its later rows get O = 0, LSE = -inf.  There is no
+ *   attention across sequences.  causal != 0 masks key j > query i within a
+ *   sequence.  Unlike the SLL page, O is not divided by max_seq_len, and the
+ *   caller passes sm_scale (1.0 reproduces that page's unscaled logits).
+ *   workspace   DEVICE scratch of at least jagged_attn_workspace_bytes(...)
+ *               bytes, used for the on-device tile plan; its contents on entry
+ *               are ignored.  Calls that share a workspace must not overlap.
+ */
+int jagged_attn_fwd(attn_dtype dtype,
+                    const void* q, attn_strides3 q_strides,
+                    const void* k, attn_strides3 k_strides,
+                    const void* v, attn_strides3 v_strides,
+                    void* o, attn_strides3 o_strides,
+                    float* lse,
+                    const int64_t* offsets,
+                    int64_t num_seqs, int64_t H, int64_t total_len, int64_t D,
+                    int64_t max_seq_len, float sm_scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text for a status code (host, static storage). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_ATTN_H */

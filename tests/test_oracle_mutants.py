@@ -1,0 +1,110 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that the pins catch every one of them.
+
+Each mutant is the oracle's source with one textual change (a dropped term, a
+wrong sign or index, an operand swapped).  The checks below are the same kinds
+of pins as tests/test_oracle.py -- independent library, finite differences,
+brute-force sums, invariants -- run against the mutated module; at least one
+must fail for every mutant, and none may fail for the unmodified source.
+"""
+
+import inspect
+import math
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+MUTANTS = {
+    "drop_rho": ("tp = p * (ts - rho[:, None])", "tp = p * ts"),
+    "drop_p_tv": ("tp @ v + p @ tv", "tp @ v"),
+    "causal_off_by_one": ("cols[None, :] <= row_pos[r0:r1, None]", "cols[None, :] < row_pos[r0:r1, None]"),
+    "causal_flipped": ("cols[None, :] <= row_pos[r0:r1, None]", "cols[None, :] >= row_pos[r0:r1, None]"),
+    "tangent_operand_swapped": ("q[r0:r1] @ tk.T", "tq[r0:r1] @ k.T"),
+    "lse_base2": ("m + np.log(safe)", "m + np.log2(safe)"),
+    "lse_no_shift": ("m + np.log(safe)", "np.log(safe)"),
+    "scale_dropped": ("s = scale * (q[r0:r1] @ k.T)", "s = (q[r0:r1] @ k.T)"),
+    "tangent_scale_dropped": ("ts = scale * (tq[r0:r1] @ k.T", "ts = (tq[r0:r1] @ k.T"),
+    "unnormalised": ("p = e / safe[:, None]", "p = e"),
+    "keys_not_truncated": [("k[h, begin:begin + used], v[h, begin:begin + used]", "k[h, begin:end], v[h, begin:end]"),
+                           ("kv_len = np.where(np.arange(n) < used, used, 0)", "kv_len = np.where(np.arange(n) < used, n, 0)")],
+    "truncated_rows_attend": ("kv_len = np.where(np.arange(n) < used, used, 0)", "kv_len = np.where(np.arange(n) < used, used, used)"),
+    "transposed_value_product": ("p @ v, 0.0)", "(v.T @ p.T).T[:, ::-1], 0.0)"),
+}
+
+
+def _module(src):
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def rnd(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, k, v, scale, causal):
+    t = torch.from_numpy
+    with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+        return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal, scale=scale).numpy()
+
+
+def _pins_hold(m) -> bool:
+    """True when the module passes every pin used here."""
+    try:
+        q, k, v = rnd((1, 2, 6, 4), 1), rnd((1, 2, 6, 4), 2), rnd((1, 2, 6, 4), 3)
+        tq, tk, tv = rnd(q.shape, 4), rnd(k.shape, 5), rnd(v.shape, 6)
+        for causal in (False, True):
+            o, lse = m.attention(q, k, v, 0.6, causal)
+            if not np.allclose(o, _sdpa(q, k, v, 0.6, causal), atol=1e-12, rtol=0):
+                return False
+            # LSE by direct summation
+            for h in range(2):
+                for i in range(6):
+                    js = range(i + 1) if causal else range(6)
+                    ref = math.log(math.fsum(math.exp(0.6 * float(q[0, h, i] @ k[0, h, j])) for j in js))
+                    if abs(lse[0, h, i] - ref) > 1e-12:
+                        return False
+            # JVP by central differences
+            _, to, _ = m.attention_jvp(q, k, v, tq, tk, tv, 0.6, causal)
+            e = 1e-6
+            op, _ = m.attention(q + e * tq, k + e * tk, v + e * tv, 0.6, causal)
+            om, _ = m.attention(q - e * tq, k - e * tk, v - e * tv, 0.6, causal)
+            if not np.allclose(to, (op - om) / (2 * e), atol=1e-8, rtol=0):
+                return False
+        # jagged with truncation equals dense attention on each sequence's leading rows
+        lengths, M = [5, 2, 7], 4
+        off = np.concatenate([[0], np.cumsum(lengths)])
+        jq, jk, jv = rnd((2, 14, 4), 7), rnd((2, 14, 4), 8), rnd((2, 14, 4), 9)
+        o, lse = m.jagged_attention(jq, jk, jv, off, M, 0.5, False)
+        for s in range(3):
+            a, b = off[s], off[s + 1]
+            u = min(b - a, M)
+            od = _sdpa(jq[None, :, a:a + u], jk[None, :, a:a + u], jv[None, :, a:a + u], 0.5, False)[0]
+            if not np.allclose(o[:, a:a + u], od, atol=1e-12, rtol=0):
+                return False
+            if not (np.all(o[:, a + u:b] == 0) and np.all(np.isneginf(lse[:, a + u:b]))):
+                return False
+        return True
+    except Exception:
+        return False
+
+
+SOURCE = inspect.getsource(oracle)
+
+
+def test_unmodified_oracle_passes_the_pins():
+    assert _pins_hold(_module(SOURCE))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    edits = MUTANTS[name]
+    mutated = SOURCE
+    for old, new in (edits if isinstance(edits, list) else [edits]):
+        assert mutated.count(old) >= 1, f"mutation site for {name} not found in the oracle source"
+        mutated = mutated.replace(old, new, 1)
+    assert not _pins_hold(_module(mutated)), f"pins did not catch mutant {name}"
