@@ -1,0 +1,243 @@
+// Host side of libattn_mi355x.so: argument validation, kernel selection and
+// launches behind the C ABI of include/attn.h.  Every check runs on the host
+// before anything is enqueued; launches are asynchronous on the caller's
+// stream.  With ATTN_MI355X_DEBUG=1 in the environment each call also
+// synchronises its stream and reports kernel errors as ATTN_ERR_HIP.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "../../include/attn.h"
+#include "attn_common.h"
+#include "attn_fwd_bf16.h"
+#include "attn_fwd_f32.h"
+#include "jagged_plan.h"
+
+namespace attn {
+namespace {
+
+// Tile shapes of the compiled kernels.
+constexpr int kBnDense = 64;  // keys per tile, plain forward
+constexpr int kBnJvp = 32;    // keys per tile, JVP (two more streamed tensors)
+constexpr int kPlanBmMin = 64;  // smallest query tile of any kernel (workspace bound)
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("ATTN_MI355X_DEBUG");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+int finish(hipStream_t stream) {
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+  if (debug_sync() && hipStreamSynchronize(stream) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A stride is usable when its dimension is trivial or it keeps 16-byte rows.
+bool stride_ok(int64_t stride, int64_t extent, int64_t vec) {
+  if (stride < 0) return false;
+  return extent <= 1 || stride % vec == 0;
+}
+
+int check_common(int dtype, int64_t D, float sm_scale) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(sm_scale) || sm_scale < 0.f) return ATTN_ERR_INVALID;
+  if (D != 64 && D != 128) return D <= 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int check_s4(const attn_strides4& s, int64_t B, int64_t H, int64_t N, int64_t vec) {
+  if (s.d != 1) return ATTN_ERR_INVALID;
+  if (s.b < 0 || s.h < 0 || s.n < 0) return ATTN_ERR_INVALID;
+  if (!stride_ok(s.b, B, vec) || !stride_ok(s.h, H, vec) || !stride_ok(s.n, N, vec)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int check_s3(const attn_strides3& s, int64_t H, int64_t T, int64_t vec) {
+  if (s.d != 1) return ATTN_ERR_INVALID;
+  if (s.h < 0 || s.t < 0) return ATTN_ERR_INVALID;
+  if (!stride_ok(s.h, H, vec) || !stride_ok(s.t, T, vec)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+template <typename K>
+int launch(K kernel, int grid, int lds, hipStream_t stream, const FwdArgs& a) {
+  if (lds > 65536 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return ATTN_ERR_HIP;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, stream, a);
+  return ATTN_OK;
+}
+
+// Launch the forward kernel matching (dtype, D, jvp) over `grid` workgroups.
+int launch_fwd(int dtype, int D, bool jvp, int grid, hipStream_t stream, const FwdArgs& a) {
+  if (dtype == ATTN_BF16) {
+    if (!jvp) {
+      if (D == 64) return launch(attn_fwd_bf16_kernel<64, kBnDense, false>, grid, Bf16Cfg<64, kBnDense, false>::LDS, stream, a);
+      return launch(attn_fwd_bf16_kernel<128, kBnDense, false>, grid, Bf16Cfg<128, kBnDense, false>::LDS, stream, a);
+    }
+    if (D == 64) return launch(attn_fwd_bf16_kernel<64, kBnJvp, true>, grid, Bf16Cfg<64, kBnJvp, true>::LDS, stream, a);
+    return launch(attn_fwd_bf16_kernel<128, kBnJvp, true>, grid, Bf16Cfg<128, kBnJvp, true>::LDS, stream, a);
+  }
+  if (!jvp) {
+    if (D == 64) return launch(attn_fwd_f32_kernel<64, false>, grid, F32Cfg<64, false>::LDS, stream, a);
+    return launch(attn_fwd_f32_kernel<128, false>, grid, F32Cfg<128, false>::LDS, stream, a);
+  }
+  if (D == 64) return launch(attn_fwd_f32_kernel<64, true>, grid, F32Cfg<64, true>::LDS, stream, a);
+  return launch(attn_fwd_f32_kernel<128, true>, grid, F32Cfg<128, true>::LDS, stream, a);
+}
+
+int query_tile(int dtype) { return dtype == ATTN_BF16 ? Bf16Cfg<64, kBnDense, false>::BM : F32Cfg<64, false>::BM; }
+int key_tile(int dtype, bool jvp) { return dtype == ATTN_BF16 ? (jvp ? kBnJvp : kBnDense) : F32Cfg<64, false>::BN; }
+
+int dense(int dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk, const void* tv,
+          attn_strides4 sq, attn_strides4 sk, attn_strides4 sv, void* o, void* to, attn_strides4 so, float* lse,
+          int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal, void* stream,
+          bool jvp) {
+  int rc = check_common(dtype, D, sm_scale);
+  if (rc) return rc;
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
+  if (causal && Nq != Nkv) return ATTN_ERR_CAUSAL_SHAPE;
+  if (B * H * Nq == 0) return ATTN_OK;
+  if (Nq > INT_MAX || Nkv > INT_MAX || B > INT_MAX || H > INT_MAX) return ATTN_ERR_INVALID;
+  const int64_t vec = dtype == ATTN_BF16 ? 8 : 4;
+  if (!q || !o || !lse) return ATTN_ERR_INVALID;
+  if (Nkv > 0 && (!k || !v)) return ATTN_ERR_INVALID;
+  if (jvp && (!to || !tq || (Nkv > 0 && (!tk || !tv)))) return ATTN_ERR_INVALID;
+  if ((rc = check_s4(sq, B, H, Nq, vec)) || (rc = check_s4(so, B, H, Nq, vec))) return rc;
+  if (Nkv > 0 && ((rc = check_s4(sk, B, H, Nkv, vec)) || (rc = check_s4(sv, B, H, Nkv, vec)))) return rc;
+  const void* ptrs[] = {q, k, v, o, tq, tk, tv, to};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+
+  const int BM = query_tile(dtype);
+  const int64_t n_qtiles = (Nq + BM - 1) / BM;
+  const int64_t grid = B * H * n_qtiles;
+  if (grid > INT_MAX) return ATTN_ERR_INVALID;
+
+  FwdArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv; a.o = o; a.to = to; a.lse = lse;
+  a.q_sb = sq.b; a.q_sh = sq.h; a.q_sn = sq.n;
+  a.k_sb = sk.b; a.k_sh = sk.h; a.k_sn = sk.n;
+  a.v_sb = sv.b; a.v_sh = sv.h; a.v_sn = sv.n;
+  a.o_sb = so.b; a.o_sh = so.h; a.o_sn = so.n;
+  a.B = (int)B; a.H = (int)H; a.Nq = (int)Nq; a.Nkv = (int)Nkv;
+  a.n_qtiles = (int)n_qtiles;
+  a.sm_scale = sm_scale;
+  a.c = sm_scale * kLog2e;
+  if (a.c == 0.f) a.c = 1.17549435e-38f;  // sm_scale == 0: keep exp2 arguments exactly 0 and -inf masks -inf
+  a.causal = causal ? 1 : 0;
+  a.offsets = nullptr;
+  a.plan = nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();  // clear a stale error so that finish() reports only ours
+  rc = launch_fwd(dtype, (int)D, jvp, (int)grid, st, a);
+  if (rc) return rc;
+  return finish(st);
+}
+
+int64_t plan_capacity(int64_t num_seqs, int64_t total_len, int BM) {
+  // sum_s ceil(len_s / BM) <= floor((total_len + num_seqs (BM - 1)) / BM)
+  return (total_len + num_seqs * (BM - 1)) / BM;
+}
+
+}  // namespace
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" {
+
+int attn_fwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const void* k, attn_strides4 k_strides,
+             const void* v, attn_strides4 v_strides, void* o, attn_strides4 o_strides, float* lse, int64_t B,
+             int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal, void* stream) {
+  return dense((int)dtype, q, k, v, nullptr, nullptr, nullptr, q_strides, k_strides, v_strides, o, nullptr,
+               o_strides, lse, B, H, Nq, Nkv, D, sm_scale, causal, stream, false);
+}
+
+int attn_fwd_jvp(attn_dtype dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk,
+                 const void* tv, attn_strides4 q_strides, attn_strides4 k_strides, attn_strides4 v_strides, void* o,
+                 void* to, attn_strides4 o_strides, float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
+                 int64_t D, float sm_scale, int causal, void* stream) {
+  return dense((int)dtype, q, k, v, tq, tk, tv, q_strides, k_strides, v_strides, o, to, o_strides, lse, B, H, Nq,
+               Nkv, D, sm_scale, causal, stream, true);
+}
+
+size_t jagged_attn_workspace_bytes(int64_t num_seqs, int64_t total_len) {
+  if (num_seqs < 0 || total_len < 0 || num_seqs > INT_MAX - 1 || total_len > INT_MAX) return 0;
+  const int64_t cap = plan_capacity(num_seqs, total_len, kPlanBmMin);
+  return (size_t)(16 + 8 * cap);
+}
+
+int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, const void* k, attn_strides3 k_strides,
+                    const void* v, attn_strides3 v_strides, void* o, attn_strides3 o_strides, float* lse,
+                    const int64_t* offsets, int64_t num_seqs, int64_t H, int64_t total_len, int64_t D,
+                    int64_t max_seq_len, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int rc = check_common((int)dtype, D, sm_scale);
+  if (rc) return rc;
+  if (num_seqs < 0 || H < 0 || total_len < 0 || max_seq_len < 1) return ATTN_ERR_INVALID;
+  if (num_seqs > INT_MAX - 1 || H > INT_MAX || total_len > INT_MAX) return ATTN_ERR_INVALID;
+  if (num_seqs == 0 || H == 0 || total_len == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !offsets) return ATTN_ERR_INVALID;
+  const int64_t vec = dtype == ATTN_BF16 ? 8 : 4;
+  if ((rc = check_s3(q_strides, H, total_len, vec)) || (rc = check_s3(k_strides, H, total_len, vec)) ||
+      (rc = check_s3(v_strides, H, total_len, vec)) || (rc = check_s3(o_strides, H, total_len, vec)))
+    return rc;
+  const void* ptrs[] = {q, k, v, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  const int BM = query_tile((int)dtype);
+  const int64_t cap = plan_capacity(num_seqs, total_len, BM);
+  if (!workspace || workspace_bytes < (size_t)(16 + 8 * cap) || ((uintptr_t)workspace & 15u)) return ATTN_ERR_WORKSPACE;
+  const int64_t grid = cap * H;
+  if (grid > INT_MAX) return ATTN_ERR_INVALID;
+  const int mlen = (int)(max_seq_len < INT_MAX ? max_seq_len : INT_MAX);
+
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  int32_t* plan = (int32_t*)workspace;
+  hipLaunchKernelGGL(jagged_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, offsets, (int)num_seqs, total_len,
+                     mlen, causal ? 1 : 0, BM, key_tile((int)dtype, false), plan, (int)cap);
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+
+  FwdArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.q_sh = q_strides.h; a.q_sn = q_strides.t;
+  a.k_sh = k_strides.h; a.k_sn = k_strides.t;
+  a.v_sh = v_strides.h; a.v_sn = v_strides.t;
+  a.o_sh = o_strides.h; a.o_sn = o_strides.t;
+  a.B = (int)num_seqs; a.H = (int)H; a.Nq = 0; a.Nkv = 0; a.n_qtiles = 0;
+  a.sm_scale = sm_scale;
+  a.c = sm_scale * kLog2e;
+  if (a.c == 0.f) a.c = 1.17549435e-38f;
+  a.causal = causal ? 1 : 0;
+  a.offsets = offsets;
+  a.plan = plan;
+  a.total_len = (int)total_len;
+  a.max_seq_len = mlen;
+  rc = launch_fwd((int)dtype, (int)D, false, (int)grid, st, a);
+  if (rc) return rc;
+  return finish(st);
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (dtype, head dim or alignment)";
+    case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires Nq == Nkv";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// Shared device-side definitions: vector types, kernel arguments and the
+// mapping of a workgroup to its (batch|sequence, head, query tile).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) char lds_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Arguments of every forward kernel (passed by value).  Strides are in
+// elements; the head-dim stride is 1.  Tangents use the primal strides and
+// tO uses the strides of O.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* tq;
+  const void* tk;
+  const void* tv;
+  void* o;
+  void* to;
+  float* lse;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int32_t B, H, Nq, Nkv;
+  int32_t n_qtiles;  // dense: number of query tiles per (batch, head)
+  float c;           // sm_scale * log2(e): scores go to the exp2 domain
+  float sm_scale;
+  int32_t causal;
+  // jagged layout (offsets != nullptr): q/k/v/o are [H, total_len, D]
+  const int64_t* offsets;
+  const int32_t* plan;  // [0] item count, items (seq, q-tile) from index 4
+  int32_t total_len;
+  int32_t max_seq_len;
+};
+
+// One workgroup's share of the problem.
+struct Tile {
+  int64_t q_off, k_off, v_off, o_off;  // element offset of row 0 of this (batch|seq, head)
+  int64_t lse_off;                     // element offset of row 0 in the fp32 LSE buffer
+  int qt;                              // query tile index
+  int Lstore;                          // rows [0, Lstore) exist and are written
+  int Lattend;                         // rows [0, Lattend) attend keys; later rows attend none
+  int Lkv;                             // keys [0, Lkv)
+  bool valid;
+};
+
+// Workgroup -> tile.  Dense: the hardware hands workgroup i to XCD i % 8, so
+// each XCD is given a contiguous run of the (batch, head)-major work list:
+// the query tiles of a head then run on one XCD and share its L2 copy of
+// that head's K and V.  Causal tiles run heaviest first within a head.
+// Jagged: the device-built plan lists (sequence, query tile) items, most
+// key tiles first; the head is the fastest index.
+template <int BM>
+__device__ __forceinline__ Tile resolve_tile(const FwdArgs& a, int bid) {
+  Tile t;
+  if (a.offsets == nullptr) {
+    const int total = a.B * a.H * a.n_qtiles;
+    int logical = bid;
+    if ((total & 7) == 0) logical = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int bh = logical / a.n_qtiles;
+    int qt = logical - bh * a.n_qtiles;
+    if (a.causal) qt = a.n_qtiles - 1 - qt;
+    const int b = bh / a.H, h = bh - b * a.H;
+    t.q_off = b * a.q_sb + h * a.q_sh;
+    t.k_off = b * a.k_sb + h * a.k_sh;
+    t.v_off = b * a.v_sb + h * a.v_sh;
+    t.o_off = b * a.o_sb + h * a.o_sh;
+    t.lse_off = (int64_t)bh * a.Nq;
+    t.qt = qt;
+    t.Lstore = a.Nq;
+    t.Lattend = a.Nq;
+    t.Lkv = a.Nkv;
+    t.valid = true;
+  } else {
+    const int item = bid / a.H, h = bid - item * a.H;
+    t.valid = item < a.plan[0];
+    if (!t.valid) return t;
+    const int seq = a.plan[4 + 2 * item], qt = a.plan[5 + 2 * item];
+    const int64_t T = a.total_len;
+    int64_t begin = a.offsets[seq], end = a.offsets[seq + 1];
+    begin = begin < 0 ? 0 : (begin > T ? T : begin);
+    end = end < begin ? begin : (end > T ? T : end);
+    const int len = (int)(end - begin);
+    const int used = len < a.max_seq_len ? len : a.max_seq_len;
+    t.q_off = h * a.q_sh + begin * a.q_sn;
+    t.k_off = h * a.k_sh + begin * a.k_sn;
+    t.v_off = h * a.v_sh + begin * a.v_sn;
+    t.o_off = h * a.o_sh + begin * a.o_sn;
+    t.lse_off = (int64_t)h * a.total_len + begin;
+    t.qt = qt;
+    t.Lstore = len;
+    t.Lattend = used;
+    t.Lkv = used;
+    t.valid = qt * BM < len;
+  }
+  return t;
+}
+
+// Number of keys row i may attend (keys [0, limit) minus nothing else):
+// causal rows stop at the diagonal; rows past Lattend attend none.
+__device__ __forceinline__ int kv_limit(const Tile& t, int causal, int i) {
+  if (i >= t.Lattend) return 0;
+  return causal ? (i + 1 < t.Lkv ? i + 1 : t.Lkv) : t.Lkv;
+}
+
+}  // namespace attn

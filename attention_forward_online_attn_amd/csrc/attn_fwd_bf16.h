@@ -1,0 +1,339 @@
+// bf16 fused attention forward for gfx950 (CDNA4): S = K Q^T and O^T = V^T P^T
+// on v_mfma_f32_32x32x16_bf16, online softmax in fp32 registers, K/V tiles
+// double-buffered in LDS.  Optional fused forward-mode JVP.
+//
+// What is computed follows the pages' forward kernels (Triton fused attention
+// tutorial with JVP: _attn_fwd_inner / _attn_fwd; Flash Attention v2 with JVP:
+// _attn_fwd_inner / _attn_fwd; FBGEMM SLL jagged attention:
+// _multi_head_jagged_flash_attention_fwd_kernel): per key tile, scores, a
+// running row max m and row sum l, rescale by exp2(m_old - m_new), then
+// acc += p V; epilogue O = acc / l, LSE = (m + log2 l) ln 2.  The JVP adds
+// tS = tQ K^T + Q tK^T, H = p * tS (from fp32 p, as the JVP page orders it),
+// r += rowsum(H), accA += p tV, accB += H V and the epilogue
+// tO = (accA + accB - r O) / l.
+//
+// Layout on the chip (one workgroup = 4 waves = 128 query rows, 32 per wave):
+// * Each wave computes S^T for its 32 queries, so a lane owns ONE query
+//   (lane % 32) and 16 of every 32 keys; the other 16 sit in lane ^ 32.  Row
+//   max/sum are in-lane plus one v_permlane32_swap.
+// * The MFMA rows of S^T are keys in a permuted order (kperm below) chosen so
+//   that the accumulator registers of S^T are, unchanged, the B operand of the
+//   P^T product with 8 CONSECUTIVE keys per lane -- no shuffles between the two
+//   products.
+// * O^T keeps the same lane = query ownership, so the softmax rescale and the
+//   epilogue are lane-local.
+// * K and V live in LDS in their natural [key][d] layout with a 16-byte chunk
+//   XOR swizzle; K fragments are ds_read_b128, V^T fragments come from the
+//   transposing ds_read_b64_tr_b16.  Both are bank-conflict free.
+// * Lazy rescaling: the running max used for p only moves when a row's max
+//   grows by more than kTau (in log2 units), so p <= 2^kTau and the O
+//   rescale is skipped on almost every tile; m, l and acc always share the
+//   same reference, so the result is the same identity up to rounding.
+#pragma once
+
+#include "attn_common.h"
+
+namespace attn {
+
+constexpr float kTau = 8.0f;
+
+// 16-byte-chunk XOR swizzle of a [rows][D] bf16 tile in LDS.  Conflict free
+// for: 16 lanes reading one chunk of 16 different rows (K fragments), the
+// transposing reads of 4 consecutive rows x 64 bytes (V fragments), and
+// 16 lanes writing consecutive chunks (tile stores).
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int chunk) {
+  int f;
+  if constexpr (D == 128) {
+    const int u = row & 15;
+    f = ((u & 3) << 2) | (u >> 2);
+  } else {
+    const int u = (row >> 1) & 7;
+    f = ((u & 1) << 2) | (u >> 1);
+  }
+  return row * (D * 2) + ((chunk ^ f) << 4);
+}
+
+// Key (within a 32-key block) that MFMA row m of S^T holds: swaps bits 2 and 3
+// of m, so that accumulator register r of lane half h is key
+// 16 (r / 8) + 8 h + (r % 8).
+__device__ __forceinline__ int kperm(int m) {
+  return (m & 16) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
+}
+
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A operand of O^T += V^T P^T for output columns 32*db .. 32*db+31 and keys
+// key0 .. key0+15: lane (d = lane % 32, half h) gets V[key0 + 8h + i][32 db + d],
+// i = 0..7, from two transposing reads.  Within each 16-lane block the
+// transposing read hands lane j element j % 4 of the 8-byte rows addressed by
+// lanes 4i + j / 4, so lane s of the block addresses key (key0 + 8h + s / 4)
+// at columns 32 db + 16 (block % 2) + 4 (s % 4) .. +3.
+template <int D>
+__device__ __forceinline__ bf16x8 v_frag(const lds_t* vt, int key0, int db, int lane) {
+  const int blk = lane >> 4, s = lane & 15;
+  const int d = 32 * db + 16 * (blk & 1) + 4 * (s & 3);
+  const int key = key0 + 8 * (blk >> 1) + (s >> 2);
+  const int within = (d & 7) << 1;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + swz_off<D>(key, d >> 3) + within));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + swz_off<D>(key + 4, d >> 3) + within));
+  const i16x4 v8[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v8);
+}
+
+template <int D, int BN, bool JVP>
+struct Bf16Cfg {
+  static constexpr int BM = 128;            // query rows per workgroup (4 waves x 32)
+  static constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
+  static constexpr int TILE = BN * D * 2;   // bytes of one K (or V, tK, tV) tile
+  static constexpr int NTEN = JVP ? 4 : 2;  // tensors streamed per key tile
+  static constexpr int STAGE = NTEN * TILE; // bytes of one pipeline stage
+  static constexpr int LDS = 2 * STAGE;     // double buffered
+  static constexpr int LOADS = BN * CPR / 256;
+  static constexpr int WAVES_PER_EU = (JVP && D == 128) ? 1 : 2;
+  static_assert((BN * CPR) % 256 == 0, "tile must split evenly over 256 threads");
+  static_assert(BN % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
+};
+
+template <int D, int BN, bool JVP>
+__global__ void __launch_bounds__(256, (Bf16Cfg<D, BN, JVP>::WAVES_PER_EU))
+attn_fwd_bf16_kernel(FwdArgs a) {
+  using C = Bf16Cfg<D, BN, JVP>;
+  constexpr int BM = C::BM, CPR = C::CPR, TILE = C::TILE, NTEN = C::NTEN, STAGE = C::STAGE;
+  constexpr int LOADS = C::LOADS;
+  constexpr int NB = BN / 32;  // 32-key blocks per tile
+  constexpr int KD = D / 16;   // MFMA steps over the head dim
+  constexpr int DB = D / 32;   // 32-column output blocks
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  lds_t* smem = (lds_t*)smem_raw;
+
+  const Tile t = resolve_tile<BM>(a, blockIdx.x);
+  if (!t.valid) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n32 = lane & 31, h32 = lane >> 5;
+  const bf16* Q = (const bf16*)a.q + t.q_off;
+  const bf16* K = (const bf16*)a.k + t.k_off;
+  const bf16* V = (const bf16*)a.v + t.v_off;
+  const bf16* TQ = JVP ? (const bf16*)a.tq + t.q_off : nullptr;
+  const bf16* TK = JVP ? (const bf16*)a.tk + t.k_off : nullptr;
+  const bf16* TV = JVP ? (const bf16*)a.tv + t.v_off : nullptr;
+
+  // ---- row bookkeeping (lane % 32 is this lane's query row)
+  const int row0 = t.qt * BM;
+  const int my_row = row0 + wave * 32 + n32;
+  const int my_lim = kv_limit(t, a.causal, my_row < t.Lstore ? my_row : t.Lstore - 1);
+  const int w0 = row0 + wave * 32;
+  const int w1 = min(w0 + 31, t.Lstore - 1);
+  int wave_max = 0, wave_min = 0;  // max / min key limit over the wave's rows
+  if (w0 <= w1) {
+    wave_max = w0 < t.Lattend ? kv_limit(t, a.causal, min(w1, t.Lattend - 1)) : 0;
+    wave_min = w1 >= t.Lattend ? 0 : kv_limit(t, a.causal, w0);
+  }
+  const int b1 = min(row0 + BM, t.Lattend) - 1;
+  const int blk_max = row0 <= b1 ? kv_limit(t, a.causal, b1) : 0;
+  const int n_tiles = (blk_max + BN - 1) / BN;
+
+  // ---- Q (and tQ) fragments, resident for the whole key loop: the B operand
+  // of S^T = K Q^T, lane (query n32, half h32) holds Q[row][16 kk + 8 h32 + 0..7]
+  bf16x8 qf[KD];
+  bf16x8 tqf[JVP ? KD : 1];
+  {
+    const int r = my_row < t.Lstore ? my_row : t.Lstore - 1;
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) qf[kk] = *(const bf16x8*)(Q + r * a.q_sn + 16 * kk + 8 * h32);
+    if constexpr (JVP) {
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) tqf[kk] = *(const bf16x8*)(TQ + r * a.q_sn + 16 * kk + 8 * h32);
+    }
+  }
+
+  // ---- global -> register staging of one key tile, register -> LDS stores
+  u32x4 stg[NTEN][LOADS];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int id = tid + 256 * it;
+      const int row = id / CPR, ch = id % CPR;
+      int key = j * BN + row;
+      key = key < t.Lkv ? key : t.Lkv - 1;  // tail rows re-read a valid key; they are masked
+      stg[0][it] = *(const u32x4*)(K + key * a.k_sn + ch * 8);
+      stg[1][it] = *(const u32x4*)(V + key * a.v_sn + ch * 8);
+      if constexpr (JVP) {
+        stg[2][it] = *(const u32x4*)(TK + key * a.k_sn + ch * 8);
+        stg[3][it] = *(const u32x4*)(TV + key * a.v_sn + ch * 8);
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    lds_t* base = smem + stage * STAGE;
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int id = tid + 256 * it;
+      const int off = swz_off<D>(id / CPR, id % CPR);
+#pragma unroll
+      for (int x = 0; x < NTEN; ++x) *(__attribute__((address_space(3))) u32x4*)(base + x * TILE + off) = stg[x][it];
+    }
+  };
+
+  f32x16 acc[DB];
+  f32x16 accA[JVP ? DB : 1], accB[JVP ? DB : 1];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    acc[i] = f32x16{};
+    if constexpr (JVP) { accA[i] = f32x16{}; accB[i] = f32x16{}; }
+  }
+  float m_run = -INFINITY;  // running max, exp2 domain (scores times c)
+  float l_run = 0.f;        // this lane's partial row sum (its 16 of every 32 keys)
+  float r_run = 0.f;        // JVP: partial rowsum of p * (tQ K^T + Q tK^T)
+  const int krow = kperm(n32);
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+  for (int j = 0; j < n_tiles; ++j) {
+    const int stage = j & 1;
+    const bool more = j + 1 < n_tiles;
+    if (more) load_tile(j + 1);  // in flight while this tile computes
+
+    if (j * BN < wave_max) {  // wave-uniform: skip tiles this wave cannot see
+      const lds_t* kt = smem + stage * STAGE;
+      const lds_t* vt = kt + TILE;
+      const lds_t* tkt = kt + 2 * TILE;
+      const lds_t* tvt = kt + 3 * TILE;
+
+      // S^T = K Q^T (and the tangent scores tQ K^T + Q tK^T)
+      f32x16 s[NB];
+      f32x16 ts[JVP ? NB : 1];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        s[b] = f32x16{};
+        if constexpr (JVP) ts[b] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          const int off = swz_off<D>(32 * b + krow, 2 * kk + h32);
+          const bf16x8 ka = *(const __attribute__((address_space(3))) bf16x8*)(kt + off);
+          s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[b], 0, 0, 0);
+          if constexpr (JVP) {
+            const bf16x8 tka = *(const __attribute__((address_space(3))) bf16x8*)(tkt + off);
+            ts[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tka, qf[kk], ts[b], 0, 0, 0);
+            ts[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, tqf[kk], ts[b], 0, 0, 0);
+          }
+        }
+      }
+
+      // mask keys past this row's limit (ragged tail, causal diagonal,
+      // jagged truncation) -- only on tiles that reach some row's limit
+      if ((j + 1) * BN > wave_min) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j * BN + 32 * b + 16 * (r >> 3) + 8 * h32 + (r & 7);
+            if (key >= my_lim) s[b][r] = -INFINITY;
+          }
+      }
+
+      // online softmax: tile row max (in-lane, then the other half-wave)
+      float mx = s[0][0];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+      mx = xhalf_max(mx);
+      const float m_new = mx * a.c;
+      const bool upd = m_new > m_run + kTau;
+      if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+        const float m_next = upd ? m_new : m_run;
+        const float alpha = m_next == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_next);
+#pragma unroll
+        for (int i = 0; i < DB; ++i) {
+          acc[i] *= alpha;
+          if constexpr (JVP) { accA[i] *= alpha; accB[i] *= alpha; }
+        }
+        l_run *= alpha;
+        r_run *= alpha;
+        m_run = m_next;
+      }
+      const float msub = m_run == -INFINITY ? 0.f : m_run;
+
+      // p = exp2(s c - m); P (and H = p tS) as bf16 B operands: registers
+      // 8 c16 .. 8 c16 + 7 of block b are keys 32 b + 16 c16 + 8 h32 + 0..7
+      bf16x8 pf[NB][2];
+      bf16x8 hf[JVP ? NB : 1][2];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], a.c, -msub));
+          l_run += p;
+          pf[b][r >> 3][r & 7] = (bf16)p;
+          if constexpr (JVP) {
+            const float hv = p * ts[b][r];
+            r_run += hv;
+            hf[b][r >> 3][r & 7] = (bf16)hv;
+          }
+        }
+
+      // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int c16 = 0; c16 < 2; ++c16) {
+            const bf16x8 va = v_frag<D>(vt, 32 * b + 16 * c16, db, lane);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[b][c16], acc[db], 0, 0, 0);
+            if constexpr (JVP) {
+              accB[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, hf[b][c16], accB[db], 0, 0, 0);
+              const bf16x8 tva = v_frag<D>(tvt, 32 * b + 16 * c16, db, lane);
+              accA[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tva, pf[b][c16], accA[db], 0, 0, 0);
+            }
+          }
+    }
+
+    if (more) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln2, tO = (accA + accB - r O) / l
+  const float l_tot = xhalf_sum(l_run);
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  const float lse = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
+  const float r_tot = JVP ? xhalf_sum(r_run) * a.sm_scale : 0.f;
+  if (my_row < t.Lstore) {
+    bf16* orow = (bf16*)a.o + t.o_off + my_row * a.o_sn;
+    bf16* torow = JVP ? (bf16*)a.to + t.o_off + my_row * a.o_sn : nullptr;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * h32;  // registers 4g..4g+3 are columns d..d+3
+        bf16x4 ov;
+        bf16x4 tov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float o = acc[db][4 * g + e] * inv;
+          ov[e] = (bf16)o;
+          if constexpr (JVP)
+            tov[e] = (bf16)((accA[db][4 * g + e] + a.sm_scale * accB[db][4 * g + e] - r_tot * o) * inv);
+        }
+        *(bf16x4*)(orow + d) = ov;
+        if constexpr (JVP) *(bf16x4*)(torow + d) = tov;
+      }
+    if (h32 == 0) a.lse[t.lse_off + my_row] = lse;
+  }
+}
+
+}  // namespace attn

@@ -1,0 +1,154 @@
+// fp32 fused attention forward (dense, causal, jagged, optional JVP).
+//
+// Same streaming algorithm as the bf16 kernel -- per key tile: scores, running
+// row max and sum, rescale by exp2(m_old - m_new), accumulate p V (pages:
+// _attn_fwd_inner of the tutorial and JVP pages; the SLL jagged forward
+// kernel) -- but every product stays in fp32 on the vector ALUs, so fp32
+// callers get fp32 accuracy.  It is the precision path, not the throughput
+// path: four lanes share a query row (each owns every 4th head-dim column),
+// dot products are reduced across the four lanes, K/V tiles of 32 keys are
+// staged in LDS and read as broadcasts.
+#pragma once
+
+#include "attn_common.h"
+
+namespace attn {
+
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  return x;
+}
+
+template <int D, bool JVP>
+struct F32Cfg {
+  static constexpr int BM = 64;   // query rows per workgroup (256 threads, 4 per row)
+  static constexpr int BN = 32;   // keys per tile
+  static constexpr int NTEN = JVP ? 4 : 2;
+  static constexpr int LDS = NTEN * BN * D * 4;
+};
+
+template <int D, bool JVP>
+__global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
+  using C = F32Cfg<D, JVP>;
+  constexpr int BM = C::BM, BN = C::BN, NTEN = C::NTEN;
+  constexpr int DQ = D / 4;               // columns owned by each lane of a quad
+  constexpr int F4 = BN * D / 4;          // float4 per tensor tile
+  static_assert(F4 % 256 == 0, "tile must split evenly over 256 threads");
+  extern __shared__ __attribute__((aligned(16))) float fsm[];
+
+  const Tile t = resolve_tile<BM>(a, blockIdx.x);
+  if (!t.valid) return;
+  const int tid = threadIdx.x, u = tid & 3;
+  const int my_row = t.qt * BM + (tid >> 2);
+  const int rr = my_row < t.Lstore ? my_row : t.Lstore - 1;
+  const int my_lim = kv_limit(t, a.causal, rr);
+  const int row0 = t.qt * BM;
+  const int b1 = min(row0 + BM, t.Lattend) - 1;
+  const int blk_max = row0 <= b1 ? kv_limit(t, a.causal, b1) : 0;
+  const int n_tiles = (blk_max + BN - 1) / BN;
+
+  const float* Q = (const float*)a.q + t.q_off;
+  const float* K = (const float*)a.k + t.k_off;
+  const float* V = (const float*)a.v + t.v_off;
+  const float* TQ = JVP ? (const float*)a.tq + t.q_off : nullptr;
+  const float* TK = JVP ? (const float*)a.tk + t.k_off : nullptr;
+  const float* TV = JVP ? (const float*)a.tv + t.v_off : nullptr;
+  const float* srcs[4] = {K, V, TK, TV};
+  const int64_t sns[4] = {a.k_sn, a.v_sn, a.k_sn, a.v_sn};
+
+  float qr[DQ], tqr[JVP ? DQ : 1];
+  float acc[DQ], accA[JVP ? DQ : 1], accB[JVP ? DQ : 1];
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) {
+    qr[i] = Q[rr * a.q_sn + 4 * i + u];
+    acc[i] = 0.f;
+    if constexpr (JVP) {
+      tqr[i] = TQ[rr * a.q_sn + 4 * i + u];
+      accA[i] = 0.f;
+      accB[i] = 0.f;
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f, r_run = 0.f;
+
+  for (int j = 0; j < n_tiles; ++j) {
+    __syncthreads();  // the previous tile is no longer being read
+#pragma unroll
+    for (int x = 0; x < NTEN; ++x)
+#pragma unroll
+      for (int it = 0; it < F4 / 256; ++it) {
+        const int id = tid + 256 * it;
+        const int row = id / (D / 4), c4 = id % (D / 4);
+        int key = j * BN + row;
+        key = key < t.Lkv ? key : t.Lkv - 1;
+        *(f32x4*)(fsm + x * BN * D + row * D + 4 * c4) = *(const f32x4*)(srcs[x] + key * sns[x] + 4 * c4);
+      }
+    __syncthreads();
+    const float* kt = fsm;
+    const float* vt = fsm + BN * D;
+    const float* tkt = fsm + 2 * BN * D;
+    const float* tvt = fsm + 3 * BN * D;
+
+    float s[BN], ts[JVP ? BN : 1];
+#pragma unroll
+    for (int jj = 0; jj < BN; ++jj) {
+      float part = 0.f, tpart = 0.f;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) {
+        const float kv = kt[jj * D + 4 * i + u];
+        part = __builtin_fmaf(qr[i], kv, part);
+        if constexpr (JVP) tpart = __builtin_fmaf(tqr[i], kv, __builtin_fmaf(qr[i], tkt[jj * D + 4 * i + u], tpart));
+      }
+      s[jj] = quad_sum(part);
+      if constexpr (JVP) ts[jj] = quad_sum(tpart);
+      if (j * BN + jj >= my_lim) s[jj] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int jj = 1; jj < BN; ++jj) mx = fmaxf(mx, s[jj]);
+    const float m_new = fmaxf(m_run, mx * a.c);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    const float msub = m_new == -INFINITY ? 0.f : m_new;
+    l_run *= alpha;
+    r_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) {
+      acc[i] *= alpha;
+      if constexpr (JVP) { accA[i] *= alpha; accB[i] *= alpha; }
+    }
+#pragma unroll
+    for (int jj = 0; jj < BN; ++jj) {
+      const float p = exp2f(__builtin_fmaf(s[jj], a.c, -msub));
+      l_run += p;
+      const float hv = JVP ? p * ts[jj] : 0.f;
+      r_run += hv;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) {
+        const float vv = vt[jj * D + 4 * i + u];
+        acc[i] = __builtin_fmaf(p, vv, acc[i]);
+        if constexpr (JVP) {
+          accB[i] = __builtin_fmaf(hv, vv, accB[i]);
+          accA[i] = __builtin_fmaf(p, tvt[jj * D + 4 * i + u], accA[i]);
+        }
+      }
+    }
+    m_run = m_new;
+  }
+
+  const bool empty = !(l_run > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_run;
+  if (my_row < t.Lstore) {
+    float* orow = (float*)a.o + t.o_off + my_row * a.o_sn;
+    float* torow = JVP ? (float*)a.to + t.o_off + my_row * a.o_sn : nullptr;
+    const float r_tot = r_run * a.sm_scale;
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) {
+      const float o = acc[i] * inv;
+      orow[4 * i + u] = o;
+      if constexpr (JVP) torow[4 * i + u] = (accA[i] + a.sm_scale * accB[i] - r_tot * o) * inv;
+    }
+    if (u == 0) a.lse[t.lse_off + my_row] = empty ? -INFINITY : (m_run + log2f(l_run)) * kLn2;
+  }
+}
+
+}  // namespace attn

@@ -49,6 +49,9 @@
 extern "C" {
 #endif
 
+/* Exported entry points (the library is built with hidden visibility). */
+#define ATTN_API __attribute__((visibility("default")))
+
 /* Status codes (every entry point returns one). */
 enum {
   ATTN_OK = 0,
@@ -77,7 +80,7 @@ typedef struct attn_strides3 { int64_t h, t, d; } attn_strides3;
  *   the pages' on-band stage); requires Nq == Nkv.
  * B*H*Nq == 0 is a no-op returning ATTN_OK.
  */
-int attn_fwd(attn_dtype dtype,
+ATTN_API int attn_fwd(attn_dtype dtype,
              const void* q, attn_strides4 q_strides,
              const void* k, attn_strides4 k_strides,
              const void* v, attn_strides4 v_strides,
@@ -96,7 +99,7 @@ int attn_fwd(attn_dtype dtype,
  * alongside o and lse in the same pass.  Tangents use the primal strides;
  * `to` uses o_strides.  Other arguments as attn_fwd.
  */
-int attn_fwd_jvp(attn_dtype dtype,
+ATTN_API int attn_fwd_jvp(attn_dtype dtype,
                  const void* q, const void* k, const void* v,
                  const void* tq, const void* tk, const void* tv,
                  attn_strides4 q_strides, attn_strides4 k_strides, attn_strides4 v_strides,
@@ -109,7 +112,7 @@ int attn_fwd_jvp(attn_dtype dtype,
  * Bytes of device workspace jagged_attn_fwd needs (host function, no GPU
  * access).  Returns 0 for invalid sizes.
  */
-size_t jagged_attn_workspace_bytes(int64_t num_seqs, int64_t total_len);
+ATTN_API size_t jagged_attn_workspace_bytes(int64_t num_seqs, int64_t total_len);
 
 /*
  * Jagged multi-head attention forward (FBGEMM SLL page,
@@ -131,7 +134,7 @@ size_t jagged_attn_workspace_bytes(int64_t num_seqs, int64_t total_len);
  *               bytes, used for the on-device tile plan; its contents on entry
  *               are ignored.  Calls that share a workspace must not overlap.
  */
-int jagged_attn_fwd(attn_dtype dtype,
+ATTN_API int jagged_attn_fwd(attn_dtype dtype,
                     const void* q, attn_strides3 q_strides,
                     const void* k, attn_strides3 k_strides,
                     const void* v, attn_strides3 v_strides,
@@ -143,7 +146,7 @@ int jagged_attn_fwd(attn_dtype dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable text for a status code (host, static storage). */
-const char* attn_status_string(int status);
+ATTN_API const char* attn_status_string(int status);
 
 #ifdef __cplusplus
 }

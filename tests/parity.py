@@ -1,0 +1,59 @@
+"""Comparison helpers for the GPU parity tests (HIP path vs the fp64 oracle)."""
+
+import numpy as np
+import torch
+
+# Max-abs bounds.  bf16 inputs with fp32 accumulation: O 1e-2, LSE 1e-3,
+# tO 3e-2 relative to max|tO|; fp32 inputs: 1e-4 for each.
+TOL = {
+    torch.bfloat16: dict(o=1e-2, lse=1e-3, to=3e-2),
+    torch.float32: dict(o=1e-4, lse=1e-4, to=1e-4),
+}
+
+
+def host64(t):
+    t = t.detach().cpu()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.numpy().astype(np.float64)
+
+
+def lse_err(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    ninf_ref, ninf_got = np.isneginf(ref), np.isneginf(got)
+    if np.any(ninf_ref != ninf_got):
+        return np.inf
+    fin = ~ninf_ref
+    return float(np.max(np.abs(got[fin] - ref[fin]), initial=0.0))
+
+
+def max_err(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if got.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(got)):
+        return np.inf
+    return float(np.max(np.abs(got - ref)))
+
+
+def bf16_floor(ref):
+    """max |bf16(x) - x|: what storing the exact result in bf16 alone costs."""
+    r = torch.from_numpy(np.ascontiguousarray(ref)).float()
+    return float((r.bfloat16().double() - torch.from_numpy(np.ascontiguousarray(ref))).abs().max()) if r.numel() else 0.0
+
+
+def assert_close(dtype, o, lse, o_ref, lse_ref, to=None, to_ref=None, label=""):
+    tol = TOL[dtype]
+    eo = max_err(o, o_ref)
+    el = lse_err(lse, lse_ref)
+    msg = f"{label}: max|dO|={eo:.3e} (tol {tol['o']:.0e}), max|dLSE|={el:.3e} (tol {tol['lse']:.0e})"
+    if dtype == torch.bfloat16:
+        msg += f", bf16 floor of O={bf16_floor(o_ref):.3e}"
+    ok = eo <= tol["o"] and el <= tol["lse"]
+    if to is not None:
+        scale = max(float(np.max(np.abs(to_ref), initial=0.0)), 1e-30)
+        et = max_err(to, to_ref) / scale
+        msg += f", max|dtO|/max|tO|={et:.3e} (tol {tol['to']:.0e})"
+        ok = ok and et <= tol["to"]
+    print(msg, flush=True)
+    assert ok, msg

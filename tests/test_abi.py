@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/attn.h declares, and rejects bad arguments on the host before
+anything is enqueued (status codes as documented in the header)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_forward_online_attn_amd as attn
+from attention_forward_online_attn_amd.binding import Strides3, Strides4
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn.h")
+
+OK, INVALID, UNSUPPORTED, CAUSAL, WORKSPACE = 0, -1, -2, -3, -4
+BF16, FP32 = 0, 1
+P = 1 << 20  # a 16-byte aligned fake device address: validation fails before any use
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.library_path()):
+        pytest.fail("libattn_mi355x.so is not built (run __graft_entry__.build())")
+    return attn.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ATTN_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == sorted(
+        ["attn_fwd", "attn_fwd_jvp", "jagged_attn_workspace_bytes", "jagged_attn_fwd", "attn_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    # and nothing of the implementation leaks (hidden visibility)
+    out = os.popen(f"nm -D --defined-only {attn.library_path()}").read()
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == set(declared_symbols()), exported
+
+
+def dense_strides(B, H, N, D):
+    return Strides4(H * N * D, N * D, D, 1)
+
+
+def call_fwd(lib, dtype=BF16, B=1, H=2, Nq=128, Nkv=128, D=64, scale=0.125, causal=0,
+             q=P, k=P, v=P, o=P, lse=P, sq=None, so=None):
+    sq = sq or dense_strides(B, H, Nq, D)
+    sk = dense_strides(B, H, Nkv, D)
+    so = so or dense_strides(B, H, Nq, D)
+    return lib.attn_fwd(dtype, q, sq, k, sk, v, sk, o, so, lse, B, H, Nq, Nkv, D, scale, causal, None)
+
+
+def test_status_strings(lib):
+    assert lib.attn_status_string(0) == b"ok"
+    for rc in (INVALID, UNSUPPORTED, CAUSAL, WORKSPACE, -5):
+        assert lib.attn_status_string(rc) not in (b"ok", b"unknown status")
+    assert lib.attn_status_string(7) == b"unknown status"
+
+
+def test_dense_validation(lib):
+    assert call_fwd(lib, D=96) == UNSUPPORTED
+    assert call_fwd(lib, D=0) == INVALID
+    assert call_fwd(lib, dtype=5) == UNSUPPORTED
+    assert call_fwd(lib, causal=1, Nkv=64) == CAUSAL
+    assert call_fwd(lib, scale=-0.5) == INVALID
+    assert call_fwd(lib, scale=float("nan")) == INVALID
+    assert call_fwd(lib, scale=float("inf")) == INVALID
+    assert call_fwd(lib, Nq=-1) == INVALID
+    assert call_fwd(lib, q=0) == INVALID
+    assert call_fwd(lib, lse=0) == INVALID
+    assert call_fwd(lib, k=0) == INVALID
+    assert call_fwd(lib, q=P + 2) == UNSUPPORTED                      # misaligned base
+    assert call_fwd(lib, sq=Strides4(2 * 128 * 64, 128 * 64, 64, 2)) == INVALID  # head dim not unit stride
+    assert call_fwd(lib, sq=Strides4(2 * 128 * 64, 128 * 64, 65, 1)) == UNSUPPORTED  # row stride not 16 B
+    # no work: nothing is enqueued, null data pointers are fine
+    assert call_fwd(lib, B=0, q=0, k=0, v=0, o=0, lse=0) == OK
+    assert call_fwd(lib, Nq=0, q=0, k=0, v=0, o=0, lse=0) == OK
+
+
+def test_jvp_validation(lib):
+    s = dense_strides(1, 1, 64, 64)
+    args = lambda tq=P, to=P, D=64: lib.attn_fwd_jvp(BF16, P, P, P, tq, P, P, s, s, s, P, to, s, P,
+                                                     1, 1, 64, 64, D, 0.125, 0, None)
+    assert args(tq=0) == INVALID
+    assert args(to=0) == INVALID
+    assert args(D=32) == UNSUPPORTED
+
+
+def test_jagged_validation(lib):
+    H, T, D, S = 2, 100, 64, 3
+    st = Strides3(T * D, D, 1)
+    need = lib.jagged_attn_workspace_bytes(S, T)
+    assert need >= 16 + 8 * ((T + S * 63) // 64)
+    assert lib.jagged_attn_workspace_bytes(-1, T) == 0
+
+    def call(ws=P, ws_bytes=need, msl=64, D=64, offsets=P):
+        return lib.jagged_attn_fwd(BF16, P, st, P, st, P, st, P, st, P, offsets, S, H, T, D, msl,
+                                   0.125, 0, ws, ws_bytes, None)
+    assert call(ws=0) == WORKSPACE
+    assert call(ws_bytes=16) == WORKSPACE
+    assert call(ws=P + 8) == WORKSPACE
+    assert call(msl=0) == INVALID
+    assert call(offsets=0) == INVALID
+    assert call(D=48) == UNSUPPORTED
+    assert lib.jagged_attn_fwd(BF16, 0, st, 0, st, 0, st, 0, st, 0, 0, 0, H, 0, D, 64,
+                               0.125, 0, 0, 0, None) == OK

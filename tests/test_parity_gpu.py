@@ -1,0 +1,245 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded inputs.
+
+Full element-by-element comparisons at sizes the oracle finishes in seconds
+(spanning several 128-row query tiles and 64-key tiles with ragged tails),
+and, at the full benchmark sizes, comparisons on sampled query rows that the
+oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import attention_forward_online_attn_amd as attn
+from attention_forward_online_attn_amd import workloads as wl
+from parity import assert_close, host64
+
+pytestmark = pytest.mark.gpu
+
+BF16, FP32 = torch.bfloat16, torch.float32
+DT = {"bf16": BF16, "fp32": FP32}
+
+
+def cuda(*ts):
+    return [t.cuda() for t in ts]
+
+
+def dense_case(B, H, Nq, Nkv, D, dtype, causal, scale=None, seed=0, label=""):
+    q, k, v = wl.dense_inputs(B, H, Nq, Nkv, D, dtype, seed)
+    scale = D ** -0.5 if scale is None else scale
+    o, lse = attn.fwd(*cuda(q, k, v), causal=causal, sm_scale=scale)
+    ro, rl = oracle.attention(q, k, v, oracle.scale_as_passed(scale), causal)
+    assert_close(DT[dtype], host64(o), host64(lse), ro, rl, label=label or f"dense {B,H,Nq,Nkv,D} {dtype} causal={causal}")
+
+
+def jvp_case(B, H, Nq, Nkv, D, dtype, causal, scale=None, seed=0, zero=None, label=""):
+    ts = list(wl.dense_inputs(B, H, Nq, Nkv, D, dtype, seed, tangents=True))
+    if zero is not None:
+        ts[3 + zero] = torch.zeros_like(ts[3 + zero])
+    scale = D ** -0.5 if scale is None else scale
+    o, to, lse = attn.fwd_jvp(*cuda(*ts), causal=causal, sm_scale=scale)
+    ro, rto, rl = oracle.attention_jvp(*ts, oracle.scale_as_passed(scale), causal)
+    assert_close(DT[dtype], host64(o), host64(lse), ro, rl, host64(to), rto,
+                 label=label or f"jvp {B,H,Nq,Nkv,D} {dtype} causal={causal} zero={zero}")
+
+
+def sampled_rows(B, H, N, n_rows, tile=128, seed=0):
+    """Rows at tile edges, the first/last rows and random ones, over random heads."""
+    rng = np.random.default_rng(seed)
+    picks = {0, 1, N - 1, N - 2, tile - 1, tile, min(N - 1, 2 * tile + 5)}
+    picks |= set(int(x) for x in rng.integers(0, N, n_rows))
+    return [(int(rng.integers(0, B)), int(rng.integers(0, H)), i) for i in sorted(picks)]
+
+
+# ----------------------------------------------------------------- the workloads
+
+
+def test_tiny_fp32_dense(gpu_lib):
+    w = wl.WORKLOADS["tiny_fp32"]
+    dense_case(w.B, w.H, w.N, w.N, w.D, "fp32", False, label="tiny fp32 [1,2,128,64]")
+
+
+def test_causal_d64_full(gpu_lib):
+    w = wl.WORKLOADS["causal_d64"]
+    dense_case(w.B, w.H, w.N, w.N, w.D, "bf16", True, label="causal bf16 [4,16,1024,64]")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_d128_sampled(gpu_lib, causal):
+    w = wl.WORKLOADS["long_d128"]
+    q, k, v = wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "bf16", 0)
+    o, lse = attn.fwd(*cuda(q, k, v), causal=causal, sm_scale=w.sm_scale)
+    rows = sampled_rows(w.B, w.H, w.N, 160)
+    ro, rl = oracle.attention_sampled(q, k, v, oracle.scale_as_passed(w.sm_scale), causal, rows)
+    oc, lc = host64(o), host64(lse)
+    go = np.stack([oc[b, h, i] for b, h, i in rows])
+    gl = np.array([lc[b, h, i] for b, h, i in rows])
+    assert_close(BF16, go, gl, ro, rl, label=f"long bf16 [4,32,4096,128] causal={causal}, {len(rows)} sampled rows")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_jvp_d64_sampled(gpu_lib, causal):
+    w = wl.WORKLOADS["jvp_d64"]
+    ts = wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "bf16", 0, tangents=True)
+    o, to, lse = attn.fwd_jvp(*cuda(*ts), causal=causal, sm_scale=w.sm_scale)
+    rows = sampled_rows(w.B, w.H, w.N, 160)
+    ro, rto, rl = oracle.attention_sampled(*ts[:3], oracle.scale_as_passed(w.sm_scale), causal, rows, tangents=ts[3:])
+    oc, toc, lc = host64(o), host64(to), host64(lse)
+    pick = lambda a: np.stack([a[b, h, i] for b, h, i in rows])
+    assert_close(BF16, pick(oc), np.array([lc[b, h, i] for b, h, i in rows]), ro, rl, pick(toc), rto,
+                 label=f"jvp bf16 [4,16,2048,64] causal={causal}, {len(rows)} sampled rows")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_jvp_full_reduced(gpu_lib, causal):
+    jvp_case(1, 4, 2048, 2048, 64, "bf16", causal)
+
+
+def test_jagged_d128_sampled_sequences(gpu_lib):
+    w = wl.WORKLOADS["jagged_d128"]
+    lengths = wl.jagged_lengths(w.num_seqs, w.max_len, 0)
+    q, k, v, off = wl.jagged_inputs(lengths, w.H, w.D, "bf16", 0)
+    o, lse = attn.jagged_fwd(*cuda(q, k, v, off), max_seq_len=w.max_len, sm_scale=w.sm_scale)
+    oc, lc = host64(o), host64(lse)
+    L = lengths.numpy()
+    seqs = sorted(set([int(np.argmax(L)), int(np.argmin(L)), 0, len(L) - 1]) |
+                  set(int(x) for x in np.random.default_rng(1).integers(0, len(L), 20)))
+    offs = off.numpy()
+    parts = [slice(offs[s], offs[s + 1]) for s in seqs]
+    sub = lambda x: np.concatenate([host64(x)[:, p] for p in parts], axis=1)
+    sub_off = np.concatenate([[0], np.cumsum([L[s] for s in seqs])])
+    ro, rl = oracle.jagged_attention(sub(q), sub(k), sub(v), sub_off, w.max_len, oracle.scale_as_passed(w.sm_scale))
+    go = np.concatenate([oc[:, p] for p in parts], axis=1)
+    gl = np.concatenate([lc[:, p] for p in parts], axis=1)
+    assert_close(BF16, go, gl, ro, rl, label=f"jagged bf16 H=8 D=128, {len(seqs)} of 256 sequences")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+# ----------------------------------------------------------------- edge sweeps
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("N", [1, 15, 127, 999, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_ragged_sweep(gpu_lib, dtype, D, N, causal):
+    dense_case(1, 2, N, N, D, dtype, causal, seed=N)
+
+
+@pytest.mark.parametrize("Nq,Nkv", [(256, 1024), (1024, 256), (1000, 515), (15, 1), (1, 700), (130, 65)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_cross_attention_shapes(gpu_lib, Nq, Nkv, dtype):
+    dense_case(2, 3, Nq, Nkv, 64, dtype, False, seed=Nq + Nkv)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_no_keys_gives_empty_rows(gpu_lib, dtype):
+    q = wl.dense_inputs(1, 2, 70, 1, 64, dtype, 3)[0].cuda()
+    e = torch.empty((1, 2, 0, 64), dtype=q.dtype, device="cuda")
+    o, lse = attn.fwd(q, e, e)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    o, to, lse = attn.fwd_jvp(q, e, e, q, e, e)
+    assert torch.all(o == 0) and torch.all(to == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0, 0.02])
+@pytest.mark.parametrize("causal", [False, True])
+def test_other_scales(gpu_lib, scale, causal):
+    """Scales other than D^-0.5.  For sm_scale = 1 the queries are scaled by
+    1/8 so that the logits keep the workloads' spread (std 1, not 8): with
+    std-8 logits the softmax is nearly one-hot and bf16 rounding of |O| ~ 4
+    alone reaches the O tolerance."""
+    q, k, v = wl.dense_inputs(1, 2, 300, 300, 64, "bf16", 11 + causal)
+    if scale == 1.0:
+        q = (q.float() * 0.125).bfloat16()
+    o, lse = attn.fwd(*cuda(q, k, v), causal=causal, sm_scale=scale)
+    ro, rl = oracle.attention(q, k, v, oracle.scale_as_passed(scale), causal)
+    assert_close(BF16, host64(o), host64(lse), ro, rl, label=f"sm_scale={scale} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("N", [1, 15, 999])
+@pytest.mark.parametrize("causal", [False, True])
+def test_jvp_sweep(gpu_lib, dtype, D, N, causal):
+    jvp_case(1, 2, N, N, D, dtype, causal, seed=N + D)
+
+
+@pytest.mark.parametrize("zero", [0, 1, 2])
+def test_jvp_each_tangent_zeroed(gpu_lib, zero):
+    jvp_case(1, 2, 333, 333, 64, "bf16", True, zero=zero, seed=5)
+
+
+def test_jvp_cross_attention(gpu_lib):
+    jvp_case(2, 2, 200, 515, 64, "bf16", False, seed=6)
+    jvp_case(1, 2, 515, 15, 128, "bf16", False, seed=7)
+
+
+def test_strided_layouts(gpu_lib):
+    """[B, N, H, D] storage (the FA-bias page's layout) and packed QKV
+    [B, N, 3, H, D] reach the kernel through strides only."""
+    B, N, H, D = 2, 300, 3, 64
+    g = torch.Generator().manual_seed(9)
+    qkv = torch.randn(B, N, 3, H, D, generator=g).bfloat16()
+    q, k, v = (qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3))  # [B, H, N, D] views
+    qkv_d = qkv.cuda()
+    qd, kd, vd = (qkv_d[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+    assert not qd.is_contiguous()
+    for causal in (False, True):
+        o, lse = attn.fwd(qd, kd, vd, causal=causal)
+        ro, rl = oracle.attention(q, k, v, oracle.scale_as_passed(D ** -0.5), causal)
+        assert_close(BF16, host64(o), host64(lse), ro, rl, label=f"packed qkv strided causal={causal}")
+
+
+def test_deterministic(gpu_lib):
+    q, k, v = cuda(*wl.dense_inputs(2, 4, 777, 777, 128, "bf16", 2))
+    o1, l1 = attn.fwd(q, k, v, causal=True)
+    o2, l2 = attn.fwd(q, k, v, causal=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------- jagged edges
+
+
+def jagged_case(lengths, H, D, dtype, max_seq_len, causal=False, scale=None, seed=0, label=""):
+    lengths = torch.as_tensor(lengths, dtype=torch.int64)
+    q, k, v, off = wl.jagged_inputs(lengths, H, D, dtype, seed)
+    scale = D ** -0.5 if scale is None else scale
+    o, lse = attn.jagged_fwd(*cuda(q, k, v, off), max_seq_len=max_seq_len, causal=causal, sm_scale=scale)
+    ro, rl = oracle.jagged_attention(q, k, v, off.numpy(), max_seq_len, oracle.scale_as_passed(scale), causal)
+    assert_close(DT[dtype], host64(o), host64(lse), ro, rl,
+                 label=label or f"jagged {lengths.tolist()[:6]}.. H={H} D={D} {dtype} msl={max_seq_len} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_jagged_edges(gpu_lib, dtype, causal):
+    # empty sequences, a length above max_seq_len (truncated), ragged tails
+    jagged_case([0, 5, 300, 0, 129, 1, 700, 64], 3, 64, dtype, 256, causal, seed=1)
+    jagged_case([1000], 2, 128, dtype, 1024, causal, seed=2)          # single sequence
+    jagged_case([3, 0, 0], 2, 128, dtype, 2, causal, seed=3)         # truncation to 2
+
+
+def test_jagged_equal_lengths_match_dense(gpu_lib):
+    S, L, H, D = 4, 200, 2, 128
+    q, k, v, off = wl.jagged_inputs(torch.full((S,), L), H, D, "bf16", 4)
+    o, lse = attn.jagged_fwd(*cuda(q, k, v, off), max_seq_len=L)
+    dense = lambda x: x.reshape(H, S, L, D).permute(1, 0, 2, 3).contiguous()
+    od, ld = attn.fwd(*cuda(dense(q), dense(k), dense(v)))
+    # same arithmetic on the same rows: identical results
+    assert torch.equal(dense(o.cpu()), od.cpu())
+    assert torch.equal(lse.cpu().reshape(H, S, L).permute(1, 0, 2), ld.cpu())
+
+
+def test_jagged_unscaled_logits(gpu_lib):
+    """sm_scale = 1 reproduces the SLL page's raw q.k logits (inputs scaled
+    down so that the softmax is not one-hot)."""
+    lengths = torch.tensor([37, 250, 1])
+    q, k, v, off = wl.jagged_inputs(lengths, 2, 64, "bf16", 5)
+    q = (q.float() * 0.125).bfloat16()
+    o, lse = attn.jagged_fwd(*cuda(q, k, v, off), max_seq_len=512, sm_scale=1.0)
+    ro, rl = oracle.jagged_attention(q, k, v, off.numpy(), 512, 1.0)
+    assert_close(BF16, host64(o), host64(lse), ro, rl, label="jagged sm_scale=1")
