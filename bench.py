@@ -1,0 +1,250 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one forward pass (attn_fwd) over the long-context workload
+B=4, H=32, N=4096, D=128, bf16, non-causal (the headline "attention fwd
+TFLOP/s" workload); `value` is its throughput in TFLOP/s with the pages' flop
+convention 4 B H Nq Nkv D (x0.5 causal, x3 for the fused JVP forward).  The
+same run also times the fused JVP forward (B=4, H=16, N=2048, D=64) -- the
+"+ JVP fwd TFLOP/s" half of the metric -- the causal variants, the causal
+D=64 workload and the jagged workload, and reports them under `extra`.
+
+Timing: inputs are resident in HBM before the timed region; W untimed steps,
+then exactly K steps between two device synchronisations; per-launch HIP
+events on the launch stream give the kernel's average duration for the
+`roofline` object.  `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of the same workload (a few heads) on this host's cores.
+
+Profiling modes (for rocprofv3 runs): --only {fwd,fwd_causal,jvp,jvp_causal,
+causal_d64,jagged} runs just that kernel K times; --copy-calibration runs a
+plain device copy of known size (the scale for FETCH_SIZE / WRITE_SIZE).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["attn_common.h", "attn_fwd_bf16.h", "attn_fwd_f32.h", "jagged_plan.h", "attn_abi.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "attention_forward_online_attn_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def dense_flops(B, H, Nq, Nkv, D, causal, jvp=False):
+    f = 4.0 * B * H * Nq * Nkv * D
+    if causal:
+        f *= 0.5
+    if jvp:
+        f *= 3.0
+    return f
+
+
+def jagged_flops(lengths, H, D, causal=False):
+    s = sum(int(x) * int(x) for x in lengths)
+    return 4.0 * H * D * s * (0.5 if causal else 1.0)
+
+
+class Case:
+    """One workload bound to resident device inputs."""
+
+    def __init__(self, name, run, flops, bytes_, desc):
+        self.name, self.run, self.flops, self.bytes, self.desc = name, run, flops, bytes_, desc
+
+
+def make_cases(torch, attn, wl):
+    dev = torch.device("cuda:0")
+    cases = {}
+
+    w = wl.WORKLOADS["long_d128"]
+    q, k, v = (t.to(dev) for t in wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "bf16", 0))
+    io_bytes = 4 * q.numel() * 2 + w.B * w.H * w.N * 4
+    for causal in (False, True):
+        nm = "fwd_causal" if causal else "fwd"
+        cases[nm] = Case(nm, (lambda c=causal: attn.fwd(q, k, v, causal=c, sm_scale=w.sm_scale)),
+                         dense_flops(w.B, w.H, w.N, w.N, w.D, causal), io_bytes,
+                         f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} bf16 causal={causal}")
+
+    w4 = wl.WORKLOADS["jvp_d64"]
+    ts = [t.to(dev) for t in wl.dense_inputs(w4.B, w4.H, w4.N, w4.N, w4.D, "bf16", 0, tangents=True)]
+    io4 = 8 * ts[0].numel() * 2 + w4.B * w4.H * w4.N * 4
+    for causal in (False, True):
+        nm = "jvp_causal" if causal else "jvp"
+        cases[nm] = Case(nm, (lambda c=causal: attn.fwd_jvp(*ts, causal=c, sm_scale=w4.sm_scale)),
+                         dense_flops(w4.B, w4.H, w4.N, w4.N, w4.D, causal, jvp=True), io4,
+                         f"{w4.name}: B={w4.B} H={w4.H} N={w4.N} D={w4.D} bf16 causal={causal} (O, tO, LSE)")
+
+    w2 = wl.WORKLOADS["causal_d64"]
+    q2, k2, v2 = (t.to(dev) for t in wl.dense_inputs(w2.B, w2.H, w2.N, w2.N, w2.D, "bf16", 0))
+    cases["causal_d64"] = Case("causal_d64", lambda: attn.fwd(q2, k2, v2, causal=True, sm_scale=w2.sm_scale),
+                               dense_flops(w2.B, w2.H, w2.N, w2.N, w2.D, True), 4 * q2.numel() * 2 + w2.B * w2.H * w2.N * 4,
+                               f"{w2.name}: B={w2.B} H={w2.H} N={w2.N} D={w2.D} bf16 causal")
+
+    w5 = wl.WORKLOADS["jagged_d128"]
+    lengths = wl.jagged_lengths(w5.num_seqs, w5.max_len, 0)
+    jq, jk, jv, off = (t.to(dev) for t in wl.jagged_inputs(lengths, w5.H, w5.D, "bf16", 0))
+    ws = torch.empty(attn.jagged_workspace_bytes(w5.num_seqs, jq.shape[1]), dtype=torch.uint8, device=dev)
+    cases["jagged"] = Case("jagged", lambda: attn.jagged_fwd(jq, jk, jv, off, w5.max_len, sm_scale=w5.sm_scale, workspace=ws),
+                           jagged_flops(lengths.tolist(), w5.H, w5.D), 4 * jq.numel() * 2 + jq.shape[0] * jq.shape[1] * 4,
+                           f"{w5.name}: 256 sequences U[1,1024], H=8 D=128 bf16, total_len={jq.shape[1]}")
+    return cases
+
+
+def time_case(torch, case, steps, warmup):
+    """Average per-launch duration from HIP events on the launch stream, and
+    the wall time of `steps` back-to-back launches."""
+    for _ in range(warmup):
+        case.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        case.run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) for a, b in evs]  # ms
+    return sum(durs) / len(durs), min(durs), wall
+
+
+def load_traffic(kernel_hash):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_hash:
+        return None  # counters were taken on another version of the kernel
+    return rec.get("fwd_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """The fp64 oracle on a bounded sample of the headline workload: whole
+    (batch, head) slices of the same seeded B=4, H=32, N=4096, D=128 inputs,
+    one after another until the time budget is spent (at most all 128)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    w = wl.WORKLOADS["long_d128"]
+    q, k, v = wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "bf16", 0)
+    scale = oracle.scale_as_passed(w.sm_scale)
+    oracle.attention(q[:1, :1, :64], k[:1, :1, :64], v[:1, :1, :64], scale, False)  # warm the BLAS pool
+    heads, t0 = 0, time.perf_counter()
+    while heads < w.B * w.H and (heads == 0 or time.perf_counter() - t0 < budget_s):
+        b, h = divmod(heads, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attention(q[sl], k[sl], v[sl], scale, False)
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = dense_flops(1, heads, w.N, w.N, w.D, False)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of the 128 (batch, head) slices of the B=4 H=32 N=4096 D=128 non-causal "
+                      f"forward in {dt:.1f} s (fp64 numpy oracle, BLAS threads = cores)"}
+
+
+def copy_calibration(torch, steps):
+    """A plain device copy of 1 GiB (reads 1 GiB, writes 1 GiB) for scaling
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": 1 << 30, "launches": steps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default=None)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (each (batch, head) is "
+              "independent; see the sharding notes in DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_forward_online_attn_amd as attn
+    from attention_forward_online_attn_amd import workloads as wl
+
+    attn.load_library()
+    if args.copy_calibration:
+        copy_calibration(torch, args.steps)
+        return
+    cases = make_cases(torch, attn, wl)
+    if args.only:
+        c = cases[args.only]
+        avg, mn, _ = time_case(torch, c, args.steps, args.warmup)
+        print(json.dumps({"case": c.name, "desc": c.desc, "avg_ms": avg, "min_ms": mn,
+                          "tflops": c.flops / (avg * 1e-3) / 1e12}), flush=True)
+        return
+
+    head = cases["fwd"]
+    avg, mn, wall = time_case(torch, head, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    value = head.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = head.flops / (avg * 1e-3) / 1e12
+    extra = {}
+    for name in ("fwd_causal", "jvp", "jvp_causal", "causal_d64", "jagged"):
+        c = cases[name]
+        a, m, _ = time_case(torch, c, max(5, args.steps // 2), 3)
+        extra[name] = {"workload": c.desc, "avg_ms": round(a, 4), "tflops": round(c.flops / (a * 1e-3) / 1e12, 2),
+                       "frac_of_mfma_peak": round(c.flops / (a * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "gbps_compulsory": round(c.bytes / (a * 1e-3) / 1e9, 1)}
+    traffic = load_traffic(kernel_source_hash())
+    out = {
+        "metric": "attention fwd TFLOP/s (bf16, N=4096, D=128) + JVP fwd TFLOP/s, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs)",
+        "config": {"workload": head.desc, "jvp_workload": cases["jvp"].desc,
+                   "flops_per_step": head.flops, "flop_convention": "4*B*H*Nq*Nkv*D (x0.5 causal, x3 JVP)"},
+        "jvp_value": extra["jvp"]["tflops"],
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128,64,false>",
+                     "avg_launch_ms": round(avg, 4), "min_launch_ms": round(mn, 4)},
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
