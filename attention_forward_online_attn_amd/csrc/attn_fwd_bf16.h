@@ -31,6 +31,8 @@
 //   same reference, so the result is the same identity up to rounding.
 #pragma once
 
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace attn {
@@ -76,16 +78,27 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // i = 0..7, from two transposing reads.  Within each 16-lane block the
 // transposing read hands lane j element j % 4 of the 8-byte rows addressed by
 // lanes 4i + j / 4, so lane s of the block addresses key (key0 + 8h + s / 4)
-// at columns 32 db + 16 (block % 2) + 4 (s % 4) .. +3.
+// (and 4 keys further for the second read) at columns
+// 32 db + 16 (block % 2) + 4 (s % 4) .. +3.
+//
+// The swizzle of a row depends only on the row modulo 16 and key0 is a
+// multiple of 16, so the lane-dependent part of the two addresses is computed
+// once (v_frag_offsets) and key0 enters as an immediate offset.
 template <int D>
-__device__ __forceinline__ bf16x8 v_frag(const lds_t* vt, int key0, int db, int lane) {
+__device__ __forceinline__ void v_frag_offsets(int lane, int db, int& lo, int& hi) {
   const int blk = lane >> 4, s = lane & 15;
   const int d = 32 * db + 16 * (blk & 1) + 4 * (s & 3);
-  const int key = key0 + 8 * (blk >> 1) + (s >> 2);
+  const int key = 8 * (blk >> 1) + (s >> 2);
   const int within = (d & 7) << 1;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + swz_off<D>(key, d >> 3) + within));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + swz_off<D>(key + 4, d >> 3) + within));
-  const i16x4 v8[2] = {lo, hi};
+  lo = swz_off<D>(key, d >> 3) + within;
+  hi = swz_off<D>(key + 4, d >> 3) + within;
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 v_frag(const lds_t* vt, int key0, int lo, int hi) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + lo + key0 * (D * 2)));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vt + hi + key0 * (D * 2)));
+  const i16x4 v8[2] = {a, b};
   return __builtin_bit_cast(bf16x8, v8);
 }
 
@@ -156,32 +169,62 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
-  // ---- global -> register staging of one key tile, register -> LDS stores
+  // ---- global -> register staging of one key tile, register -> LDS stores.
+  // Thread `tid` moves chunks id = tid + 256 it (row id / CPR, 16-byte chunk
+  // id % CPR).  Full tiles use a uniform tile base plus loop-invariant 32-bit
+  // byte offsets; only a ragged last tile clamps rows to the last valid key
+  // (those rows are masked).
+  uint32_t goff_k[LOADS], goff_v[LOADS];
+  int lds_off[LOADS];
+#pragma unroll
+  for (int it = 0; it < LOADS; ++it) {
+    const int id = tid + 256 * it;
+    const int row = id / CPR, ch = id % CPR;
+    goff_k[it] = (uint32_t)((row * a.k_sn + ch * 8) * 2);
+    goff_v[it] = (uint32_t)((row * a.v_sn + ch * 8) * 2);
+    lds_off[it] = swz_off<D>(row, ch);
+  }
   u32x4 stg[NTEN][LOADS];
   auto load_tile = [&](int j) {
+    const int64_t k0 = (int64_t)j * BN;
+    const char* kb = (const char*)K + k0 * a.k_sn * 2;
+    const char* vb = (const char*)V + k0 * a.v_sn * 2;
+    const char* tkb = JVP ? (const char*)TK + k0 * a.k_sn * 2 : nullptr;
+    const char* tvb = JVP ? (const char*)TV + k0 * a.v_sn * 2 : nullptr;
+    if (k0 + BN <= t.Lkv) {
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int id = tid + 256 * it;
-      const int row = id / CPR, ch = id % CPR;
-      int key = j * BN + row;
-      key = key < t.Lkv ? key : t.Lkv - 1;  // tail rows re-read a valid key; they are masked
-      stg[0][it] = *(const u32x4*)(K + key * a.k_sn + ch * 8);
-      stg[1][it] = *(const u32x4*)(V + key * a.v_sn + ch * 8);
-      if constexpr (JVP) {
-        stg[2][it] = *(const u32x4*)(TK + key * a.k_sn + ch * 8);
-        stg[3][it] = *(const u32x4*)(TV + key * a.v_sn + ch * 8);
+      for (int it = 0; it < LOADS; ++it) {
+        stg[0][it] = *(const u32x4*)(kb + goff_k[it]);
+        stg[1][it] = *(const u32x4*)(vb + goff_v[it]);
+        if constexpr (JVP) {
+          stg[2][it] = *(const u32x4*)(tkb + goff_k[it]);
+          stg[3][it] = *(const u32x4*)(tvb + goff_v[it]);
+        }
+      }
+    } else {
+      const int last = t.Lkv - 1 - (int)k0;  // last valid row of this tile
+#pragma unroll
+      for (int it = 0; it < LOADS; ++it) {
+        const int id = tid + 256 * it;
+        int row = id / CPR;
+        row = row < last ? row : last;
+        const int ch = id % CPR;
+        const uint32_t ok = (uint32_t)((row * a.k_sn + ch * 8) * 2);
+        const uint32_t ov = (uint32_t)((row * a.v_sn + ch * 8) * 2);
+        stg[0][it] = *(const u32x4*)(kb + ok);
+        stg[1][it] = *(const u32x4*)(vb + ov);
+        if constexpr (JVP) {
+          stg[2][it] = *(const u32x4*)(tkb + ok);
+          stg[3][it] = *(const u32x4*)(tvb + ov);
+        }
       }
     }
   };
-  auto store_tile = [&](int stage) {
-    lds_t* base = smem + stage * STAGE;
+  auto store_tile = [&](lds_t* base) {
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int id = tid + 256 * it;
-      const int off = swz_off<D>(id / CPR, id % CPR);
+    for (int it = 0; it < LOADS; ++it)
 #pragma unroll
-      for (int x = 0; x < NTEN; ++x) *(__attribute__((address_space(3))) u32x4*)(base + x * TILE + off) = stg[x][it];
-    }
+      for (int x = 0; x < NTEN; ++x) *(__attribute__((address_space(3))) u32x4*)(base + x * TILE + lds_off[it]) = stg[x][it];
   };
 
   f32x16 acc[DB];
@@ -194,20 +237,29 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // running max, exp2 domain (scores times c)
   float l_run = 0.f;        // this lane's partial row sum (its 16 of every 32 keys)
   float r_run = 0.f;        // JVP: partial rowsum of p * (tQ K^T + Q tK^T)
+  // lane-dependent LDS offsets of the K fragments (per head-dim step) and of
+  // the V^T fragments (per output column block); tile, block and stage
+  // positions are added as immediates.  The swizzle depends on the row mod 16,
+  // which 32-key blocks do not change.
   const int krow = kperm(n32);
+  int koff[KD];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) koff[kk] = swz_off<D>(krow, 2 * kk + h32);
+  int vlo[DB], vhi[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) v_frag_offsets<D>(lane, db, vlo[db], vhi[db]);
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
-  for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
+  // One key tile: prefetch tile j+1 into registers, compute on LDS stage S,
+  // store the prefetched tile into the other stage, barrier.  S is a
+  // compile-time constant so every LDS address is a hoisted register plus an
+  // immediate offset.
+  auto step = [&](int j, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
     const bool more = j + 1 < n_tiles;
     if (more) load_tile(j + 1);  // in flight while this tile computes
 
     if (j * BN < wave_max) {  // wave-uniform: skip tiles this wave cannot see
-      const lds_t* kt = smem + stage * STAGE;
+      const lds_t* kt = smem + S * STAGE;
       const lds_t* vt = kt + TILE;
       const lds_t* tkt = kt + 2 * TILE;
       const lds_t* tvt = kt + 3 * TILE;
@@ -221,7 +273,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         if constexpr (JVP) ts[b] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk) {
-          const int off = swz_off<D>(32 * b + krow, 2 * kk + h32);
+          const int off = koff[kk] + 32 * b * (D * 2);
           const bf16x8 ka = *(const __attribute__((address_space(3))) bf16x8*)(kt + off);
           s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[b], 0, 0, 0);
           if constexpr (JVP) {
@@ -292,18 +344,33 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int c16 = 0; c16 < 2; ++c16) {
-            const bf16x8 va = v_frag<D>(vt, 32 * b + 16 * c16, db, lane);
+            const bf16x8 va = v_frag<D>(vt, 32 * b + 16 * c16, vlo[db], vhi[db]);
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[b][c16], acc[db], 0, 0, 0);
             if constexpr (JVP) {
               accB[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, hf[b][c16], accB[db], 0, 0, 0);
-              const bf16x8 tva = v_frag<D>(tvt, 32 * b + 16 * c16, db, lane);
+              const bf16x8 tva = v_frag<D>(tvt, 32 * b + 16 * c16, vlo[db], vhi[db]);
               accA[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tva, pf[b][c16], accA[db], 0, 0, 0);
             }
           }
     }
 
-    if (more) store_tile(stage ^ 1);
+    if (more) store_tile(smem + (1 - S) * STAGE);
     __syncthreads();
+  };
+
+  // The loop sits inside the prologue's branch: on every path into it the
+  // Q-fragment loads have completed, so no wait for the next tile's prefetch
+  // is needed inside the loop.
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(smem);
+    __syncthreads();
+    int j = 0;
+    for (; j + 2 <= n_tiles; j += 2) {
+      step(j, std::integral_constant<int, 0>{});
+      step(j + 1, std::integral_constant<int, 1>{});
+    }
+    if (j < n_tiles) step(j, std::integral_constant<int, 0>{});
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln2, tO = (accA + accB - r O) / l
