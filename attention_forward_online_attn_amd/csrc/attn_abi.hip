@@ -19,9 +19,9 @@
 namespace attn {
 namespace {
 
-// Tile shapes of the compiled kernels.
-constexpr int kBnDense = 64;  // keys per tile, plain forward
-constexpr int kBnJvp = 32;    // keys per tile, JVP (two more streamed tensors)
+// Tile shapes of the bf16 kernel (query tile 128 rows = 4 waves x 32).
+constexpr int kBnDense = 64;    // keys per tile, plain forward
+constexpr int kBnJvp = 32;      // keys per tile, JVP (four streamed tensors)
 constexpr int kPlanBmMin = 64;  // smallest query tile of any kernel (workspace bound)
 
 bool debug_sync() {
@@ -67,35 +67,36 @@ int check_s3(const attn_strides3& s, int64_t H, int64_t T, int64_t vec) {
   return ATTN_OK;
 }
 
-template <typename K>
-int launch(K kernel, int grid, int lds, hipStream_t stream, const FwdArgs& a) {
-  if (lds > 65536 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+// One compiled forward kernel with its tile shape.
+struct KernelChoice {
+  void (*fn)(FwdArgs);
+  int BM;       // query rows per workgroup
+  int BN;       // keys per tile
+  int lds;      // dynamic LDS bytes
+  int threads;  // workgroup size
+};
+
+template <int D, int BN, bool JVP>
+KernelChoice r32() { return {attn_fwd_bf16_kernel<D, BN, JVP>, Bf16Cfg<D, BN, JVP>::BM, BN, Bf16Cfg<D, BN, JVP>::LDS, 256}; }
+template <int D, bool JVP>
+KernelChoice f32k() { return {attn_fwd_f32_kernel<D, JVP>, F32Cfg<D, JVP>::BM, F32Cfg<D, JVP>::BN, F32Cfg<D, JVP>::LDS, 256}; }
+
+KernelChoice choose(int dtype, int D, bool jvp) {
+  if (dtype == ATTN_BF16) {
+    if (!jvp) return D == 64 ? r32<64, kBnDense, false>() : r32<128, kBnDense, false>();
+    return D == 64 ? r32<64, kBnJvp, true>() : r32<128, kBnJvp, true>();
+  }
+  if (!jvp) return D == 64 ? f32k<64, false>() : f32k<128, false>();
+  return D == 64 ? f32k<64, true>() : f32k<128, true>();
+}
+
+int launch(const KernelChoice& k, int grid, hipStream_t stream, const FwdArgs& a) {
+  if (k.lds > 65536 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(k.fn), hipFuncAttributeMaxDynamicSharedMemorySize, k.lds) != hipSuccess)
     return ATTN_ERR_HIP;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(k.fn, dim3(grid), dim3(k.threads), k.lds, stream, a);
   return ATTN_OK;
 }
-
-// Launch the forward kernel matching (dtype, D, jvp) over `grid` workgroups.
-int launch_fwd(int dtype, int D, bool jvp, int grid, hipStream_t stream, const FwdArgs& a) {
-  if (dtype == ATTN_BF16) {
-    if (!jvp) {
-      if (D == 64) return launch(attn_fwd_bf16_kernel<64, kBnDense, false>, grid, Bf16Cfg<64, kBnDense, false>::LDS, stream, a);
-      return launch(attn_fwd_bf16_kernel<128, kBnDense, false>, grid, Bf16Cfg<128, kBnDense, false>::LDS, stream, a);
-    }
-    if (D == 64) return launch(attn_fwd_bf16_kernel<64, kBnJvp, true>, grid, Bf16Cfg<64, kBnJvp, true>::LDS, stream, a);
-    return launch(attn_fwd_bf16_kernel<128, kBnJvp, true>, grid, Bf16Cfg<128, kBnJvp, true>::LDS, stream, a);
-  }
-  if (!jvp) {
-    if (D == 64) return launch(attn_fwd_f32_kernel<64, false>, grid, F32Cfg<64, false>::LDS, stream, a);
-    return launch(attn_fwd_f32_kernel<128, false>, grid, F32Cfg<128, false>::LDS, stream, a);
-  }
-  if (D == 64) return launch(attn_fwd_f32_kernel<64, true>, grid, F32Cfg<64, true>::LDS, stream, a);
-  return launch(attn_fwd_f32_kernel<128, true>, grid, F32Cfg<128, true>::LDS, stream, a);
-}
-
-int query_tile(int dtype) { return dtype == ATTN_BF16 ? Bf16Cfg<64, kBnDense, false>::BM : F32Cfg<64, false>::BM; }
-int key_tile(int dtype, bool jvp) { return dtype == ATTN_BF16 ? (jvp ? kBnJvp : kBnDense) : F32Cfg<64, false>::BN; }
 
 int dense(int dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk, const void* tv,
           attn_strides4 sq, attn_strides4 sk, attn_strides4 sv, void* o, void* to, attn_strides4 so, float* lse,
@@ -117,7 +118,8 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return ATTN_ERR_UNSUPPORTED;
 
-  const int BM = query_tile(dtype);
+  const KernelChoice kc = choose(dtype, (int)D, jvp);
+  const int BM = kc.BM;
   const int64_t n_qtiles = (Nq + BM - 1) / BM;
   const int64_t grid = B * H * n_qtiles;
   if (grid > INT_MAX) return ATTN_ERR_INVALID;
@@ -138,7 +140,7 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   a.plan = nullptr;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // clear a stale error so that finish() reports only ours
-  rc = launch_fwd(dtype, (int)D, jvp, (int)grid, st, a);
+  rc = launch(kc, (int)grid, st, a);
   if (rc) return rc;
   return finish(st);
 }
@@ -194,7 +196,8 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   const void* ptrs[] = {q, k, v, o};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
-  const int BM = query_tile((int)dtype);
+  const KernelChoice kc = choose((int)dtype, (int)D, false);
+  const int BM = kc.BM;
   const int64_t cap = plan_capacity(num_seqs, total_len, BM);
   if (!workspace || workspace_bytes < (size_t)(16 + 8 * cap) || ((uintptr_t)workspace & 15u)) return ATTN_ERR_WORKSPACE;
   const int64_t grid = cap * H;
@@ -205,7 +208,7 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   (void)hipGetLastError();
   int32_t* plan = (int32_t*)workspace;
   hipLaunchKernelGGL(jagged_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, offsets, (int)num_seqs, total_len,
-                     mlen, causal ? 1 : 0, BM, key_tile((int)dtype, false), plan, (int)cap);
+                     mlen, causal ? 1 : 0, BM, kc.BN, plan, (int)cap);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
 
   FwdArgs a = {};
@@ -223,7 +226,7 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   a.plan = plan;
   a.total_len = (int)total_len;
   a.max_seq_len = mlen;
-  rc = launch_fwd((int)dtype, (int)D, false, (int)grid, st, a);
+  rc = launch(kc, (int)grid, st, a);
   if (rc) return rc;
   return finish(st);
 }

@@ -29,6 +29,12 @@
 //   grows by more than kTau (in log2 units), so p <= 2^kTau and the O
 //   rescale is skipped on almost every tile; m, l and acc always share the
 //   same reference, so the result is the same identity up to rounding.
+// * Per key tile: the next tile's global loads are issued first and stay in
+//   flight through the tile's two MFMA sections (scores, then PV), whose LDS
+//   fragment reads run a fixed distance ahead of their MFMAs; the prefetched
+//   tile is stored to the other LDS stage and one barrier ends the tile.
+//   Two workgroups share each CU (two waves per SIMD), so one wave's softmax
+//   overlaps the other's MFMAs.
 #pragma once
 
 #include <type_traits>
@@ -102,6 +108,89 @@ __device__ __forceinline__ bf16x8 v_frag(const lds_t* vt, int key0, int lo, int 
   return __builtin_bit_cast(bf16x8, v8);
 }
 
+// ---- MFMA sections with software-pipelined LDS fragment reads.
+//
+// A section is a fixed list of MFMA steps, each fed by fragments read from
+// LDS.  Reads run FD steps ahead of their MFMA through a ring of FD + 1
+// fragment buffers, and a scheduling fence after every step keeps exactly
+// that order: the MFMA pipe sees back-to-back work while at most FD reads are
+// in flight, and the register footprint stays fixed (left alone, the
+// scheduler hoists every read of a section to its top and spills).
+constexpr int kFragDist = 4;
+// Raised wave priority while a wave streams MFMAs: when two waves share a
+// SIMD the one feeding the matrix core is issued first.
+constexpr int kMfmaPrio = 1;
+
+// S^T = K Q^T for one [NB*32]-key tile (JVP: plus tS^T = tK Q^T + K tQ^T).
+// Step i is key block i / KD, head-dim step i % KD.
+template <int D, int NB, bool JVP>
+__device__ __forceinline__ void scores_section(const lds_t* kt, const lds_t* tkt, const int (&koff)[D / 16],
+                                               const bf16x8 (&qf)[D / 16],
+                                               const bf16x8 (&tqf)[JVP ? D / 16 : 1], f32x16 (&s)[NB],
+                                               f32x16 (&ts)[JVP ? NB : 1]) {
+  constexpr int KD = D / 16, N = NB * KD, R = kFragDist + 1, F = JVP ? 2 : 1;
+  bf16x8 ring[R][F];
+  auto issue = [&](int i, bf16x8 (&f)[F]) {
+    const int off = koff[i % KD] + 32 * (i / KD) * (D * 2);
+    f[0] = *(const __attribute__((address_space(3))) bf16x8*)(kt + off);
+    if constexpr (JVP) f[F - 1] = *(const __attribute__((address_space(3))) bf16x8*)(tkt + off);
+  };
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    s[b] = f32x16{};
+    if constexpr (JVP) ts[b] = f32x16{};
+  }
+  __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+  for (int i = 0; i < kFragDist && i < N; ++i) issue(i, ring[i % R]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + kFragDist < N) issue(i + kFragDist, ring[(i + kFragDist) % R]);
+    const int b = i / KD, kk = i % KD;
+    const bf16x8* f = ring[i % R];
+    s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], qf[kk], s[b], 0, 0, 0);
+    if constexpr (JVP) {
+      ts[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[F - 1], qf[kk], ts[b], 0, 0, 0);
+      ts[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], tqf[kk], ts[b], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// O^T += V^T P^T for one tile (JVP: accB += V^T H^T, accA += tV^T P^T).
+// Step i is output block i / (2 NB), key chunk i % (2 NB).
+template <int D, int NB, bool JVP>
+__device__ __forceinline__ void pv_section(const lds_t* vt, const lds_t* tvt, const int (&vlo)[D / 32],
+                                           const int (&vhi)[D / 32],
+                                           const bf16x8 (&pf)[NB][2], const bf16x8 (&hf)[JVP ? NB : 1][2],
+                                           f32x16 (&acc)[D / 32], f32x16 (&accA)[JVP ? D / 32 : 1],
+                                           f32x16 (&accB)[JVP ? D / 32 : 1]) {
+  constexpr int DB = D / 32, KC = 2 * NB, N = DB * KC, R = kFragDist + 1, F = JVP ? 2 : 1;
+  bf16x8 ring[R][F];
+  auto issue = [&](int i, bf16x8 (&f)[F]) {
+    const int db = i / KC, key0 = 16 * (i % KC);
+    f[0] = v_frag<D>(vt, key0, vlo[db], vhi[db]);
+    if constexpr (JVP) f[F - 1] = v_frag<D>(tvt, key0, vlo[db], vhi[db]);
+  };
+  __builtin_amdgcn_s_setprio(kMfmaPrio);
+#pragma unroll
+  for (int i = 0; i < kFragDist && i < N; ++i) issue(i, ring[i % R]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + kFragDist < N) issue(i + kFragDist, ring[(i + kFragDist) % R]);
+    const int db = i / KC, c = i % KC;
+    const bf16x8* f = ring[i % R];
+    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], pf[c >> 1][c & 1], acc[db], 0, 0, 0);
+    if constexpr (JVP) {
+      accB[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], hf[c >> 1][c & 1], accB[db], 0, 0, 0);
+      accA[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[F - 1], pf[c >> 1][c & 1], accA[db], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
 template <int D, int BN, bool JVP>
 struct Bf16Cfg {
   static constexpr int BM = 128;            // query rows per workgroup (4 waves x 32)
@@ -131,7 +220,8 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   const Tile t = resolve_tile<BM>(a, blockIdx.x);
   if (!t.valid) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: per-wave branches stay scalar
   const int n32 = lane & 31, h32 = lane >> 5;
   const bf16* Q = (const bf16*)a.q + t.q_off;
   const bf16* K = (const bf16*)a.k + t.k_off;
@@ -267,22 +357,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       // S^T = K Q^T (and the tangent scores tQ K^T + Q tK^T)
       f32x16 s[NB];
       f32x16 ts[JVP ? NB : 1];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        s[b] = f32x16{};
-        if constexpr (JVP) ts[b] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          const int off = koff[kk] + 32 * b * (D * 2);
-          const bf16x8 ka = *(const __attribute__((address_space(3))) bf16x8*)(kt + off);
-          s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[b], 0, 0, 0);
-          if constexpr (JVP) {
-            const bf16x8 tka = *(const __attribute__((address_space(3))) bf16x8*)(tkt + off);
-            ts[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tka, qf[kk], ts[b], 0, 0, 0);
-            ts[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, tqf[kk], ts[b], 0, 0, 0);
-          }
-        }
-      }
+      scores_section<D, NB, JVP>(kt, tkt, koff, qf, tqf, s, ts);
 
       // mask keys past this row's limit (ragged tail, causal diagonal,
       // jagged truncation) -- only on tiles that reach some row's limit
@@ -338,20 +413,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         }
 
       // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int c16 = 0; c16 < 2; ++c16) {
-            const bf16x8 va = v_frag<D>(vt, 32 * b + 16 * c16, vlo[db], vhi[db]);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[b][c16], acc[db], 0, 0, 0);
-            if constexpr (JVP) {
-              accB[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, hf[b][c16], accB[db], 0, 0, 0);
-              const bf16x8 tva = v_frag<D>(tvt, 32 * b + 16 * c16, vlo[db], vhi[db]);
-              accA[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tva, pf[b][c16], accA[db], 0, 0, 0);
-            }
-          }
+      pv_section<D, NB, JVP>(vt, tvt, vlo, vhi, pf, hf, acc, accA, accB);
     }
 
     if (more) store_tile(smem + (1 - S) * STAGE);
