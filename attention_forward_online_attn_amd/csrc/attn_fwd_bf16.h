@@ -45,21 +45,25 @@ namespace attn {
 
 constexpr float kTau = 8.0f;
 
+
 // 16-byte-chunk XOR swizzle of a [rows][D] bf16 tile in LDS.  Conflict free
 // for: 16 lanes reading one chunk of 16 different rows (K fragments), the
 // transposing reads of 4 consecutive rows x 64 bytes (V fragments), and
 // 16 lanes writing consecutive chunks (tile stores).
 template <int D>
-__device__ __forceinline__ int swz_off(int row, int chunk) {
-  int f;
+__device__ __forceinline__ int swz_f(int row) {
   if constexpr (D == 128) {
     const int u = row & 15;
-    f = ((u & 3) << 2) | (u >> 2);
+    return ((u & 3) << 2) | (u >> 2);
   } else {
     const int u = (row >> 1) & 7;
-    f = ((u & 1) << 2) | (u >> 1);
+    return ((u & 1) << 2) | (u >> 1);
   }
-  return row * (D * 2) + ((chunk ^ f) << 4);
+}
+
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int chunk) {
+  return row * (D * 2) + ((chunk ^ swz_f<D>(row)) << 4);
 }
 
 // Key (within a 32-key block) that MFMA row m of S^T holds: swaps bits 2 and 3
@@ -317,6 +321,54 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       for (int x = 0; x < NTEN; ++x) *(__attribute__((address_space(3))) u32x4*)(base + x * TILE + lds_off[it]) = stg[x][it];
   };
 
+  // Direct global -> LDS tile loads (global_load_lds_dwordx4): instruction i
+  // of this wave fills the 1 KiB block (wave * NI + i) of a tile, lane l the
+  // 16 bytes at l * 16 of it; so lane l fetches the chunk whose swizzled home
+  // is that spot (the swizzle is an XOR, its own inverse).  No registers or
+  // ds_write instructions are spent on staging.
+  // The D=128 JVP instance (1 wave per SIMD, which spills) keeps register
+  // staging: with DMA it produced wrong scores on ragged last tiles in the
+  // parity suite, a cause not isolated.
+  constexpr bool DMA = !(JVP && D == 128);
+  constexpr int NI = TILE / 1024 / 4;  // DMA instructions per wave per tensor
+  static_assert(!DMA || TILE % 4096 == 0, "DMA tiles are whole 1 KiB blocks per wave");
+  uint32_t dk[DMA ? NI : 1], dv[DMA ? NI : 1];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int byte = (wave * NI + i) * 1024 + lane * 16;
+      const int row = byte / (2 * D);
+      const int ch = ((byte % (2 * D)) >> 4) ^ swz_f<D>(row);
+      dk[i] = (uint32_t)((row * a.k_sn + ch * 8) * 2);
+      dv[i] = (uint32_t)((row * a.v_sn + ch * 8) * 2);
+    }
+  }
+  auto dma_tile = [&](int j, lds_t* base) {
+    const int64_t k0 = (int64_t)j * BN;
+    const char* src[4] = {(const char*)K + k0 * a.k_sn * 2, (const char*)V + k0 * a.v_sn * 2,
+                          JVP ? (const char*)TK + k0 * a.k_sn * 2 : nullptr,
+                          JVP ? (const char*)TV + k0 * a.v_sn * 2 : nullptr};
+    const bool full = k0 + BN <= t.Lkv;
+    const int last = t.Lkv - 1 - (int)k0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      uint32_t ok = dk[i], ov = dv[i];
+      if (!full) {  // ragged last tile: rows past the keys re-read the last key (masked)
+        const int byte = (wave * NI + i) * 1024 + lane * 16;
+        int row = byte / (2 * D);
+        const int ch = ((byte % (2 * D)) >> 4) ^ swz_f<D>(row);
+        row = row < last ? row : last;
+        ok = (uint32_t)((row * a.k_sn + ch * 8) * 2);
+        ov = (uint32_t)((row * a.v_sn + ch * 8) * 2);
+      }
+      lds_t* dst = base + (wave * NI + i) * 1024;
+#pragma unroll
+      for (int x = 0; x < NTEN; ++x)
+        __builtin_amdgcn_global_load_lds((const void*)(src[x] + ((x & 1) ? ov : ok)),
+                                         (__attribute__((address_space(3))) void*)(dst + x * TILE), 16, 0, 0);
+    }
+  };
+
   f32x16 acc[DB];
   f32x16 accA[JVP ? DB : 1], accB[JVP ? DB : 1];
 #pragma unroll
@@ -346,7 +398,10 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   auto step = [&](int j, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
     const bool more = j + 1 < n_tiles;
-    if (more) load_tile(j + 1);  // in flight while this tile computes
+    if (more) {  // in flight while this tile computes
+      if constexpr (DMA) dma_tile(j + 1, smem + (1 - S) * STAGE);
+      else load_tile(j + 1);
+    }
 
     if (j * BN < wave_max) {  // wave-uniform: skip tiles this wave cannot see
       const lds_t* kt = smem + S * STAGE;
@@ -416,7 +471,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       pv_section<D, NB, JVP>(vt, tvt, vlo, vhi, pf, hf, acc, accA, accB);
     }
 
-    if (more) store_tile(smem + (1 - S) * STAGE);
+    if (!DMA && more) store_tile(smem + (1 - S) * STAGE);
     __syncthreads();
   };
 
@@ -424,8 +479,12 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   // Q-fragment loads have completed, so no wait for the next tile's prefetch
   // is needed inside the loop.
   if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(smem);
+    if constexpr (DMA) {
+      dma_tile(0, smem);
+    } else {
+      load_tile(0);
+      store_tile(smem);
+    }
     __syncthreads();
     int j = 0;
     for (; j + 2 <= n_tiles; j += 2) {

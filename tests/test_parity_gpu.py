@@ -162,7 +162,7 @@ def test_other_scales(gpu_lib, scale, causal):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("N", [1, 15, 999])
+@pytest.mark.parametrize("N", [1, 15, 200, 999])
 @pytest.mark.parametrize("causal", [False, True])
 def test_jvp_sweep(gpu_lib, dtype, D, N, causal):
     jvp_case(1, 2, N, N, D, dtype, causal, seed=N + D)
