@@ -77,7 +77,10 @@ struct KernelChoice {
 };
 
 template <int D, int BN, bool JVP>
-KernelChoice r32() { return {attn_fwd_bf16_kernel<D, BN, JVP>, Bf16Cfg<D, BN, JVP>::BM, BN, Bf16Cfg<D, BN, JVP>::LDS, 256}; }
+KernelChoice r32() {
+  using C = Bf16Cfg<D, BN, JVP>;
+  return {attn_fwd_bf16_kernel<D, BN, JVP>, C::BM, BN, C::LDS, C::THREADS};
+}
 template <int D, bool JVP>
 KernelChoice f32k() { return {attn_fwd_f32_kernel<D, JVP>, F32Cfg<D, JVP>::BM, F32Cfg<D, JVP>::BN, F32Cfg<D, JVP>::LDS, 256}; }
 

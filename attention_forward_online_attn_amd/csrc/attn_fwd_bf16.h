@@ -197,24 +197,30 @@ __device__ __forceinline__ void pv_section(const lds_t* vt, const lds_t* tvt, co
 
 template <int D, int BN, bool JVP>
 struct Bf16Cfg {
-  static constexpr int BM = 128;            // query rows per workgroup (4 waves x 32)
+  static constexpr int NW = 4;              // waves per workgroup (32 query rows each)
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BM = 32 * NW;        // query rows per workgroup
   static constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
   static constexpr int TILE = BN * D * 2;   // bytes of one K (or V, tK, tV) tile
   static constexpr int NTEN = JVP ? 4 : 2;  // tensors streamed per key tile
   static constexpr int STAGE = NTEN * TILE; // bytes of one pipeline stage
-  static constexpr int LDS = 2 * STAGE;     // double buffered
-  static constexpr int LOADS = BN * CPR / 256;
+  static constexpr bool DMA = !(JVP && D == 128);  // direct global -> LDS tile loads
+  // LDS stages: three (the newest fetch stays in flight across a barrier)
+  // where two workgroups per CU still fit in LDS, i.e. for D = 64.
+  static constexpr int STAGES = (DMA && D == 64) ? 3 : 2;
+  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int LOADS = (BN * CPR + THREADS - 1) / THREADS;
   static constexpr int WAVES_PER_EU = (JVP && D == 128) ? 1 : 2;
-  static_assert((BN * CPR) % 256 == 0, "tile must split evenly over 256 threads");
+  static_assert((BN * CPR) % THREADS == 0 || BN * CPR < THREADS, "tile must split evenly over the workgroup");
   static_assert(BN % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
 };
 
 template <int D, int BN, bool JVP>
-__global__ void __launch_bounds__(256, (Bf16Cfg<D, BN, JVP>::WAVES_PER_EU))
+__global__ void __launch_bounds__((Bf16Cfg<D, BN, JVP>::THREADS), (Bf16Cfg<D, BN, JVP>::WAVES_PER_EU))
 attn_fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BN, JVP>;
   constexpr int BM = C::BM, CPR = C::CPR, TILE = C::TILE, NTEN = C::NTEN, STAGE = C::STAGE;
-  constexpr int LOADS = C::LOADS;
+  constexpr int LOADS = C::LOADS, THREADS = C::THREADS, NW = C::NW;
   constexpr int NB = BN / 32;  // 32-key blocks per tile
   constexpr int KD = D / 16;   // MFMA steps over the head dim
   constexpr int DB = D / 32;   // 32-column output blocks
@@ -236,7 +242,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 
   // ---- row bookkeeping (lane % 32 is this lane's query row)
   const int row0 = t.qt * BM;
-  const int my_row = row0 + wave * 32 + n32;
+  const int my_row = row0 + wave * 32 + n32;  // (NW waves x 32 rows)
   const int my_lim = kv_limit(t, a.causal, my_row < t.Lstore ? my_row : t.Lstore - 1);
   const int w0 = row0 + wave * 32;
   const int w1 = min(w0 + 31, t.Lstore - 1);
@@ -272,14 +278,16 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   int lds_off[LOADS];
 #pragma unroll
   for (int it = 0; it < LOADS; ++it) {
-    const int id = tid + 256 * it;
+    const int id = tid + THREADS * it;
     const int row = id / CPR, ch = id % CPR;
     goff_k[it] = (uint32_t)((row * a.k_sn + ch * 8) * 2);
     goff_v[it] = (uint32_t)((row * a.v_sn + ch * 8) * 2);
     lds_off[it] = swz_off<D>(row, ch);
   }
+  const bool stager = BN * CPR >= THREADS || tid < BN * CPR;  // threads that move tile chunks
   u32x4 stg[NTEN][LOADS];
   auto load_tile = [&](int j) {
+    if (!stager) return;
     const int64_t k0 = (int64_t)j * BN;
     const char* kb = (const char*)K + k0 * a.k_sn * 2;
     const char* vb = (const char*)V + k0 * a.v_sn * 2;
@@ -299,7 +307,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       const int last = t.Lkv - 1 - (int)k0;  // last valid row of this tile
 #pragma unroll
       for (int it = 0; it < LOADS; ++it) {
-        const int id = tid + 256 * it;
+        const int id = tid + THREADS * it;
         int row = id / CPR;
         row = row < last ? row : last;
         const int ch = id % CPR;
@@ -315,6 +323,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     }
   };
   auto store_tile = [&](lds_t* base) {
+    if (!stager) return;
 #pragma unroll
     for (int it = 0; it < LOADS; ++it)
 #pragma unroll
@@ -329,9 +338,12 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   // The D=128 JVP instance (1 wave per SIMD, which spills) keeps register
   // staging: with DMA it produced wrong scores on ragged last tiles in the
   // parity suite, a cause not isolated.
-  constexpr bool DMA = !(JVP && D == 128);
-  constexpr int NI = TILE / 1024 / 4;  // DMA instructions per wave per tensor
-  static_assert(!DMA || TILE % 4096 == 0, "DMA tiles are whole 1 KiB blocks per wave");
+  constexpr bool DMA = C::DMA;
+  constexpr int STAGES = C::STAGES;
+  constexpr int NBLK = TILE / 1024;                    // 1 KiB blocks per tile
+  constexpr int NI = NBLK >= NW ? NBLK / NW : 1;       // DMA instructions per wave per tensor
+  static_assert(!DMA || NBLK % NW == 0 || NBLK < NW, "DMA tiles are whole 1 KiB blocks per wave");
+  const bool dma_wave = NBLK >= NW || wave < NBLK;    // waves past the tile's blocks fetch nothing
   uint32_t dk[DMA ? NI : 1], dv[DMA ? NI : 1];
   if constexpr (DMA) {
 #pragma unroll
@@ -344,6 +356,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     }
   }
   auto dma_tile = [&](int j, lds_t* base) {
+    if (!dma_wave) return;
     const int64_t k0 = (int64_t)j * BN;
     const char* src[4] = {(const char*)K + k0 * a.k_sn * 2, (const char*)V + k0 * a.v_sn * 2,
                           JVP ? (const char*)TK + k0 * a.k_sn * 2 : nullptr,
@@ -391,15 +404,29 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) v_frag_offsets<D>(lane, db, vlo[db], vhi[db]);
 
-  // One key tile: prefetch tile j+1 into registers, compute on LDS stage S,
-  // store the prefetched tile into the other stage, barrier.  S is a
-  // compile-time constant so every LDS address is a hoisted register plus an
-  // immediate offset.
+  // DMA instructions this wave has in flight per tile (vmcnt units)
+  constexpr int NPT = DMA ? NTEN * NI : 0;
+  auto wait_vm = [&](bool keep_one_tile) {  // and all LDS reads done (stage reuse)
+    if (keep_one_tile) __builtin_amdgcn_s_waitcnt((NPT & 15) | ((NPT >> 4) << 14) | (7 << 4));
+    else __builtin_amdgcn_s_waitcnt(7 << 4);
+  };
+  auto block_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One key tile on LDS stage S = j % STAGES: fetch tile j + STAGES - 1 into
+  // the stage freed by the previous tile, compute, then make tile j + 1
+  // complete and visible (with three stages the newest fetch stays in flight
+  // across the barrier).  S is a compile-time constant so every LDS address
+  // is a hoisted register plus an immediate offset.
   auto step = [&](int j, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
-    const bool more = j + 1 < n_tiles;
-    if (more) {  // in flight while this tile computes
-      if constexpr (DMA) dma_tile(j + 1, smem + (1 - S) * STAGE);
+    constexpr int SN = (S + STAGES - 1) % STAGES;
+    const bool ahead = j + STAGES - 1 < n_tiles;
+    if (ahead) {  // in flight while this tile computes
+      if constexpr (DMA) dma_tile(j + STAGES - 1, smem + SN * STAGE);
       else load_tile(j + 1);
     }
 
@@ -471,8 +498,13 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       pv_section<D, NB, JVP>(vt, tvt, vlo, vhi, pf, hf, acc, accA, accB);
     }
 
-    if (!DMA && more) store_tile(smem + (1 - S) * STAGE);
-    __syncthreads();
+    if constexpr (STAGES == 2) {
+      if (!DMA && ahead) store_tile(smem + SN * STAGE);
+      __syncthreads();
+    } else {
+      wait_vm(ahead);
+      block_barrier();
+    }
   };
 
   // The loop sits inside the prologue's branch: on every path into it the
@@ -481,17 +513,25 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   if (n_tiles > 0) {
     if constexpr (DMA) {
       dma_tile(0, smem);
+      if (STAGES == 3 && n_tiles > 1) dma_tile(1, smem + STAGE);
     } else {
       load_tile(0);
       store_tile(smem);
     }
-    __syncthreads();
+    if constexpr (STAGES == 2) {
+      __syncthreads();
+    } else {
+      wait_vm(n_tiles > 1);
+      block_barrier();
+    }
     int j = 0;
-    for (; j + 2 <= n_tiles; j += 2) {
+    for (; j + STAGES <= n_tiles; j += STAGES) {
       step(j, std::integral_constant<int, 0>{});
       step(j + 1, std::integral_constant<int, 1>{});
+      if constexpr (STAGES == 3) step(j + 2, std::integral_constant<int, 2 % STAGES>{});
     }
     if (j < n_tiles) step(j, std::integral_constant<int, 0>{});
+    if (STAGES == 3 && j + 1 < n_tiles) step(j + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln2, tO = (accA + accB - r O) / l
