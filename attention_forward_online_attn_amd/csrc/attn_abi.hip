@@ -5,6 +5,7 @@
 // synchronises its stream and reports kernel errors as ATTN_ERR_HIP.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -76,16 +77,41 @@ struct KernelChoice {
   int threads;  // workgroup size
 };
 
-template <int D, int BN, bool JVP>
+template <int D, int BN, bool JVP, int NW = 4>
 KernelChoice r32() {
-  using C = Bf16Cfg<D, BN, JVP>;
-  return {attn_fwd_bf16_kernel<D, BN, JVP>, C::BM, BN, C::LDS, C::THREADS};
+  using C = Bf16Cfg<D, BN, JVP, NW>;
+  return {attn_fwd_bf16_kernel<D, BN, JVP, NW>, C::BM, BN, C::LDS, C::THREADS};
 }
 template <int D, bool JVP>
 KernelChoice f32k() { return {attn_fwd_f32_kernel<D, JVP>, F32Cfg<D, JVP>::BM, F32Cfg<D, JVP>::BN, F32Cfg<D, JVP>::LDS, 256}; }
 
-KernelChoice choose(int dtype, int D, bool jvp) {
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Dense causal work is paired (an 8-wave workgroup takes q-tiles p and
+// n-1-p) when the unpaired grid is small -- at most four workgroups per CU,
+// where the heaviest q-tiles would otherwise set the finish time; larger
+// grids balance well enough by heaviest-first dispatch and keep 4-wave
+// workgroups.  The D=128 JVP instance runs one wave per SIMD and is never
+// paired.
+bool use_pairs(int dtype, int D, bool jvp, bool dense_causal, int64_t unpaired_grid) {
+  return dtype == ATTN_BF16 && dense_causal && !(jvp && D == 128) && unpaired_grid <= 4 * (int64_t)cu_count();
+}
+
+KernelChoice choose(int dtype, int D, bool jvp, bool paired) {
   if (dtype == ATTN_BF16) {
+    if (paired) return !jvp ? (D == 64 ? r32<64, kBnDense, false, 8>() : r32<128, kBnDense, false, 8>())
+                            : r32<64, kBnJvp, true, 8>();
     if (!jvp) return D == 64 ? r32<64, kBnDense, false>() : r32<128, kBnDense, false>();
     return D == 64 ? r32<64, kBnJvp, true>() : r32<128, kBnJvp, true>();
   }
@@ -121,10 +147,12 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return ATTN_ERR_UNSUPPORTED;
 
-  const KernelChoice kc = choose(dtype, (int)D, jvp);
+  const int64_t n_qtiles = (Nq + 127) / 128;  // every bf16 instance uses 128-row q-tiles
+  const bool paired = use_pairs(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
+  const KernelChoice kc = choose(dtype, (int)D, jvp, paired);
   const int BM = kc.BM;
-  const int64_t n_qtiles = (Nq + BM - 1) / BM;
-  const int64_t grid = B * H * n_qtiles;
+  const int64_t n_qtiles_k = (Nq + BM - 1) / BM;
+  const int64_t grid = B * H * (paired ? (n_qtiles_k + 1) / 2 : n_qtiles_k);
   if (grid > INT_MAX) return ATTN_ERR_INVALID;
 
   FwdArgs a = {};
@@ -134,7 +162,8 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   a.v_sb = sv.b; a.v_sh = sv.h; a.v_sn = sv.n;
   a.o_sb = so.b; a.o_sh = so.h; a.o_sn = so.n;
   a.B = (int)B; a.H = (int)H; a.Nq = (int)Nq; a.Nkv = (int)Nkv;
-  a.n_qtiles = (int)n_qtiles;
+  a.n_qtiles = (int)n_qtiles_k;
+  a.paired = paired ? 1 : 0;
   a.sm_scale = sm_scale;
   a.c = sm_scale * kLog2e;
   if (a.c == 0.f) a.c = 1.17549435e-38f;  // sm_scale == 0: keep exp2 arguments exactly 0 and -inf masks -inf
@@ -199,7 +228,7 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   const void* ptrs[] = {q, k, v, o};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
-  const KernelChoice kc = choose((int)dtype, (int)D, false);
+  const KernelChoice kc = choose((int)dtype, (int)D, false, false);
   const int BM = kc.BM;
   const int64_t cap = plan_capacity(num_seqs, total_len, BM);
   if (!workspace || workspace_bytes < (size_t)(16 + 8 * cap) || ((uintptr_t)workspace & 15u)) return ATTN_ERR_WORKSPACE;

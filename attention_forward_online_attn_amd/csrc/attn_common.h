@@ -40,6 +40,7 @@ struct FwdArgs {
   int64_t o_sb, o_sh, o_sn;
   int32_t B, H, Nq, Nkv;
   int32_t n_qtiles;  // dense: number of query tiles per (batch, head)
+  int32_t paired;    // dense causal: one workgroup takes q-tiles p and n_qtiles-1-p
   float c;           // sm_scale * log2(e): scores go to the exp2 domain
   float sm_scale;
   int32_t causal;
@@ -55,6 +56,7 @@ struct Tile {
   int64_t q_off, k_off, v_off, o_off;  // element offset of row 0 of this (batch|seq, head)
   int64_t lse_off;                     // element offset of row 0 in the fp32 LSE buffer
   int qt;                              // query tile index
+  int qt2;                             // second query tile of a paired workgroup, or -1
   int Lstore;                          // rows [0, Lstore) exist and are written
   int Lattend;                         // rows [0, Lattend) attend keys; later rows attend none
   int Lkv;                             // keys [0, Lkv)
@@ -64,19 +66,29 @@ struct Tile {
 // Workgroup -> tile.  Dense: the hardware hands workgroup i to XCD i % 8, so
 // each XCD is given a contiguous run of the (batch, head)-major work list:
 // the query tiles of a head then run on one XCD and share its L2 copy of
-// that head's K and V.  Causal tiles run heaviest first within a head.
+// that head's K and V.  Causal: with pairing, workgroup p of a head takes
+// query tiles p and n-1-p (equal work for every workgroup; the shorter key
+// range is a prefix of the longer one, so both share the K/V tiles);
+// without it, tiles run heaviest first within a head.
 // Jagged: the device-built plan lists (sequence, query tile) items, most
 // key tiles first; the head is the fastest index.
 template <int BM>
 __device__ __forceinline__ Tile resolve_tile(const FwdArgs& a, int bid) {
   Tile t;
+  t.qt2 = -1;
   if (a.offsets == nullptr) {
-    const int total = a.B * a.H * a.n_qtiles;
+    const int per_head = a.paired ? (a.n_qtiles + 1) >> 1 : a.n_qtiles;
+    const int total = a.B * a.H * per_head;
     int logical = bid;
     if ((total & 7) == 0) logical = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int bh = logical / a.n_qtiles;
-    int qt = logical - bh * a.n_qtiles;
-    if (a.causal) qt = a.n_qtiles - 1 - qt;
+    const int bh = logical / per_head;
+    int qt = logical - bh * per_head;
+    if (a.paired) {
+      const int other = a.n_qtiles - 1 - qt;
+      t.qt2 = other != qt ? other : -1;
+    } else if (a.causal) {
+      qt = a.n_qtiles - 1 - qt;
+    }
     const int b = bh / a.H, h = bh - b * a.H;
     t.q_off = b * a.q_sb + h * a.q_sh;
     t.k_off = b * a.k_sb + h * a.k_sh;

@@ -195,11 +195,11 @@ __device__ __forceinline__ void pv_section(const lds_t* vt, const lds_t* tvt, co
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <int D, int BN, bool JVP>
+template <int D, int BN, bool JVP, int NW_ = 4>
 struct Bf16Cfg {
-  static constexpr int NW = 4;              // waves per workgroup (32 query rows each)
+  static constexpr int NW = NW_;            // waves per workgroup (32 query rows each)
   static constexpr int THREADS = 64 * NW;
-  static constexpr int BM = 32 * NW;        // query rows per workgroup
+  static constexpr int BM = 128;            // query rows per q-tile (4 waves); 8 waves take two q-tiles
   static constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
   static constexpr int TILE = BN * D * 2;   // bytes of one K (or V, tK, tV) tile
   static constexpr int NTEN = JVP ? 4 : 2;  // tensors streamed per key tile
@@ -215,10 +215,10 @@ struct Bf16Cfg {
   static_assert(BN % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
 };
 
-template <int D, int BN, bool JVP>
-__global__ void __launch_bounds__((Bf16Cfg<D, BN, JVP>::THREADS), (Bf16Cfg<D, BN, JVP>::WAVES_PER_EU))
+template <int D, int BN, bool JVP, int NW_ = 4>
+__global__ void __launch_bounds__((Bf16Cfg<D, BN, JVP, NW_>::THREADS), (Bf16Cfg<D, BN, JVP, NW_>::WAVES_PER_EU))
 attn_fwd_bf16_kernel(FwdArgs a) {
-  using C = Bf16Cfg<D, BN, JVP>;
+  using C = Bf16Cfg<D, BN, JVP, NW_>;
   constexpr int BM = C::BM, CPR = C::CPR, TILE = C::TILE, NTEN = C::NTEN, STAGE = C::STAGE;
   constexpr int LOADS = C::LOADS, THREADS = C::THREADS, NW = C::NW;
   constexpr int NB = BN / 32;  // 32-key blocks per tile
@@ -241,18 +241,22 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   const bf16* TV = JVP ? (const bf16*)a.tv + t.v_off : nullptr;
 
   // ---- row bookkeeping (lane % 32 is this lane's query row)
-  const int row0 = t.qt * BM;
-  const int my_row = row0 + wave * 32 + n32;  // (NW waves x 32 rows)
+  // waves 0-3 take q-tile t.qt; with 8 waves, waves 4-7 take q-tile t.qt2
+  // (none when it is -1: those waves only help stage K/V)
+  const int my_qt = (NW == 8 && wave >= 4) ? t.qt2 : t.qt;
+  const int row0 = my_qt * BM;
+  const int w0 = my_qt < 0 ? t.Lstore : row0 + (wave & 3) * 32;
+  const int my_row = w0 + n32;
   const int my_lim = kv_limit(t, a.causal, my_row < t.Lstore ? my_row : t.Lstore - 1);
-  const int w0 = row0 + wave * 32;
   const int w1 = min(w0 + 31, t.Lstore - 1);
   int wave_max = 0, wave_min = 0;  // max / min key limit over the wave's rows
   if (w0 <= w1) {
     wave_max = w0 < t.Lattend ? kv_limit(t, a.causal, min(w1, t.Lattend - 1)) : 0;
     wave_min = w1 >= t.Lattend ? 0 : kv_limit(t, a.causal, w0);
   }
-  const int b1 = min(row0 + BM, t.Lattend) - 1;
-  const int blk_max = row0 <= b1 ? kv_limit(t, a.causal, b1) : 0;
+  const int last_qt = t.qt2 > t.qt ? t.qt2 : t.qt;  // the workgroup's later q-tile
+  const int b1 = min(last_qt * BM + BM, t.Lattend) - 1;
+  const int blk_max = last_qt * BM <= b1 ? kv_limit(t, a.causal, b1) : 0;
   const int n_tiles = (blk_max + BN - 1) / BN;
 
   // ---- Q (and tQ) fragments, resident for the whole key loop: the B operand
