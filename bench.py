@@ -237,7 +237,7 @@ def main():
         "jvp_value": extra["jvp"]["tflops"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128,64,false>",
+                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128,64,false,4>",
                      "avg_launch_ms": round(avg, 4), "min_launch_ms": round(mn, 4)},
         "extra": extra,
     }
