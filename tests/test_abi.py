@@ -110,3 +110,12 @@ def test_jagged_validation(lib):
     assert call(D=48) == UNSUPPORTED
     assert lib.jagged_attn_fwd(BF16, 0, st, 0, st, 0, st, 0, st, 0, 0, 0, H, 0, D, 64,
                                0.125, 0, 0, 0, None) == OK
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(attn.AttnError):
+        attn.fwd(x, x, x)
+    with pytest.raises(attn.AttnError):
+        attn.fwd(x.float(), x, x)

@@ -243,3 +243,65 @@ def test_jagged_unscaled_logits(gpu_lib):
     o, lse = attn.jagged_fwd(*cuda(q, k, v, off), max_seq_len=512, sm_scale=1.0)
     ro, rl = oracle.jagged_attention(q, k, v, off.numpy(), 512, 1.0)
     assert_close(BF16, host64(o), host64(lse), ro, rl, label="jagged sm_scale=1")
+
+
+def test_jagged_repeatable_and_workspace_independent(gpu_lib):
+    """The tile plan is built with atomics, so the order of work items varies;
+    every item is computed alone, so results must be bitwise identical, and the
+    workspace's previous contents must not matter."""
+    w = wl.WORKLOADS["jagged_d128"]
+    lengths = wl.jagged_lengths(64, w.max_len, 3)
+    q, k, v, off = cuda(*wl.jagged_inputs(lengths, w.H, w.D, "bf16", 3))
+    need = attn.jagged_workspace_bytes(64, q.shape[1])
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)
+    o1, l1 = attn.jagged_fwd(q, k, v, off, w.max_len, workspace=ws)
+    ws.fill_(0x5A)
+    o2, l2 = attn.jagged_fwd(q, k, v, off, w.max_len, workspace=ws)
+    o3, l3 = attn.jagged_fwd(q, k, v, off, w.max_len)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_jagged_many_short_sequences(gpu_lib, D):
+    """Thousands of short sequences (the plan kernel loops over them in
+    strides of its workgroup), including empty ones.  Rows with few keys put
+    |O| near max|v|, where the bf16 rounding of P and of O itself count most;
+    lengths run past the 32-key bound of the kernel's split-P pass."""
+    g = torch.Generator().manual_seed(11)
+    lengths = torch.randint(0, 65, (3000,), generator=g)
+    jagged_case(lengths, 2, D, "bf16", 48, seed=11,
+                label=f"jagged 3000 sequences of 0..64 rows, max_seq_len 48, D={D}")
+
+
+@pytest.mark.parametrize("jvp", [False, True])
+def test_causal_short_rows_many_heads(gpu_lib, jvp):
+    """Causal attention over 64 positions and many heads: every row attends
+    1..64 keys, so the first rows follow one or two keys closely."""
+    if jvp:
+        jvp_case(16, 16, 64, 64, 64, "bf16", True, seed=21)
+    else:
+        dense_case(16, 16, 64, 64, 128, "bf16", True, seed=21)
+
+
+def test_jagged_strided_layout(gpu_lib):
+    """Values stored [total_len, H, D] and viewed as [H, total_len, D]."""
+    lengths = torch.tensor([100, 37, 260])
+    T, H, D = int(lengths.sum()), 3, 128
+    g = torch.Generator().manual_seed(12)
+    base = [torch.randn(T, H, D, generator=g).bfloat16() for _ in range(3)]
+    q, k, v = (x.permute(1, 0, 2) for x in base)  # [H, T, D] views, row stride H*D
+    off = wl.offsets_from_lengths(lengths)
+    dev = [x.cuda().permute(1, 0, 2) for x in base]
+    assert not dev[0].is_contiguous()
+    o, lse = attn.jagged_fwd(*dev, off.cuda(), max_seq_len=512)
+    ro, rl = oracle.jagged_attention(q, k, v, off.numpy(), 512, oracle.scale_as_passed(D ** -0.5))
+    assert_close(BF16, host64(o), host64(lse), ro, rl, label="jagged [T,H,D] storage")
+
+
+@pytest.mark.parametrize("N", [300, 640])
+def test_causal_pairing_odd_and_even_tile_counts(gpu_lib, N):
+    """Causal grids small enough to be paired: 3 q-tiles (the middle one runs
+    alone) and 5 q-tiles, for the forward and the JVP."""
+    dense_case(2, 3, N, N, 128, "bf16", True, seed=N)
+    jvp_case(2, 3, N, N, 64, "bf16", True, seed=N + 1)
