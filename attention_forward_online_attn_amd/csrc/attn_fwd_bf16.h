@@ -38,6 +38,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "attn_common.h"
 
@@ -118,6 +119,45 @@ __device__ __forceinline__ bf16x8 v_frag(const lds_t* vt, int key0, int lo, int 
   return __builtin_bit_cast(bf16x8, v8);
 }
 
+// Compile-time unrolled loop: f(std::integral_constant<int, i>) for i < N,
+// so that i can feed immediate operands of inline assembly.
+template <int... Is, class F>
+__device__ __forceinline__ void static_for_seq(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(std::make_integer_sequence<int, N>{}, f);
+}
+
+// V^T fragment read for the main PV product, as inline assembly.  The
+// compiler treats the transposing-read builtin as possibly aliasing every
+// global->LDS tile copy in flight and waits for all of them (vmcnt(0)) before
+// it: that would expose the next tile's prefetch on every tile.  The stage
+// read here was completed by the barrier that ended the previous tile, so no
+// such wait is needed.  The compiler does not count these reads, so the
+// caller waits for them itself (lds_wait) before the fragment is used; a
+// count that also covers reads the compiler issued later only waits longer,
+// since LDS reads complete in order.
+template <int OFF>
+__device__ __forceinline__ bf16x8 v_frag_async(uint32_t lo, uint32_t hi) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset is 16 bits");
+  i16x4 a, b;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(a) : "v"(lo), "i"(OFF));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(b) : "v"(hi), "i"(OFF));
+  const i16x4 v8[2] = {a, b};
+  return __builtin_bit_cast(bf16x8, v8);
+}
+
+// Wait until at most N LDS reads of this wave are outstanding; the fragments
+// passed are read-modify-write operands, so their uses stay after the wait.
+template <int N, int F>
+__device__ __forceinline__ void lds_wait(bf16x8 (&f)[F]) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+  if constexpr (F == 1) asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f[0]) : "n"(N));
+  else asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(f[0]), "+v"(f[1]) : "n"(N));
+}
+
 // ---- MFMA sections with software-pipelined LDS fragment reads.
 //
 // A section is a fixed list of MFMA steps, each fed by fragments read from
@@ -169,27 +209,35 @@ __device__ __forceinline__ void scores_section(const lds_t* kt, const lds_t* tkt
 }
 
 // O^T += V^T P^T for one tile (JVP: accB += V^T H^T, accA += tV^T P^T).
-// Step i is output block i / (2 NB), key chunk i % (2 NB).
-template <int D, int NB, bool JVP>
-__device__ __forceinline__ void pv_section(const lds_t* vt, const lds_t* tvt, const int (&vlo)[D / 32],
-                                           const int (&vhi)[D / 32],
+// Step i is output block i / (2 NB), key chunk i % (2 NB).  V^T (tV^T) sits
+// at byte VOFF (TVOFF) of LDS; lds_base is the LDS address of byte 0 and
+// vlo/vhi the lane's fragment offsets.
+template <int D, int NB, bool JVP, int VOFF, int TVOFF>
+__device__ __forceinline__ void pv_section(uint32_t lds_base, const int (&vlo)[D / 32], const int (&vhi)[D / 32],
                                            const bf16x8 (&pf)[NB][2], const bf16x8 (&hf)[JVP ? NB : 1][2],
                                            f32x16 (&acc)[D / 32], f32x16 (&accA)[JVP ? D / 32 : 1],
                                            f32x16 (&accB)[JVP ? D / 32 : 1]) {
   constexpr int DB = D / 32, KC = 2 * NB, N = DB * KC, R = kFragDist + 1, F = JVP ? 2 : 1;
+  constexpr int RPF = 2 * F;  // LDS reads per issued step
   bf16x8 ring[R][F];
-  auto issue = [&](int i, bf16x8 (&f)[F]) {
-    const int db = i / KC, key0 = 16 * (i % KC);
-    f[0] = v_frag<D>(vt, key0, vlo[db], vhi[db]);
-    if constexpr (JVP) f[F - 1] = v_frag<D>(tvt, key0, vlo[db], vhi[db]);
+  auto issue = [&](auto i_tag) {
+    constexpr int i = decltype(i_tag)::value;
+    if constexpr (i < N) {
+      constexpr int db = i / KC, key0 = 16 * (i % KC);
+      const uint32_t lo = lds_base + vlo[db], hi = lds_base + vhi[db];
+      ring[i % R][0] = v_frag_async<VOFF + key0 * D * 2>(lo, hi);
+      if constexpr (JVP) ring[i % R][F - 1] = v_frag_async<TVOFF + key0 * D * 2>(lo, hi);
+    }
   };
   __builtin_amdgcn_s_setprio(kMfmaPrio);
-#pragma unroll
-  for (int i = 0; i < kFragDist && i < N; ++i) issue(i, ring[i % R]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i + kFragDist < N) issue(i + kFragDist, ring[(i + kFragDist) % R]);
-    const int db = i / KC, c = i % KC;
+  static_for<kFragDist>(issue);
+  static_for<N>([&](auto i_tag) {
+    constexpr int i = decltype(i_tag)::value;
+    issue(std::integral_constant<int, i + kFragDist>{});
+    // reads issued after step i's own: those of steps i+1 .. min(i+kFragDist, N-1)
+    constexpr int later = RPF * ((N - 1 - i) < kFragDist ? (N - 1 - i) : kFragDist);
+    lds_wait<(later < 15 ? later : 15), F>(ring[i % R]);
+    constexpr int db = i / KC, c = i % KC;
     const bf16x8* f = ring[i % R];
     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], pf[c >> 1][c & 1], acc[db], 0, 0, 0);
     if constexpr (JVP) {
@@ -197,7 +245,7 @@ __device__ __forceinline__ void pv_section(const lds_t* vt, const lds_t* tvt, co
       accA[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[F - 1], pf[c >> 1][c & 1], accA[db], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-  }
+  });
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -246,6 +294,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int DB = D / 32;   // 32-column output blocks
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   lds_t* smem = (lds_t*)smem_raw;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
 
   const Tile t = resolve_tile<BM>(a, blockIdx.x);
   if (!t.valid) return;
@@ -458,7 +507,6 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       const lds_t* kt = smem + S * STAGE;
       const lds_t* vt = kt + TILE;
       const lds_t* tkt = kt + 2 * TILE;
-      const lds_t* tvt = kt + 3 * TILE;
 
       // S^T = K Q^T (and the tangent scores tQ K^T + Q tK^T)
       f32x16 s[NB];
@@ -541,7 +589,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         }
 
       // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
-      pv_section<D, NB, JVP>(vt, tvt, vlo, vhi, pf, hf, acc, accA, accB);
+      pv_section<D, NB, JVP, S * STAGE + TILE, S * STAGE + 3 * TILE>(lds_base, vlo, vhi, pf, hf, acc, accA, accB);
     }
 
     if constexpr (STAGES == 2) {
