@@ -171,19 +171,35 @@ constexpr int kFragDist = 4;
 // SIMD the one feeding the matrix core is issued first.
 constexpr int kMfmaPrio = 1;
 
+// K fragment read (16 bytes per lane) as inline assembly at a register
+// address plus an immediate offset; the caller waits for it (lds_wait).
+template <int OFF>
+__device__ __forceinline__ bf16x8 k_frag_async(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset is 16 bits");
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
 // S^T = K Q^T for one [NB*32]-key tile (JVP: plus tS^T = tK Q^T + K tQ^T).
-// Step i is key block i / KD, head-dim step i % KD.
-template <int D, int NB, bool JVP>
-__device__ __forceinline__ void scores_section(const lds_t* kt, const lds_t* tkt, const int (&koff)[D / 16],
-                                               const bf16x8 (&qf)[D / 16],
+// Step i is key block i / KD, head-dim step i % KD.  K (tK) sits at byte KOFF
+// (TKOFF) of LDS; kaddr[kk] is the lane's LDS address of its fragment for
+// head-dim step kk in block 0 of a tile at byte 0.  The reads are inline
+// assembly for the same reason as the V^T reads (they would otherwise be
+// re-addressed every tile), with the same explicit waits.
+template <int D, int NB, bool JVP, int KOFF, int TKOFF>
+__device__ __forceinline__ void scores_section(const uint32_t (&kaddr)[D / 16], const bf16x8 (&qf)[D / 16],
                                                const bf16x8 (&tqf)[JVP ? D / 16 : 1], f32x16 (&s)[NB],
                                                f32x16 (&ts)[JVP ? NB : 1]) {
   constexpr int KD = D / 16, N = NB * KD, R = kFragDist + 1, F = JVP ? 2 : 1;
   bf16x8 ring[R][F];
-  auto issue = [&](int i, bf16x8 (&f)[F]) {
-    const int off = koff[i % KD] + 32 * (i / KD) * (D * 2);
-    f[0] = *(const __attribute__((address_space(3))) bf16x8*)(kt + off);
-    if constexpr (JVP) f[F - 1] = *(const __attribute__((address_space(3))) bf16x8*)(tkt + off);
+  auto issue = [&](auto i_tag) {
+    constexpr int i = decltype(i_tag)::value;
+    if constexpr (i < N) {
+      constexpr int blk = 32 * (i / KD) * (D * 2);
+      ring[i % R][0] = k_frag_async<KOFF + blk>(kaddr[i % KD]);
+      if constexpr (JVP) ring[i % R][F - 1] = k_frag_async<TKOFF + blk>(kaddr[i % KD]);
+    }
   };
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -191,12 +207,13 @@ __device__ __forceinline__ void scores_section(const lds_t* kt, const lds_t* tkt
     if constexpr (JVP) ts[b] = f32x16{};
   }
   __builtin_amdgcn_s_setprio(kMfmaPrio);
-#pragma unroll
-  for (int i = 0; i < kFragDist && i < N; ++i) issue(i, ring[i % R]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i + kFragDist < N) issue(i + kFragDist, ring[(i + kFragDist) % R]);
-    const int b = i / KD, kk = i % KD;
+  static_for<kFragDist>(issue);
+  static_for<N>([&](auto i_tag) {
+    constexpr int i = decltype(i_tag)::value;
+    issue(std::integral_constant<int, i + kFragDist>{});
+    constexpr int later = F * ((N - 1 - i) < kFragDist ? (N - 1 - i) : kFragDist);
+    lds_wait<(later < 15 ? later : 15), F>(ring[i % R]);
+    constexpr int b = i / KD, kk = i % KD;
     const bf16x8* f = ring[i % R];
     s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], qf[kk], s[b], 0, 0, 0);
     if constexpr (JVP) {
@@ -204,7 +221,7 @@ __device__ __forceinline__ void scores_section(const lds_t* kt, const lds_t* tkt
       ts[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], tqf[kk], ts[b], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-  }
+  });
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -404,10 +421,13 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   };
 
   // Direct global -> LDS tile loads (global_load_lds_dwordx4): instruction i
-  // of this wave fills the 1 KiB block (wave * NI + i) of a tile, lane l the
-  // 16 bytes at l * 16 of it; so lane l fetches the chunk whose swizzled home
-  // is that spot (the swizzle is an XOR, its own inverse).  No registers or
-  // ds_write instructions are spent on staging.
+  // of this wave fills the 1 KiB block NW * i + wave of a tile (RPB rows), lane
+  // l the 16 bytes at l * 16 of it, so lane l fetches the chunk whose swizzled
+  // home is that spot (the swizzle is an XOR, its own inverse).  A wave's
+  // consecutive blocks lie RSTEP rows apart, a multiple of 16, and the
+  // swizzle depends on the row modulo 16 only: one per-lane byte offset
+  // serves every instruction, which adds a uniform i * RSTEP rows.  No
+  // registers or ds_write instructions are spent on staging.
   // The D=128 JVP instance (1 wave per SIMD, which spills) keeps register
   // staging: with DMA it produced wrong scores on ragged last tiles in the
   // parity suite, a cause not isolated.
@@ -415,43 +435,50 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int STAGES = C::STAGES;
   constexpr int NBLK = TILE / 1024;                    // 1 KiB blocks per tile
   constexpr int NI = NBLK >= NW ? NBLK / NW : 1;       // DMA instructions per wave per tensor
+  constexpr int RPB = 1024 / (2 * D);                  // rows per block
+  constexpr int RSTEP = NW * RPB;                      // rows between a wave's blocks
   static_assert(!DMA || NBLK % NW == 0 || NBLK < NW, "DMA tiles are whole 1 KiB blocks per wave");
+  static_assert(!DMA || NI == 1 || RSTEP % 16 == 0, "per-lane swizzle must repeat every RSTEP rows");
   const bool dma_wave = NBLK >= NW || wave < NBLK;    // waves past the tile's blocks fetch nothing
-  uint32_t dk[DMA ? NI : 1], dv[DMA ? NI : 1];
-  if constexpr (DMA) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int byte = (wave * NI + i) * 1024 + lane * 16;
-      const int row = byte / (2 * D);
-      const int ch = ((byte % (2 * D)) >> 4) ^ swz_f<D>(row);
-      dk[i] = (uint32_t)((row * a.k_sn + ch * 8) * 2);
-      dv[i] = (uint32_t)((row * a.v_sn + ch * 8) * 2);
-    }
-  }
+  const int drow = RPB * wave + (lane * 16) / (2 * D);             // row of instruction 0
+  const int dch = (lane % (D / 8)) ^ swz_f<D>(drow);                // source chunk of that row
+  const uint32_t dk0 = (uint32_t)((drow * a.k_sn + dch * 8) * 2);  // byte offsets, instruction 0
+  const uint32_t dv0 = (uint32_t)((drow * a.v_sn + dch * 8) * 2);
   auto dma_tile = [&](int j, lds_t* base) {
     if (!dma_wave) return;
     const int64_t k0 = (int64_t)j * BN;
     const char* src[4] = {(const char*)K + k0 * a.k_sn * 2, (const char*)V + k0 * a.v_sn * 2,
                           JVP ? (const char*)TK + k0 * a.k_sn * 2 : nullptr,
                           JVP ? (const char*)TV + k0 * a.v_sn * 2 : nullptr};
-    const bool full = k0 + BN <= t.Lkv;
-    const int last = t.Lkv - 1 - (int)k0;
+    const int64_t step_b[2] = {(int64_t)RSTEP * a.k_sn * 2, (int64_t)RSTEP * a.v_sn * 2};
+    if (k0 + BN <= t.Lkv) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      uint32_t ok = dk[i], ov = dv[i];
-      if (!full) {  // ragged last tile: rows past the keys re-read the last key (masked)
-        const int byte = (wave * NI + i) * 1024 + lane * 16;
-        int row = byte / (2 * D);
-        const int ch = ((byte % (2 * D)) >> 4) ^ swz_f<D>(row);
-        row = row < last ? row : last;
-        ok = (uint32_t)((row * a.k_sn + ch * 8) * 2);
-        ov = (uint32_t)((row * a.v_sn + ch * 8) * 2);
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int x = 0; x < NTEN; ++x) {
+          // the uniform part of the address stays an SGPR pair (saddr form:
+          // scalar base + 32-bit lane offset); with several instructions per
+          // tensor the compiler would otherwise fold it into per-lane 64-bit
+          // addresses held across the loop
+          const char* b = src[x] + i * step_b[x & 1];
+          if constexpr (NI > 1) asm("" : "+s"(b));
+          __builtin_amdgcn_global_load_lds((const void*)(b + ((x & 1) ? dv0 : dk0)),
+                                           (__attribute__((address_space(3))) void*)(base + (NW * i + wave) * 1024 + x * TILE),
+                                           16, 0, 0);
+        }
+    } else {  // ragged last tile: rows past the keys re-read the last key (masked)
+      const int last = t.Lkv - 1 - (int)k0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = min(drow + RSTEP * i, last);
+        const uint32_t ok = (uint32_t)((row * a.k_sn + dch * 8) * 2);
+        const uint32_t ov = (uint32_t)((row * a.v_sn + dch * 8) * 2);
+#pragma unroll
+        for (int x = 0; x < NTEN; ++x)
+          __builtin_amdgcn_global_load_lds((const void*)(src[x] + ((x & 1) ? ov : ok)),
+                                           (__attribute__((address_space(3))) void*)(base + (NW * i + wave) * 1024 + x * TILE),
+                                           16, 0, 0);
       }
-      lds_t* dst = base + (wave * NI + i) * 1024;
-#pragma unroll
-      for (int x = 0; x < NTEN; ++x)
-        __builtin_amdgcn_global_load_lds((const void*)(src[x] + ((x & 1) ? ov : ok)),
-                                         (__attribute__((address_space(3))) void*)(dst + x * TILE), 16, 0, 0);
     }
   };
 
@@ -470,9 +497,9 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   // positions are added as immediates.  The swizzle depends on the row mod 16,
   // which 32-key blocks do not change.
   const int krow = kperm(n32);
-  int koff[KD];
+  uint32_t kaddr[KD];
 #pragma unroll
-  for (int kk = 0; kk < KD; ++kk) koff[kk] = swz_off<D>(krow, 2 * kk + h32);
+  for (int kk = 0; kk < KD; ++kk) kaddr[kk] = lds_base + swz_off<D>(krow, 2 * kk + h32);
   int vlo[DB], vhi[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) v_frag_offsets<D>(lane, db, vlo[db], vhi[db]);
@@ -504,14 +531,12 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     }
 
     if (j * BN < wave_max) {  // wave-uniform: skip tiles this wave cannot see
-      const lds_t* kt = smem + S * STAGE;
-      const lds_t* vt = kt + TILE;
-      const lds_t* tkt = kt + 2 * TILE;
+      const lds_t* vt = smem + S * STAGE + TILE;  // V tile (the cold residual pass reads it)
 
       // S^T = K Q^T (and the tangent scores tQ K^T + Q tK^T)
       f32x16 s[NB];
       f32x16 ts[JVP ? NB : 1];
-      scores_section<D, NB, JVP>(kt, tkt, koff, qf, tqf, s, ts);
+      scores_section<D, NB, JVP, S * STAGE, S * STAGE + 2 * TILE>(kaddr, qf, tqf, s, ts);
 
       // mask keys past this row's limit (ragged tail, causal diagonal,
       // jagged truncation) -- only on tiles that reach some row's limit
