@@ -290,10 +290,7 @@ struct Bf16Cfg {
   static constexpr int NTEN = JVP ? 4 : 2;  // tensors streamed per key tile
   static constexpr int STAGE = NTEN * TILE; // bytes of one pipeline stage
   static constexpr bool DMA = !(JVP && D == 128);  // direct global -> LDS tile loads
-  // LDS stages: three (the newest fetch stays in flight across a barrier)
-  // where two workgroups per CU still fit in LDS, i.e. for D = 64.
-  static constexpr int STAGES = (DMA && D == 64) ? 3 : 2;
-  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int LDS = 2 * STAGE;     // double-buffered key tiles
   static constexpr int LOADS = (BN * CPR + THREADS - 1) / THREADS;
   static constexpr int WAVES_PER_EU = (JVP && D == 128) ? 1 : 2;
   static_assert((BN * CPR) % THREADS == 0 || BN * CPR < THREADS, "tile must split evenly over the workgroup");
@@ -432,7 +429,6 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   // staging: with DMA it produced wrong scores on ragged last tiles in the
   // parity suite, a cause not isolated.
   constexpr bool DMA = C::DMA;
-  constexpr int STAGES = C::STAGES;
   constexpr int NBLK = TILE / 1024;                    // 1 KiB blocks per tile
   constexpr int NI = NBLK >= NW ? NBLK / NW : 1;       // DMA instructions per wave per tensor
   constexpr int RPB = 1024 / (2 * D);                  // rows per block
@@ -504,29 +500,16 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) v_frag_offsets<D>(lane, db, vlo[db], vhi[db]);
 
-  // DMA instructions this wave has in flight per tile (vmcnt units)
-  constexpr int NPT = DMA ? NTEN * NI : 0;
-  auto wait_vm = [&](bool keep_one_tile) {  // and all LDS reads done (stage reuse)
-    if (keep_one_tile) __builtin_amdgcn_s_waitcnt((NPT & 15) | ((NPT >> 4) << 14) | (7 << 4));
-    else __builtin_amdgcn_s_waitcnt(7 << 4);
-  };
-  auto block_barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // One key tile on LDS stage S = j % STAGES: fetch tile j + STAGES - 1 into
-  // the stage freed by the previous tile, compute, then make tile j + 1
-  // complete and visible (with three stages the newest fetch stays in flight
-  // across the barrier).  S is a compile-time constant so every LDS address
-  // is a hoisted register plus an immediate offset.
+  // One key tile on LDS stage S = j % 2: fetch tile j + 1 into the other
+  // stage (freed by the barrier that ended the previous tile), compute, then
+  // one barrier makes tile j + 1 complete and visible.  S is a compile-time
+  // constant so every LDS address is a hoisted register plus an immediate.
   auto step = [&](int j, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
-    constexpr int SN = (S + STAGES - 1) % STAGES;
-    const bool ahead = j + STAGES - 1 < n_tiles;
+    constexpr int SN = S ^ 1;
+    const bool ahead = j + 1 < n_tiles;
     if (ahead) {  // in flight while this tile computes
-      if constexpr (DMA) dma_tile(j + STAGES - 1, smem + SN * STAGE);
+      if constexpr (DMA) dma_tile(j + 1, smem + SN * STAGE);
       else load_tile(j + 1);
     }
 
@@ -617,13 +600,8 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       pv_section<D, NB, JVP, S * STAGE + TILE, S * STAGE + 3 * TILE>(lds_base, vlo, vhi, pf, hf, acc, accA, accB);
     }
 
-    if constexpr (STAGES == 2) {
-      if (!DMA && ahead) store_tile(smem + SN * STAGE);
-      __syncthreads();
-    } else {
-      wait_vm(ahead);
-      block_barrier();
-    }
+    if (!DMA && ahead) store_tile(smem + SN * STAGE);
+    __syncthreads();
   };
 
   // The loop sits inside the prologue's branch: on every path into it the
@@ -632,25 +610,17 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   if (n_tiles > 0) {
     if constexpr (DMA) {
       dma_tile(0, smem);
-      if (STAGES == 3 && n_tiles > 1) dma_tile(1, smem + STAGE);
     } else {
       load_tile(0);
       store_tile(smem);
     }
-    if constexpr (STAGES == 2) {
-      __syncthreads();
-    } else {
-      wait_vm(n_tiles > 1);
-      block_barrier();
-    }
+    __syncthreads();
     int j = 0;
-    for (; j + STAGES <= n_tiles; j += STAGES) {
+    for (; j + 2 <= n_tiles; j += 2) {
       step(j, std::integral_constant<int, 0>{});
       step(j + 1, std::integral_constant<int, 1>{});
-      if constexpr (STAGES == 3) step(j + 2, std::integral_constant<int, 2 % STAGES>{});
     }
     if (j < n_tiles) step(j, std::integral_constant<int, 0>{});
-    if (STAGES == 3 && j + 1 < n_tiles) step(j + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln2, tO = (accA + accB - r O) / l

@@ -179,8 +179,8 @@ def copy_calibration(torch, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -214,7 +214,7 @@ def main():
     extra = {}
     for name in ("fwd_causal", "jvp", "jvp_causal", "causal_d64", "jagged"):
         c = cases[name]
-        a, m, _ = time_case(torch, c, max(5, args.steps // 2), 3)
+        a, m, _ = time_case(torch, c, max(5, args.steps // 2), 10)
         extra[name] = {"workload": c.desc, "avg_ms": round(a, 4), "tflops": round(c.flops / (a * 1e-3) / 1e12, 2),
                        "frac_of_mfma_peak": round(c.flops / (a * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                        "gbps_compulsory": round(c.bytes / (a * 1e-3) / 1e9, 1)}
