@@ -226,21 +226,23 @@ __device__ __forceinline__ void scores_section(const uint32_t (&kaddr)[D / 16], 
 }
 
 // O^T += V^T P^T for one tile (JVP: accB += V^T H^T, accA += tV^T P^T).
-// Step i is output block i / (2 NB), key chunk i % (2 NB).  V^T (tV^T) sits
-// at byte VOFF (TVOFF) of LDS; lds_base is the LDS address of byte 0 and
-// vlo/vhi the lane's fragment offsets.
-template <int D, int NB, bool JVP, int VOFF, int TVOFF>
+// Step i is key chunk i / DB (16 keys), output block i % DB: the chunks of P
+// are consumed in order, so the caller's softmax for chunk c+1 (inter(i),
+// placed after the MFMAs of step i) runs on the vector ALU while the matrix
+// core works through chunk c.  V^T (tV^T) sits at byte VOFF (TVOFF) of LDS;
+// lds_base is the LDS address of byte 0 and vlo/vhi the lane's offsets.
+template <int D, int NB, bool JVP, int VOFF, int TVOFF, class Inter>
 __device__ __forceinline__ void pv_section(uint32_t lds_base, const int (&vlo)[D / 32], const int (&vhi)[D / 32],
                                            const bf16x8 (&pf)[NB][2], const bf16x8 (&hf)[JVP ? NB : 1][2],
                                            f32x16 (&acc)[D / 32], f32x16 (&accA)[JVP ? D / 32 : 1],
-                                           f32x16 (&accB)[JVP ? D / 32 : 1]) {
+                                           f32x16 (&accB)[JVP ? D / 32 : 1], Inter&& inter) {
   constexpr int DB = D / 32, KC = 2 * NB, N = DB * KC, R = kFragDist + 1, F = JVP ? 2 : 1;
   constexpr int RPF = 2 * F;  // LDS reads per issued step
   bf16x8 ring[R][F];
   auto issue = [&](auto i_tag) {
     constexpr int i = decltype(i_tag)::value;
     if constexpr (i < N) {
-      constexpr int db = i / KC, key0 = 16 * (i % KC);
+      constexpr int db = i % DB, key0 = 16 * (i / DB);
       const uint32_t lo = lds_base + vlo[db], hi = lds_base + vhi[db];
       ring[i % R][0] = v_frag_async<VOFF + key0 * D * 2>(lo, hi);
       if constexpr (JVP) ring[i % R][F - 1] = v_frag_async<TVOFF + key0 * D * 2>(lo, hi);
@@ -254,13 +256,14 @@ __device__ __forceinline__ void pv_section(uint32_t lds_base, const int (&vlo)[D
     // reads issued after step i's own: those of steps i+1 .. min(i+kFragDist, N-1)
     constexpr int later = RPF * ((N - 1 - i) < kFragDist ? (N - 1 - i) : kFragDist);
     lds_wait<(later < 15 ? later : 15), F>(ring[i % R]);
-    constexpr int db = i / KC, c = i % KC;
+    constexpr int db = i % DB, c = i / DB;
     const bf16x8* f = ring[i % R];
     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], pf[c >> 1][c & 1], acc[db], 0, 0, 0);
     if constexpr (JVP) {
       accB[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], hf[c >> 1][c & 1], accB[db], 0, 0, 0);
       accA[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[F - 1], pf[c >> 1][c & 1], accA[db], 0, 0, 0);
     }
+    inter(i_tag);
     __builtin_amdgcn_sched_barrier(0);
   });
   __builtin_amdgcn_s_setprio(0);
@@ -579,25 +582,34 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       }
 
       // p = exp2(s c - m); P (and H = p tS) as bf16 B operands: registers
-      // 8 c16 .. 8 c16 + 7 of block b are keys 32 b + 16 c16 + 8 h32 + 0..7
+      // 8 c16 .. 8 c16 + 7 of block b are keys 32 b + 16 c16 + 8 h32 + 0..7,
+      // i.e. key chunk 2 b + c16 of the PV product.  Chunk 0 is computed
+      // first; chunk c+1 is computed in slices after the MFMAs of chunk c.
       bf16x8 pf[NB][2];
       bf16x8 hf[JVP ? NB : 1][2];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], a.c, -msub));
-          l_run += p;
-          pf[b][r >> 3][r & 7] = (bf16)p;
-          if constexpr (JVP) {
-            const float hv = p * ts[b][r];
-            r_run += hv;
-            hf[b][r >> 3][r & 7] = (bf16)hv;
-          }
+      auto soft = [&](auto e_tag) {  // one element e of this lane's 16 NB scores
+        constexpr int e = decltype(e_tag)::value, b = e / 16, r = e % 16;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], a.c, -msub));
+        l_run += p;
+        pf[b][r >> 3][r & 7] = (bf16)p;
+        if constexpr (JVP) {
+          const float hv = p * ts[b][r];
+          r_run += hv;
+          hf[b][r >> 3][r & 7] = (bf16)hv;
         }
-
+      };
+      constexpr int EPS = 8 / DB;  // elements of the next chunk per PV step
+      static_for<8>(soft);
       // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
-      pv_section<D, NB, JVP, S * STAGE + TILE, S * STAGE + 3 * TILE>(lds_base, vlo, vhi, pf, hf, acc, accA, accB);
+      pv_section<D, NB, JVP, S * STAGE + TILE, S * STAGE + 3 * TILE>(
+          lds_base, vlo, vhi, pf, hf, acc, accA, accB, [&](auto i_tag) {
+            constexpr int i = decltype(i_tag)::value, c = i / DB;
+            if constexpr (c + 1 < 2 * NB) {
+              static_for<EPS>([&](auto k_tag) {
+                soft(std::integral_constant<int, 8 * (c + 1) + (i % DB) * EPS + decltype(k_tag)::value>{});
+              });
+            }
+          });
     }
 
     if (!DMA && ahead) store_tile(smem + SN * STAGE);
