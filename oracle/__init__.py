@@ -31,6 +31,15 @@ those kernels is an exact identity, so the streamed result equals this one):
   [offsets[s], offsets[s+1]); only its first min(len_s, max_seq_len) rows take
   part, as queries and as keys; there is no attention across sequences.
 
+* Backward (the gradient of the forward above for a loss L with dL/dO = dO) --
+  Triton fused attention tutorial with JVP, ``_attn_bwd_preprocess``,
+  ``_attn_bwd_dkdv``, ``_attn_bwd_dq`` (the steps, in that page's order):
+      delta_i = sum_d O_id dO_id                 (preprocess)
+      dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta 1^T)
+      dQ = sm_scale * dS K,  dK = sm_scale * dS^T Q
+  P is the forward's softmax (0 where masked); rows without keys give dQ = 0
+  and contribute nothing to dK, dV.
+
 Readings where the pages are silent or differ (each is also listed in the
 design notes):
 * LSE is the natural log, fp32 on the GPU side (the JVP page stores
@@ -62,6 +71,9 @@ __all__ = [
     "attention_sampled",
     "jagged_attention",
     "jagged_attention_jvp",
+    "attend_rows_bwd",
+    "attention_bwd",
+    "jagged_attention_bwd",
 ]
 
 # Rows of S materialised at a time.  Only bounds memory: every row is still
@@ -257,3 +269,91 @@ def jagged_attention(q, k, v, offsets, max_seq_len, sm_scale, causal=False):
 def jagged_attention_jvp(q, k, v, tq, tk, tv, offsets, max_seq_len, sm_scale, causal=False):
     """Jagged attention with the forward-mode JVP.  Returns (o, to, lse)."""
     return _jagged(q, k, v, offsets, max_seq_len, sm_scale, causal, (tq, tk, tv))
+
+
+def attend_rows_bwd(q, k, v, do, sm_scale, causal=False, row_pos=None, kv_len=None):
+    """Backward of ``attend_rows`` for some query rows of one (batch, head).
+
+    q: [M, D], k: [N, D], v: [N, Dv], do: [M, Dv] (the gradient of the loss
+    with respect to those rows of O).  row_pos / kv_len as in attend_rows.
+    Returns (dq [M, D], dk [N, D], dv [N, Dv]); dk and dv collect the
+    contributions of the given rows only.
+    """
+    q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    M, N = q.shape[0], k.shape[0]
+    scale = float(sm_scale)
+    if row_pos is None:
+        row_pos = np.arange(M)
+    row_pos = np.asarray(row_pos, dtype=np.int64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if N == 0 or M == 0:
+        return dq, dk, dv
+
+    cols = np.arange(N)
+    for r0 in range(0, M, _ROW_BLOCK):
+        r1 = min(M, r0 + _ROW_BLOCK)
+        # forward of these rows: S, the mask and P = softmax(S)
+        s = scale * (q[r0:r1] @ k.T)
+        allowed = np.ones_like(s, dtype=bool)
+        if causal:  # key j is seen by query i only for i >= j
+            allowed &= row_pos[r0:r1, None] >= cols[None, :]
+        if kv_len is not None:
+            allowed &= cols[None, :] < np.asarray(kv_len)[r0:r1, None]
+        s = np.where(allowed, s, -np.inf)
+        has_key = allowed.any(axis=1)
+        m = np.where(has_key, s.max(axis=1, initial=-np.inf), 0.0)
+        e = np.where(allowed, np.exp(s - m[:, None]), 0.0)
+        denom = np.where(has_key, e.sum(axis=1), 1.0)
+        p = e / denom[:, None]
+        o = p @ v
+        g = do[r0:r1]
+        # preprocess: delta_i = sum_d O_id dO_id
+        delta = (o * g).sum(axis=1)
+        # dV = P^T dO; dP = dO V^T; dS = P (dP - delta); dQ, dK through S = scale Q K^T
+        dv += p.T @ g
+        dp = g @ v.T
+        ds = p * (dp - delta[:, None])
+        dq[r0:r1] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[r0:r1])
+    return dq, dk, dv
+
+
+def attention_bwd(q, k, v, do, sm_scale, causal=False):
+    """Dense attention backward.  q: [B,H,Nq,D], k/v: [B,H,Nkv,D], do: [B,H,Nq,Dv].
+    Returns (dq, dk, dv) in float64, shaped like q, k, v."""
+    q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    _check_dense(q, k, v, causal)
+    B, H = q.shape[:2]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = attend_rows_bwd(q[b, h], k[b, h], v[b, h], do[b, h], sm_scale, causal)
+    return dq, dk, dv
+
+
+def jagged_attention_bwd(q, k, v, do, offsets, max_seq_len, sm_scale, causal=False):
+    """Jagged attention backward.  q/k/v/do: [H, total_len, D]; rows and keys
+    at positions >= max_seq_len inside their sequence take no part (their
+    gradients are 0).  Returns (dq, dk, dv) in float64."""
+    q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    if q.ndim != 3:
+        raise ValueError("jagged tensors are [H, total_len, D]")
+    if max_seq_len < 1:
+        raise ValueError("max_seq_len must be >= 1")
+    H, T, _ = q.shape
+    if offsets[0] != 0 or offsets[-1] != T or np.any(np.diff(offsets) < 0):
+        raise ValueError("offsets must start at 0, be non-decreasing and end at total_len")
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for s in range(len(offsets) - 1):
+        begin, end = int(offsets[s]), int(offsets[s + 1])
+        used = min(end - begin, int(max_seq_len))
+        if used == 0:
+            continue
+        for h in range(H):
+            a, b_, c = attend_rows_bwd(q[h, begin:begin + used], k[h, begin:begin + used], v[h, begin:begin + used],
+                                       do[h, begin:begin + used], sm_scale, causal)
+            dq[h, begin:begin + used], dk[h, begin:begin + used], dv[h, begin:begin + used] = a, b_, c
+    return dq, dk, dv

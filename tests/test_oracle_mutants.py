@@ -33,6 +33,16 @@ MUTANTS = {
                            ("kv_len = np.where(np.arange(n) < used, used, 0)", "kv_len = np.where(np.arange(n) < used, n, 0)")],
     "truncated_rows_attend": ("kv_len = np.where(np.arange(n) < used, used, 0)", "kv_len = np.where(np.arange(n) < used, used, used)"),
     "transposed_value_product": ("p @ v, 0.0)", "(v.T @ p.T).T[:, ::-1], 0.0)"),
+    # backward
+    "bwd_drop_delta": ("ds = p * (dp - delta[:, None])", "ds = p * dp"),
+    "bwd_delta_sign": ("ds = p * (dp - delta[:, None])", "ds = p * (dp + delta[:, None])"),
+    "bwd_dk_scale_dropped": ("dk += scale * (ds.T @ q[r0:r1])", "dk += (ds.T @ q[r0:r1])"),
+    "bwd_dq_scale_dropped": ("dq[r0:r1] = scale * (ds @ k)", "dq[r0:r1] = (ds @ k)"),
+    "bwd_dv_untransposed": ("dv += p.T @ g", "dv += p @ g"),
+    "bwd_dk_wrong_operand": ("dk += scale * (ds.T @ q[r0:r1])", "dk += scale * (ds.T @ g)"),
+    "bwd_dp_wrong_operand": ("dp = g @ v.T", "dp = g @ k.T"),
+    "bwd_causal_dropped": ("allowed &= row_pos[r0:r1, None] >= cols[None, :]", "pass"),
+    "bwd_delta_from_wrong_rows": ("delta = (o * g).sum(axis=1)", "delta = (o * g).sum(axis=0).sum() / o.shape[0] + 0 * g[:, 0]"),
 }
 
 
@@ -75,6 +85,16 @@ def _pins_hold(m) -> bool:
             om, _ = m.attention(q - e * tq, k - e * tk, v - e * tv, 0.6, causal)
             if not np.allclose(to, (op - om) / (2 * e), atol=1e-8, rtol=0):
                 return False
+        # backward: torch's fp64 reverse-mode autodiff of its own attention
+        for causal in (False, True):
+            qq, kk, vv, dd = rnd((1, 2, 7, 4), 11), rnd((1, 2, 7, 4), 12), rnd((1, 2, 7, 4), 13), rnd((1, 2, 7, 4), 14)
+            tt = [torch.from_numpy(x).requires_grad_(True) for x in (qq, kk, vv)]
+            with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+                oo = torch.nn.functional.scaled_dot_product_attention(*tt, is_causal=causal, scale=0.6)
+            oo.backward(torch.from_numpy(dd))
+            for got, ref in zip(m.attention_bwd(qq, kk, vv, dd, 0.6, causal), tt):
+                if not np.allclose(got, ref.grad.numpy(), atol=1e-12, rtol=0):
+                    return False
         # jagged with truncation equals dense attention on each sequence's leading rows
         lengths, M = [5, 2, 7], 4
         off = np.concatenate([[0], np.cumsum(lengths)])
