@@ -1,5 +1,6 @@
 """MI355X (gfx950) fused attention forward: dense, causal, forward-mode JVP and
-jagged multi-head variants, behind the C ABI declared in include/attn.h.
+jagged multi-head variants, and the dense backward, behind the C ABI declared
+in include/attn.h.
 
 The Python layer only marshals arguments: every step of the computation runs
 in the HIP kernels of libattn_mi355x.so.  torch supplies device memory and the
@@ -8,6 +9,8 @@ current stream.
 
 from .binding import (  # noqa: F401
     AttnError,
+    bwd,
+    bwd_workspace_bytes,
     fwd,
     fwd_jvp,
     jagged_fwd,

@@ -63,6 +63,11 @@ def load_library():
     lib.jagged_attn_fwd.argtypes = [i32, vp, S3, vp, S3, vp, S3, vp, S3, vp, vp,
                                     i64, i64, i64, i64, i64, f32, i32, vp, ctypes.c_size_t, vp]
     lib.jagged_attn_fwd.restype = i32
+    lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [i32, vp, S4, vp, S4, vp, S4, vp, S4, vp, S4, vp, vp, S4, vp, S4, vp, S4,
+                             i64, i64, i64, i64, i64, f32, i32, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -170,3 +175,33 @@ def jagged_fwd(q, k, v, offsets, max_seq_len, causal=False, sm_scale=None, works
                                int(max_seq_len), float(sm_scale), int(bool(causal)),
                                _ptr(workspace), workspace.numel(), _stream(q)))
     return o, lse
+
+
+def bwd_workspace_bytes(B, H, Nq) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(int(B), int(H), int(Nq)))
+
+
+def bwd(q, k, v, o, do, lse, causal=False, sm_scale=None, workspace=None):
+    """Dense backward (bf16).  q/o/do [B,H,Nq,D], k/v [B,H,Nkv,D], lse fp32
+    [B,H,Nq] from fwd with the same q, k, v -> (dq, dk, dv) shaped like q, k, v."""
+    lib = load_library()
+    _same(q, k, v, o, do)
+    if lse.dtype != torch.float32 or lse.device != q.device:
+        raise AttnError("lse must be a float32 tensor on the same device")
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if lse.shape != (B, H, Nq) or not lse.is_contiguous():
+        raise AttnError("lse must be a contiguous [B, H, Nq] tensor")
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    need = bwd_workspace_bytes(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    _check(lib.attn_bwd(_dtype_code(q), _ptr(q), _s4(q), _ptr(k), _s4(k), _ptr(v), _s4(v), _ptr(o), _s4(o),
+                        _ptr(do), _s4(do), _ptr(lse), _ptr(dq), _s4(dq), _ptr(dk), _s4(dk), _ptr(dv), _s4(dv),
+                        B, H, Nq, Nkv, D, float(sm_scale), int(bool(causal)),
+                        _ptr(workspace), workspace.numel(), _stream(q)))
+    return dq, dk, dv

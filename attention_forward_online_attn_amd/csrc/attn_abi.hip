@@ -13,6 +13,7 @@
 
 #include "../../include/attn.h"
 #include "attn_common.h"
+#include "attn_bwd_bf16.h"
 #include "attn_fwd_bf16.h"
 #include "attn_fwd_f32.h"
 #include "jagged_plan.h"
@@ -177,6 +178,34 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   return finish(st);
 }
 
+template <class F>
+int launch_fn(F* fn, int grid, int threads, int lds, hipStream_t stream, const BwdArgs& a) {
+  if (grid <= 0) return ATTN_OK;
+  if (lds > 65536 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return ATTN_ERR_HIP;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), lds, stream, a);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+// Key tiles of the dQ kernel (keys streamed per step).
+constexpr int kBnBwdDq = 32;
+
+template <int D>
+int bwd_launch(hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv) {
+  const int64_t rows = B * H * Nq;
+  constexpr int rpb = 256 / (D / 8);
+  int rc = launch_fn(attn_bwd_prep_kernel<D>, (int)((rows + rpb - 1) / rpb), 256, 0, st, a);
+  if (rc) return rc;
+  using Cq = BwdDqCfg<D, kBnBwdDq>;
+  a.n_tiles = (int)((Nq + Cq::BM - 1) / Cq::BM);
+  rc = launch_fn(attn_bwd_dq_kernel<D, kBnBwdDq>, (int)(B * H * a.n_tiles), Cq::THREADS, Cq::LDS, st, a);
+  if (rc) return rc;
+  using Ck = BwdDkdvCfg<D>;
+  a.n_tiles = (int)((Nkv + Ck::BN - 1) / Ck::BN);
+  return launch_fn(attn_bwd_dkdv_kernel<D>, (int)(B * H * a.n_tiles), Ck::THREADS, Ck::LDS, st, a);
+}
+
 int64_t plan_capacity(int64_t num_seqs, int64_t total_len, int BM) {
   // sum_s ceil(len_s / BM) <= floor((total_len + num_seqs (BM - 1)) / BM)
   return (total_len + num_seqs * (BM - 1)) / BM;
@@ -259,6 +288,67 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   a.total_len = (int)total_len;
   a.max_seq_len = mlen;
   rc = launch(kc, (int)grid, st, a);
+  if (rc) return rc;
+  return finish(st);
+}
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
+  if (B < 0 || H < 0 || Nq < 0) return 0;
+  const int64_t rows = B * H * Nq;
+  if (rows > ((int64_t)1 << 40)) return 0;
+  return (size_t)(8 * rows);
+}
+
+int attn_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const void* k, attn_strides4 k_strides,
+             const void* v, attn_strides4 v_strides, const void* o, attn_strides4 o_strides, const void* d_o,
+             attn_strides4 do_strides, const float* lse, void* dq, attn_strides4 dq_strides, void* dk,
+             attn_strides4 dk_strides, void* dv, attn_strides4 dv_strides, int64_t B, int64_t H, int64_t Nq,
+             int64_t Nkv, int64_t D, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  int rc = check_common((int)dtype, D, sm_scale);
+  if (rc) return rc;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
+  if (causal && Nq != Nkv) return ATTN_ERR_CAUSAL_SHAPE;
+  if (B * H * (Nq + Nkv) == 0) return ATTN_OK;
+  if (Nq > INT_MAX || Nkv > INT_MAX || B > INT_MAX || H > INT_MAX) return ATTN_ERR_INVALID;
+  if (Nq > 0 && (!q || !o || !d_o || !lse || !dq)) return ATTN_ERR_INVALID;
+  if (Nkv > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVALID;
+  const int64_t vec = 8;
+  if ((rc = check_s4(q_strides, B, H, Nq, vec)) || (rc = check_s4(o_strides, B, H, Nq, vec)) ||
+      (rc = check_s4(do_strides, B, H, Nq, vec)) || (rc = check_s4(dq_strides, B, H, Nq, vec)))
+    return rc;
+  if ((rc = check_s4(k_strides, B, H, Nkv, vec)) || (rc = check_s4(v_strides, B, H, Nkv, vec)) ||
+      (rc = check_s4(dk_strides, B, H, Nkv, vec)) || (rc = check_s4(dv_strides, B, H, Nkv, vec)))
+    return rc;
+  const void* ptrs[] = {q, k, v, o, d_o, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  const int64_t rows = B * H * Nq;
+  if (rows > 0 && (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, Nq) || ((uintptr_t)workspace & 15u)))
+    return ATTN_ERR_WORKSPACE;
+  if (B * H * ((Nq + 127) / 128) > INT_MAX || B * H * ((Nkv + 127) / 128) > INT_MAX || rows / 16 > INT_MAX)
+    return ATTN_ERR_INVALID;
+
+  BwdArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = d_o; a.lse = lse; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.delta = (float*)workspace;
+  a.lse2 = (float*)workspace + rows;
+  a.q_sb = q_strides.b; a.q_sh = q_strides.h; a.q_sn = q_strides.n;
+  a.k_sb = k_strides.b; a.k_sh = k_strides.h; a.k_sn = k_strides.n;
+  a.v_sb = v_strides.b; a.v_sh = v_strides.h; a.v_sn = v_strides.n;
+  a.o_sb = o_strides.b; a.o_sh = o_strides.h; a.o_sn = o_strides.n;
+  a.do_sb = do_strides.b; a.do_sh = do_strides.h; a.do_sn = do_strides.n;
+  a.dq_sb = dq_strides.b; a.dq_sh = dq_strides.h; a.dq_sn = dq_strides.n;
+  a.dk_sb = dk_strides.b; a.dk_sh = dk_strides.h; a.dk_sn = dk_strides.n;
+  a.dv_sb = dv_strides.b; a.dv_sh = dv_strides.h; a.dv_sn = dv_strides.n;
+  a.B = (int)B; a.H = (int)H; a.Nq = (int)Nq; a.Nkv = (int)Nkv;
+  a.sm_scale = sm_scale;
+  a.c = sm_scale * kLog2e;
+  a.causal = causal ? 1 : 0;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  rc = D == 64 ? bwd_launch<64>(st, a, B, H, Nq, Nkv) : bwd_launch<128>(st, a, B, H, Nq, Nkv);
   if (rc) return rc;
   return finish(st);
 }

@@ -1,0 +1,417 @@
+// bf16 attention backward for gfx950: the gradients dQ, dK, dV of the fused
+// forward for a given dO, from the forward's O and LSE.
+//
+// What is computed follows the backward of the Triton fused attention
+// tutorial with JVP (_attn_bwd_preprocess, _attn_bwd_dkdv, _attn_bwd_dq):
+//   delta_i = sum_d O_id dO_id,   P = exp(S - LSE) with S = sm_scale Q K^T,
+//   dV = P^T dO,   dP = dO V^T,   dS = P (dP - delta),
+//   dQ = sm_scale dS K,   dK = sm_scale dS^T Q,
+// with P and dS rounded to bf16 for their products (the page rounds them to
+// the input type) and fp32 accumulation.
+//
+// Three kernels on one stream:
+// * attn_bwd_prep_kernel: delta and LSE log2(e) per query row (workspace).
+// * attn_bwd_dq_kernel: the forward's layout -- a lane owns one query, Q and
+//   dO stay in registers, K and V tiles stream through LDS:
+//   S^T = K Q^T and dP^T = V dO^T (scores_section), dS^T in registers, and
+//   dQ^T += K^T dS^T through the transposing K reads (pv_section).
+// * attn_bwd_dkdv_kernel: the mirror image -- a lane owns one key, K and V
+//   stay in registers, Q and dO tiles (with their LSE and delta) stream
+//   through LDS: S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
+//   dK^T += Q^T dS through the transposing Q and dO reads.
+// Each output element is written once by one lane: no atomics, and the
+// result does not depend on the order of the work.
+#pragma once
+
+#include "attn_fwd_bf16.h"
+
+namespace attn {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // [B, H, Nq] natural log, as attn_fwd writes it
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace [B * H * Nq]: rowsum(O dO)
+  float* lse2;   // workspace [B * H * Nq]: LSE log2(e); rows without keys +inf
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t do_sb, do_sh, do_sn;
+  int64_t dq_sb, dq_sh, dq_sn;
+  int64_t dk_sb, dk_sh, dk_sn;
+  int64_t dv_sb, dv_sh, dv_sn;
+  int32_t B, H, Nq, Nkv;
+  int32_t n_tiles;  // q-tiles (dQ kernel) or key tiles (dK/dV kernel) per (batch, head)
+  float c;          // sm_scale * log2(e)
+  float sm_scale;
+  int32_t causal;
+};
+
+// ---- delta_i = sum_d O_id dO_id and LSE_i log2(e), one row per D/8 lanes.
+template <int D>
+__global__ void __launch_bounds__(256) attn_bwd_prep_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;          // lanes per row, 16 bytes each
+  constexpr int RPB = 256 / LPR;      // rows per workgroup
+  const int64_t rows = (int64_t)a.B * a.H * a.Nq;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const int64_t bh = row / a.Nq;
+    const int i = (int)(row - bh * a.Nq);
+    const int b = (int)(bh / a.H), h = (int)(bh - (int64_t)b * a.H);
+    const bf16* orow = (const bf16*)a.o + b * a.o_sb + h * a.o_sh + i * a.o_sn + part * 8;
+    const bf16* drow = (const bf16*)a.dout + b * a.do_sb + h * a.do_sh + i * a.do_sn + part * 8;
+    const bf16x8 ov = *(const bf16x8*)orow, dv = *(const bf16x8*)drow;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)ov[e], (float)dv[e], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && part == 0) {
+    a.delta[row] = acc;
+    const float l = a.lse[row];
+    // a row without keys (LSE = -inf) has P = 0: exp2(s c - (+inf)) = 0
+    a.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+}
+
+// Workgroup -> (batch, head, tile), XCD-aware like the forward (a run of
+// consecutive work items per XCD shares that XCD's L2 copy of a head).
+__device__ __forceinline__ void bwd_tile(const BwdArgs& a, int bid, int& b, int& h, int& t) {
+  const int per_head = a.n_tiles;
+  const int total = a.B * a.H * per_head;
+  int logical = bid;
+  if ((total & 7) == 0) logical = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int bh = logical / per_head;
+  t = logical - bh * per_head;
+  b = bh / a.H;
+  h = bh - b * a.H;
+}
+
+// Direct global -> LDS copy of ROWS rows of D bf16 (row stride sn elements)
+// into the swizzled tile at byte `dst` of LDS: instruction i of wave w fills
+// 1 KiB block NW i + w, lane l the 16 bytes at l * 16; rows at or past
+// `valid` re-read the last valid row (their results are masked or dropped).
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void bwd_dma_rows(const bf16* base, int64_t sn, int row0, int valid, lds_t* dst, int wave,
+                                             int lane) {
+  constexpr int TILE = ROWS * D * 2, NBLK = TILE / 1024, NI = NBLK >= NW ? NBLK / NW : 1;
+  constexpr int RPB = 1024 / (2 * D);
+  static_assert(NBLK % NW == 0 || NBLK < NW, "whole 1 KiB blocks per wave");
+  if (NBLK < NW && wave >= NBLK) return;
+  const int last = valid - 1 - row0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int blk = NW * i + wave;
+    const int r = RPB * blk + (lane * 16) / (2 * D);
+    const int ch = (lane % (D / 8)) ^ swz_f<D>(r);
+    const int rr = r < last ? r : last;
+    const char* src = (const char*)(base + (int64_t)(row0 + rr) * sn) + ch * 16;
+    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + blk * 1024),
+                                     16, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------- dQ kernel
+template <int D, int BN>
+struct BwdDqCfg {
+  static constexpr int NW = 4, THREADS = 256, BM = 128;
+  static constexpr int TILE = BN * D * 2;  // one K or V tile
+  static constexpr int STAGE = 2 * TILE;   // K then V
+  static constexpr int LDS = 2 * STAGE;
+};
+
+template <int D, int BN>
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
+  using C = BwdDqCfg<D, BN>;
+  constexpr int BM = C::BM, TILE = C::TILE, STAGE = C::STAGE, NW = C::NW;
+  constexpr int NB = BN / 32, KD = D / 16, DB = D / 32;
+  extern __shared__ __attribute__((aligned(256))) char smem_raw[];
+  lds_t* smem = (lds_t*)smem_raw;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+
+  int b, h, qt;
+  bwd_tile(a, blockIdx.x, b, h, qt);
+  if (a.causal) qt = a.n_tiles - 1 - qt;  // heaviest first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n32 = lane & 31, h32 = lane >> 5;
+  const bf16* Q = (const bf16*)a.q + b * a.q_sb + h * a.q_sh;
+  const bf16* K = (const bf16*)a.k + b * a.k_sb + h * a.k_sh;
+  const bf16* V = (const bf16*)a.v + b * a.v_sb + h * a.v_sh;
+  const bf16* DO = (const bf16*)a.dout + b * a.do_sb + h * a.do_sh;
+  const int64_t row_base = ((int64_t)b * a.H + h) * a.Nq;
+
+  // rows: this lane's query and the wave's key limits
+  const int w0 = qt * BM + wave * 32;
+  const int my_row = w0 + n32;
+  const int r_cl = my_row < a.Nq ? my_row : a.Nq - 1;
+  auto lim = [&](int i) { return a.causal ? min(i + 1, a.Nkv) : a.Nkv; };
+  const int my_lim = lim(r_cl);
+  const int w1 = min(w0 + 31, a.Nq - 1);
+  const int wave_max = w0 <= w1 ? lim(w1) : 0;
+  const int wave_min = w0 <= w1 ? lim(w0) : 0;
+  const int b1 = min(qt * BM + BM, a.Nq) - 1;
+  const int n_tiles = (lim(b1) + BN - 1) / BN;
+
+  // Q and dO rows of this lane (B operands of S^T = K Q^T and dP^T = V dO^T)
+  bf16x8 qf[KD], df[KD];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) {
+    qf[kk] = *(const bf16x8*)(Q + r_cl * a.q_sn + 16 * kk + 8 * h32);
+    df[kk] = *(const bf16x8*)(DO + r_cl * a.do_sn + 16 * kk + 8 * h32);
+  }
+  const float lse2 = a.lse2[row_base + r_cl];
+  const float delta = a.delta[row_base + r_cl];
+
+  const int krow = kperm(n32);
+  uint32_t kaddr[KD];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) kaddr[kk] = lds_base + swz_off<D>(krow, 2 * kk + h32);
+  int vlo[DB], vhi[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) v_frag_offsets<D>(lane, db, vlo[db], vhi[db]);
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+  f32x16 dummy_a[1], dummy_b[1];
+  bf16x8 dummy_h[1][2];
+  bf16x8 dummy_t[1];
+  f32x16 dummy_ts[1];
+
+  auto fetch = [&](int j, int stage) {
+    bwd_dma_rows<D, BN, NW>(K + (int64_t)j * BN * a.k_sn, a.k_sn, 0, a.Nkv - j * BN, smem + stage * STAGE, wave, lane);
+    bwd_dma_rows<D, BN, NW>(V + (int64_t)j * BN * a.v_sn, a.v_sn, 0, a.Nkv - j * BN, smem + stage * STAGE + TILE, wave,
+                            lane);
+  };
+
+  auto step = [&](int j, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    if (j + 1 < n_tiles) fetch(j + 1, S ^ 1);
+    if (j * BN < wave_max) {
+      f32x16 s[NB], dp[NB];
+      scores_section<D, NB, false, S * STAGE, 0>(kaddr, qf, dummy_t, s, dummy_ts);          // S^T = K Q^T
+      scores_section<D, NB, false, S * STAGE + TILE, 0>(kaddr, df, dummy_t, dp, dummy_ts);  // dP^T = V dO^T
+      if ((j + 1) * BN > wave_min) {  // keys past this row's limit: P = 0
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j * BN + 32 * bb + 16 * (r >> 3) + 8 * h32 + (r & 7);
+            if (key >= my_lim) s[bb][r] = -INFINITY;
+          }
+      }
+      // dS^T = P^T (dP^T - delta) as the bf16 B operand (keys 8 per register group)
+      bf16x8 dsf[NB][2];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], a.c, -lse2));
+          dsf[bb][r >> 3][r & 7] = (bf16)(p * (dp[bb][r] - delta));
+        }
+      // dQ^T += K^T dS^T (transposing reads of the K tile)
+      pv_section<D, NB, false, S * STAGE, 0>(lds_base, vlo, vhi, dsf, dummy_h, acc, dummy_a, dummy_b, [](auto) {});
+    }
+    __syncthreads();
+  };
+
+  if (n_tiles > 0) {
+    fetch(0, 0);
+    __syncthreads();
+    int j = 0;
+    for (; j + 2 <= n_tiles; j += 2) {
+      step(j, std::integral_constant<int, 0>{});
+      step(j + 1, std::integral_constant<int, 1>{});
+    }
+    if (j < n_tiles) step(j, std::integral_constant<int, 0>{});
+  }
+
+  if (my_row < a.Nq) {
+    bf16* orow = (bf16*)a.dq + b * a.dq_sb + h * a.dq_sh + my_row * a.dq_sn;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * h32;
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[db][4 * g + e] * a.sm_scale);
+        *(bf16x4*)(orow + d) = ov;
+      }
+  }
+}
+
+// ------------------------------------------------------------- dK/dV kernel
+template <int D>
+struct BwdDkdvCfg {
+  static constexpr int NW = 4, THREADS = 256, BN = 128;  // keys per workgroup, 32 per wave
+  static constexpr int BMQ = 32;                         // query rows per streamed tile
+  static constexpr int TILE = BMQ * D * 2;               // one Q or dO tile
+  static constexpr int STAGE = 2 * TILE + 2 * BMQ * 4;   // Q, dO, then lse2 and delta of those rows
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int WAVES_PER_EU = D == 128 ? 1 : 2;  // D=128 holds K, V, dK, dV: 1 wave per SIMD
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_dkdv_kernel(BwdArgs a) {
+  using C = BwdDkdvCfg<D>;
+  constexpr int BN = C::BN, BMQ = C::BMQ, TILE = C::TILE, STAGE = C::STAGE, NW = C::NW;
+  constexpr int KD = D / 16, DB = D / 32;
+  extern __shared__ __attribute__((aligned(256))) char smem_raw[];
+  lds_t* smem = (lds_t*)smem_raw;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+
+  int b, h, kt;
+  bwd_tile(a, blockIdx.x, b, h, kt);  // causal: low key tiles see the most queries and run first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n32 = lane & 31, h32 = lane >> 5;
+  const bf16* Q = (const bf16*)a.q + b * a.q_sb + h * a.q_sh;
+  const bf16* K = (const bf16*)a.k + b * a.k_sb + h * a.k_sh;
+  const bf16* V = (const bf16*)a.v + b * a.v_sb + h * a.v_sh;
+  const bf16* DO = (const bf16*)a.dout + b * a.do_sb + h * a.do_sh;
+  const int64_t row_base = ((int64_t)b * a.H + h) * a.Nq;
+
+  // keys: this lane's key; the queries that can see the wave's keys
+  const int k0 = kt * BN + wave * 32;
+  const int my_key = k0 + n32;
+  const int k_cl = my_key < a.Nkv ? my_key : a.Nkv - 1;
+  const bool wave_keys = k0 < a.Nkv;
+  const int q_first = a.causal ? kt * BN : 0;        // first query any key of the workgroup sees
+  const int wave_q_first = a.causal ? k0 : 0;        // first query any key of this wave sees
+  const int jq0 = q_first / BMQ;
+  const int n_qt = (a.Nq + BMQ - 1) / BMQ;
+
+  // K and V rows of this lane (B operands of S = Q K^T and dP = dO V^T)
+  bf16x8 kf[KD], vf[KD];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) {
+    kf[kk] = *(const bf16x8*)(K + k_cl * a.k_sn + 16 * kk + 8 * h32);
+    vf[kk] = *(const bf16x8*)(V + k_cl * a.v_sn + 16 * kk + 8 * h32);
+  }
+
+  const int qrow = kperm(n32);
+  uint32_t qaddr[KD];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) qaddr[kk] = lds_base + swz_off<D>(qrow, 2 * kk + h32);
+  int vlo[DB], vhi[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) v_frag_offsets<D>(lane, db, vlo[db], vhi[db]);
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+  f32x16 dummy_a[1], dummy_b[1];
+  bf16x8 dummy_h[1][2];
+  bf16x8 dummy_t[1];
+  f32x16 dummy_ts[1];
+
+  // tile jq: Q and dO rows, then 32 lse2 and 32 delta values (4 bytes per
+  // lane of wave 0: lanes 0-31 lse2, lanes 32-63 delta)
+  auto fetch = [&](int jq, int stage) {
+    const int q0 = jq * BMQ;
+    lds_t* base = smem + stage * STAGE;
+    bwd_dma_rows<D, BMQ, NW>(Q, a.q_sn, q0, a.Nq, base, wave, lane);
+    bwd_dma_rows<D, BMQ, NW>(DO, a.do_sn, q0, a.Nq, base + TILE, wave, lane);
+    if (wave == 0) {
+      const int qi = min(q0 + n32, a.Nq - 1);
+      const float* src = (h32 ? a.delta : a.lse2) + row_base + qi;
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(base + 2 * TILE),
+                                       4, 0, 0);
+    }
+  };
+
+  auto step = [&](int jq, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    if (jq + 1 < n_qt) fetch(jq + 1, S ^ 1);
+    const int q0 = jq * BMQ;
+    if (wave_keys && q0 + BMQ > wave_q_first) {  // wave-uniform: some key of the wave sees some query
+      f32x16 s[1], dp[1];
+      scores_section<D, 1, false, S * STAGE, 0>(qaddr, kf, dummy_t, s, dummy_ts);          // S = Q K^T
+      scores_section<D, 1, false, S * STAGE + TILE, 0>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
+      // register r holds query q0 + 16 (r / 8) + 8 h32 + r % 8: its lse2 and delta
+      const lds_t* st = smem + S * STAGE + 2 * TILE;
+      float l2[16], dl[16];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int qo = (16 * c + 8 * h32) * 4;
+        const f32x4 a0 = *(const __attribute__((address_space(3))) f32x4*)(st + qo);
+        const f32x4 a1 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 16);
+        const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(st + BMQ * 4 + qo);
+        const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(st + BMQ * 4 + qo + 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l2[8 * c + e] = a0[e];
+          l2[8 * c + 4 + e] = a1[e];
+          dl[8 * c + e] = d0[e];
+          dl[8 * c + 4 + e] = d1[e];
+        }
+      }
+      // masked pairs (query past Nq; causal: key after query) get P = 0
+      const bool edge = q0 + BMQ > a.Nq || (a.causal && q0 < k0 + 32);
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = q0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
+          if (qi >= a.Nq || (a.causal && my_key > qi)) s[0][r] = -INFINITY;
+        }
+      }
+      bf16x8 pf[1][2], dsf[1][2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], a.c, -l2[r]));
+        pf[0][r >> 3][r & 7] = (bf16)p;
+        dsf[0][r >> 3][r & 7] = (bf16)(p * (dp[0][r] - dl[r]));
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (transposing reads of the dO and Q tiles)
+      pv_section<D, 1, false, S * STAGE + TILE, 0>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b, [](auto) {});
+      pv_section<D, 1, false, S * STAGE, 0>(lds_base, vlo, vhi, dsf, dummy_h, dk, dummy_a, dummy_b, [](auto) {});
+    }
+    __syncthreads();
+  };
+
+  if (jq0 < n_qt) {
+    fetch(jq0, 0);
+    __syncthreads();
+    int jq = jq0;
+    for (; jq + 2 <= n_qt; jq += 2) {
+      step(jq, std::integral_constant<int, 0>{});
+      step(jq + 1, std::integral_constant<int, 1>{});
+    }
+    if (jq < n_qt) step(jq, std::integral_constant<int, 0>{});
+  }
+
+  if (my_key < a.Nkv) {
+    bf16* krow_o = (bf16*)a.dk + b * a.dk_sb + h * a.dk_sh + my_key * a.dk_sn;
+    bf16* vrow_o = (bf16*)a.dv + b * a.dv_sb + h * a.dv_sh + my_key * a.dv_sn;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * h32;
+        bf16x4 kv, vv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv[e] = (bf16)(dk[db][4 * g + e] * a.sm_scale);
+          vv[e] = (bf16)dv[db][4 * g + e];
+        }
+        *(bf16x4*)(krow_o + d) = kv;
+        *(bf16x4*)(vrow_o + d) = vv;
+      }
+  }
+}
+
+}  // namespace attn

@@ -6,7 +6,8 @@ inputs from it.
 
 Recipe (the same on every machine, independent of the device):
 * one CPU ``torch.Generator`` per tensor, seeded ``seed_base + i`` with
-  i = 0..5 for Q, K, V, tQ, tK, tV and i = 6 for the jagged lengths;
+  i = 0..5 for Q, K, V, tQ, tK, tV, i = 6 for the jagged lengths and i = 7
+  for the backward's dO;
 * values i.i.d. N(0, 1) drawn in fp32 and rounded to the working dtype
   (round-to-nearest-even for bf16) on the CPU;
 * jagged lengths uniform in [1, max_len], offsets = exclusive prefix sum (int64).
@@ -44,6 +45,12 @@ def dense_inputs(B, H, Nq, Nkv, D, dtype="bf16", seed_base=0, tangents=False):
     tk = _normal((B, H, Nkv, D), seed_base + 4, dt)
     tv = _normal((B, H, Nkv, D), seed_base + 5, dt)
     return q, k, v, tq, tk, tv
+
+
+def grad_output(shape, dtype="bf16", seed_base=0):
+    """dO for the backward: i.i.d. N(0, 1), seeded seed_base + 7 (CPU)."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    return _normal(shape, seed_base + 7, dt)
 
 
 def jagged_lengths(num_seqs, max_len, seed_base=0, min_len=1):

@@ -13,7 +13,9 @@ D=64 workload and the jagged workload, and reports them under `extra`.
 Timing: inputs are resident in HBM before the timed region; W untimed steps,
 then exactly K steps between two device synchronisations; per-launch HIP
 events on the launch stream give the kernel's average duration for the
-`roofline` object.  `cpu_baseline` times the fp64 CPU oracle on a bounded
+`roofline` object.  Each entry of `extra` also reports the median and minimum
+launch and a cold-cache median (a 512 MiB buffer is rewritten before every
+launch, outside the events, which evicts L2 and the Infinity Cache).  `cpu_baseline` times the fp64 CPU oracle on a bounded
 sample of the same workload (a few heads) on this host's cores.
 
 Profiling modes (for rocprofv3 runs): --only {fwd,fwd_causal,jvp,jvp_causal,
@@ -38,7 +40,7 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["attn_common.h", "attn_fwd_bf16.h", "attn_fwd_f32.h", "jagged_plan.h", "attn_abi.hip"]
+KERNEL_SOURCES = ["attn_common.h", "attn_fwd_bf16.h", "attn_fwd_f32.h", "jagged_plan.h", "attn_bwd_bf16.h", "attn_abi.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -111,20 +113,36 @@ def make_cases(torch, attn, wl):
 def time_case(torch, case, steps, warmup):
     """Average per-launch duration from HIP events on the launch stream, and
     the wall time of `steps` back-to-back launches."""
+    durs, wall = time_launches(torch, case, steps, warmup)
+    return sum(durs) / len(durs), min(durs), wall
+
+
+def time_launches(torch, case, steps, warmup, flush=None):
+    """Per-launch durations (ms) from HIP events on the launch stream around
+    each launch, and the wall time of the whole loop.  With `flush` (a device
+    buffer larger than L2 + MALL), the buffer is rewritten before every launch
+    (outside the events), so each launch starts with cold caches."""
     for _ in range(warmup):
         case.run()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for a, b in evs:
+    for i, (a, b) in enumerate(evs):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
         a.record(stream)
         case.run()
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = [a.elapsed_time(b) for a, b in evs]  # ms
-    return sum(durs) / len(durs), min(durs), wall
+    return [a.elapsed_time(b) for a, b in evs], wall
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
 
 
 def load_traffic(kernel_hash):
@@ -158,7 +176,14 @@ def cpu_baseline(wl, budget_s=15.0):
     dt = time.perf_counter() - t0
     flops = dense_flops(1, heads, w.N, w.N, w.D, False)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model, "host_logical_cpus": os.cpu_count(),
             "sample": f"{heads} of the 128 (batch, head) slices of the B=4 H=32 N=4096 D=128 non-causal "
                       f"forward in {dt:.1f} s (fp64 numpy oracle, BLAS threads = cores)"}
 
@@ -207,17 +232,36 @@ def main():
         return
 
     head = cases["fwd"]
-    avg, mn, wall = time_case(torch, head, args.steps, args.warmup)
+    durs, wall = time_launches(torch, head, args.steps, args.warmup)
+    avg, mn = sum(durs) / len(durs), min(durs)
     ms_per_step = wall * 1e3 / args.steps
     value = head.flops / (ms_per_step * 1e-3) / 1e12
     achieved = head.flops / (avg * 1e-3) / 1e12
-    extra = {}
+    # cold caches: a 512 MiB buffer (more than 8 x 4 MB L2 + 256 MB MALL) is
+    # rewritten before every launch, outside the timed events
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    n_cold = max(5, args.steps // 2)
+
+    def summary(c, durs_w, durs_c):
+        mw, mc = median(durs_w), median(durs_c)
+        return {"workload": c.desc, "avg_ms": round(sum(durs_w) / len(durs_w), 4), "median_ms": round(mw, 4),
+                "min_ms": round(min(durs_w), 4), "tflops": round(c.flops / (mw * 1e-3) / 1e12, 2),
+                "frac_of_mfma_peak": round(c.flops / (mw * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "gbps_compulsory": round(c.bytes / (mw * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(c.bytes / (mw * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "cold_median_ms": round(mc, 4), "cold_min_ms": round(min(durs_c), 4),
+                "cold_tflops": round(c.flops / (mc * 1e-3) / 1e12, 2)}
+
+    extra = {"fwd": summary(head, durs, time_launches(torch, head, n_cold, 2, flush)[0])}
     for name in ("fwd_causal", "jvp", "jvp_causal", "causal_d64", "jagged"):
         c = cases[name]
-        a, m, _ = time_case(torch, c, max(5, args.steps // 2), 10)
-        extra[name] = {"workload": c.desc, "avg_ms": round(a, 4), "tflops": round(c.flops / (a * 1e-3) / 1e12, 2),
-                       "frac_of_mfma_peak": round(c.flops / (a * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                       "gbps_compulsory": round(c.bytes / (a * 1e-3) / 1e9, 1)}
+        dw, _ = time_launches(torch, c, max(5, args.steps // 2), 10)
+        dc, _ = time_launches(torch, c, n_cold, 2, flush)
+        extra[name] = summary(c, dw, dc)
+    del flush
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+              "compute_units": props.multi_processor_count}
     traffic = load_traffic(kernel_source_hash())
     out = {
         "metric": "attention fwd TFLOP/s (bf16, N=4096, D=128) + JVP fwd TFLOP/s, 1 GPU",
@@ -233,7 +277,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": head.desc, "jvp_workload": cases["jvp"].desc,
-                   "flops_per_step": head.flops, "flop_convention": "4*B*H*Nq*Nkv*D (x0.5 causal, x3 JVP)"},
+                   "flops_per_step": head.flops, "flop_convention": "4*B*H*Nq*Nkv*D (x0.5 causal, x3 JVP)",
+                   "device": device},
         "jvp_value": extra["jvp"]["tflops"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -145,6 +145,48 @@ ATTN_API int jagged_attn_fwd(attn_dtype dtype,
                     int64_t max_seq_len, float sm_scale, int causal,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace attn_bwd needs (host function, no GPU access):
+ * two fp32 values per query row.  Returns 0 for invalid sizes.
+ */
+ATTN_API size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
+
+/*
+ * Dense attention backward: the gradients of attn_fwd's output o for a given
+ * d_o = dL/do (tutorial page: _attn_bwd_preprocess, _attn_bwd_dkdv,
+ * _attn_bwd_dq and _attn_bwd):
+ *     delta_i = sum_d o_id d_o_id,   P = exp(sm_scale q k^T - lse)  (0 where masked),
+ *     dv = P^T d_o,   dP = d_o v^T,   dS = P * (dP - delta),
+ *     dq = sm_scale dS k,   dk = sm_scale dS^T q.
+ *   q, o, d_o, dq  [B, H, Nq, D]   k, v, dk, dv  [B, H, Nkv, D]  (bf16 only)
+ *   lse            [B, H, Nq] contiguous fp32: the natural-log LSE that
+ *                  attn_fwd wrote for these q, k, v (a row with LSE = -inf
+ *                  gets dq = 0 and adds nothing to dk, dv)
+ *   o              the forward's output (delta is formed from it, as the page does)
+ *   dq, dk, dv     written (every element; rows with no attended key get 0)
+ *   workspace      DEVICE scratch of at least attn_bwd_workspace_bytes(B, H, Nq)
+ *                  bytes, 16-byte aligned; contents on entry are ignored.
+ *                  Calls that share a workspace must not overlap.
+ * Strides, alignment, sm_scale, causal (Nq == Nkv) and D in {64, 128} as for
+ * attn_fwd.  P and dS are rounded to bf16 for their products, with fp32
+ * accumulation.  Each output element is written by exactly one thread: the
+ * result is deterministic.  ATTN_FP32 returns ATTN_ERR_UNSUPPORTED.  Three
+ * kernels are enqueued on `stream`; B*H*(Nq+Nkv) == 0 is a no-op.
+ */
+ATTN_API int attn_bwd(attn_dtype dtype,
+             const void* q, attn_strides4 q_strides,
+             const void* k, attn_strides4 k_strides,
+             const void* v, attn_strides4 v_strides,
+             const void* o, attn_strides4 o_strides,
+             const void* d_o, attn_strides4 do_strides,
+             const float* lse,
+             void* dq, attn_strides4 dq_strides,
+             void* dk, attn_strides4 dk_strides,
+             void* dv, attn_strides4 dv_strides,
+             int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+             float sm_scale, int causal,
+             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable text for a status code (host, static storage). */
 ATTN_API const char* attn_status_string(int status);
 

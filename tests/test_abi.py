@@ -32,7 +32,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(
-        ["attn_fwd", "attn_fwd_jvp", "jagged_attn_workspace_bytes", "jagged_attn_fwd", "attn_status_string"])
+        ["attn_fwd", "attn_fwd_jvp", "jagged_attn_workspace_bytes", "jagged_attn_fwd", "attn_bwd_workspace_bytes",
+         "attn_bwd", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -119,3 +120,31 @@ def test_binding_rejects_host_tensors(lib):
         attn.fwd(x, x, x)
     with pytest.raises(attn.AttnError):
         attn.fwd(x.float(), x, x)
+
+
+def test_bwd_validation(lib):
+    B, H, N, D = 1, 2, 128, 64
+    st = dense_strides(B, H, N, D)
+    need = lib.attn_bwd_workspace_bytes(B, H, N)
+    assert need == 8 * B * H * N
+    assert lib.attn_bwd_workspace_bytes(-1, H, N) == 0
+
+    def call(dtype=BF16, D=64, causal=0, Nkv=N, ws=P, ws_bytes=need, q=P, dq=P, lse=P, scale=0.125, sq=st):
+        sk = dense_strides(B, H, Nkv, D)
+        return lib.attn_bwd(dtype, q, sq, P, sk, P, sk, P, st, P, st, lse, dq, st, P, sk, P, sk,
+                            B, H, N, Nkv, D, scale, causal, ws, ws_bytes, None)
+    assert call(dtype=FP32) == UNSUPPORTED
+    assert call(D=96) == UNSUPPORTED
+    assert call(causal=1, Nkv=64) == CAUSAL
+    assert call(ws=0) == WORKSPACE
+    assert call(ws_bytes=need - 4) == WORKSPACE
+    assert call(ws=P + 4) == WORKSPACE
+    assert call(q=0) == INVALID
+    assert call(dq=0) == INVALID
+    assert call(lse=0) == INVALID
+    assert call(scale=-1.0) == INVALID
+    assert call(q=P + 2) == UNSUPPORTED
+    assert call(sq=Strides4(H * N * D, N * D, D, 2)) == INVALID
+    zero = lib.attn_bwd(BF16, 0, st, 0, st, 0, st, 0, st, 0, st, 0, 0, st, 0, st, 0, st,
+                        0, H, N, N, D, 0.125, 0, 0, 0, None)
+    assert zero == OK
