@@ -19,7 +19,7 @@ launch, outside the events, which evicts L2 and the Infinity Cache).  `cpu_basel
 sample of the same workload (a few heads) on this host's cores.
 
 Profiling modes (for rocprofv3 runs): --only {fwd,fwd_causal,jvp,jvp_causal,
-causal_d64,jagged} runs just that kernel K times; --copy-calibration runs a
+causal_d64,jagged,bwd,bwd_causal} runs just that workload K times; --copy-calibration runs a
 plain device copy of known size (the scale for FETCH_SIZE / WRITE_SIZE).
 """
 
@@ -40,7 +40,9 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["attn_common.h", "attn_fwd_bf16.h", "attn_fwd_f32.h", "jagged_plan.h", "attn_bwd_bf16.h", "attn_abi.hip"]
+# sources of the headline kernel (attn_fwd_bf16_kernel and its tile mapping): the
+# stored HBM traffic figure is valid only while they are unchanged
+KERNEL_SOURCES = ["attn_common.h", "attn_fwd_bf16.h"]
 
 
 def kernel_source_hash() -> str:
@@ -99,6 +101,18 @@ def make_cases(torch, attn, wl):
     cases["causal_d64"] = Case("causal_d64", lambda: attn.fwd(q2, k2, v2, causal=True, sm_scale=w2.sm_scale),
                                dense_flops(w2.B, w2.H, w2.N, w2.N, w2.D, True), 4 * q2.numel() * 2 + w2.B * w2.H * w2.N * 4,
                                f"{w2.name}: B={w2.B} H={w2.H} N={w2.N} D={w2.D} bf16 causal")
+
+    # backward over the headline shape: the forward's O and LSE, a seeded dO
+    do = wl.grad_output(q.shape, "bf16", 0).to(dev)
+    bwd_io = 8 * q.numel() * 2 + w.B * w.H * w.N * 4
+    for causal in (False, True):
+        nm = "bwd_causal" if causal else "bwd"
+        o_f, lse_f = attn.fwd(q, k, v, causal=causal, sm_scale=w.sm_scale)
+        ws_b = torch.empty(attn.bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+        cases[nm] = Case(nm, (lambda c=causal, o_f=o_f, lse_f=lse_f, ws_b=ws_b: attn.bwd(
+                             q, k, v, o_f, do, lse_f, causal=c, sm_scale=w.sm_scale, workspace=ws_b)),
+                         2.5 * dense_flops(w.B, w.H, w.N, w.N, w.D, causal), bwd_io,
+                         f"{w.name} backward: B={w.B} H={w.H} N={w.N} D={w.D} bf16 causal={causal} (dQ, dK, dV)")
 
     w5 = wl.WORKLOADS["jagged_d128"]
     lengths = wl.jagged_lengths(w5.num_seqs, w5.max_len, 0)
@@ -253,7 +267,7 @@ def main():
                 "cold_tflops": round(c.flops / (mc * 1e-3) / 1e12, 2)}
 
     extra = {"fwd": summary(head, durs, time_launches(torch, head, n_cold, 2, flush)[0])}
-    for name in ("fwd_causal", "jvp", "jvp_causal", "causal_d64", "jagged"):
+    for name in ("fwd_causal", "jvp", "jvp_causal", "causal_d64", "jagged", "bwd", "bwd_causal"):
         c = cases[name]
         dw, _ = time_launches(torch, c, max(5, args.steps // 2), 10)
         dc, _ = time_launches(torch, c, n_cold, 2, flush)
@@ -277,7 +291,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": head.desc, "jvp_workload": cases["jvp"].desc,
-                   "flops_per_step": head.flops, "flop_convention": "4*B*H*Nq*Nkv*D (x0.5 causal, x3 JVP)",
+                   "flops_per_step": head.flops,
+                   "flop_convention": "4*B*H*Nq*Nkv*D (x0.5 causal, x3 JVP, x2.5 backward)",
                    "device": device},
         "jvp_value": extra["jvp"]["tflops"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
