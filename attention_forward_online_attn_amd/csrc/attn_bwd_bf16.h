@@ -210,17 +210,24 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
             if (key >= my_lim) s[bb][r] = -INFINITY;
           }
       }
-      // dS^T = P^T (dP^T - delta) as the bf16 B operand (keys 8 per register group)
+      // dS^T = P^T (dP^T - delta) as the bf16 B operand (keys 8 per register
+      // group = key chunk e / 8); chunk 0 first, chunk c+1 computed after the
+      // MFMAs of chunk c of the product below
       bf16x8 dsf[NB][2];
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], a.c, -lse2));
-          dsf[bb][r >> 3][r & 7] = (bf16)(p * (dp[bb][r] - delta));
-        }
+      auto dsel = [&](auto e_tag) {
+        constexpr int e = decltype(e_tag)::value, bb = e / 16, r = e % 16;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], a.c, -lse2));
+        dsf[bb][r >> 3][r & 7] = (bf16)(p * (dp[bb][r] - delta));
+      };
+      static_for<8>(dsel);
       // dQ^T += K^T dS^T (transposing reads of the K tile)
-      pv_section<D, NB, false, S * STAGE, 0>(lds_base, vlo, vhi, dsf, dummy_h, acc, dummy_a, dummy_b, [](auto) {});
+      pv_section<D, NB, false, S * STAGE, 0>(lds_base, vlo, vhi, dsf, dummy_h, acc, dummy_a, dummy_b, [&](auto i_tag) {
+        constexpr int i = decltype(i_tag)::value, c = i / DB, EPS = 8 / DB;
+        if constexpr (c + 1 < 2 * NB)
+          static_for<EPS>([&](auto k_tag) {
+            dsel(std::integral_constant<int, 8 * (c + 1) + (i % DB) * EPS + decltype(k_tag)::value>{});
+          });
+      });
     }
     __syncthreads();
   };
@@ -342,24 +349,6 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
       f32x16 s[1], dp[1];
       scores_section<D, 1, false, S * STAGE, 0>(qaddr, kf, dummy_t, s, dummy_ts);          // S = Q K^T
       scores_section<D, 1, false, S * STAGE + TILE, 0>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
-      // register r holds query q0 + 16 (r / 8) + 8 h32 + r % 8: its lse2 and delta
-      const lds_t* st = smem + S * STAGE + 2 * TILE;
-      float l2[16], dl[16];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int qo = (16 * c + 8 * h32) * 4;
-        const f32x4 a0 = *(const __attribute__((address_space(3))) f32x4*)(st + qo);
-        const f32x4 a1 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 16);
-        const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(st + BMQ * 4 + qo);
-        const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(st + BMQ * 4 + qo + 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          l2[8 * c + e] = a0[e];
-          l2[8 * c + 4 + e] = a1[e];
-          dl[8 * c + e] = d0[e];
-          dl[8 * c + 4 + e] = d1[e];
-        }
-      }
       // masked pairs (query past Nq; causal: key after query) get P = 0
       const bool edge = q0 + BMQ > a.Nq || (a.causal && q0 < k0 + 32);
       if (edge) {
@@ -369,15 +358,31 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
           if (qi >= a.Nq || (a.causal && my_key > qi)) s[0][r] = -INFINITY;
         }
       }
+      // register r holds query q0 + 16 (r / 8) + 8 h32 + r % 8; chunk c (the
+      // 8 registers 8c..8c+7) needs the lse2 and delta of 8 consecutive queries
+      const lds_t* st = smem + S * STAGE + 2 * TILE;
       bf16x8 pf[1][2], dsf[1][2];
+      auto chunk = [&](auto c_tag) {
+        constexpr int c = decltype(c_tag)::value;
+        constexpr int qo = 16 * c * 4;
+        const f32x4 a0 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 32 * h32);
+        const f32x4 a1 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 32 * h32 + 16);
+        const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(st + BMQ * 4 + qo + 32 * h32);
+        const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(st + BMQ * 4 + qo + 32 * h32 + 16);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], a.c, -l2[r]));
-        pf[0][r >> 3][r & 7] = (bf16)p;
-        dsf[0][r >> 3][r & 7] = (bf16)(p * (dp[0][r] - dl[r]));
-      }
+        for (int e = 0; e < 8; ++e) {
+          const float l2 = e < 4 ? a0[e & 3] : a1[e & 3];
+          const float dl = e < 4 ? d0[e & 3] : d1[e & 3];
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][8 * c + e], a.c, -l2));
+          pf[0][c][e] = (bf16)p;
+          dsf[0][c][e] = (bf16)(p * (dp[0][8 * c + e] - dl));
+        }
+      };
+      chunk(std::integral_constant<int, 0>{});
       // dV^T += dO^T P and dK^T += Q^T dS (transposing reads of the dO and Q tiles)
-      pv_section<D, 1, false, S * STAGE + TILE, 0>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b, [](auto) {});
+      pv_section<D, 1, false, S * STAGE + TILE, 0>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b, [&](auto i_tag) {
+        if constexpr (decltype(i_tag)::value == 0) chunk(std::integral_constant<int, 1>{});  // after the first MFMA
+      });
       pv_section<D, 1, false, S * STAGE, 0>(lds_base, vlo, vhi, dsf, dummy_h, dk, dummy_a, dummy_b, [](auto) {});
     }
     __syncthreads();
