@@ -55,7 +55,7 @@ def load_library():
     lib.attn_fwd.argtypes = [i32, vp, S4, vp, S4, vp, S4, vp, S4, vp,
                              i64, i64, i64, i64, i64, f32, i32, vp]
     lib.attn_fwd.restype = i32
-    lib.attn_fwd_jvp.argtypes = [i32, vp, vp, vp, vp, vp, vp, S4, S4, S4, vp, vp, S4, vp,
+    lib.attn_fwd_jvp.argtypes = [i32, vp, vp, vp, vp, vp, vp, S4, S4, S4, vp, vp, S4, vp, vp,
                                  i64, i64, i64, i64, i64, f32, i32, vp]
     lib.attn_fwd_jvp.restype = i32
     lib.jagged_attn_workspace_bytes.argtypes = [i64, i64]
@@ -128,9 +128,10 @@ def fwd(q, k, v, causal=False, sm_scale=None):
     return o, lse
 
 
-def fwd_jvp(q, k, v, tq, tk, tv, causal=False, sm_scale=None):
-    """Dense forward fused with the JVP -> (o, to, lse).  Tangents must have
-    the strides of their primals."""
+def fwd_jvp(q, k, v, tq, tk, tv, causal=False, sm_scale=None, return_tlse=False):
+    """Dense forward fused with the JVP -> (o, to, lse), or (o, to, lse, tlse)
+    with return_tlse (tlse fp32 [B,H,Nq], the tangent of lse).  Tangents must
+    have the strides of their primals."""
     lib = load_library()
     _same(q, k, v, tq, tk, tv)
     for t, p in ((tq, q), (tk, k), (tv, v)):
@@ -143,10 +144,11 @@ def fwd_jvp(q, k, v, tq, tk, tv, causal=False, sm_scale=None):
     o = torch.empty((B, H, Nq, D), dtype=q.dtype, device=q.device)
     to = torch.empty_like(o)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    tlse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if return_tlse else None
     _check(lib.attn_fwd_jvp(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
-                            _s4(q), _s4(k), _s4(v), _ptr(o), _ptr(to), _s4(o), _ptr(lse),
+                            _s4(q), _s4(k), _s4(v), _ptr(o), _ptr(to), _s4(o), _ptr(lse), _ptr(tlse),
                             B, H, Nq, Nkv, D, float(sm_scale), int(bool(causal)), _stream(q)))
-    return o, to, lse
+    return (o, to, lse, tlse) if return_tlse else (o, to, lse)
 
 
 def jagged_workspace_bytes(num_seqs, total_len) -> int:

@@ -130,8 +130,8 @@ int launch(const KernelChoice& k, int grid, hipStream_t stream, const FwdArgs& a
 
 int dense(int dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk, const void* tv,
           attn_strides4 sq, attn_strides4 sk, attn_strides4 sv, void* o, void* to, attn_strides4 so, float* lse,
-          int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal, void* stream,
-          bool jvp) {
+          float* tlse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal,
+          void* stream, bool jvp) {
   int rc = check_common(dtype, D, sm_scale);
   if (rc) return rc;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
@@ -157,7 +157,7 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   if (grid > INT_MAX) return ATTN_ERR_INVALID;
 
   FwdArgs a = {};
-  a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv; a.o = o; a.to = to; a.lse = lse;
+  a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv; a.o = o; a.to = to; a.lse = lse; a.tlse = tlse;
   a.q_sb = sq.b; a.q_sh = sq.h; a.q_sn = sq.n;
   a.k_sb = sk.b; a.k_sh = sk.h; a.k_sn = sk.n;
   a.v_sb = sv.b; a.v_sh = sv.h; a.v_sn = sv.n;
@@ -222,15 +222,15 @@ int attn_fwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const voi
              const void* v, attn_strides4 v_strides, void* o, attn_strides4 o_strides, float* lse, int64_t B,
              int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal, void* stream) {
   return dense((int)dtype, q, k, v, nullptr, nullptr, nullptr, q_strides, k_strides, v_strides, o, nullptr,
-               o_strides, lse, B, H, Nq, Nkv, D, sm_scale, causal, stream, false);
+               o_strides, lse, nullptr, B, H, Nq, Nkv, D, sm_scale, causal, stream, false);
 }
 
 int attn_fwd_jvp(attn_dtype dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk,
                  const void* tv, attn_strides4 q_strides, attn_strides4 k_strides, attn_strides4 v_strides, void* o,
-                 void* to, attn_strides4 o_strides, float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
-                 int64_t D, float sm_scale, int causal, void* stream) {
-  return dense((int)dtype, q, k, v, tq, tk, tv, q_strides, k_strides, v_strides, o, to, o_strides, lse, B, H, Nq,
-               Nkv, D, sm_scale, causal, stream, true);
+                 void* to, attn_strides4 o_strides, float* lse, float* tlse, int64_t B, int64_t H, int64_t Nq,
+                 int64_t Nkv, int64_t D, float sm_scale, int causal, void* stream) {
+  return dense((int)dtype, q, k, v, tq, tk, tv, q_strides, k_strides, v_strides, o, to, o_strides, lse, tlse, B, H,
+               Nq, Nkv, D, sm_scale, causal, stream, true);
 }
 
 size_t jagged_attn_workspace_bytes(int64_t num_seqs, int64_t total_len) {

@@ -34,6 +34,7 @@ struct FwdArgs {
   void* o;
   void* to;
   float* lse;
+  float* tlse;  // JVP: tangent of LSE per row (nullptr: not written)
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
   int64_t v_sb, v_sh, v_sn;

@@ -635,7 +635,8 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     if (j < n_tiles) step(j, std::integral_constant<int, 0>{});
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln2, tO = (accA + accB - r O) / l
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln2, tO = (accA + accB - r O) / l,
+  // tLSE = r / l
   const float l_tot = xhalf_sum(l_run);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
@@ -662,6 +663,9 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         if constexpr (JVP) *(bf16x4*)(torow + d) = tov;
       }
     if (h32 == 0) a.lse[t.lse_off + my_row] = lse;
+    // tangent of LSE: rowsum(P tS) = r / l (0 for a row without keys)
+    if constexpr (JVP)
+      if (h32 == 0 && a.tlse != nullptr) a.tlse[t.lse_off + my_row] = r_tot * inv;
   }
 }
 

@@ -148,6 +148,8 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
       if constexpr (JVP) torow[4 * i + u] = (accA[i] + a.sm_scale * accB[i] - r_tot * o) * inv;
     }
     if (u == 0) a.lse[t.lse_off + my_row] = empty ? -INFINITY : (m_run + log2f(l_run)) * kLn2;
+    if constexpr (JVP)
+      if (u == 0 && a.tlse != nullptr) a.tlse[t.lse_off + my_row] = r_tot * inv;
   }
 }
 

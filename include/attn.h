@@ -97,14 +97,18 @@ ATTN_API int attn_fwd(attn_dtype dtype,
  *     tS = sm_scale (tq k^T + q tk^T),  tP = P * (tS - rowsum(P * tS)),
  *     to = tP v + P tv
  * alongside o and lse in the same pass.  Tangents use the primal strides;
- * `to` uses o_strides.  Other arguments as attn_fwd.
+ * `to` uses o_strides.
+ *   tlse  optional [B, H, Nq] contiguous fp32 (NULL: not written): the
+ *         tangent of lse, rowsum(P * tS) (0 for a row without keys) -- the
+ *         term that merging JVPs of key-sharded attention needs.
+ * Other arguments as attn_fwd.
  */
 ATTN_API int attn_fwd_jvp(attn_dtype dtype,
                  const void* q, const void* k, const void* v,
                  const void* tq, const void* tk, const void* tv,
                  attn_strides4 q_strides, attn_strides4 k_strides, attn_strides4 v_strides,
                  void* o, void* to, attn_strides4 o_strides,
-                 float* lse,
+                 float* lse, float* tlse,
                  int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
                  float sm_scale, int causal, void* stream);
 

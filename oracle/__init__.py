@@ -97,7 +97,7 @@ def scale_as_passed(sm_scale: float) -> float:
 
 
 def attend_rows(q, k, v, sm_scale, causal=False, row_pos=None,
-                tq=None, tk=None, tv=None, kv_len=None):
+                tq=None, tk=None, tv=None, kv_len=None, with_tlse=False):
     """Attention of some query rows of one (batch, head) over all its keys.
 
     q:  [M, D] query rows;  k: [N, D];  v: [N, Dv].
@@ -107,7 +107,9 @@ def attend_rows(q, k, v, sm_scale, causal=False, row_pos=None,
              (the jagged truncation); keys j >= kv_len[i] are masked.
     tq/tk/tv: optional tangents shaped like q/k/v; when given the JVP output
              tO is returned as well.
-    Returns (o [M, Dv], lse [M]) or (o, to, lse).
+    with_tlse: with tangents, also return the tangent of LSE,
+             rho_i = sum_j P_ij tS_ij (0 for a row without keys).
+    Returns (o [M, Dv], lse [M]), (o, to, lse) or (o, to, lse, tlse).
     """
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     M, N = q.shape[0], k.shape[0]
@@ -122,8 +124,15 @@ def attend_rows(q, k, v, sm_scale, causal=False, row_pos=None,
     o = np.zeros((M, v.shape[1]))
     lse = np.full(M, -np.inf)
     to = np.zeros((M, v.shape[1])) if jvp else None
+    tlse = np.zeros(M) if jvp else None
+
+    def result():
+        if not jvp:
+            return o, lse
+        return (o, to, lse, tlse) if with_tlse else (o, to, lse)
+
     if N == 0 or M == 0:
-        return (o, to, lse) if jvp else (o, lse)
+        return result()
 
     cols = np.arange(N)
     for r0 in range(0, M, _ROW_BLOCK):
@@ -154,7 +163,8 @@ def attend_rows(q, k, v, sm_scale, causal=False, row_pos=None,
             rho = (p * ts).sum(axis=1)            # = tangent of LSE
             tp = p * (ts - rho[:, None])          # tangent of the softmax
             to[r0:r1] = np.where(has_key[:, None], tp @ v + p @ tv, 0.0)
-    return (o, to, lse) if jvp else (o, lse)
+            tlse[r0:r1] = np.where(has_key, rho, 0.0)
+    return result()
 
 
 def _check_dense(q, k, v, causal):
@@ -178,9 +188,9 @@ def attention(q, k, v, sm_scale, causal=False):
     return o, lse
 
 
-def attention_jvp(q, k, v, tq, tk, tv, sm_scale, causal=False):
+def attention_jvp(q, k, v, tq, tk, tv, sm_scale, causal=False, with_tlse=False):
     """Dense attention forward with its forward-mode JVP.
-    Returns (o, to, lse) in float64."""
+    Returns (o, to, lse), or (o, to, lse, tlse) with with_tlse, in float64."""
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     tq, tk, tv = as_f64(tq), as_f64(tk), as_f64(tv)
     _check_dense(q, k, v, causal)
@@ -188,12 +198,13 @@ def attention_jvp(q, k, v, tq, tk, tv, sm_scale, causal=False):
     o = np.zeros((B, H, Nq, v.shape[3]))
     to = np.zeros_like(o)
     lse = np.zeros((B, H, Nq))
+    tlse = np.zeros((B, H, Nq))
     for b in range(B):
         for h in range(H):
-            o[b, h], to[b, h], lse[b, h] = attend_rows(
+            o[b, h], to[b, h], lse[b, h], tlse[b, h] = attend_rows(
                 q[b, h], k[b, h], v[b, h], sm_scale, causal,
-                tq=tq[b, h], tk=tk[b, h], tv=tv[b, h])
-    return o, to, lse
+                tq=tq[b, h], tk=tk[b, h], tv=tv[b, h], with_tlse=True)
+    return (o, to, lse, tlse) if with_tlse else (o, to, lse)
 
 
 def attention_sampled(q, k, v, sm_scale, causal, rows, tangents=None):

@@ -86,7 +86,7 @@ def test_dense_validation(lib):
 
 def test_jvp_validation(lib):
     s = dense_strides(1, 1, 64, 64)
-    args = lambda tq=P, to=P, D=64: lib.attn_fwd_jvp(BF16, P, P, P, tq, P, P, s, s, s, P, to, s, P,
+    args = lambda tq=P, to=P, D=64: lib.attn_fwd_jvp(BF16, P, P, P, tq, P, P, s, s, s, P, to, s, P, None,
                                                      1, 1, 64, 64, D, 0.125, 0, None)
     assert args(tq=0) == INVALID
     assert args(to=0) == INVALID

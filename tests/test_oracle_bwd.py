@@ -153,3 +153,30 @@ def test_jagged_bwd_is_dense_bwd_per_sequence():
             # rows and keys past max_seq_len take no part
             for g in (dq, dk, dv):
                 assert np.all(g[:, a + u:b] == 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tlse_is_derivative_of_lse(causal):
+    """tLSE = d/de LSE(q + e tq, k + e tk): central differences of the
+    (separately pinned) forward oracle's LSE, and torch forward-mode autodiff of
+    logsumexp over the masked scores."""
+    N, D, scale = 9, 8, 0.6
+    q, k, v = rnd((1, 2, N, D), 40), rnd((1, 2, N, D), 41), rnd((1, 2, N, D), 42)
+    tq, tk, tv = rnd(q.shape, 43), rnd(k.shape, 44), rnd(v.shape, 45)
+    _, _, _, tlse = oracle.attention_jvp(q, k, v, tq, tk, tv, scale, causal, with_tlse=True)
+    h = 1e-6
+    _, lp = oracle.attention(q + h * tq, k + h * tk, v, scale, causal)
+    _, lm = oracle.attention(q - h * tq, k - h * tk, v, scale, causal)
+    np.testing.assert_allclose(tlse, (lp - lm) / (2 * h), rtol=0, atol=1e-8)
+
+    def lse_fn(a, b):
+        s = scale * a @ b.transpose(-1, -2)
+        if causal:
+            s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+        return torch.logsumexp(s, dim=-1)
+    t = torch.from_numpy
+    _, ref = torch.func.jvp(lse_fn, (t(q), t(k)), (t(tq), t(tk)))
+    np.testing.assert_allclose(tlse, ref.numpy(), rtol=0, atol=1e-12)
+    # the value tangent does not move the LSE
+    _, _, _, tlse2 = oracle.attention_jvp(q, k, v, tq, tk, 5.0 * tv, scale, causal, with_tlse=True)
+    np.testing.assert_array_equal(tlse, tlse2)

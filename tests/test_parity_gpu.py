@@ -305,3 +305,23 @@ def test_causal_pairing_odd_and_even_tile_counts(gpu_lib, N):
     alone) and 5 q-tiles, for the forward and the JVP."""
     dense_case(2, 3, N, N, 128, "bf16", True, seed=N)
     jvp_case(2, 3, N, N, 64, "bf16", True, seed=N + 1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_jvp_tlse(gpu_lib, dtype, causal):
+    """The tangent of LSE (rowsum(P tS)) written next to O, tO and LSE.  Bound:
+    the LSE's own (1e-3 absolute for bf16 inputs, 1e-4 for fp32) -- it is
+    formed from fp32 p and fp32 tangent scores like the LSE from fp32 row sums."""
+    B, H, N, D = 2, 3, 333, 64
+    ts = wl.dense_inputs(B, H, N, N, D, dtype, 31, tangents=True)
+    o, to, lse, tlse = attn.fwd_jvp(*cuda(*ts), causal=causal, return_tlse=True)
+    ro, rto, rl, rtl = oracle.attention_jvp(*ts, oracle.scale_as_passed(D ** -0.5), causal, with_tlse=True)
+    assert_close(DT[dtype], host64(o), host64(lse), ro, rl, host64(to), rto, label=f"jvp+tlse {dtype} causal={causal}")
+    err = float(np.max(np.abs(host64(tlse) - rtl)))
+    bound = 1e-3 if dtype == "bf16" else 1e-4
+    print(f"max|dtLSE| = {err:.3e} (bound {bound:.0e}, max|tLSE| {np.abs(rtl).max():.2f})", flush=True)
+    assert err <= bound
+    # without the request nothing else changes
+    o2, to2, lse2 = attn.fwd_jvp(*cuda(*ts), causal=causal)
+    assert torch.equal(o, o2) and torch.equal(to, to2) and torch.equal(lse, lse2)
