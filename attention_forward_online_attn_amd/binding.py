@@ -18,6 +18,7 @@ _lib = None
 
 ATTN_BF16 = 0
 ATTN_FP32 = 1
+ATTN_FP16 = 2
 
 
 class AttnError(RuntimeError):
@@ -85,7 +86,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return ATTN_BF16
     if t.dtype == torch.float32:
         return ATTN_FP32
-    raise AttnError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+    if t.dtype == torch.float16:
+        return ATTN_FP16
+    raise AttnError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
 
 
 def _ptr(t):

@@ -49,7 +49,7 @@ bool stride_ok(int64_t stride, int64_t extent, int64_t vec) {
 }
 
 int check_common(int dtype, int64_t D, float sm_scale) {
-  if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP32 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale) || sm_scale < 0.f) return ATTN_ERR_INVALID;
   if (D != 64 && D != 128) return D <= 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
@@ -78,10 +78,10 @@ struct KernelChoice {
   int threads;  // workgroup size
 };
 
-template <int D, int BN, bool JVP, int NW = 4>
+template <int D, int BN, bool JVP, int NW = 4, bool F16 = false>
 KernelChoice r32() {
   using C = Bf16Cfg<D, BN, JVP, NW>;
-  return {attn_fwd_bf16_kernel<D, BN, JVP, NW>, C::BM, BN, C::LDS, C::THREADS};
+  return {attn_fwd_bf16_kernel<D, BN, JVP, NW, F16>, C::BM, BN, C::LDS, C::THREADS};
 }
 template <int D, bool JVP>
 KernelChoice f32k() { return {attn_fwd_f32_kernel<D, JVP>, F32Cfg<D, JVP>::BM, F32Cfg<D, JVP>::BN, F32Cfg<D, JVP>::LDS, 256}; }
@@ -106,16 +106,20 @@ int cu_count() {
 // workgroups.  The D=128 JVP instance runs one wave per SIMD and is never
 // paired.
 bool use_pairs(int dtype, int D, bool jvp, bool dense_causal, int64_t unpaired_grid) {
-  return dtype == ATTN_BF16 && dense_causal && !(jvp && D == 128) && unpaired_grid <= 4 * (int64_t)cu_count();
+  return dtype != ATTN_FP32 && dense_causal && !(jvp && D == 128) && unpaired_grid <= 4 * (int64_t)cu_count();
+}
+
+template <bool F16>
+KernelChoice choose16(int D, bool jvp, bool paired) {
+  if (paired) return !jvp ? (D == 64 ? r32<64, kBnDense, false, 8, F16>() : r32<128, kBnDense, false, 8, F16>())
+                          : r32<64, kBnJvp, true, 8, F16>();
+  if (!jvp) return D == 64 ? r32<64, kBnDense, false, 4, F16>() : r32<128, kBnDense, false, 4, F16>();
+  return D == 64 ? r32<64, kBnJvp, true, 4, F16>() : r32<128, kBnJvp, true, 4, F16>();
 }
 
 KernelChoice choose(int dtype, int D, bool jvp, bool paired) {
-  if (dtype == ATTN_BF16) {
-    if (paired) return !jvp ? (D == 64 ? r32<64, kBnDense, false, 8>() : r32<128, kBnDense, false, 8>())
-                            : r32<64, kBnJvp, true, 8>();
-    if (!jvp) return D == 64 ? r32<64, kBnDense, false>() : r32<128, kBnDense, false>();
-    return D == 64 ? r32<64, kBnJvp, true>() : r32<128, kBnJvp, true>();
-  }
+  if (dtype == ATTN_BF16) return choose16<false>(D, jvp, paired);
+  if (dtype == ATTN_FP16) return choose16<true>(D, jvp, paired);
   if (!jvp) return D == 64 ? f32k<64, false>() : f32k<128, false>();
   return D == 64 ? f32k<64, true>() : f32k<128, true>();
 }
@@ -138,7 +142,7 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   if (causal && Nq != Nkv) return ATTN_ERR_CAUSAL_SHAPE;
   if (B * H * Nq == 0) return ATTN_OK;
   if (Nq > INT_MAX || Nkv > INT_MAX || B > INT_MAX || H > INT_MAX) return ATTN_ERR_INVALID;
-  const int64_t vec = dtype == ATTN_BF16 ? 8 : 4;
+  const int64_t vec = dtype == ATTN_FP32 ? 4 : 8;
   if (!q || !o || !lse) return ATTN_ERR_INVALID;
   if (Nkv > 0 && (!k || !v)) return ATTN_ERR_INVALID;
   if (jvp && (!to || !tq || (Nkv > 0 && (!tk || !tv)))) return ATTN_ERR_INVALID;
@@ -250,7 +254,7 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   if (num_seqs > INT_MAX - 1 || H > INT_MAX || total_len > INT_MAX) return ATTN_ERR_INVALID;
   if (num_seqs == 0 || H == 0 || total_len == 0) return ATTN_OK;
   if (!q || !k || !v || !o || !lse || !offsets) return ATTN_ERR_INVALID;
-  const int64_t vec = dtype == ATTN_BF16 ? 8 : 4;
+  const int64_t vec = dtype == ATTN_FP32 ? 4 : 8;
   if ((rc = check_s3(q_strides, H, total_len, vec)) || (rc = check_s3(k_strides, H, total_len, vec)) ||
       (rc = check_s3(v_strides, H, total_len, vec)) || (rc = check_s3(o_strides, H, total_len, vec)))
     return rc;

@@ -52,6 +52,34 @@ constexpr float kTau = 8.0f;
 // max|v|, and the rounding errors of P average out in O.
 constexpr int kSplitKeys = 32;
 
+// 16-bit element formats of the MFMA kernels: bf16, or IEEE fp16 when F16.
+// Tiles and fragments move raw 16-bit data in bf16-typed registers either
+// way; only the MFMA opcode and the float <-> 16-bit conversions differ.
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma16(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Round to the element format (to nearest even); the bits in a bf16 slot.
+template <bool F16>
+__device__ __forceinline__ bf16 to16(float x) {
+  if constexpr (F16) return __builtin_bit_cast(bf16, (f16)x);
+  else return (bf16)x;
+}
+
+template <bool F16>
+__device__ __forceinline__ float from16(bf16 x) {
+  if constexpr (F16) return (float)__builtin_bit_cast(f16, x);
+  else return (float)x;
+}
+
 
 // 16-byte-chunk XOR swizzle of a [rows][D] bf16 tile in LDS.  Conflict free
 // for: 16 lanes reading one chunk of 16 different rows (K fragments), the
@@ -187,7 +215,7 @@ __device__ __forceinline__ bf16x8 k_frag_async(uint32_t addr) {
 // head-dim step kk in block 0 of a tile at byte 0.  The reads are inline
 // assembly for the same reason as the V^T reads (they would otherwise be
 // re-addressed every tile), with the same explicit waits.
-template <int D, int NB, bool JVP, int KOFF, int TKOFF>
+template <int D, int NB, bool JVP, int KOFF, int TKOFF, bool F16 = false>
 __device__ __forceinline__ void scores_section(const uint32_t (&kaddr)[D / 16], const bf16x8 (&qf)[D / 16],
                                                const bf16x8 (&tqf)[JVP ? D / 16 : 1], f32x16 (&s)[NB],
                                                f32x16 (&ts)[JVP ? NB : 1]) {
@@ -215,10 +243,10 @@ __device__ __forceinline__ void scores_section(const uint32_t (&kaddr)[D / 16], 
     lds_wait<(later < 15 ? later : 15), F>(ring[i % R]);
     constexpr int b = i / KD, kk = i % KD;
     const bf16x8* f = ring[i % R];
-    s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], qf[kk], s[b], 0, 0, 0);
+    s[b] = mfma16<F16>(f[0], qf[kk], s[b]);
     if constexpr (JVP) {
-      ts[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[F - 1], qf[kk], ts[b], 0, 0, 0);
-      ts[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], tqf[kk], ts[b], 0, 0, 0);
+      ts[b] = mfma16<F16>(f[F - 1], qf[kk], ts[b]);
+      ts[b] = mfma16<F16>(f[0], tqf[kk], ts[b]);
     }
     __builtin_amdgcn_sched_barrier(0);
   });
@@ -231,7 +259,7 @@ __device__ __forceinline__ void scores_section(const uint32_t (&kaddr)[D / 16], 
 // placed after the MFMAs of step i) runs on the vector ALU while the matrix
 // core works through chunk c.  V^T (tV^T) sits at byte VOFF (TVOFF) of LDS;
 // lds_base is the LDS address of byte 0 and vlo/vhi the lane's offsets.
-template <int D, int NB, bool JVP, int VOFF, int TVOFF, class Inter>
+template <int D, int NB, bool JVP, int VOFF, int TVOFF, bool F16 = false, class Inter>
 __device__ __forceinline__ void pv_section(uint32_t lds_base, const int (&vlo)[D / 32], const int (&vhi)[D / 32],
                                            const bf16x8 (&pf)[NB][2], const bf16x8 (&hf)[JVP ? NB : 1][2],
                                            f32x16 (&acc)[D / 32], f32x16 (&accA)[JVP ? D / 32 : 1],
@@ -258,10 +286,10 @@ __device__ __forceinline__ void pv_section(uint32_t lds_base, const int (&vlo)[D
     lds_wait<(later < 15 ? later : 15), F>(ring[i % R]);
     constexpr int db = i % DB, c = i / DB;
     const bf16x8* f = ring[i % R];
-    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], pf[c >> 1][c & 1], acc[db], 0, 0, 0);
+    acc[db] = mfma16<F16>(f[0], pf[c >> 1][c & 1], acc[db]);
     if constexpr (JVP) {
-      accB[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], hf[c >> 1][c & 1], accB[db], 0, 0, 0);
-      accA[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[F - 1], pf[c >> 1][c & 1], accA[db], 0, 0, 0);
+      accB[db] = mfma16<F16>(f[0], hf[c >> 1][c & 1], accB[db]);
+      accA[db] = mfma16<F16>(f[F - 1], pf[c >> 1][c & 1], accA[db]);
     }
     inter(i_tag);
     __builtin_amdgcn_sched_barrier(0);
@@ -273,13 +301,13 @@ __device__ __forceinline__ void pv_section(uint32_t lds_base, const int (&vlo)[D
 // the bf16 rounding residual of P (so P enters O to about 16 bits).  Only
 // waves whose rows attend a few keys run it, on one or two blocks; the
 // compiler schedules its reads.
-template <int D>
+template <int D, bool F16 = false>
 __device__ __forceinline__ void pv_lo_block(const lds_t* vt, const int (&vlo)[D / 32], const int (&vhi)[D / 32],
                                             int b, const bf16x8 (&plo)[2], f32x16 (&acc)[D / 32]) {
 #pragma unroll
   for (int i = 0; i < 2 * (D / 32); ++i) {
     const bf16x8 f = v_frag<D>(vt, 32 * b + 16 * (i & 1), vlo[i >> 1], vhi[i >> 1]);
-    acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, plo[i & 1], acc[i >> 1], 0, 0, 0);
+    acc[i >> 1] = mfma16<F16>(f, plo[i & 1], acc[i >> 1]);
   }
 }
 
@@ -300,7 +328,7 @@ struct Bf16Cfg {
   static_assert(BN % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
 };
 
-template <int D, int BN, bool JVP, int NW_ = 4>
+template <int D, int BN, bool JVP, int NW_ = 4, bool F16 = false>
 __global__ void __launch_bounds__((Bf16Cfg<D, BN, JVP, NW_>::THREADS), (Bf16Cfg<D, BN, JVP, NW_>::WAVES_PER_EU))
 attn_fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BN, JVP, NW_>;
@@ -522,7 +550,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       // S^T = K Q^T (and the tangent scores tQ K^T + Q tK^T)
       f32x16 s[NB];
       f32x16 ts[JVP ? NB : 1];
-      scores_section<D, NB, JVP, S * STAGE, S * STAGE + 2 * TILE>(kaddr, qf, tqf, s, ts);
+      scores_section<D, NB, JVP, S * STAGE, S * STAGE + 2 * TILE, F16>(kaddr, qf, tqf, s, ts);
 
       // mask keys past this row's limit (ragged tail, causal diagonal,
       // jagged truncation) -- only on tiles that reach some row's limit
@@ -575,9 +603,9 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], a.c, nm));
-            plo[r >> 3][r & 7] = (bf16)(p - (float)(bf16)p);
+            plo[r >> 3][r & 7] = to16<F16>(p - from16<F16>(to16<F16>(p)));
           }
-          pv_lo_block<D>(vt, vlo, vhi, b, plo, acc);
+          pv_lo_block<D, F16>(vt, vlo, vhi, b, plo, acc);
         }
       }
 
@@ -591,17 +619,17 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         constexpr int e = decltype(e_tag)::value, b = e / 16, r = e % 16;
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], a.c, -msub));
         l_run += p;
-        pf[b][r >> 3][r & 7] = (bf16)p;
+        pf[b][r >> 3][r & 7] = to16<F16>(p);
         if constexpr (JVP) {
           const float hv = p * ts[b][r];
           r_run += hv;
-          hf[b][r >> 3][r & 7] = (bf16)hv;
+          hf[b][r >> 3][r & 7] = to16<F16>(hv);
         }
       };
       constexpr int EPS = 8 / DB;  // elements of the next chunk per PV step
       static_for<8>(soft);
       // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
-      pv_section<D, NB, JVP, S * STAGE + TILE, S * STAGE + 3 * TILE>(
+      pv_section<D, NB, JVP, S * STAGE + TILE, S * STAGE + 3 * TILE, F16>(
           lds_base, vlo, vhi, pf, hf, acc, accA, accB, [&](auto i_tag) {
             constexpr int i = decltype(i_tag)::value, c = i / DB;
             if constexpr (c + 1 < 2 * NB) {
@@ -655,9 +683,9 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float o = acc[db][4 * g + e] * inv;
-          ov[e] = (bf16)o;
+          ov[e] = to16<F16>(o);
           if constexpr (JVP)
-            tov[e] = (bf16)((accA[db][4 * g + e] + a.sm_scale * accB[db][4 * g + e] - r_tot * o) * inv);
+            tov[e] = to16<F16>((accA[db][4 * g + e] + a.sm_scale * accB[db][4 * g + e] - r_tot * o) * inv);
         }
         *(bf16x4*)(orow + d) = ov;
         if constexpr (JVP) *(bf16x4*)(torow + d) = tov;

@@ -24,7 +24,7 @@ import math
 
 import torch
 
-DTYPES = {"bf16": torch.bfloat16, "fp32": torch.float32}
+DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 
 def _normal(shape, seed, dtype):

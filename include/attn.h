@@ -62,7 +62,13 @@ enum {
   ATTN_ERR_HIP = -5           /* the HIP runtime reported an error while enqueuing */
 };
 
-typedef enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype;
+/*
+ * Element type of q, k, v (and tangents), o, to.  ATTN_BF16 and ATTN_FP16
+ * run on the 16-bit MFMA kernels (P and H rounded to the input format for
+ * their products, fp32 accumulation); ATTN_FP32 runs an fp32 vector-ALU
+ * kernel with no rounding below fp32.  LSE is fp32 in every case.
+ */
+typedef enum attn_dtype { ATTN_BF16 = 0, ATTN_FP32 = 1, ATTN_FP16 = 2 } attn_dtype;
 
 /* Element strides of a dense [B, H, N, D] view. */
 typedef struct attn_strides4 { int64_t b, h, n, d; } attn_strides4;

@@ -14,7 +14,7 @@ from attention_forward_online_attn_amd.binding import Strides3, Strides4
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn.h")
 
 OK, INVALID, UNSUPPORTED, CAUSAL, WORKSPACE = 0, -1, -2, -3, -4
-BF16, FP32 = 0, 1
+BF16, FP32, FP16 = 0, 1, 2
 P = 1 << 20  # a 16-byte aligned fake device address: validation fails before any use
 
 
@@ -68,6 +68,8 @@ def test_dense_validation(lib):
     assert call_fwd(lib, D=96) == UNSUPPORTED
     assert call_fwd(lib, D=0) == INVALID
     assert call_fwd(lib, dtype=5) == UNSUPPORTED
+    assert call_fwd(lib, dtype=FP16, D=96) == UNSUPPORTED
+    assert call_fwd(lib, dtype=FP16, B=0) == OK
     assert call_fwd(lib, causal=1, Nkv=64) == CAUSAL
     assert call_fwd(lib, scale=-0.5) == INVALID
     assert call_fwd(lib, scale=float("nan")) == INVALID
@@ -134,6 +136,7 @@ def test_bwd_validation(lib):
         return lib.attn_bwd(dtype, q, sq, P, sk, P, sk, P, st, P, st, lse, dq, st, P, sk, P, sk,
                             B, H, N, Nkv, D, scale, causal, ws, ws_bytes, None)
     assert call(dtype=FP32) == UNSUPPORTED
+    assert call(dtype=FP16) == UNSUPPORTED
     assert call(D=96) == UNSUPPORTED
     assert call(causal=1, Nkv=64) == CAUSAL
     assert call(ws=0) == WORKSPACE

@@ -18,8 +18,8 @@ from parity import assert_close, host64
 
 pytestmark = pytest.mark.gpu
 
-BF16, FP32 = torch.bfloat16, torch.float32
-DT = {"bf16": BF16, "fp32": FP32}
+BF16, FP32, FP16 = torch.bfloat16, torch.float32, torch.float16
+DT = {"bf16": BF16, "fp32": FP32, "fp16": FP16}
 
 
 def cuda(*ts):
@@ -325,3 +325,38 @@ def test_jvp_tlse(gpu_lib, dtype, causal):
     # without the request nothing else changes
     o2, to2, lse2 = attn.fwd_jvp(*cuda(*ts), causal=causal)
     assert torch.equal(o, o2) and torch.equal(to, to2) and torch.equal(lse, lse2)
+
+
+
+# ------------------------------------------------------------- fp16 inputs
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_dense(gpu_lib, D, causal):
+    """fp16 inputs on the 16-bit MFMA kernels (fp16 products, P rounded to fp16)."""
+    dense_case(2, 3, 300, 300, D, "fp16", causal, seed=40 + D)
+    dense_case(1, 2, 1000, 1000, D, "fp16", causal, seed=41 + D)
+
+
+def test_fp16_cross_attention_and_tails(gpu_lib):
+    dense_case(2, 2, 77, 333, 64, "fp16", False, seed=42)
+    dense_case(1, 1, 1, 1, 128, "fp16", False, seed=43)
+    dense_case(1, 2, 129, 129, 128, "fp16", True, seed=44)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_jvp(gpu_lib, causal):
+    jvp_case(2, 3, 400, 400, 64, "fp16", causal, seed=45)
+    jvp_case(1, 2, 200, 200, 128, "fp16", causal, seed=46)
+
+
+def test_fp16_jagged(gpu_lib):
+    jagged_case([5, 0, 300, 64, 129], 3, 128, "fp16", 256, seed=47)
+    jagged_case([33, 1000], 2, 64, "fp16", 1024, True, seed=48)
+
+
+def test_fp16_paired_causal_grid(gpu_lib):
+    """A small causal grid takes the paired 8-wave instances."""
+    dense_case(2, 2, 640, 640, 64, "fp16", True, seed=49)
+    dense_case(2, 2, 640, 640, 128, "fp16", True, seed=50)
