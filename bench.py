@@ -19,7 +19,7 @@ launch, outside the events, which evicts L2 and the Infinity Cache).  `cpu_basel
 sample of the same workload (a few heads) on this host's cores.
 
 Profiling modes (for rocprofv3 runs): --only {fwd,fwd_causal,jvp,jvp_causal,
-causal_d64,jagged,bwd,bwd_causal} runs just that workload K times; --copy-calibration runs a
+causal_d64,jagged,bwd,bwd_causal,fwd_fp16} runs just that workload K times; --copy-calibration runs a
 plain device copy of known size (the scale for FETCH_SIZE / WRITE_SIZE).
 """
 
@@ -86,6 +86,12 @@ def make_cases(torch, attn, wl):
         cases[nm] = Case(nm, (lambda c=causal: attn.fwd(q, k, v, causal=c, sm_scale=w.sm_scale)),
                          dense_flops(w.B, w.H, w.N, w.N, w.D, causal), io_bytes,
                          f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} bf16 causal={causal}")
+
+    # the headline shape with fp16 inputs (same 16-bit MFMA peak)
+    qh, kh, vh = (t.to(dev) for t in wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "fp16", 0))
+    cases["fwd_fp16"] = Case("fwd_fp16", lambda: attn.fwd(qh, kh, vh, causal=False, sm_scale=w.sm_scale),
+                             dense_flops(w.B, w.H, w.N, w.N, w.D, False), io_bytes,
+                             f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} fp16 causal=False")
 
     w4 = wl.WORKLOADS["jvp_d64"]
     ts = [t.to(dev) for t in wl.dense_inputs(w4.B, w4.H, w4.N, w4.N, w4.D, "bf16", 0, tangents=True)]
@@ -267,7 +273,7 @@ def main():
                 "cold_tflops": round(c.flops / (mc * 1e-3) / 1e12, 2)}
 
     extra = {"fwd": summary(head, durs, time_launches(torch, head, n_cold, 2, flush)[0])}
-    for name in ("fwd_causal", "jvp", "jvp_causal", "causal_d64", "jagged", "bwd", "bwd_causal"):
+    for name in ("fwd_causal", "fwd_fp16", "jvp", "jvp_causal", "causal_d64", "jagged", "bwd", "bwd_causal"):
         c = cases[name]
         dw, _ = time_launches(torch, c, max(5, args.steps // 2), 10)
         dc, _ = time_launches(torch, c, n_cold, 2, flush)
@@ -297,7 +303,7 @@ def main():
         "jvp_value": extra["jvp"]["tflops"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128,64,false,4>",
+                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128,64,false,4,false>",
                      "avg_launch_ms": round(avg, 4), "min_launch_ms": round(mn, 4)},
         "extra": extra,
     }

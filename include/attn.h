@@ -23,13 +23,14 @@
  *   default stream).  Calls are asynchronous: nothing synchronises the host.
  * - Strides are in ELEMENTS.  The innermost (head-dim) stride must be 1.
  *   Base pointers must be 16-byte aligned and every other stride a multiple of
- *   16 bytes (8 bf16 elements, 4 fp32 elements); contiguous torch tensors
- *   satisfy this.  Anything else is ATTN_ERR_UNSUPPORTED.
+ *   16 bytes (8 bf16 or fp16 elements, 4 fp32 elements); contiguous torch
+ *   tensors satisfy this.  Anything else is ATTN_ERR_UNSUPPORTED.
  * - Tangent tensors (JVP) share the strides of their primals, and tO shares
  *   the strides of O (as the JVP page's wrapper requires).
- * - Supported head dims: 64 and 128.  dtype ATTN_BF16 computes the products on
- *   bf16 MFMA with fp32 accumulation and rounds O/tO to bf16 (RNE); ATTN_FP32
- *   computes everything in fp32.  LSE is always fp32.
+ * - Supported head dims: 64 and 128.  dtype ATTN_BF16 (ATTN_FP16) computes
+ *   the products on bf16 (fp16) MFMA with fp32 accumulation and rounds O/tO to
+ *   the input format (RNE); ATTN_FP32 computes everything in fp32.  LSE is
+ *   always fp32.
  * - sm_scale must be finite and >= 0 (every page uses a positive scale,
  *   by default D^-0.5).
  * - A query row with no key to attend (Nkv == 0, or a jagged row beyond
@@ -180,7 +181,7 @@ ATTN_API size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
  * Strides, alignment, sm_scale, causal (Nq == Nkv) and D in {64, 128} as for
  * attn_fwd.  P and dS are rounded to bf16 for their products, with fp32
  * accumulation.  Each output element is written by exactly one thread: the
- * result is deterministic.  ATTN_FP32 returns ATTN_ERR_UNSUPPORTED.  Three
+ * result is deterministic.  ATTN_FP32 and ATTN_FP16 return ATTN_ERR_UNSUPPORTED.  Three
  * kernels are enqueued on `stream`; B*H*(Nq+Nkv) == 0 is a no-op.
  */
 ATTN_API int attn_bwd(attn_dtype dtype,
