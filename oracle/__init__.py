@@ -31,6 +31,15 @@ those kernels is an exact identity, so the streamed result equals this one):
   [offsets[s], offsets[s+1]); only its first min(len_s, max_seq_len) rows take
   part, as queries and as keys; there is no attention across sequences.
 
+* Additive bias and boolean mask -- flash attention with bias page
+  (``flash_attention.py``), ``_attn_fwd_inner`` and ``_flash_attn_fwd``: a
+  float bias [B, H, Nq, Nkv] is added to the scores in natural-log units (the
+  wrapper divides it by ln 2 before the kernel's base-2 add, so the two
+  agree), a boolean mask keeps key j for query i only where it is True:
+      S = sm_scale * Q K^T + bias,   S_ij = -inf where mask_ij is False
+  Both combine with the causal mask.  The bias has no tangent (it is not an
+  input of the JVP), so tS is unchanged; its gradient is dS.
+
 * Backward (the gradient of the forward above for a loss L with dL/dO = dO) --
   Triton fused attention tutorial with JVP, ``_attn_bwd_preprocess``,
   ``_attn_bwd_dkdv``, ``_attn_bwd_dq`` (the steps, in that page's order):
@@ -51,6 +60,10 @@ design notes):
   normalisation is not applied here: O = softmax(S) V like every other page.
 * The jagged page applies no sm_scale; here the caller passes one (1.0
   reproduces that page's raw logits).
+* The bias page masks with an additive -1e6, so a row whose mask is all
+  False would attend every key; here masked scores are exactly -inf and such
+  a row is empty (O = 0, LSE = -inf) like every other row without keys.  A
+  bias of -inf masks its key the same way.
 
 Everything is computed in float64 from the exact values the GPU receives
 (bf16 -> fp64 and fp32 -> fp64 are exact); ``sm_scale`` is taken as the fp32
@@ -74,6 +87,8 @@ __all__ = [
     "attend_rows_bwd",
     "attention_bwd",
     "jagged_attention_bwd",
+    "dense_bias",
+    "dense_mask",
 ]
 
 # Rows of S materialised at a time.  Only bounds memory: every row is still
@@ -97,7 +112,8 @@ def scale_as_passed(sm_scale: float) -> float:
 
 
 def attend_rows(q, k, v, sm_scale, causal=False, row_pos=None,
-                tq=None, tk=None, tv=None, kv_len=None, with_tlse=False):
+                tq=None, tk=None, tv=None, kv_len=None, with_tlse=False,
+                bias=None, mask=None):
     """Attention of some query rows of one (batch, head) over all its keys.
 
     q:  [M, D] query rows;  k: [N, D];  v: [N, Dv].
@@ -109,9 +125,15 @@ def attend_rows(q, k, v, sm_scale, causal=False, row_pos=None,
              tO is returned as well.
     with_tlse: with tangents, also return the tangent of LSE,
              rho_i = sum_j P_ij tS_ij (0 for a row without keys).
+    bias:    [M, N] optional float bias added to the scaled scores.
+    mask:    [M, N] optional bool; False masks the key for that row.
     Returns (o [M, Dv], lse [M]), (o, to, lse) or (o, to, lse, tlse).
     """
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    if bias is not None:
+        bias = as_f64(bias)
+    if mask is not None:
+        mask = np.asarray(mask, dtype=bool)
     M, N = q.shape[0], k.shape[0]
     scale = float(sm_scale)
     jvp = tq is not None
@@ -137,9 +159,14 @@ def attend_rows(q, k, v, sm_scale, causal=False, row_pos=None,
     cols = np.arange(N)
     for r0 in range(0, M, _ROW_BLOCK):
         r1 = min(M, r0 + _ROW_BLOCK)
-        # scores S = sm_scale * Q K^T for this block of rows
+        # scores S = sm_scale * Q K^T (+ bias) for this block of rows
         s = scale * (q[r0:r1] @ k.T)
         allowed = np.ones_like(s, dtype=bool)
+        if bias is not None:
+            s = s + bias[r0:r1]
+            allowed &= bias[r0:r1] != -np.inf  # a -inf bias masks the key
+        if mask is not None:
+            allowed &= mask[r0:r1]
         if causal:  # query i attends key j only for j <= i
             allowed &= cols[None, :] <= row_pos[r0:r1, None]
         if kv_len is not None:
@@ -174,27 +201,50 @@ def _check_dense(q, k, v, causal):
         raise ValueError("causal attention needs Nq == Nkv (top-left aligned mask)")
 
 
-def attention(q, k, v, sm_scale, causal=False):
-    """Dense attention forward.  q: [B,H,Nq,D], k/v: [B,H,Nkv,D].
+def dense_bias(bias, B, H, Nq, Nkv):
+    """A float bias broadcast to [B, H, Nq, Nkv] (float64), or None."""
+    return None if bias is None else np.broadcast_to(as_f64(bias), (B, H, Nq, Nkv))
+
+
+def dense_mask(mask, B, H, Nq, Nkv):
+    """A boolean mask (any nonzero value keeps the key) broadcast to
+    [B, H, Nq, Nkv], or None."""
+    if mask is None:
+        return None
+    if hasattr(mask, "detach"):
+        mask = mask.detach().cpu().numpy()
+    return np.broadcast_to(np.asarray(mask) != 0, (B, H, Nq, Nkv))
+
+
+def attention(q, k, v, sm_scale, causal=False, bias=None, mask=None):
+    """Dense attention forward.  q: [B,H,Nq,D], k/v: [B,H,Nkv,D]; optional
+    bias / mask broadcastable to [B,H,Nq,Nkv].
     Returns (o [B,H,Nq,Dv], lse [B,H,Nq]) in float64."""
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     _check_dense(q, k, v, causal)
     B, H, Nq, _ = q.shape
+    Nkv = k.shape[2]
+    bias, mask = dense_bias(bias, B, H, Nq, Nkv), dense_mask(mask, B, H, Nq, Nkv)
     o = np.zeros((B, H, Nq, v.shape[3]))
     lse = np.zeros((B, H, Nq))
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = attend_rows(q[b, h], k[b, h], v[b, h], sm_scale, causal)
+            o[b, h], lse[b, h] = attend_rows(q[b, h], k[b, h], v[b, h], sm_scale, causal,
+                                             bias=None if bias is None else bias[b, h],
+                                             mask=None if mask is None else mask[b, h])
     return o, lse
 
 
-def attention_jvp(q, k, v, tq, tk, tv, sm_scale, causal=False, with_tlse=False):
-    """Dense attention forward with its forward-mode JVP.
+def attention_jvp(q, k, v, tq, tk, tv, sm_scale, causal=False, with_tlse=False, bias=None, mask=None):
+    """Dense attention forward with its forward-mode JVP (bias and mask as in
+    ``attention``; the bias has no tangent).
     Returns (o, to, lse), or (o, to, lse, tlse) with with_tlse, in float64."""
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     tq, tk, tv = as_f64(tq), as_f64(tk), as_f64(tv)
     _check_dense(q, k, v, causal)
     B, H, Nq, _ = q.shape
+    Nkv = k.shape[2]
+    bias, mask = dense_bias(bias, B, H, Nq, Nkv), dense_mask(mask, B, H, Nq, Nkv)
     o = np.zeros((B, H, Nq, v.shape[3]))
     to = np.zeros_like(o)
     lse = np.zeros((B, H, Nq))
@@ -203,18 +253,22 @@ def attention_jvp(q, k, v, tq, tk, tv, sm_scale, causal=False, with_tlse=False):
         for h in range(H):
             o[b, h], to[b, h], lse[b, h], tlse[b, h] = attend_rows(
                 q[b, h], k[b, h], v[b, h], sm_scale, causal,
-                tq=tq[b, h], tk=tk[b, h], tv=tv[b, h], with_tlse=True)
+                tq=tq[b, h], tk=tk[b, h], tv=tv[b, h], with_tlse=True,
+                bias=None if bias is None else bias[b, h], mask=None if mask is None else mask[b, h])
     return (o, to, lse, tlse) if with_tlse else (o, to, lse)
 
 
-def attention_sampled(q, k, v, sm_scale, causal, rows, tangents=None):
+def attention_sampled(q, k, v, sm_scale, causal, rows, tangents=None, bias=None, mask=None):
     """Dense attention evaluated only at sampled outputs.
 
     rows: iterable of (b, h, i) query coordinates.  Each one is computed from
     its own full row of scores, so large problems can be checked row by row.
+    bias / mask as in ``attention``.
     Returns (o [R, Dv], lse [R]) or, with tangents=(tq, tk, tv), (o, to, lse).
     """
     rows = list(rows)
+    B, H, Nq, Nkv = q.shape[0], q.shape[1], q.shape[2], k.shape[2]
+    bias, mask = dense_bias(bias, B, H, Nq, Nkv), dense_mask(mask, B, H, Nq, Nkv)
     R = len(rows)
     o = np.zeros((R, v.shape[3]))
     lse = np.zeros(R)
@@ -224,6 +278,10 @@ def attention_sampled(q, k, v, sm_scale, causal, rows, tangents=None):
         if tangents is not None:
             tq, tk, tv = tangents
             kw = dict(tq=as_f64(tq[b, h, i:i + 1]), tk=as_f64(tk[b, h]), tv=as_f64(tv[b, h]))
+        if bias is not None:
+            kw["bias"] = bias[b, h, i:i + 1]
+        if mask is not None:
+            kw["mask"] = mask[b, h, i:i + 1]
         res = attend_rows(as_f64(q[b, h, i:i + 1]), as_f64(k[b, h]), as_f64(v[b, h]),
                           sm_scale, causal, row_pos=[i], **kw)
         if tangents is not None:
@@ -282,15 +340,22 @@ def jagged_attention_jvp(q, k, v, tq, tk, tv, offsets, max_seq_len, sm_scale, ca
     return _jagged(q, k, v, offsets, max_seq_len, sm_scale, causal, (tq, tk, tv))
 
 
-def attend_rows_bwd(q, k, v, do, sm_scale, causal=False, row_pos=None, kv_len=None):
+def attend_rows_bwd(q, k, v, do, sm_scale, causal=False, row_pos=None, kv_len=None,
+                    bias=None, mask=None, with_dbias=False):
     """Backward of ``attend_rows`` for some query rows of one (batch, head).
 
     q: [M, D], k: [N, D], v: [N, Dv], do: [M, Dv] (the gradient of the loss
     with respect to those rows of O).  row_pos / kv_len as in attend_rows.
-    Returns (dq [M, D], dk [N, D], dv [N, Dv]); dk and dv collect the
-    contributions of the given rows only.
+    bias / mask as in attend_rows; with_dbias also returns dbias [M, N] = dS,
+    the gradient with respect to the bias (0 where masked).
+    Returns (dq [M, D], dk [N, D], dv [N, Dv]) (+ dbias); dk and dv collect
+    the contributions of the given rows only.
     """
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    if bias is not None:
+        bias = as_f64(bias)
+    if mask is not None:
+        mask = np.asarray(mask, dtype=bool)
     M, N = q.shape[0], k.shape[0]
     scale = float(sm_scale)
     if row_pos is None:
@@ -299,8 +364,13 @@ def attend_rows_bwd(q, k, v, do, sm_scale, causal=False, row_pos=None, kv_len=No
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    dbias = np.zeros((M, N))
+
+    def result():
+        return (dq, dk, dv, dbias) if with_dbias else (dq, dk, dv)
+
     if N == 0 or M == 0:
-        return dq, dk, dv
+        return result()
 
     cols = np.arange(N)
     for r0 in range(0, M, _ROW_BLOCK):
@@ -308,6 +378,11 @@ def attend_rows_bwd(q, k, v, do, sm_scale, causal=False, row_pos=None, kv_len=No
         # forward of these rows: S, the mask and P = softmax(S)
         s = scale * (q[r0:r1] @ k.T)
         allowed = np.ones_like(s, dtype=bool)
+        if bias is not None:
+            s = s + bias[r0:r1]
+            allowed &= bias[r0:r1] != -np.inf
+        if mask is not None:
+            allowed &= mask[r0:r1]
         if causal:  # key j is seen by query i only for i >= j
             allowed &= row_pos[r0:r1, None] >= cols[None, :]
         if kv_len is not None:
@@ -328,20 +403,30 @@ def attend_rows_bwd(q, k, v, do, sm_scale, causal=False, row_pos=None, kv_len=No
         ds = p * (dp - delta[:, None])
         dq[r0:r1] = scale * (ds @ k)
         dk += scale * (ds.T @ q[r0:r1])
-    return dq, dk, dv
+        dbias[r0:r1] = ds
+    return result()
 
 
-def attention_bwd(q, k, v, do, sm_scale, causal=False):
-    """Dense attention backward.  q: [B,H,Nq,D], k/v: [B,H,Nkv,D], do: [B,H,Nq,Dv].
-    Returns (dq, dk, dv) in float64, shaped like q, k, v."""
+def attention_bwd(q, k, v, do, sm_scale, causal=False, bias=None, mask=None, with_dbias=False):
+    """Dense attention backward.  q: [B,H,Nq,D], k/v: [B,H,Nkv,D], do: [B,H,Nq,Dv];
+    bias / mask as in ``attention``.
+    Returns (dq, dk, dv) in float64, shaped like q, k, v, and with with_dbias
+    also dbias [B,H,Nq,Nkv] = dS (sum it over broadcast dimensions for the
+    gradient of a broadcast bias)."""
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     _check_dense(q, k, v, causal)
-    B, H = q.shape[:2]
+    B, H, Nq = q.shape[:3]
+    Nkv = k.shape[2]
+    bias, mask = dense_bias(bias, B, H, Nq, Nkv), dense_mask(mask, B, H, Nq, Nkv)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dbias = np.zeros((B, H, Nq, Nkv))
     for b in range(B):
         for h in range(H):
-            dq[b, h], dk[b, h], dv[b, h] = attend_rows_bwd(q[b, h], k[b, h], v[b, h], do[b, h], sm_scale, causal)
-    return dq, dk, dv
+            res = attend_rows_bwd(q[b, h], k[b, h], v[b, h], do[b, h], sm_scale, causal,
+                                  bias=None if bias is None else bias[b, h],
+                                  mask=None if mask is None else mask[b, h], with_dbias=True)
+            dq[b, h], dk[b, h], dv[b, h], dbias[b, h] = res
+    return (dq, dk, dv, dbias) if with_dbias else (dq, dk, dv)
 
 
 def jagged_attention_bwd(q, k, v, do, offsets, max_seq_len, sm_scale, causal=False):

@@ -43,6 +43,16 @@ MUTANTS = {
     "bwd_dp_wrong_operand": ("dp = g @ v.T", "dp = g @ k.T"),
     "bwd_causal_dropped": ("allowed &= row_pos[r0:r1, None] >= cols[None, :]", "pass"),
     "bwd_delta_from_wrong_rows": ("delta = (o * g).sum(axis=1)", "delta = (o * g).sum(axis=0).sum() / o.shape[0] + 0 * g[:, 0]"),
+    # additive bias and boolean mask
+    "bias_sign": ("s = s + bias[r0:r1]", "s = s - bias[r0:r1]"),
+    "bias_log2_units": ("s = s + bias[r0:r1]", "s = s + bias[r0:r1] / np.log(2.0)"),
+    "bias_times_scale": ("s = s + bias[r0:r1]", "s = s + scale * bias[r0:r1]"),
+    "bias_transposed": ("bias=None if bias is None else bias[b, h],\n", "bias=None if bias is None else bias[b, h].T,\n"),
+    "mask_inverted": ("allowed &= mask[r0:r1]", "allowed &= ~mask[r0:r1]"),
+    "mask_ignored": ("allowed &= mask[r0:r1]", "pass"),
+    "neg_inf_bias_not_masked": ("allowed &= bias[r0:r1] != -np.inf  # a -inf bias masks the key", "pass"),
+    "bwd_bias_dropped": ("            s = s + bias[r0:r1]\n            allowed &= bias[r0:r1] != -np.inf\n", "            pass\n"),
+    "dbias_is_p": ("dbias[r0:r1] = ds", "dbias[r0:r1] = p"),
 }
 
 
@@ -107,6 +117,42 @@ def _pins_hold(m) -> bool:
             if not np.allclose(o[:, a:a + u], od, atol=1e-12, rtol=0):
                 return False
             if not (np.all(o[:, a + u:b] == 0) and np.all(np.isneginf(lse[:, a + u:b]))):
+                return False
+        # bias and mask: torch's attention with the same attn_mask, a fully
+        # masked row, a -inf bias row, and the gradients (bias included)
+        bq, bk, bv = rnd((1, 2, 5, 4), 21), rnd((1, 2, 7, 4), 22), rnd((1, 2, 7, 4), 23)
+        bias, msk = rnd((1, 2, 5, 7), 24), np.random.default_rng(25).random((1, 2, 5, 7)) < 0.6
+        msk[..., 1] = True
+        o, _ = m.attention(bq, bk, bv, 0.6, bias=bias, mask=msk)
+        tt = [torch.from_numpy(x) for x in (bq, bk, bv)]
+        with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                *tt, attn_mask=torch.from_numpy(np.where(msk, bias, -np.inf)), scale=0.6).numpy()
+        if not np.allclose(o, ref, atol=1e-12, rtol=0):
+            return False
+        sq, sk, sv = rnd((1, 1, 6, 4), 26), rnd((1, 1, 6, 4), 27), rnd((1, 1, 6, 4), 28)
+        ob, lb = m.attention(sq, sk, sv, 0.5, bias=rnd((1, 1, 6, 6), 29))
+        ot, lt = m.attention(sq, sk, sv, 0.5, bias=rnd((1, 1, 6, 6), 29).transpose(0, 1, 3, 2))
+        sb = rnd((1, 1, 6, 6), 29)
+        with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+            rb = torch.nn.functional.scaled_dot_product_attention(
+                *[torch.from_numpy(x) for x in (sq, sk, sv)], attn_mask=torch.from_numpy(sb), scale=0.5).numpy()
+        if not np.allclose(ob, rb, atol=1e-12, rtol=0):
+            return False
+        em = np.ones((1, 1, 6, 6), bool)
+        em[0, 0, 2] = False
+        oe, le = m.attention(sq, sk, sv, 0.5, mask=em)
+        oi, li = m.attention(sq, sk, sv, 0.5, bias=np.where(em, 0.0, -np.inf))
+        for oo_, ll_ in ((oe, le), (oi, li)):
+            if not (np.all(oo_[0, 0, 2] == 0) and np.isneginf(ll_[0, 0, 2]) and np.all(np.isfinite(oo_))):
+                return False
+        bd = rnd((1, 2, 5, 4), 30)
+        tb = [torch.from_numpy(x).requires_grad_(True) for x in (bq, bk, bv, bias)]
+        sc = (0.6 * tb[0] @ tb[1].transpose(-1, -2) + tb[3]).masked_fill(torch.from_numpy(~msk), float("-inf"))
+        (torch.softmax(sc, dim=-1) @ tb[2]).backward(torch.from_numpy(bd))
+        got = m.attention_bwd(bq, bk, bv, bd, 0.6, bias=bias, mask=msk, with_dbias=True)
+        for g, r in zip(got, tb):
+            if not np.allclose(g, r.grad.numpy(), atol=1e-12, rtol=0):
                 return False
         return True
     except Exception:
