@@ -1,6 +1,6 @@
-"""MI355X (gfx950) fused attention forward: dense, causal, forward-mode JVP and
-jagged multi-head variants, and the dense backward, behind the C ABI declared
-in include/attn.h.
+"""MI355X (gfx950) fused attention forward: dense, causal, forward-mode JVP,
+additive bias / boolean mask and jagged multi-head variants, and the dense
+backward, behind the C ABI declared in include/attn.h.
 
 The Python layer only marshals arguments: every step of the computation runs
 in the HIP kernels of libattn_mi355x.so.  torch supplies device memory and the
@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     bwd,
     bwd_workspace_bytes,
     fwd,
+    fwd_bias,
     fwd_jvp,
     jagged_fwd,
     jagged_workspace_bytes,

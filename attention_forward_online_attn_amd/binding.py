@@ -19,6 +19,8 @@ _lib = None
 ATTN_BF16 = 0
 ATTN_FP32 = 1
 ATTN_FP16 = 2
+ATTN_BIAS_ADD = 1
+ATTN_BIAS_MASK = 2
 
 
 class AttnError(RuntimeError):
@@ -56,6 +58,9 @@ def load_library():
     lib.attn_fwd.argtypes = [i32, vp, S4, vp, S4, vp, S4, vp, S4, vp,
                              i64, i64, i64, i64, i64, f32, i32, vp]
     lib.attn_fwd.restype = i32
+    lib.attn_fwd_bias.argtypes = [i32, vp, S4, vp, S4, vp, S4, vp, S4, vp, vp, i32, S4,
+                                  i64, i64, i64, i64, i64, f32, i32, vp]
+    lib.attn_fwd_bias.restype = i32
     lib.attn_fwd_jvp.argtypes = [i32, vp, vp, vp, vp, vp, vp, S4, S4, S4, vp, vp, S4, vp, vp,
                                  i64, i64, i64, i64, i64, f32, i32, vp]
     lib.attn_fwd_jvp.restype = i32
@@ -128,6 +133,35 @@ def fwd(q, k, v, causal=False, sm_scale=None):
     _check(lib.attn_fwd(_dtype_code(q), _ptr(q), _s4(q), _ptr(k), _s4(k), _ptr(v), _s4(v),
                         _ptr(o), _s4(o), _ptr(lse), B, H, Nq, Nkv, D,
                         float(sm_scale), int(bool(causal)), _stream(q)))
+    return o, lse
+
+
+def fwd_bias(q, k, v, bias=None, mask=None, causal=False, sm_scale=None):
+    """Dense forward with an additive bias (dtype of q) or a boolean mask
+    (torch.bool or uint8; False / 0 removes the key), either broadcastable to
+    [B,H,Nq,Nkv] with the key dimension contiguous; broadcast dimensions are
+    passed as stride 0, never materialised.  -> (o, lse) as fwd."""
+    lib = load_library()
+    _same(q, k, v)
+    if (bias is None) == (mask is None):
+        raise AttnError("pass exactly one of bias and mask")
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if bias is not None:
+        if bias.dtype != q.dtype or bias.device != q.device:
+            raise AttnError("bias must have the dtype and device of q")
+        op, kind = bias.expand(B, H, Nq, Nkv), ATTN_BIAS_ADD
+    else:
+        if mask.dtype not in (torch.bool, torch.uint8) or mask.device != q.device:
+            raise AttnError("mask must be a bool or uint8 tensor on the device of q")
+        op, kind = mask.expand(B, H, Nq, Nkv), ATTN_BIAS_MASK
+    o = torch.empty((B, H, Nq, D), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check(lib.attn_fwd_bias(_dtype_code(q), _ptr(q), _s4(q), _ptr(k), _s4(k), _ptr(v), _s4(v),
+                             _ptr(o), _s4(o), _ptr(lse), _ptr(op), kind, _s4(op), B, H, Nq, Nkv, D,
+                             float(sm_scale), int(bool(causal)), _stream(q)))
     return o, lse
 
 

@@ -78,13 +78,15 @@ struct KernelChoice {
   int threads;  // workgroup size
 };
 
-template <int D, int BN, bool JVP, int NW = 4, bool F16 = false>
+template <int D, int BN, bool JVP, int NW = 4, bool F16 = false, int BIAS = kNoBias>
 KernelChoice r32() {
   using C = Bf16Cfg<D, BN, JVP, NW>;
-  return {attn_fwd_bf16_kernel<D, BN, JVP, NW, F16>, C::BM, BN, C::LDS, C::THREADS};
+  return {attn_fwd_bf16_kernel<D, BN, JVP, NW, F16, BIAS>, C::BM, BN, C::LDS, C::THREADS};
 }
-template <int D, bool JVP>
-KernelChoice f32k() { return {attn_fwd_f32_kernel<D, JVP>, F32Cfg<D, JVP>::BM, F32Cfg<D, JVP>::BN, F32Cfg<D, JVP>::LDS, 256}; }
+template <int D, bool JVP, int BIAS = kNoBias>
+KernelChoice f32k() {
+  return {attn_fwd_f32_kernel<D, JVP, BIAS>, F32Cfg<D, JVP>::BM, F32Cfg<D, JVP>::BN, F32Cfg<D, JVP>::LDS, 256};
+}
 
 // Compute units of the current device (queried once per device).
 int cu_count() {
@@ -117,7 +119,19 @@ KernelChoice choose16(int D, bool jvp, bool paired) {
   return D == 64 ? r32<64, kBnJvp, true, 4, F16>() : r32<128, kBnJvp, true, 4, F16>();
 }
 
-KernelChoice choose(int dtype, int D, bool jvp, bool paired) {
+// Biased forward (no JVP, never paired): one instance per dtype, D and kind.
+template <int BIAS>
+KernelChoice choose_bias(int dtype, int D) {
+  if (dtype == ATTN_BF16)
+    return D == 64 ? r32<64, kBnDense, false, 4, false, BIAS>() : r32<128, kBnDense, false, 4, false, BIAS>();
+  if (dtype == ATTN_FP16)
+    return D == 64 ? r32<64, kBnDense, false, 4, true, BIAS>() : r32<128, kBnDense, false, 4, true, BIAS>();
+  return D == 64 ? f32k<64, false, BIAS>() : f32k<128, false, BIAS>();
+}
+
+KernelChoice choose(int dtype, int D, bool jvp, bool paired, int bias_kind) {
+  if (bias_kind == kAddBias) return choose_bias<kAddBias>(dtype, D);
+  if (bias_kind == kMaskBias) return choose_bias<kMaskBias>(dtype, D);
   if (dtype == ATTN_BF16) return choose16<false>(D, jvp, paired);
   if (dtype == ATTN_FP16) return choose16<true>(D, jvp, paired);
   if (!jvp) return D == 64 ? f32k<64, false>() : f32k<128, false>();
@@ -132,10 +146,17 @@ int launch(const KernelChoice& k, int grid, hipStream_t stream, const FwdArgs& a
   return ATTN_OK;
 }
 
+// Optional bias / mask operand of the dense forward.
+struct BiasOperand {
+  const void* ptr = nullptr;
+  int kind = kNoBias;
+  attn_strides4 strides = {0, 0, 0, 1};
+};
+
 int dense(int dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk, const void* tv,
           attn_strides4 sq, attn_strides4 sk, attn_strides4 sv, void* o, void* to, attn_strides4 so, float* lse,
           float* tlse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal,
-          void* stream, bool jvp) {
+          void* stream, bool jvp, const BiasOperand& bias = BiasOperand()) {
   int rc = check_common(dtype, D, sm_scale);
   if (rc) return rc;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
@@ -151,10 +172,18 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   const void* ptrs[] = {q, k, v, o, tq, tk, tv, to};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  if (bias.kind != kNoBias && Nkv > 0) {
+    // additive bias: 16-byte chunks of the input element type; mask: 8-byte chunks
+    const int64_t bvec = bias.kind == kAddBias ? vec : 8;
+    if (!bias.ptr) return ATTN_ERR_INVALID;
+    if ((rc = check_s4(bias.strides, B, H, Nq, bvec))) return rc;
+    if ((reinterpret_cast<uintptr_t>(bias.ptr) & (bias.kind == kAddBias ? 15u : 7u)) != 0) return ATTN_ERR_UNSUPPORTED;
+  }
+  const int bias_kind = Nkv > 0 ? bias.kind : kNoBias;  // no key: nothing to read
 
   const int64_t n_qtiles = (Nq + 127) / 128;  // every bf16 instance uses 128-row q-tiles
-  const bool paired = use_pairs(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
-  const KernelChoice kc = choose(dtype, (int)D, jvp, paired);
+  const bool paired = bias_kind == kNoBias && use_pairs(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
+  const KernelChoice kc = choose(dtype, (int)D, jvp, paired, bias_kind);
   const int BM = kc.BM;
   const int64_t n_qtiles_k = (Nq + BM - 1) / BM;
   const int64_t grid = B * H * (paired ? (n_qtiles_k + 1) / 2 : n_qtiles_k);
@@ -166,6 +195,10 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   a.k_sb = sk.b; a.k_sh = sk.h; a.k_sn = sk.n;
   a.v_sb = sv.b; a.v_sh = sv.h; a.v_sn = sv.n;
   a.o_sb = so.b; a.o_sh = so.h; a.o_sn = so.n;
+  if (bias_kind != kNoBias) {
+    a.bias = bias.ptr;
+    a.bias_sb = bias.strides.b; a.bias_sh = bias.strides.h; a.bias_sn = bias.strides.n;
+  }
   a.B = (int)B; a.H = (int)H; a.Nq = (int)Nq; a.Nkv = (int)Nkv;
   a.n_qtiles = (int)n_qtiles_k;
   a.paired = paired ? 1 : 0;
@@ -229,6 +262,19 @@ int attn_fwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const voi
                o_strides, lse, nullptr, B, H, Nq, Nkv, D, sm_scale, causal, stream, false);
 }
 
+int attn_fwd_bias(attn_dtype dtype, const void* q, attn_strides4 q_strides, const void* k, attn_strides4 k_strides,
+                  const void* v, attn_strides4 v_strides, void* o, attn_strides4 o_strides, float* lse,
+                  const void* bias, attn_bias_kind bias_kind, attn_strides4 bias_strides, int64_t B, int64_t H,
+                  int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal, void* stream) {
+  if (bias_kind != ATTN_BIAS_ADD && bias_kind != ATTN_BIAS_MASK) return ATTN_ERR_UNSUPPORTED;
+  BiasOperand b;
+  b.ptr = bias;
+  b.kind = bias_kind == ATTN_BIAS_ADD ? kAddBias : kMaskBias;
+  b.strides = bias_strides;
+  return dense((int)dtype, q, k, v, nullptr, nullptr, nullptr, q_strides, k_strides, v_strides, o, nullptr,
+               o_strides, lse, nullptr, B, H, Nq, Nkv, D, sm_scale, causal, stream, false, b);
+}
+
 int attn_fwd_jvp(attn_dtype dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk,
                  const void* tv, attn_strides4 q_strides, attn_strides4 k_strides, attn_strides4 v_strides, void* o,
                  void* to, attn_strides4 o_strides, float* lse, float* tlse, int64_t B, int64_t H, int64_t Nq,
@@ -261,7 +307,7 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   const void* ptrs[] = {q, k, v, o};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
-  const KernelChoice kc = choose((int)dtype, (int)D, false, false);
+  const KernelChoice kc = choose((int)dtype, (int)D, false, false, kNoBias);
   const int BM = kc.BM;
   const int64_t cap = plan_capacity(num_seqs, total_len, BM);
   if (!workspace || workspace_bytes < (size_t)(16 + 8 * cap) || ((uintptr_t)workspace & 15u)) return ATTN_ERR_WORKSPACE;

@@ -21,6 +21,11 @@ typedef __attribute__((address_space(3))) char lds_t;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Optional score operand of the dense forward (flash attention with bias
+// page, _attn_fwd_inner): none, an additive bias in the input element type,
+// or a uint8 mask (0 removes the key for that query).
+enum BiasKind { kNoBias = 0, kAddBias = 1, kMaskBias = 2 };
+
 // Arguments of every forward kernel (passed by value).  Strides are in
 // elements; the head-dim stride is 1.  Tangents use the primal strides and
 // tO uses the strides of O.
@@ -35,6 +40,10 @@ struct FwdArgs {
   void* to;
   float* lse;
   float* tlse;  // JVP: tangent of LSE per row (nullptr: not written)
+  // optional [B, H, Nq, Nkv] additive bias (element type of q) or uint8 mask
+  // (dense only; key stride 1, the other strides may be 0 to broadcast)
+  const void* bias;
+  int64_t bias_sb, bias_sh, bias_sn;
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
   int64_t v_sb, v_sh, v_sn;
@@ -56,6 +65,7 @@ struct FwdArgs {
 struct Tile {
   int64_t q_off, k_off, v_off, o_off;  // element offset of row 0 of this (batch|seq, head)
   int64_t lse_off;                     // element offset of row 0 in the fp32 LSE buffer
+  int64_t bias_off;                    // element offset of row 0 in the bias / mask (dense)
   int qt;                              // query tile index
   int qt2;                             // second query tile of a paired workgroup, or -1
   int Lstore;                          // rows [0, Lstore) exist and are written
@@ -96,6 +106,7 @@ __device__ __forceinline__ Tile resolve_tile(const FwdArgs& a, int bid) {
     t.v_off = b * a.v_sb + h * a.v_sh;
     t.o_off = b * a.o_sb + h * a.o_sh;
     t.lse_off = (int64_t)bh * a.Nq;
+    t.bias_off = b * a.bias_sb + h * a.bias_sh;
     t.qt = qt;
     t.Lstore = a.Nq;
     t.Lattend = a.Nq;
@@ -117,6 +128,7 @@ __device__ __forceinline__ Tile resolve_tile(const FwdArgs& a, int bid) {
     t.v_off = h * a.v_sh + begin * a.v_sn;
     t.o_off = h * a.o_sh + begin * a.o_sn;
     t.lse_off = (int64_t)h * a.total_len + begin;
+    t.bias_off = 0;
     t.qt = qt;
     t.Lstore = len;
     t.Lattend = used;

@@ -28,7 +28,11 @@
 // * Lazy rescaling: the running max used for p only moves when a row's max
 //   grows by more than kTau (in log2 units), so p <= 2^kTau and the O
 //   rescale is skipped on almost every tile; m, l and acc always share the
-//   same reference, so the result is the same identity up to rounding.
+//   same reference, so the result is the same identity up to rounding.  The
+//   biased kernels keep the exact running max instead: with it the largest p
+//   of a row is exp2(0) = 1, which the 16-bit P holds exactly, and a bias
+//   makes rows peaked enough that the rounding of that one term would
+//   otherwise show in O.
 // * Per key tile: the next tile's global loads are issued first and stay in
 //   flight through the tile's two MFMA sections (scores, then PV), whose LDS
 //   fragment reads run a fixed distance ahead of their MFMAs; the prefetched
@@ -44,7 +48,8 @@
 
 namespace attn {
 
-constexpr float kTau = 8.0f;
+constexpr float kTau = 8.0f;       // lazy rescale threshold (log2 units)
+constexpr float kTauBias = 0.0f;   // biased kernels: exact running max
 
 // Waves whose rows attend at most this many keys add P's bf16 rounding
 // residual to the PV product (the lo pass below).  With more keys the
@@ -328,7 +333,7 @@ struct Bf16Cfg {
   static_assert(BN % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
 };
 
-template <int D, int BN, bool JVP, int NW_ = 4, bool F16 = false>
+template <int D, int BN, bool JVP, int NW_ = 4, bool F16 = false, int BIAS = kNoBias>
 __global__ void __launch_bounds__((Bf16Cfg<D, BN, JVP, NW_>::THREADS), (Bf16Cfg<D, BN, JVP, NW_>::WAVES_PER_EU))
 attn_fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BN, JVP, NW_>;
@@ -516,6 +521,63 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     acc[i] = f32x16{};
     if constexpr (JVP) { accA[i] = f32x16{}; accB[i] = f32x16{}; }
   }
+  // ---- bias / mask: lane (query n32, half h32) needs, of each tile, the
+  // 8-key chunks c = 0 .. 2 NB - 1 at keys 16 c + 8 h32 of its own row: chunk
+  // c is accumulator registers 8 (c % 2) .. 8 (c % 2) + 7 of s[c / 2].  The
+  // chunks of tile j + 1 are loaded into register slot (j + 1) % 2 at the start
+  // of tile j, ahead of that tile's K/V fetch, so the barrier that ends tile j
+  // has also completed them.  With an additive bias the scores are moved to
+  // the exp2 domain once (s c + bias log2 e) and the scale below becomes 1.
+  constexpr int BCH = 2 * NB;                      // chunks per lane per tile
+  constexpr int BWD = BIAS == kAddBias ? 4 : 2;    // dwords per chunk: 8 x 16-bit, or 8 bytes
+  constexpr int BEL = BIAS == kAddBias ? 2 : 1;    // bytes per element
+  unsigned bsl[BIAS ? 2 : 1][BIAS ? BCH : 1][BWD];
+  const char* brow = nullptr;
+  if constexpr (BIAS != kNoBias) {
+    const int r = my_row < t.Lstore ? my_row : t.Lstore - 1;
+    brow = (const char*)a.bias + (t.bias_off + (int64_t)r * a.bias_sn) * BEL;
+  }
+  auto bias_load = [&](int j, auto slot_tag) {
+    if constexpr (BIAS != kNoBias) {
+      constexpr int SL = decltype(slot_tag)::value;
+      const int kb = j * BN + 8 * h32;
+      if (j * BN + BN <= t.Lkv) {
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) {
+          const char* src = brow + (int64_t)(kb + 16 * c) * BEL;
+          if constexpr (BIAS == kAddBias) {
+            const u32x4 w = *(const u32x4*)src;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) bsl[SL][c][x] = w[x];
+          } else {
+            const u32x2 w = *(const u32x2*)src;
+            bsl[SL][c][0] = w[0];
+            bsl[SL][c][1] = w[1];
+          }
+        }
+      } else {  // ragged last tile: element loads of the keys that exist
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) {
+#pragma unroll
+          for (int x = 0; x < BWD; ++x) bsl[SL][c][x] = 0u;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = kb + 16 * c + e;
+            if (key < t.Lkv) {
+              if constexpr (BIAS == kAddBias)
+                bsl[SL][c][e >> 1] |= (unsigned)(*(const unsigned short*)(brow + 2 * (int64_t)key)) << (16 * (e & 1));
+              else
+                bsl[SL][c][e >> 2] |= (unsigned)(*(const unsigned char*)(brow + key)) << (8 * (e & 3));
+            }
+          }
+        }
+      }
+    }
+  };
+  // scale of the scores into the exp2 domain at the softmax (1 once an
+  // additive bias has been applied)
+  const float cs = BIAS == kAddBias ? 1.f : a.c;
+
   float m_run = -INFINITY;  // running max, exp2 domain (scores times c)
   float l_run = 0.f;        // this lane's partial row sum (its 16 of every 32 keys)
   float r_run = 0.f;        // JVP: partial rowsum of p * (tQ K^T + Q tK^T)
@@ -540,6 +602,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     constexpr int SN = S ^ 1;
     const bool ahead = j + 1 < n_tiles;
     if (ahead) {  // in flight while this tile computes
+      bias_load(j + 1, std::integral_constant<int, SN>{});
       if constexpr (DMA) dma_tile(j + 1, smem + SN * STAGE);
       else load_tile(j + 1);
     }
@@ -563,6 +626,24 @@ attn_fwd_bf16_kernel(FwdArgs a) {
             if (key >= my_lim) s[b][r] = -INFINITY;
           }
       }
+      if constexpr (BIAS == kAddBias) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned w = bsl[S][2 * b + (r >> 3)][(r & 7) >> 1];
+            const unsigned short h = (unsigned short)((r & 1) ? (w >> 16) : (w & 0xffffu));
+            s[b][r] = __builtin_fmaf(s[b][r], a.c, from16<F16>(__builtin_bit_cast(bf16, h)) * kLog2e);
+          }
+      } else if constexpr (BIAS == kMaskBias) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned w = bsl[S][2 * b + (r >> 3)][(r & 7) >> 2];
+            if (((w >> (8 * (r & 3))) & 0xffu) == 0u) s[b][r] = -INFINITY;
+          }
+      }
 
       // online softmax: tile row max (in-lane, then the other half-wave)
       float mx = s[0][0];
@@ -571,8 +652,8 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
       mx = xhalf_max(mx);
-      const float m_new = mx * a.c;
-      const bool upd = m_new > m_run + kTau;
+      const float m_new = mx * cs;
+      const bool upd = m_new > m_run + (BIAS != kNoBias ? kTauBias : kTau);
       if (__builtin_amdgcn_ballot_w64(upd) != 0) {
         const float m_next = upd ? m_new : m_run;
         const float alpha = m_next == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_next);
@@ -602,7 +683,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
           bf16x8 plo[2];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], a.c, nm));
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], cs, nm));
             plo[r >> 3][r & 7] = to16<F16>(p - from16<F16>(to16<F16>(p)));
           }
           pv_lo_block<D, F16>(vt, vlo, vhi, b, plo, acc);
@@ -617,7 +698,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       bf16x8 hf[JVP ? NB : 1][2];
       auto soft = [&](auto e_tag) {  // one element e of this lane's 16 NB scores
         constexpr int e = decltype(e_tag)::value, b = e / 16, r = e % 16;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], a.c, -msub));
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], cs, -msub));
         l_run += p;
         pf[b][r >> 3][r & 7] = to16<F16>(p);
         if constexpr (JVP) {
@@ -648,6 +729,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   // Q-fragment loads have completed, so no wait for the next tile's prefetch
   // is needed inside the loop.
   if (n_tiles > 0) {
+    bias_load(0, std::integral_constant<int, 0>{});
     if constexpr (DMA) {
       dma_tile(0, smem);
     } else {

@@ -28,7 +28,7 @@ struct F32Cfg {
   static constexpr int LDS = NTEN * BN * D * 4;
 };
 
-template <int D, bool JVP>
+template <int D, bool JVP, int BIAS = kNoBias>
 __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
   using C = F32Cfg<D, JVP>;
   constexpr int BM = C::BM, BN = C::BN, NTEN = C::NTEN;
@@ -70,6 +70,12 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
     }
   }
   float m_run = -INFINITY, l_run = 0.f, r_run = 0.f;
+  // bias / mask row of this lane's query (every lane of the quad reads it);
+  // an additive bias moves the scores to the exp2 domain before the max
+  const char* brow = nullptr;
+  if constexpr (BIAS != kNoBias)
+    brow = (const char*)a.bias + (t.bias_off + (int64_t)rr * a.bias_sn) * (BIAS == kAddBias ? 4 : 1);
+  const float cs = BIAS == kAddBias ? 1.f : a.c;
 
   for (int j = 0; j < n_tiles; ++j) {
     __syncthreads();  // the previous tile is no longer being read
@@ -103,10 +109,43 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
       if constexpr (JVP) ts[jj] = quad_sum(tpart);
       if (j * BN + jj >= my_lim) s[jj] = -INFINITY;
     }
+    if constexpr (BIAS != kNoBias) {
+      const bool full = j * BN + BN <= t.Lkv;
+#pragma unroll
+      for (int c = 0; c < BN / 8; ++c) {  // 8 keys per step
+        float bv[8];
+        if (full) {
+          if constexpr (BIAS == kAddBias) {
+            const f32x4 x0 = *(const f32x4*)(brow + 4 * (int64_t)(j * BN + 8 * c));
+            const f32x4 x1 = *(const f32x4*)(brow + 4 * (int64_t)(j * BN + 8 * c + 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { bv[e] = x0[e]; bv[4 + e] = x1[e]; }
+          } else {
+            const u32x2 w = *(const u32x2*)(brow + j * BN + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[e] = (float)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
+          }
+        } else {  // ragged last tile: keys past the end are already masked
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = j * BN + 8 * c + e;
+            bv[e] = 0.f;
+            if (key < t.Lkv)
+              bv[e] = BIAS == kAddBias ? ((const float*)brow)[key] : (float)((const unsigned char*)brow)[key];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float& x = s[8 * c + e];
+          if constexpr (BIAS == kAddBias) x = __builtin_fmaf(x, a.c, bv[e] * kLog2e);
+          else if (bv[e] == 0.f) x = -INFINITY;
+        }
+      }
+    }
     float mx = s[0];
 #pragma unroll
     for (int jj = 1; jj < BN; ++jj) mx = fmaxf(mx, s[jj]);
-    const float m_new = fmaxf(m_run, mx * a.c);
+    const float m_new = fmaxf(m_run, mx * cs);
     const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
     const float msub = m_new == -INFINITY ? 0.f : m_new;
     l_run *= alpha;
@@ -118,7 +157,7 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int jj = 0; jj < BN; ++jj) {
-      const float p = exp2f(__builtin_fmaf(s[jj], a.c, -msub));
+      const float p = exp2f(__builtin_fmaf(s[jj], cs, -msub));
       l_run += p;
       const float hv = JVP ? p * ts[jj] : 0.f;
       r_run += hv;

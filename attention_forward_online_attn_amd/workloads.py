@@ -6,8 +6,8 @@ inputs from it.
 
 Recipe (the same on every machine, independent of the device):
 * one CPU ``torch.Generator`` per tensor, seeded ``seed_base + i`` with
-  i = 0..5 for Q, K, V, tQ, tK, tV, i = 6 for the jagged lengths and i = 7
-  for the backward's dO;
+  i = 0..5 for Q, K, V, tQ, tK, tV, i = 6 for the jagged lengths, i = 7
+  for the backward's dO, i = 8 for an additive bias and i = 9 for a mask;
 * values i.i.d. N(0, 1) drawn in fp32 and rounded to the working dtype
   (round-to-nearest-even for bf16) on the CPU;
 * jagged lengths uniform in [1, max_len], offsets = exclusive prefix sum (int64).
@@ -51,6 +51,22 @@ def grad_output(shape, dtype="bf16", seed_base=0):
     """dO for the backward: i.i.d. N(0, 1), seeded seed_base + 7 (CPU)."""
     dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
     return _normal(shape, seed_base + 7, dt)
+
+
+def score_bias(shape, dtype="bf16", seed_base=0, scale=1.0):
+    """Additive score bias: i.i.d. N(0, scale^2), seeded seed_base + 8 (CPU)."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed_base + 8))
+    return (torch.randn(*shape, generator=g, dtype=torch.float32) * scale).to(dt)
+
+
+def score_mask(shape, keep=0.75, seed_base=0):
+    """Boolean mask, each entry True (key kept) with probability `keep`,
+    seeded seed_base + 9 (CPU)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed_base + 9))
+    return torch.rand(*shape, generator=g) < keep
 
 
 def jagged_lengths(num_seqs, max_len, seed_base=0, min_len=1):

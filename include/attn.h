@@ -96,6 +96,44 @@ ATTN_API int attn_fwd(attn_dtype dtype,
              int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
              float sm_scale, int causal, void* stream);
 
+/* Kind of the score operand of attn_fwd_bias. */
+typedef enum attn_bias_kind {
+  ATTN_BIAS_ADD = 1,  /* additive float bias, element type = dtype */
+  ATTN_BIAS_MASK = 2  /* uint8 boolean mask: 0 removes the key, nonzero keeps it */
+} attn_bias_kind;
+
+/*
+ * Dense attention forward with an additive bias or a boolean mask on the
+ * scores (flash attention with bias page: _attn_fwd_inner, _attn_fwd and
+ * the wrapper _flash_attn_fwd):
+ *     S_ij = sm_scale <q_i, k_j> + bias_ij        (ATTN_BIAS_ADD)
+ *     S_ij = -inf where mask_ij == 0              (ATTN_BIAS_MASK)
+ * combined with the causal mask when causal != 0; O and LSE as attn_fwd.
+ *   bias          [B, H, Nq, Nkv] read through bias_strides = {b, h, n, d}
+ *                 (n: query row, d: key).  d must be 1; b, h and n may be 0
+ *                 to broadcast, e.g. {0, 0, 0, 1} for one key-padding row
+ *                 shared by every query, or {Nq*Nkv, 0, Nkv, 1} for a
+ *                 per-batch bias shared by the heads.
+ *   ATTN_BIAS_ADD: element type `dtype`, in the units of the scores (natural
+ *                 log: the page's wrapper divides by ln 2 for its base-2
+ *                 kernel; the result is the same).  Values must be finite or
+ *                 -inf (which removes the key); +inf and NaN give NaN rows.
+ *                 Base 16-byte aligned, b/h/n strides multiples of 16 bytes.
+ *   ATTN_BIAS_MASK: uint8; base 8-byte aligned, b/h/n strides multiples of 8.
+ *   A row left with no key gets O = 0, LSE = -inf (the page's additive -1e6
+ *   mask would instead attend every key of such a row).
+ *   bias may be NULL only when Nkv == 0.  Other arguments as attn_fwd.
+ */
+ATTN_API int attn_fwd_bias(attn_dtype dtype,
+                  const void* q, attn_strides4 q_strides,
+                  const void* k, attn_strides4 k_strides,
+                  const void* v, attn_strides4 v_strides,
+                  void* o, attn_strides4 o_strides,
+                  float* lse,
+                  const void* bias, attn_bias_kind bias_kind, attn_strides4 bias_strides,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                  float sm_scale, int causal, void* stream);
+
 /*
  * Dense attention forward fused with its forward-mode JVP (tutorial page:
  * _attn_fwd_inner / _attn_fwd with ENABLE_JVP; JVP page: _attn_fwd_inner and

@@ -32,8 +32,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(
-        ["attn_fwd", "attn_fwd_jvp", "jagged_attn_workspace_bytes", "jagged_attn_fwd", "attn_bwd_workspace_bytes",
-         "attn_bwd", "attn_status_string"])
+        ["attn_fwd", "attn_fwd_bias", "attn_fwd_jvp", "jagged_attn_workspace_bytes", "jagged_attn_fwd",
+         "attn_bwd_workspace_bytes", "attn_bwd", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -84,6 +84,32 @@ def test_dense_validation(lib):
     # no work: nothing is enqueued, null data pointers are fine
     assert call_fwd(lib, B=0, q=0, k=0, v=0, o=0, lse=0) == OK
     assert call_fwd(lib, Nq=0, q=0, k=0, v=0, o=0, lse=0) == OK
+
+
+def test_bias_validation(lib):
+    B, H, N, D = 1, 2, 128, 64
+    st = dense_strides(B, H, N, D)
+    full = Strides4(H * N * N, N * N, N, 1)
+    ADD, MASK = 1, 2
+
+    def call(kind=ADD, bias=P, bs=full, dtype=BF16, Nkv=N, B=B, D=D):
+        sk = dense_strides(B, H, Nkv, D)
+        return lib.attn_fwd_bias(dtype, P, st, P, sk, P, sk, P, st, P, bias, kind, bs, B, H, N, Nkv, D,
+                                 0.125, 0, None)
+    assert call(kind=0) == UNSUPPORTED
+    assert call(kind=3) == UNSUPPORTED
+    assert call(bias=0) == INVALID                                        # no bias with keys to bias
+    assert call(bs=Strides4(H * N * N, N * N, N, 2)) == INVALID           # key stride must be 1
+    assert call(bs=Strides4(-1, N * N, N, 1)) == INVALID
+    assert call(bias=P + 2) == UNSUPPORTED                                # bf16 bias base not 16-byte aligned
+    assert call(bs=Strides4(H * N * N, N * N, N + 4, 1)) == UNSUPPORTED  # row stride of 8 bytes (bf16)
+    assert call(kind=MASK, bias=P + 8, bs=Strides4(0, 0, N + 4, 1)) == UNSUPPORTED  # mask rows: 8-byte multiples
+    assert call(kind=MASK, bias=P + 4) == UNSUPPORTED
+    assert call(dtype=FP32, bs=Strides4(0, 0, N + 2, 1)) == UNSUPPORTED  # fp32 bias rows: 16-byte multiples
+    assert call(D=96) == UNSUPPORTED
+    # no work: nothing is enqueued
+    assert call(B=0) == OK
+    assert call(B=0, bias=0) == OK
 
 
 def test_jvp_validation(lib):
