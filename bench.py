@@ -19,7 +19,7 @@ launch, outside the events, which evicts L2 and the Infinity Cache).  `cpu_basel
 sample of the same workload (a few heads) on this host's cores.
 
 Profiling modes (for rocprofv3 runs): --only {fwd,fwd_causal,jvp,jvp_causal,
-causal_d64,jagged,bwd,bwd_causal,fwd_fp16} runs just that workload K times; --copy-calibration runs a
+causal_d64,jagged,bwd,bwd_causal,fwd_fp16,fwd_bias,fwd_mask} runs just that workload K times; --copy-calibration runs a
 plain device copy of known size (the scale for FETCH_SIZE / WRITE_SIZE).
 """
 
@@ -92,6 +92,17 @@ def make_cases(torch, attn, wl):
     cases["fwd_fp16"] = Case("fwd_fp16", lambda: attn.fwd(qh, kh, vh, causal=False, sm_scale=w.sm_scale),
                              dense_flops(w.B, w.H, w.N, w.N, w.D, False), io_bytes,
                              f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} fp16 causal=False")
+
+    # the headline shape with a score operand (bias page): a per-head additive
+    # bias shared by the batch, and a per-batch boolean mask shared by the heads
+    bias = wl.score_bias((1, w.H, w.N, w.N), "bf16", 0).to(dev)
+    cases["fwd_bias"] = Case("fwd_bias", lambda: attn.fwd_bias(q, k, v, bias=bias, sm_scale=w.sm_scale),
+                             dense_flops(w.B, w.H, w.N, w.N, w.D, False), io_bytes + bias.numel() * 2,
+                             f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} bf16 + bias [1,{w.H},{w.N},{w.N}] bf16")
+    mask = wl.score_mask((w.B, 1, w.N, w.N), 0.75, 0).to(dev)
+    cases["fwd_mask"] = Case("fwd_mask", lambda: attn.fwd_bias(q, k, v, mask=mask, sm_scale=w.sm_scale),
+                             dense_flops(w.B, w.H, w.N, w.N, w.D, False), io_bytes + mask.numel(),
+                             f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} bf16 + mask [{w.B},1,{w.N},{w.N}] bool")
 
     w4 = wl.WORKLOADS["jvp_d64"]
     ts = [t.to(dev) for t in wl.dense_inputs(w4.B, w4.H, w4.N, w4.N, w4.D, "bf16", 0, tangents=True)]
@@ -273,7 +284,8 @@ def main():
                 "cold_tflops": round(c.flops / (mc * 1e-3) / 1e12, 2)}
 
     extra = {"fwd": summary(head, durs, time_launches(torch, head, n_cold, 2, flush)[0])}
-    for name in ("fwd_causal", "fwd_fp16", "jvp", "jvp_causal", "causal_d64", "jagged", "bwd", "bwd_causal"):
+    for name in ("fwd_causal", "fwd_fp16", "fwd_bias", "fwd_mask", "jvp", "jvp_causal", "causal_d64", "jagged", "bwd",
+                 "bwd_causal"):
         c = cases[name]
         dw, _ = time_launches(torch, c, max(5, args.steps // 2), 10)
         dc, _ = time_launches(torch, c, n_cold, 2, flush)
