@@ -221,7 +221,7 @@ def bwd_workspace_bytes(B, H, Nq) -> int:
 
 
 def bwd(q, k, v, o, do, lse, causal=False, sm_scale=None, workspace=None):
-    """Dense backward (bf16).  q/o/do [B,H,Nq,D], k/v [B,H,Nkv,D], lse fp32
+    """Dense backward (bf16 or fp16).  q/o/do [B,H,Nq,D], k/v [B,H,Nkv,D], lse fp32
     [B,H,Nq] from fwd with the same q, k, v -> (dq, dk, dv) shaped like q, k, v."""
     lib = load_library()
     _same(q, k, v, o, do)

@@ -228,19 +228,19 @@ int launch_fn(F* fn, int grid, int threads, int lds, hipStream_t stream, const B
 // Key tiles of the dQ kernel (keys streamed per step).
 constexpr int kBnBwdDq = 32;
 
-template <int D>
+template <int D, bool F16>
 int bwd_launch(hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv) {
   const int64_t rows = B * H * Nq;
   constexpr int rpb = 256 / (D / 8);
-  int rc = launch_fn(attn_bwd_prep_kernel<D>, (int)((rows + rpb - 1) / rpb), 256, 0, st, a);
+  int rc = launch_fn(attn_bwd_prep_kernel<D, F16>, (int)((rows + rpb - 1) / rpb), 256, 0, st, a);
   if (rc) return rc;
   using Cq = BwdDqCfg<D, kBnBwdDq>;
   a.n_tiles = (int)((Nq + Cq::BM - 1) / Cq::BM);
-  rc = launch_fn(attn_bwd_dq_kernel<D, kBnBwdDq>, (int)(B * H * a.n_tiles), Cq::THREADS, Cq::LDS, st, a);
+  rc = launch_fn(attn_bwd_dq_kernel<D, kBnBwdDq, F16>, (int)(B * H * a.n_tiles), Cq::THREADS, Cq::LDS, st, a);
   if (rc) return rc;
   using Ck = BwdDkdvCfg<D>;
   a.n_tiles = (int)((Nkv + Ck::BN - 1) / Ck::BN);
-  return launch_fn(attn_bwd_dkdv_kernel<D>, (int)(B * H * a.n_tiles), Ck::THREADS, Ck::LDS, st, a);
+  return launch_fn(attn_bwd_dkdv_kernel<D, F16>, (int)(B * H * a.n_tiles), Ck::THREADS, Ck::LDS, st, a);
 }
 
 int64_t plan_capacity(int64_t num_seqs, int64_t total_len, int BM) {
@@ -357,7 +357,7 @@ int attn_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const voi
              void* stream) {
   int rc = check_common((int)dtype, D, sm_scale);
   if (rc) return rc;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
   if (causal && Nq != Nkv) return ATTN_ERR_CAUSAL_SHAPE;
   if (B * H * (Nq + Nkv) == 0) return ATTN_OK;
@@ -398,7 +398,10 @@ int attn_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const voi
   a.causal = causal ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
-  rc = D == 64 ? bwd_launch<64>(st, a, B, H, Nq, Nkv) : bwd_launch<128>(st, a, B, H, Nq, Nkv);
+  if (dtype == ATTN_FP16)
+    rc = D == 64 ? bwd_launch<64, true>(st, a, B, H, Nq, Nkv) : bwd_launch<128, true>(st, a, B, H, Nq, Nkv);
+  else
+    rc = D == 64 ? bwd_launch<64, false>(st, a, B, H, Nq, Nkv) : bwd_launch<128, false>(st, a, B, H, Nq, Nkv);
   if (rc) return rc;
   return finish(st);
 }

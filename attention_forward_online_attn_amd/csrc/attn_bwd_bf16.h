@@ -55,7 +55,7 @@ struct BwdArgs {
 };
 
 // ---- delta_i = sum_d O_id dO_id and LSE_i log2(e), one row per D/8 lanes.
-template <int D>
+template <int D, bool F16 = false>
 __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(BwdArgs a) {
   constexpr int LPR = D / 8;          // lanes per row, 16 bytes each
   constexpr int RPB = 256 / LPR;      // rows per workgroup
@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(BwdArgs a) {
     const bf16* drow = (const bf16*)a.dout + b * a.do_sb + h * a.do_sh + i * a.do_sn + part * 8;
     const bf16x8 ov = *(const bf16x8*)orow, dv = *(const bf16x8*)drow;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)ov[e], (float)dv[e], acc);
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(from16<F16>(ov[e]), from16<F16>(dv[e]), acc);
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -129,7 +129,7 @@ struct BwdDqCfg {
   static constexpr int LDS = 2 * STAGE;
 };
 
-template <int D, int BN>
+template <int D, int BN, bool F16 = false>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   using C = BwdDqCfg<D, BN>;
   constexpr int BM = C::BM, TILE = C::TILE, STAGE = C::STAGE, NW = C::NW;
@@ -199,8 +199,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     if (j + 1 < n_tiles) fetch(j + 1, S ^ 1);
     if (j * BN < wave_max) {
       f32x16 s[NB], dp[NB];
-      scores_section<D, NB, false, S * STAGE, 0>(kaddr, qf, dummy_t, s, dummy_ts);          // S^T = K Q^T
-      scores_section<D, NB, false, S * STAGE + TILE, 0>(kaddr, df, dummy_t, dp, dummy_ts);  // dP^T = V dO^T
+      scores_section<D, NB, false, S * STAGE, 0, F16>(kaddr, qf, dummy_t, s, dummy_ts);          // S^T = K Q^T
+      scores_section<D, NB, false, S * STAGE + TILE, 0, F16>(kaddr, df, dummy_t, dp, dummy_ts);  // dP^T = V dO^T
       if ((j + 1) * BN > wave_min) {  // keys past this row's limit: P = 0
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb)
@@ -217,11 +217,11 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
       auto dsel = [&](auto e_tag) {
         constexpr int e = decltype(e_tag)::value, bb = e / 16, r = e % 16;
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], a.c, -lse2));
-        dsf[bb][r >> 3][r & 7] = (bf16)(p * (dp[bb][r] - delta));
+        dsf[bb][r >> 3][r & 7] = to16<F16>(p * (dp[bb][r] - delta));
       };
       static_for<8>(dsel);
       // dQ^T += K^T dS^T (transposing reads of the K tile)
-      pv_section<D, NB, false, S * STAGE, 0>(lds_base, vlo, vhi, dsf, dummy_h, acc, dummy_a, dummy_b, [&](auto i_tag) {
+      pv_section<D, NB, false, S * STAGE, 0, F16>(lds_base, vlo, vhi, dsf, dummy_h, acc, dummy_a, dummy_b, [&](auto i_tag) {
         constexpr int i = decltype(i_tag)::value, c = i / DB, EPS = 8 / DB;
         if constexpr (c + 1 < 2 * NB)
           static_for<EPS>([&](auto k_tag) {
@@ -252,7 +252,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
         const int d = 32 * db + 8 * g + 4 * h32;
         bf16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[db][4 * g + e] * a.sm_scale);
+        for (int e = 0; e < 4; ++e) ov[e] = to16<F16>(acc[db][4 * g + e] * a.sm_scale);
         *(bf16x4*)(orow + d) = ov;
       }
   }
@@ -269,7 +269,7 @@ struct BwdDkdvCfg {
   static constexpr int WAVES_PER_EU = D == 128 ? 1 : 2;  // D=128 holds K, V, dK, dV: 1 wave per SIMD
 };
 
-template <int D>
+template <int D, bool F16 = false>
 __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_dkdv_kernel(BwdArgs a) {
   using C = BwdDkdvCfg<D>;
   constexpr int BN = C::BN, BMQ = C::BMQ, TILE = C::TILE, STAGE = C::STAGE, NW = C::NW;
@@ -347,8 +347,8 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
     const int q0 = jq * BMQ;
     if (wave_keys && q0 + BMQ > wave_q_first) {  // wave-uniform: some key of the wave sees some query
       f32x16 s[1], dp[1];
-      scores_section<D, 1, false, S * STAGE, 0>(qaddr, kf, dummy_t, s, dummy_ts);          // S = Q K^T
-      scores_section<D, 1, false, S * STAGE + TILE, 0>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
+      scores_section<D, 1, false, S * STAGE, 0, F16>(qaddr, kf, dummy_t, s, dummy_ts);          // S = Q K^T
+      scores_section<D, 1, false, S * STAGE + TILE, 0, F16>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
       // masked pairs (query past Nq; causal: key after query) get P = 0
       const bool edge = q0 + BMQ > a.Nq || (a.causal && q0 < k0 + 32);
       if (edge) {
@@ -374,16 +374,16 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
           const float l2 = e < 4 ? a0[e & 3] : a1[e & 3];
           const float dl = e < 4 ? d0[e & 3] : d1[e & 3];
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][8 * c + e], a.c, -l2));
-          pf[0][c][e] = (bf16)p;
-          dsf[0][c][e] = (bf16)(p * (dp[0][8 * c + e] - dl));
+          pf[0][c][e] = to16<F16>(p);
+          dsf[0][c][e] = to16<F16>(p * (dp[0][8 * c + e] - dl));
         }
       };
       chunk(std::integral_constant<int, 0>{});
       // dV^T += dO^T P and dK^T += Q^T dS (transposing reads of the dO and Q tiles)
-      pv_section<D, 1, false, S * STAGE + TILE, 0>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b, [&](auto i_tag) {
+      pv_section<D, 1, false, S * STAGE + TILE, 0, F16>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b, [&](auto i_tag) {
         if constexpr (decltype(i_tag)::value == 0) chunk(std::integral_constant<int, 1>{});  // after the first MFMA
       });
-      pv_section<D, 1, false, S * STAGE, 0>(lds_base, vlo, vhi, dsf, dummy_h, dk, dummy_a, dummy_b, [](auto) {});
+      pv_section<D, 1, false, S * STAGE, 0, F16>(lds_base, vlo, vhi, dsf, dummy_h, dk, dummy_a, dummy_b, [](auto) {});
     }
     __syncthreads();
   };
@@ -410,8 +410,8 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
         bf16x4 kv, vv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kv[e] = (bf16)(dk[db][4 * g + e] * a.sm_scale);
-          vv[e] = (bf16)dv[db][4 * g + e];
+          kv[e] = to16<F16>(dk[db][4 * g + e] * a.sm_scale);
+          vv[e] = to16<F16>(dv[db][4 * g + e]);
         }
         *(bf16x4*)(krow_o + d) = kv;
         *(bf16x4*)(vrow_o + d) = vv;

@@ -207,7 +207,7 @@ ATTN_API size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
  *     delta_i = sum_d o_id d_o_id,   P = exp(sm_scale q k^T - lse)  (0 where masked),
  *     dv = P^T d_o,   dP = d_o v^T,   dS = P * (dP - delta),
  *     dq = sm_scale dS k,   dk = sm_scale dS^T q.
- *   q, o, d_o, dq  [B, H, Nq, D]   k, v, dk, dv  [B, H, Nkv, D]  (bf16 only)
+ *   q, o, d_o, dq  [B, H, Nq, D]   k, v, dk, dv  [B, H, Nkv, D]  (bf16 or fp16)
  *   lse            [B, H, Nq] contiguous fp32: the natural-log LSE that
  *                  attn_fwd wrote for these q, k, v (a row with LSE = -inf
  *                  gets dq = 0 and adds nothing to dk, dv)
@@ -217,9 +217,9 @@ ATTN_API size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
  *                  bytes, 16-byte aligned; contents on entry are ignored.
  *                  Calls that share a workspace must not overlap.
  * Strides, alignment, sm_scale, causal (Nq == Nkv) and D in {64, 128} as for
- * attn_fwd.  P and dS are rounded to bf16 for their products, with fp32
- * accumulation.  Each output element is written by exactly one thread: the
- * result is deterministic.  ATTN_FP32 and ATTN_FP16 return ATTN_ERR_UNSUPPORTED.  Three
+ * attn_fwd.  P and dS are rounded to the input format for their products,
+ * with fp32 accumulation.  Each output element is written by exactly one
+ * thread: the result is deterministic.  ATTN_FP32 returns ATTN_ERR_UNSUPPORTED.  Three
  * kernels are enqueued on `stream`; B*H*(Nq+Nkv) == 0 is a no-op.
  */
 ATTN_API int attn_bwd(attn_dtype dtype,

@@ -162,7 +162,6 @@ def test_bwd_validation(lib):
         return lib.attn_bwd(dtype, q, sq, P, sk, P, sk, P, st, P, st, lse, dq, st, P, sk, P, sk,
                             B, H, N, Nkv, D, scale, causal, ws, ws_bytes, None)
     assert call(dtype=FP32) == UNSUPPORTED
-    assert call(dtype=FP16) == UNSUPPORTED
     assert call(D=96) == UNSUPPORTED
     assert call(causal=1, Nkv=64) == CAUSAL
     assert call(ws=0) == WORKSPACE

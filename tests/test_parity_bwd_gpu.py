@@ -9,7 +9,9 @@ used for the JVP's tangent output, whose error has the same sources (P
 rounded to bf16, a difference term, fp32 accumulation).  The absolute 1e-5
 only matters where a gradient vanishes exactly (one key: dq = dk = 0), where
 fp32 rounding of dP - delta leaves about 1e-7; gradients of N(0, 1) data are
-of order 0.01 to 1.  Each test prints the achieved relative error.
+of order 0.01 to 1.  fp16 inputs: 1e-2 relative (the tangent bound for fp16),
+the same sources at fp16's 11-bit significand.  Each test prints the
+achieved relative error.
 """
 
 import numpy as np
@@ -23,11 +25,12 @@ from parity import host64
 
 pytestmark = pytest.mark.gpu
 
-REL = 3e-2
+REL = {"bf16": 3e-2, "fp16": 1e-2}
 ABS = 1e-5
 
 
-def check_grads(got, ref, label):
+def check_grads(got, ref, label, dtype="bf16"):
+    rel = REL[dtype]
     msgs, ok = [], True
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         g = host64(g)
@@ -36,21 +39,21 @@ def check_grads(got, ref, label):
         if not np.all(np.isfinite(g)):
             diff = np.inf
         msgs.append(f"{name} {diff / max(gmax, 1e-30):.2e} (max|g| {gmax:.2e})")
-        ok = ok and diff <= REL * gmax + ABS
-    msg = f"{label}: max|dg|/max|g| " + ", ".join(msgs) + f" (bound {REL:.0e} relative + {ABS:.0e})"
+        ok = ok and diff <= rel * gmax + ABS
+    msg = f"{label}: max|dg|/max|g| " + ", ".join(msgs) + f" (bound {rel:.0e} relative + {ABS:.0e})"
     print(msg, flush=True)
     assert ok, msg
 
 
-def bwd_case(B, H, Nq, Nkv, D, causal, seed=0, scale=None, label=None):
-    q, k, v = wl.dense_inputs(B, H, Nq, Nkv, D, "bf16", seed)
-    do = wl.grad_output((B, H, Nq, D), "bf16", seed)
+def bwd_case(B, H, Nq, Nkv, D, causal, seed=0, scale=None, label=None, dtype="bf16"):
+    q, k, v = wl.dense_inputs(B, H, Nq, Nkv, D, dtype, seed)
+    do = wl.grad_output((B, H, Nq, D), dtype, seed)
     scale = D ** -0.5 if scale is None else scale
     qc, kc, vc, doc = (t.cuda() for t in (q, k, v, do))
     o, lse = attn.fwd(qc, kc, vc, causal=causal, sm_scale=scale)
     got = attn.bwd(qc, kc, vc, o, doc, lse, causal=causal, sm_scale=scale)
     ref = oracle.attention_bwd(q, k, v, do, oracle.scale_as_passed(scale), causal)
-    check_grads(got, ref, label or f"bwd {B, H, Nq, Nkv, D} causal={causal}")
+    check_grads(got, ref, label or f"bwd {B, H, Nq, Nkv, D} {dtype} causal={causal}", dtype)
     return got
 
 
@@ -123,3 +126,16 @@ def test_bwd_unscaled_logits(gpu_lib):
     o, lse = attn.fwd(qc, kc, vc, causal=True, sm_scale=1.0)
     got = attn.bwd(qc, kc, vc, o, doc, lse, causal=True, sm_scale=1.0)
     check_grads(got, oracle.attention_bwd(q, k, v, do, 1.0, True), "bwd sm_scale=1")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_fp16(gpu_lib, D, causal):
+    """fp16 inputs on the same kernels (fp16 MFMA products, P and dS rounded to fp16)."""
+    bwd_case(2, 3, 300, 300, D, causal, seed=8, dtype="fp16")
+    bwd_case(1, 2, 1024, 1024, D, causal, seed=9, dtype="fp16")
+
+
+def test_bwd_fp16_odd_shapes(gpu_lib):
+    bwd_case(1, 2, 1, 1, 64, True, seed=10, dtype="fp16")
+    bwd_case(1, 2, 100, 333, 128, False, seed=11, dtype="fp16")
