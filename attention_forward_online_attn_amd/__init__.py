@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     fwd,
     fwd_bias,
     fwd_jvp,
+    jagged_bwd,
+    jagged_bwd_workspace_bytes,
     jagged_fwd,
     jagged_workspace_bytes,
     library_path,

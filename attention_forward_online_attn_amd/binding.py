@@ -74,6 +74,11 @@ def load_library():
     lib.attn_bwd.argtypes = [i32, vp, S4, vp, S4, vp, S4, vp, S4, vp, S4, vp, vp, S4, vp, S4, vp, S4,
                              i64, i64, i64, i64, i64, f32, i32, vp, ctypes.c_size_t, vp]
     lib.attn_bwd.restype = i32
+    lib.jagged_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.jagged_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.jagged_attn_bwd.argtypes = [i32, vp, S3, vp, S3, vp, S3, vp, S3, vp, S3, vp, vp, S3, vp, S3, vp, S3,
+                                    vp, i64, i64, i64, i64, i64, f32, i32, vp, ctypes.c_size_t, vp]
+    lib.jagged_attn_bwd.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -243,4 +248,34 @@ def bwd(q, k, v, o, do, lse, causal=False, sm_scale=None, workspace=None):
                         _ptr(do), _s4(do), _ptr(lse), _ptr(dq), _s4(dq), _ptr(dk), _s4(dk), _ptr(dv), _s4(dv),
                         B, H, Nq, Nkv, D, float(sm_scale), int(bool(causal)),
                         _ptr(workspace), workspace.numel(), _stream(q)))
+    return dq, dk, dv
+
+
+def jagged_bwd_workspace_bytes(num_seqs, H, total_len) -> int:
+    return int(load_library().jagged_attn_bwd_workspace_bytes(int(num_seqs), int(H), int(total_len)))
+
+
+def jagged_bwd(q, k, v, o, do, lse, offsets, max_seq_len, causal=False, sm_scale=None, workspace=None):
+    """Jagged backward (bf16 or fp16).  q/k/v/o/do [H, total_len, D], lse fp32
+    [H, total_len] from jagged_fwd with the same inputs, offsets int64
+    [num_seqs+1] on the device -> (dq, dk, dv) shaped like q, k, v."""
+    lib = load_library()
+    _same(q, k, v, o, do)
+    if offsets.dtype != torch.int64 or offsets.device != q.device or offsets.dim() != 1:
+        raise AttnError("offsets must be a 1-D int64 tensor on the same device")
+    H, T, D = q.shape
+    if lse.dtype != torch.float32 or lse.device != q.device or lse.shape != (H, T) or not lse.is_contiguous():
+        raise AttnError("lse must be a contiguous float32 [H, total_len] tensor on the same device")
+    offsets = offsets.contiguous()
+    S = offsets.numel() - 1
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    need = jagged_bwd_workspace_bytes(S, H, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib.jagged_attn_bwd(_dtype_code(q), _ptr(q), _s3(q), _ptr(k), _s3(k), _ptr(v), _s3(v), _ptr(o), _s3(o),
+                               _ptr(do), _s3(do), _ptr(lse), _ptr(dq), _s3(dq), _ptr(dk), _s3(dk), _ptr(dv), _s3(dv),
+                               _ptr(offsets), S, H, T, D, int(max_seq_len), float(sm_scale), int(bool(causal)),
+                               _ptr(workspace), workspace.numel(), _stream(q)))
     return dq, dk, dv

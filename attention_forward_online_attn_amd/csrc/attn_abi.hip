@@ -228,19 +228,26 @@ int launch_fn(F* fn, int grid, int threads, int lds, hipStream_t stream, const B
 // Key tiles of the dQ kernel (keys streamed per step).
 constexpr int kBnBwdDq = 32;
 
+// Dense: B*H*Nq rows, grids over (batch, head, tile).  Jagged (a.offsets
+// set): the prep kernel sees H*total_len rows as one batch (B = 1,
+// Nq = total_len, batch strides 0) and both gradient kernels cover `items`
+// plan items per head.
 template <int D, bool F16>
-int bwd_launch(hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv) {
+int bwd_launch(hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t items = 0) {
   const int64_t rows = B * H * Nq;
   constexpr int rpb = 256 / (D / 8);
   int rc = launch_fn(attn_bwd_prep_kernel<D, F16>, (int)((rows + rpb - 1) / rpb), 256, 0, st, a);
   if (rc) return rc;
   using Cq = BwdDqCfg<D, kBnBwdDq>;
-  a.n_tiles = (int)((Nq + Cq::BM - 1) / Cq::BM);
-  rc = launch_fn(attn_bwd_dq_kernel<D, kBnBwdDq, F16>, (int)(B * H * a.n_tiles), Cq::THREADS, Cq::LDS, st, a);
-  if (rc) return rc;
   using Ck = BwdDkdvCfg<D>;
+  static_assert(Cq::BM == 128 && Ck::BN == 128, "the jagged plan's tiles are 128 rows");
+  a.n_tiles = (int)((Nq + Cq::BM - 1) / Cq::BM);
+  const int64_t gq = a.offsets ? items * H : B * H * a.n_tiles;
+  rc = launch_fn(attn_bwd_dq_kernel<D, kBnBwdDq, F16>, (int)gq, Cq::THREADS, Cq::LDS, st, a);
+  if (rc) return rc;
   a.n_tiles = (int)((Nkv + Ck::BN - 1) / Ck::BN);
-  return launch_fn(attn_bwd_dkdv_kernel<D, F16>, (int)(B * H * a.n_tiles), Ck::THREADS, Ck::LDS, st, a);
+  const int64_t gk = a.offsets ? items * H : B * H * a.n_tiles;
+  return launch_fn(attn_bwd_dkdv_kernel<D, F16>, (int)gk, Ck::THREADS, Ck::LDS, st, a);
 }
 
 int64_t plan_capacity(int64_t num_seqs, int64_t total_len, int BM) {
@@ -338,6 +345,79 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   a.total_len = (int)total_len;
   a.max_seq_len = mlen;
   rc = launch(kc, (int)grid, st, a);
+  if (rc) return rc;
+  return finish(st);
+}
+
+size_t jagged_attn_bwd_workspace_bytes(int64_t num_seqs, int64_t H, int64_t total_len) {
+  if (num_seqs < 0 || H < 0 || total_len < 0 || num_seqs > INT_MAX - 1 || total_len > INT_MAX || H > INT_MAX)
+    return 0;
+  const int64_t plan = (16 + 8 * plan_capacity(num_seqs, total_len, 128) + 15) / 16 * 16;
+  return (size_t)(plan + 8 * H * total_len);
+}
+
+int jagged_attn_bwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, const void* k, attn_strides3 k_strides,
+                    const void* v, attn_strides3 v_strides, const void* o, attn_strides3 o_strides, const void* d_o,
+                    attn_strides3 do_strides, const float* lse, void* dq, attn_strides3 dq_strides, void* dk,
+                    attn_strides3 dk_strides, void* dv, attn_strides3 dv_strides, const int64_t* offsets,
+                    int64_t num_seqs, int64_t H, int64_t total_len, int64_t D, int64_t max_seq_len, float sm_scale,
+                    int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common((int)dtype, D, sm_scale);
+  if (rc) return rc;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || H < 0 || total_len < 0 || max_seq_len < 1) return ATTN_ERR_INVALID;
+  if (num_seqs > INT_MAX - 1 || H > INT_MAX || total_len > INT_MAX) return ATTN_ERR_INVALID;
+  if (num_seqs == 0 || H == 0 || total_len == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv || !offsets) return ATTN_ERR_INVALID;
+  const attn_strides3* ss[] = {&q_strides, &k_strides, &v_strides, &o_strides, &do_strides,
+                               &dq_strides, &dk_strides, &dv_strides};
+  for (const attn_strides3* x : ss)
+    if ((rc = check_s3(*x, H, total_len, 8))) return rc;
+  const void* ptrs[] = {q, k, v, o, d_o, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  if (((uintptr_t)lse & 3u) != 0) return ATTN_ERR_UNSUPPORTED;
+  const int64_t cap = plan_capacity(num_seqs, total_len, 128);
+  const size_t need = jagged_attn_bwd_workspace_bytes(num_seqs, H, total_len);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u)) return ATTN_ERR_WORKSPACE;
+  if (cap * H > INT_MAX) return ATTN_ERR_INVALID;
+  const int mlen = (int)(max_seq_len < INT_MAX ? max_seq_len : INT_MAX);
+
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  int32_t* plan = (int32_t*)workspace;
+  hipLaunchKernelGGL(jagged_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, offsets, (int)num_seqs, total_len,
+                     mlen, causal ? 1 : 0, 128, kBnBwdDq, plan, (int)cap);
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+
+  const int64_t plan_bytes = (16 + 8 * cap + 15) / 16 * 16;
+  BwdArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = d_o; a.lse = lse; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.delta = (float*)((char*)workspace + plan_bytes);
+  a.lse2 = a.delta + H * total_len;
+  a.q_sh = q_strides.h; a.q_sn = q_strides.t;
+  a.k_sh = k_strides.h; a.k_sn = k_strides.t;
+  a.v_sh = v_strides.h; a.v_sn = v_strides.t;
+  a.o_sh = o_strides.h; a.o_sn = o_strides.t;
+  a.do_sh = do_strides.h; a.do_sn = do_strides.t;
+  a.dq_sh = dq_strides.h; a.dq_sn = dq_strides.t;
+  a.dk_sh = dk_strides.h; a.dk_sn = dk_strides.t;
+  a.dv_sh = dv_strides.h; a.dv_sn = dv_strides.t;
+  a.B = 1; a.H = (int)H; a.Nq = (int)total_len; a.Nkv = (int)total_len;  // the prep kernel's view
+  a.sm_scale = sm_scale;
+  a.c = sm_scale * kLog2e;
+  if (a.c == 0.f) a.c = 1.17549435e-38f;
+  a.causal = causal ? 1 : 0;
+  a.offsets = offsets;
+  a.plan = plan;
+  a.total_len = (int)total_len;
+  a.max_seq_len = mlen;
+  if (dtype == ATTN_FP16)
+    rc = D == 64 ? bwd_launch<64, true>(st, a, 1, H, total_len, total_len, cap)
+                 : bwd_launch<128, true>(st, a, 1, H, total_len, total_len, cap);
+  else
+    rc = D == 64 ? bwd_launch<64, false>(st, a, 1, H, total_len, total_len, cap)
+                 : bwd_launch<128, false>(st, a, 1, H, total_len, total_len, cap);
   if (rc) return rc;
   return finish(st);
 }

@@ -52,6 +52,24 @@ struct BwdArgs {
   float c;          // sm_scale * log2(e)
   float sm_scale;
   int32_t causal;
+  // jagged layout (offsets != nullptr): tensors are [H, total_len, D], the
+  // LSE and the workspace rows [H, total_len]; workgroups follow the plan
+  const int64_t* offsets;
+  const int32_t* plan;  // [0] item count, items (seq, 128-row tile) from index 4
+  int32_t total_len;
+  int32_t max_seq_len;
+};
+
+// One workgroup's share: element offsets of row 0 of its (batch|sequence,
+// head) in every tensor, and the extents of that slice.
+struct BwdTile {
+  int64_t q_off, k_off, v_off, do_off, dq_off, dk_off, dv_off;
+  int64_t row_base;  // index of row 0 in the LSE and workspace rows
+  int t;             // query tile (dQ kernel) or key tile (dK/dV kernel)
+  int Lstore;        // rows / keys [0, Lstore) exist and are written
+  int Lq;            // queries [0, Lq) take part
+  int Lkv;           // keys [0, Lkv) take part
+  bool valid;
 };
 
 // ---- delta_i = sum_d O_id dO_id and LSE_i log2(e), one row per D/8 lanes.
@@ -83,17 +101,60 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(BwdArgs a) {
   }
 }
 
-// Workgroup -> (batch, head, tile), XCD-aware like the forward (a run of
-// consecutive work items per XCD shares that XCD's L2 copy of a head).
-__device__ __forceinline__ void bwd_tile(const BwdArgs& a, int bid, int& b, int& h, int& t) {
-  const int per_head = a.n_tiles;
-  const int total = a.B * a.H * per_head;
-  int logical = bid;
-  if ((total & 7) == 0) logical = (bid & 7) * (total >> 3) + (bid >> 3);
-  const int bh = logical / per_head;
-  t = logical - bh * per_head;
-  b = bh / a.H;
-  h = bh - b * a.H;
+// Workgroup -> tile.  Dense: (batch, head, tile), XCD-aware like the forward
+// (a run of consecutive work items per XCD shares that XCD's L2 copy of a
+// head).  Jagged: item bid / H of the device-built plan, head bid % H; a
+// sequence's first min(len, max_seq_len) rows take part as queries and keys,
+// its later rows get zero gradients (SLL jagged page, backward).
+// `store_rows_are_keys` selects which extent Lstore describes (dK/dV: keys).
+__device__ __forceinline__ BwdTile bwd_tile(const BwdArgs& a, int bid, bool store_rows_are_keys) {
+  BwdTile t;
+  if (a.offsets == nullptr) {
+    const int per_head = a.n_tiles;
+    const int total = a.B * a.H * per_head;
+    int logical = bid;
+    if ((total & 7) == 0) logical = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int bh = logical / per_head;
+    t.t = logical - bh * per_head;
+    const int b = bh / a.H, h = bh - b * a.H;
+    t.q_off = b * a.q_sb + h * a.q_sh;
+    t.k_off = b * a.k_sb + h * a.k_sh;
+    t.v_off = b * a.v_sb + h * a.v_sh;
+    t.do_off = b * a.do_sb + h * a.do_sh;
+    t.dq_off = b * a.dq_sb + h * a.dq_sh;
+    t.dk_off = b * a.dk_sb + h * a.dk_sh;
+    t.dv_off = b * a.dv_sb + h * a.dv_sh;
+    t.row_base = (int64_t)bh * a.Nq;
+    t.Lq = a.Nq;
+    t.Lkv = a.Nkv;
+    t.Lstore = store_rows_are_keys ? a.Nkv : a.Nq;
+    t.valid = true;
+  } else {
+    const int item = bid / a.H, h = bid - item * a.H;
+    t.valid = item < a.plan[0];
+    if (!t.valid) return t;
+    const int seq = a.plan[4 + 2 * item];
+    t.t = a.plan[5 + 2 * item];
+    const int64_t T = a.total_len;
+    int64_t begin = a.offsets[seq], end = a.offsets[seq + 1];
+    begin = begin < 0 ? 0 : (begin > T ? T : begin);
+    end = end < begin ? begin : (end > T ? T : end);
+    const int len = (int)(end - begin);
+    const int used = len < a.max_seq_len ? len : a.max_seq_len;
+    t.q_off = h * a.q_sh + begin * a.q_sn;
+    t.k_off = h * a.k_sh + begin * a.k_sn;
+    t.v_off = h * a.v_sh + begin * a.v_sn;
+    t.do_off = h * a.do_sh + begin * a.do_sn;
+    t.dq_off = h * a.dq_sh + begin * a.dq_sn;
+    t.dk_off = h * a.dk_sh + begin * a.dk_sn;
+    t.dv_off = h * a.dv_sh + begin * a.dv_sn;
+    t.row_base = (int64_t)h * T + begin;
+    t.Lq = used;
+    t.Lkv = used;
+    t.Lstore = len;
+    t.valid = t.t * 128 < len;
+  }
+  return t;
 }
 
 // Direct global -> LDS copy of ROWS rows of D bf16 (row stride sn elements)
@@ -138,29 +199,31 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   lds_t* smem = (lds_t*)smem_raw;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
 
-  int b, h, qt;
-  bwd_tile(a, blockIdx.x, b, h, qt);
-  if (a.causal) qt = a.n_tiles - 1 - qt;  // heaviest first
+  const BwdTile t = bwd_tile(a, blockIdx.x, false);
+  if (!t.valid) return;
+  int qt = t.t;
+  if (a.causal && a.offsets == nullptr) qt = a.n_tiles - 1 - qt;  // heaviest first
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31, h32 = lane >> 5;
-  const bf16* Q = (const bf16*)a.q + b * a.q_sb + h * a.q_sh;
-  const bf16* K = (const bf16*)a.k + b * a.k_sb + h * a.k_sh;
-  const bf16* V = (const bf16*)a.v + b * a.v_sb + h * a.v_sh;
-  const bf16* DO = (const bf16*)a.dout + b * a.do_sb + h * a.do_sh;
-  const int64_t row_base = ((int64_t)b * a.H + h) * a.Nq;
+  const bf16* Q = (const bf16*)a.q + t.q_off;
+  const bf16* K = (const bf16*)a.k + t.k_off;
+  const bf16* V = (const bf16*)a.v + t.v_off;
+  const bf16* DO = (const bf16*)a.dout + t.do_off;
+  const int64_t row_base = t.row_base;
 
-  // rows: this lane's query and the wave's key limits
+  // rows: this lane's query and the wave's key limits (rows past Lq attend
+  // no key and get dQ = 0)
   const int w0 = qt * BM + wave * 32;
   const int my_row = w0 + n32;
-  const int r_cl = my_row < a.Nq ? my_row : a.Nq - 1;
-  auto lim = [&](int i) { return a.causal ? min(i + 1, a.Nkv) : a.Nkv; };
+  const int r_cl = my_row < t.Lstore ? my_row : t.Lstore - 1;
+  auto lim = [&](int i) { return i >= t.Lq ? 0 : (a.causal ? min(i + 1, t.Lkv) : t.Lkv); };
   const int my_lim = lim(r_cl);
-  const int w1 = min(w0 + 31, a.Nq - 1);
-  const int wave_max = w0 <= w1 ? lim(w1) : 0;
-  const int wave_min = w0 <= w1 ? lim(w0) : 0;
-  const int b1 = min(qt * BM + BM, a.Nq) - 1;
-  const int n_tiles = (lim(b1) + BN - 1) / BN;
+  const int w1 = min(w0 + 31, t.Lstore - 1);
+  const int wave_max = w0 <= w1 && w0 < t.Lq ? lim(min(w1, t.Lq - 1)) : 0;
+  const int wave_min = w0 <= w1 && w1 < t.Lq ? lim(w0) : 0;
+  const int b1 = min(qt * BM + BM, t.Lq) - 1;
+  const int n_tiles = qt * BM <= b1 ? (lim(b1) + BN - 1) / BN : 0;
 
   // Q and dO rows of this lane (B operands of S^T = K Q^T and dP^T = V dO^T)
   bf16x8 qf[KD], df[KD];
@@ -189,8 +252,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   f32x16 dummy_ts[1];
 
   auto fetch = [&](int j, int stage) {
-    bwd_dma_rows<D, BN, NW>(K + (int64_t)j * BN * a.k_sn, a.k_sn, 0, a.Nkv - j * BN, smem + stage * STAGE, wave, lane);
-    bwd_dma_rows<D, BN, NW>(V + (int64_t)j * BN * a.v_sn, a.v_sn, 0, a.Nkv - j * BN, smem + stage * STAGE + TILE, wave,
+    bwd_dma_rows<D, BN, NW>(K + (int64_t)j * BN * a.k_sn, a.k_sn, 0, t.Lkv - j * BN, smem + stage * STAGE, wave, lane);
+    bwd_dma_rows<D, BN, NW>(V + (int64_t)j * BN * a.v_sn, a.v_sn, 0, t.Lkv - j * BN, smem + stage * STAGE + TILE, wave,
                             lane);
   };
 
@@ -243,8 +306,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     if (j < n_tiles) step(j, std::integral_constant<int, 0>{});
   }
 
-  if (my_row < a.Nq) {
-    bf16* orow = (bf16*)a.dq + b * a.dq_sb + h * a.dq_sh + my_row * a.dq_sn;
+  if (my_row < t.Lstore) {
+    bf16* orow = (bf16*)a.dq + t.dq_off + my_row * a.dq_sn;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -278,26 +341,29 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
   lds_t* smem = (lds_t*)smem_raw;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
 
-  int b, h, kt;
-  bwd_tile(a, blockIdx.x, b, h, kt);  // causal: low key tiles see the most queries and run first
+  // dense causal: low key tiles see the most queries and run first
+  const BwdTile t = bwd_tile(a, blockIdx.x, true);
+  if (!t.valid) return;
+  const int kt = t.t;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31, h32 = lane >> 5;
-  const bf16* Q = (const bf16*)a.q + b * a.q_sb + h * a.q_sh;
-  const bf16* K = (const bf16*)a.k + b * a.k_sb + h * a.k_sh;
-  const bf16* V = (const bf16*)a.v + b * a.v_sb + h * a.v_sh;
-  const bf16* DO = (const bf16*)a.dout + b * a.do_sb + h * a.do_sh;
-  const int64_t row_base = ((int64_t)b * a.H + h) * a.Nq;
+  const bf16* Q = (const bf16*)a.q + t.q_off;
+  const bf16* K = (const bf16*)a.k + t.k_off;
+  const bf16* V = (const bf16*)a.v + t.v_off;
+  const bf16* DO = (const bf16*)a.dout + t.do_off;
+  const int64_t row_base = t.row_base;
 
-  // keys: this lane's key; the queries that can see the wave's keys
+  // keys: this lane's key; the queries that can see the wave's keys (keys
+  // past Lkv take no part and get dK = dV = 0)
   const int k0 = kt * BN + wave * 32;
   const int my_key = k0 + n32;
-  const int k_cl = my_key < a.Nkv ? my_key : a.Nkv - 1;
-  const bool wave_keys = k0 < a.Nkv;
+  const int k_cl = my_key < t.Lstore ? my_key : t.Lstore - 1;
+  const bool wave_keys = k0 < t.Lkv;
   const int q_first = a.causal ? kt * BN : 0;        // first query any key of the workgroup sees
   const int wave_q_first = a.causal ? k0 : 0;        // first query any key of this wave sees
   const int jq0 = q_first / BMQ;
-  const int n_qt = (a.Nq + BMQ - 1) / BMQ;
+  const int n_qt = (t.Lq + BMQ - 1) / BMQ;
 
   // K and V rows of this lane (B operands of S = Q K^T and dP = dO V^T)
   bf16x8 kf[KD], vf[KD];
@@ -331,10 +397,10 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
   auto fetch = [&](int jq, int stage) {
     const int q0 = jq * BMQ;
     lds_t* base = smem + stage * STAGE;
-    bwd_dma_rows<D, BMQ, NW>(Q, a.q_sn, q0, a.Nq, base, wave, lane);
-    bwd_dma_rows<D, BMQ, NW>(DO, a.do_sn, q0, a.Nq, base + TILE, wave, lane);
+    bwd_dma_rows<D, BMQ, NW>(Q, a.q_sn, q0, t.Lq, base, wave, lane);
+    bwd_dma_rows<D, BMQ, NW>(DO, a.do_sn, q0, t.Lq, base + TILE, wave, lane);
     if (wave == 0) {
-      const int qi = min(q0 + n32, a.Nq - 1);
+      const int qi = min(q0 + n32, t.Lq - 1);
       const float* src = (h32 ? a.delta : a.lse2) + row_base + qi;
       __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(base + 2 * TILE),
                                        4, 0, 0);
@@ -349,13 +415,13 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
       f32x16 s[1], dp[1];
       scores_section<D, 1, false, S * STAGE, 0, F16>(qaddr, kf, dummy_t, s, dummy_ts);          // S = Q K^T
       scores_section<D, 1, false, S * STAGE + TILE, 0, F16>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
-      // masked pairs (query past Nq; causal: key after query) get P = 0
-      const bool edge = q0 + BMQ > a.Nq || (a.causal && q0 < k0 + 32);
+      // masked pairs (query past Lq, key past Lkv; causal: key after query) get P = 0
+      const bool edge = q0 + BMQ > t.Lq || k0 + 32 > t.Lkv || (a.causal && q0 < k0 + 32);
       if (edge) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = q0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
-          if (qi >= a.Nq || (a.causal && my_key > qi)) s[0][r] = -INFINITY;
+          if (qi >= t.Lq || my_key >= t.Lkv || (a.causal && my_key > qi)) s[0][r] = -INFINITY;
         }
       }
       // register r holds query q0 + 16 (r / 8) + 8 h32 + r % 8; chunk c (the
@@ -388,7 +454,7 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
     __syncthreads();
   };
 
-  if (jq0 < n_qt) {
+  if (jq0 < n_qt && kt * BN < t.Lkv) {  // a tile of keys past Lkv only writes zeros
     fetch(jq0, 0);
     __syncthreads();
     int jq = jq0;
@@ -399,9 +465,9 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
     if (jq < n_qt) step(jq, std::integral_constant<int, 0>{});
   }
 
-  if (my_key < a.Nkv) {
-    bf16* krow_o = (bf16*)a.dk + b * a.dk_sb + h * a.dk_sh + my_key * a.dk_sn;
-    bf16* vrow_o = (bf16*)a.dv + b * a.dv_sb + h * a.dv_sh + my_key * a.dv_sn;
+  if (my_key < t.Lstore) {
+    bf16* krow_o = (bf16*)a.dk + t.dk_off + my_key * a.dk_sn;
+    bf16* vrow_o = (bf16*)a.dv + t.dv_off + my_key * a.dv_sn;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -19,7 +19,7 @@ launch, outside the events, which evicts L2 and the Infinity Cache).  `cpu_basel
 sample of the same workload (a few heads) on this host's cores.
 
 Profiling modes (for rocprofv3 runs): --only {fwd,fwd_causal,jvp,jvp_causal,
-causal_d64,jagged,bwd,bwd_causal,fwd_fp16,fwd_bias,fwd_mask} runs just that workload K times; --copy-calibration runs a
+causal_d64,jagged,bwd,bwd_causal,fwd_fp16,fwd_bias,fwd_mask,jagged_bwd} runs just that workload K times; --copy-calibration runs a
 plain device copy of known size (the scale for FETCH_SIZE / WRITE_SIZE).
 """
 
@@ -138,6 +138,14 @@ def make_cases(torch, attn, wl):
     cases["jagged"] = Case("jagged", lambda: attn.jagged_fwd(jq, jk, jv, off, w5.max_len, sm_scale=w5.sm_scale, workspace=ws),
                            jagged_flops(lengths.tolist(), w5.H, w5.D), 4 * jq.numel() * 2 + jq.shape[0] * jq.shape[1] * 4,
                            f"{w5.name}: 256 sequences U[1,1024], H=8 D=128 bf16, total_len={jq.shape[1]}")
+    # jagged backward over the same sequences, from the forward's O and LSE
+    jo, jl = attn.jagged_fwd(jq, jk, jv, off, w5.max_len, sm_scale=w5.sm_scale, workspace=ws)
+    jdo = wl.grad_output(jq.shape, "bf16", 0).to(dev)
+    jws = torch.empty(attn.jagged_bwd_workspace_bytes(w5.num_seqs, w5.H, jq.shape[1]), dtype=torch.uint8, device=dev)
+    cases["jagged_bwd"] = Case("jagged_bwd", lambda: attn.jagged_bwd(jq, jk, jv, jo, jdo, jl, off, w5.max_len,
+                                                                     sm_scale=w5.sm_scale, workspace=jws),
+                               2.5 * jagged_flops(lengths.tolist(), w5.H, w5.D), 8 * jq.numel() * 2 + jq.shape[0] * jq.shape[1] * 4,
+                               f"{w5.name} backward: 256 sequences U[1,1024], H=8 D=128 bf16 (dQ, dK, dV)")
     return cases
 
 
@@ -285,7 +293,7 @@ def main():
 
     extra = {"fwd": summary(head, durs, time_launches(torch, head, n_cold, 2, flush)[0])}
     for name in ("fwd_causal", "fwd_fp16", "fwd_bias", "fwd_mask", "jvp", "jvp_causal", "causal_d64", "jagged", "bwd",
-                 "bwd_causal"):
+                 "bwd_causal", "jagged_bwd"):
         c = cases[name]
         dw, _ = time_launches(torch, c, max(5, args.steps // 2), 10)
         dc, _ = time_launches(torch, c, n_cold, 2, flush)

@@ -236,6 +236,52 @@ ATTN_API int attn_bwd(attn_dtype dtype,
              float sm_scale, int causal,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace jagged_attn_bwd needs (host function, no GPU
+ * access): the tile plan plus two fp32 values per row of every head.
+ * Returns 0 for invalid sizes.
+ */
+ATTN_API size_t jagged_attn_bwd_workspace_bytes(int64_t num_seqs, int64_t H, int64_t total_len);
+
+/*
+ * Jagged multi-head attention backward: the gradients of jagged_attn_fwd's
+ * output for a given d_o (FBGEMM SLL page,
+ * triton_multi_head_jagged_flash_attention.py:
+ * _multi_head_jagged_flash_attention_bwd_preprocess_kernel,
+ * _multi_head_jagged_flash_attention_bwd_kernel and
+ * multi_head_jagged_flash_attention_bwd), with the steps of attn_bwd applied
+ * to each sequence (delta from this library's O, which is not divided by
+ * max_seq_len).
+ *   q, k, v, o, d_o, dq, dk, dv  [H, total_len, D]  (bf16 or fp16)
+ *   lse        [H, total_len] contiguous fp32: what jagged_attn_fwd wrote
+ *   offsets    as jagged_attn_fwd (DEVICE int64 [num_seqs + 1], not checked,
+ *              clamped so that no access leaves the buffers)
+ *   Within sequence s only the first min(len_s, max_seq_len) rows take part,
+ *   as queries and as keys; dq, dk and dv of its later rows are written as 0.
+ *   workspace  DEVICE scratch of at least jagged_attn_bwd_workspace_bytes(...)
+ *              bytes, 16-byte aligned; contents on entry are ignored.  Calls
+ *              that share a workspace must not overlap.
+ * Strides, alignment, sm_scale and D as jagged_attn_fwd; causal masks key
+ * j > query i within a sequence.  Every element of dq, dk, dv inside a
+ * sequence is written once by one thread (deterministic); rows outside every
+ * sequence are not touched.  ATTN_FP32 returns ATTN_ERR_UNSUPPORTED.  Four
+ * kernels are enqueued on `stream` (plan, prep, dQ, dK/dV).
+ */
+ATTN_API int jagged_attn_bwd(attn_dtype dtype,
+                    const void* q, attn_strides3 q_strides,
+                    const void* k, attn_strides3 k_strides,
+                    const void* v, attn_strides3 v_strides,
+                    const void* o, attn_strides3 o_strides,
+                    const void* d_o, attn_strides3 do_strides,
+                    const float* lse,
+                    void* dq, attn_strides3 dq_strides,
+                    void* dk, attn_strides3 dk_strides,
+                    void* dv, attn_strides3 dv_strides,
+                    const int64_t* offsets,
+                    int64_t num_seqs, int64_t H, int64_t total_len, int64_t D,
+                    int64_t max_seq_len, float sm_scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable text for a status code (host, static storage). */
 ATTN_API const char* attn_status_string(int status);
 

@@ -33,7 +33,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(
         ["attn_fwd", "attn_fwd_bias", "attn_fwd_jvp", "jagged_attn_workspace_bytes", "jagged_attn_fwd",
-         "attn_bwd_workspace_bytes", "attn_bwd", "attn_status_string"])
+         "attn_bwd_workspace_bytes", "attn_bwd", "jagged_attn_bwd_workspace_bytes", "jagged_attn_bwd",
+         "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -176,3 +177,25 @@ def test_bwd_validation(lib):
     zero = lib.attn_bwd(BF16, 0, st, 0, st, 0, st, 0, st, 0, st, 0, 0, st, 0, st, 0, st,
                         0, H, N, N, D, 0.125, 0, 0, 0, None)
     assert zero == OK
+
+
+def test_jagged_bwd_validation(lib):
+    H, T, D, S = 2, 100, 64, 3
+    st = Strides3(T * D, D, 1)
+    need = lib.jagged_attn_bwd_workspace_bytes(S, H, T)
+    assert need >= 16 + 8 * ((T + S * 127) // 128) + 8 * H * T and need % 16 == 0
+    assert lib.jagged_attn_bwd_workspace_bytes(-1, H, T) == 0
+
+    def call(dtype=BF16, ws=P, ws_bytes=need, msl=64, D=64, offsets=P, lse=P, dq=P, H=H):
+        return lib.jagged_attn_bwd(dtype, P, st, P, st, P, st, P, st, P, st, lse, dq, st, P, st, P, st,
+                                   offsets, S, H, T, D, msl, 0.125, 0, ws, ws_bytes, None)
+    assert call(dtype=FP32) == UNSUPPORTED
+    assert call(D=48) == UNSUPPORTED
+    assert call(ws=0) == WORKSPACE
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert call(ws=P + 8) == WORKSPACE
+    assert call(msl=0) == INVALID
+    assert call(offsets=0) == INVALID
+    assert call(lse=0) == INVALID
+    assert call(dq=0) == INVALID
+    assert call(H=0) == OK

@@ -1,0 +1,67 @@
+"""GPU parity of the jagged backward (jagged_attn_bwd through the C ABI, fed
+with jagged_attn_fwd's own O and LSE) against the fp64 oracle's gradients.
+
+Sequences of length 0, 1, odd, exactly one 128-row tile, several tiles, and
+longer than max_seq_len (whose later rows must get zero gradients); causal
+and not; D 64 and 128; bf16 and fp16.  Bound per gradient, as for the dense
+backward: max|g - g_ref| <= rel * max|g_ref| + 1e-5 with rel = 3e-2 (bf16)
+or 1e-2 (fp16).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import attention_forward_online_attn_amd as attn
+from attention_forward_online_attn_amd import workloads as wl
+from parity import host64
+
+pytestmark = pytest.mark.gpu
+
+REL = {"bf16": 3e-2, "fp16": 1e-2}
+ABS = 1e-5
+
+
+def jagged_bwd_case(lengths, H, D, dtype, max_seq_len, causal=False, seed=0):
+    lengths = torch.as_tensor(lengths, dtype=torch.int64)
+    q, k, v, off = wl.jagged_inputs(lengths, H, D, dtype, seed)
+    do = wl.grad_output(q.shape, dtype, seed)
+    scale = D ** -0.5
+    qc, kc, vc, oc, doc = (t.cuda() for t in (q, k, v, off, do))
+    o, lse = attn.jagged_fwd(qc, kc, vc, oc, max_seq_len=max_seq_len, causal=causal, sm_scale=scale)
+    got = attn.jagged_bwd(qc, kc, vc, o, doc, lse, oc, max_seq_len, causal=causal, sm_scale=scale)
+    ref = oracle.jagged_attention_bwd(q, k, v, do, off.numpy(), max_seq_len, oracle.scale_as_passed(scale), causal)
+    msgs, ok = [], True
+    offs = off.numpy()
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = host64(g)
+        gmax = float(np.max(np.abs(r), initial=0.0))
+        diff = float(np.max(np.abs(g - r), initial=0.0)) if np.all(np.isfinite(g)) else np.inf
+        ok = ok and diff <= REL[dtype] * gmax + ABS
+        msgs.append(f"{name} {diff / max(gmax, 1e-30):.2e}")
+        # rows past max_seq_len inside each sequence are exactly zero
+        for s in range(len(lengths)):
+            a, b = int(offs[s]), int(offs[s + 1])
+            ok = ok and bool(np.all(g[:, a + min(b - a, max_seq_len):b] == 0))
+    msg = (f"jagged bwd {lengths.tolist()[:6]}.. H={H} D={D} {dtype} msl={max_seq_len} causal={causal}: "
+           f"max|dg|/max|g| " + ", ".join(msgs))
+    print(msg, flush=True)
+    assert ok, msg
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_jagged_bwd_edges(gpu_lib, D, causal):
+    jagged_bwd_case([5, 0, 300, 64, 129, 1, 128, 700], 3, D, "bf16", 256, causal, seed=80 + D)
+
+
+def test_jagged_bwd_fp16(gpu_lib):
+    jagged_bwd_case([33, 1000, 0, 250], 2, 128, "fp16", 512, True, seed=81)
+    jagged_bwd_case([33, 1000, 0, 250], 2, 64, "fp16", 1024, False, seed=82)
+
+
+def test_jagged_bwd_many_sequences(gpu_lib):
+    lengths = wl.jagged_lengths(64, 300, seed_base=83)
+    jagged_bwd_case(lengths.tolist(), 2, 128, "bf16", 200, False, seed=83)
+    jagged_bwd_case(lengths.tolist(), 2, 64, "bf16", 300, True, seed=84)
