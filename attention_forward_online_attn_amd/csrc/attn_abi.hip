@@ -51,7 +51,7 @@ bool stride_ok(int64_t stride, int64_t extent, int64_t vec) {
 int check_common(int dtype, int64_t D, float sm_scale) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP32 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale) || sm_scale < 0.f) return ATTN_ERR_INVALID;
-  if (D != 64 && D != 128) return D <= 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 128) return D <= 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -67,6 +67,15 @@ int check_s3(const attn_strides3& s, int64_t H, int64_t T, int64_t vec) {
   if (s.h < 0 || s.t < 0) return ATTN_ERR_INVALID;
   if (!stride_ok(s.h, H, vec) || !stride_ok(s.t, T, vec)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
+}
+
+// Calls f(std::integral_constant<int, D>) for a supported head dim (checked
+// before: 32, 64 or 128).
+template <class F>
+auto by_dim(int64_t D, F&& f) {
+  if (D == 32) return f(std::integral_constant<int, 32>{});
+  if (D == 64) return f(std::integral_constant<int, 64>{});
+  return f(std::integral_constant<int, 128>{});
 }
 
 // One compiled forward kernel with its tile shape.
@@ -113,20 +122,22 @@ bool use_pairs(int dtype, int D, bool jvp, bool dense_causal, int64_t unpaired_g
 
 template <bool F16>
 KernelChoice choose16(int D, bool jvp, bool paired) {
-  if (paired) return !jvp ? (D == 64 ? r32<64, kBnDense, false, 8, F16>() : r32<128, kBnDense, false, 8, F16>())
-                          : r32<64, kBnJvp, true, 8, F16>();
-  if (!jvp) return D == 64 ? r32<64, kBnDense, false, 4, F16>() : r32<128, kBnDense, false, 4, F16>();
-  return D == 64 ? r32<64, kBnJvp, true, 4, F16>() : r32<128, kBnJvp, true, 4, F16>();
+  return by_dim(D, [&](auto d) {
+    constexpr int Dc = decltype(d)::value;
+    if (paired) return !jvp ? r32<Dc, kBnDense, false, 8, F16>() : r32<Dc == 128 ? 64 : Dc, kBnJvp, true, 8, F16>();
+    return !jvp ? r32<Dc, kBnDense, false, 4, F16>() : r32<Dc, kBnJvp, true, 4, F16>();
+  });
 }
 
 // Biased forward (no JVP, never paired): one instance per dtype, D and kind.
 template <int BIAS>
 KernelChoice choose_bias(int dtype, int D) {
-  if (dtype == ATTN_BF16)
-    return D == 64 ? r32<64, kBnDense, false, 4, false, BIAS>() : r32<128, kBnDense, false, 4, false, BIAS>();
-  if (dtype == ATTN_FP16)
-    return D == 64 ? r32<64, kBnDense, false, 4, true, BIAS>() : r32<128, kBnDense, false, 4, true, BIAS>();
-  return D == 64 ? f32k<64, false, BIAS>() : f32k<128, false, BIAS>();
+  return by_dim(D, [&](auto d) {
+    constexpr int Dc = decltype(d)::value;
+    if (dtype == ATTN_BF16) return r32<Dc, kBnDense, false, 4, false, BIAS>();
+    if (dtype == ATTN_FP16) return r32<Dc, kBnDense, false, 4, true, BIAS>();
+    return f32k<Dc, false, BIAS>();
+  });
 }
 
 KernelChoice choose(int dtype, int D, bool jvp, bool paired, int bias_kind) {
@@ -134,8 +145,10 @@ KernelChoice choose(int dtype, int D, bool jvp, bool paired, int bias_kind) {
   if (bias_kind == kMaskBias) return choose_bias<kMaskBias>(dtype, D);
   if (dtype == ATTN_BF16) return choose16<false>(D, jvp, paired);
   if (dtype == ATTN_FP16) return choose16<true>(D, jvp, paired);
-  if (!jvp) return D == 64 ? f32k<64, false>() : f32k<128, false>();
-  return D == 64 ? f32k<64, true>() : f32k<128, true>();
+  return by_dim(D, [&](auto d) {
+    constexpr int Dc = decltype(d)::value;
+    return jvp ? f32k<Dc, true>() : f32k<Dc, false>();
+  });
 }
 
 int launch(const KernelChoice& k, int grid, hipStream_t stream, const FwdArgs& a) {
@@ -412,12 +425,11 @@ int jagged_attn_bwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   a.plan = plan;
   a.total_len = (int)total_len;
   a.max_seq_len = mlen;
-  if (dtype == ATTN_FP16)
-    rc = D == 64 ? bwd_launch<64, true>(st, a, 1, H, total_len, total_len, cap)
-                 : bwd_launch<128, true>(st, a, 1, H, total_len, total_len, cap);
-  else
-    rc = D == 64 ? bwd_launch<64, false>(st, a, 1, H, total_len, total_len, cap)
-                 : bwd_launch<128, false>(st, a, 1, H, total_len, total_len, cap);
+  rc = by_dim(D, [&](auto d) {
+    constexpr int Dc = decltype(d)::value;
+    return dtype == ATTN_FP16 ? bwd_launch<Dc, true>(st, a, 1, H, total_len, total_len, cap)
+                              : bwd_launch<Dc, false>(st, a, 1, H, total_len, total_len, cap);
+  });
   if (rc) return rc;
   return finish(st);
 }
@@ -478,10 +490,10 @@ int attn_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const voi
   a.causal = causal ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
-  if (dtype == ATTN_FP16)
-    rc = D == 64 ? bwd_launch<64, true>(st, a, B, H, Nq, Nkv) : bwd_launch<128, true>(st, a, B, H, Nq, Nkv);
-  else
-    rc = D == 64 ? bwd_launch<64, false>(st, a, B, H, Nq, Nkv) : bwd_launch<128, false>(st, a, B, H, Nq, Nkv);
+  rc = by_dim(D, [&](auto d) {
+    constexpr int Dc = decltype(d)::value;
+    return dtype == ATTN_FP16 ? bwd_launch<Dc, true>(st, a, B, H, Nq, Nkv) : bwd_launch<Dc, false>(st, a, B, H, Nq, Nkv);
+  });
   if (rc) return rc;
   return finish(st);
 }

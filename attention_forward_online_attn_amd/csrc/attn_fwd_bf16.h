@@ -89,15 +89,20 @@ __device__ __forceinline__ float from16(bf16 x) {
 // 16-byte-chunk XOR swizzle of a [rows][D] bf16 tile in LDS.  Conflict free
 // for: 16 lanes reading one chunk of 16 different rows (K fragments), the
 // transposing reads of 4 consecutive rows x 64 bytes (V fragments), and
-// 16 lanes writing consecutive chunks (tile stores).
+// 16 lanes writing consecutive chunks (tile stores).  The 64 banks span 256
+// bytes: a row of D = 128 fills them (the chunk is XORed with a bijection of
+// row % 16), D = 64 rows share them in pairs (bijection of (row / 2) % 8),
+// D = 32 rows in fours (row 4a + b, chunk c lands in slot 4 b + (c ^ a)).
 template <int D>
 __device__ __forceinline__ int swz_f(int row) {
   if constexpr (D == 128) {
     const int u = row & 15;
     return ((u & 3) << 2) | (u >> 2);
-  } else {
+  } else if constexpr (D == 64) {
     const int u = (row >> 1) & 7;
     return ((u & 1) << 2) | (u >> 1);
+  } else {
+    return (row >> 2) & 3;
   }
 }
 
@@ -330,7 +335,7 @@ struct Bf16Cfg {
   static constexpr int LOADS = (BN * CPR + THREADS - 1) / THREADS;
   static constexpr int WAVES_PER_EU = (JVP && D == 128) ? 1 : 2;
   static_assert((BN * CPR) % THREADS == 0 || BN * CPR < THREADS, "tile must split evenly over the workgroup");
-  static_assert(BN % 32 == 0 && (D == 64 || D == 128), "unsupported tile");
+  static_assert(BN % 32 == 0 && (D == 32 || D == 64 || D == 128), "unsupported tile");
 };
 
 template <int D, int BN, bool JVP, int NW_ = 4, bool F16 = false, int BIAS = kNoBias>

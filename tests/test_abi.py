@@ -119,7 +119,7 @@ def test_jvp_validation(lib):
                                                      1, 1, 64, 64, D, 0.125, 0, None)
     assert args(tq=0) == INVALID
     assert args(to=0) == INVALID
-    assert args(D=32) == UNSUPPORTED
+    assert args(D=48) == UNSUPPORTED
 
 
 def test_jagged_validation(lib):
