@@ -61,6 +61,9 @@ def load_library():
     lib.attn_fwd_bias.argtypes = [i32, vp, S4, vp, S4, vp, S4, vp, S4, vp, vp, i32, S4,
                                   i64, i64, i64, i64, i64, f32, i32, vp]
     lib.attn_fwd_bias.restype = i32
+    lib.attn_fwd_dv.argtypes = [i32, vp, vp, vp, vp, vp, vp, S4, S4, S4, vp, vp, S4, vp, vp,
+                                i64, i64, i64, i64, i64, i64, f32, i32, vp]
+    lib.attn_fwd_dv.restype = i32
     lib.attn_fwd_jvp.argtypes = [i32, vp, vp, vp, vp, vp, vp, S4, S4, S4, vp, vp, S4, vp, vp,
                                  i64, i64, i64, i64, i64, f32, i32, vp]
     lib.attn_fwd_jvp.restype = i32
@@ -126,15 +129,22 @@ def _same(ref, *ts):
 
 
 def fwd(q, k, v, causal=False, sm_scale=None):
-    """Dense forward.  q [B,H,Nq,D], k/v [B,H,Nkv,D] -> (o [B,H,Nq,D], lse fp32 [B,H,Nq])."""
+    """Dense forward.  q [B,H,Nq,D], k [B,H,Nkv,D], v [B,H,Nkv,Dv] ->
+    (o [B,H,Nq,Dv], lse fp32 [B,H,Nq]); Dv != D goes through attn_fwd_dv."""
     lib = load_library()
     _same(q, k, v)
     B, H, Nq, D = q.shape
-    Nkv = k.shape[2]
+    Nkv, Dv = k.shape[2], v.shape[3]
     if sm_scale is None:
         sm_scale = D ** -0.5
-    o = torch.empty((B, H, Nq, D), dtype=q.dtype, device=q.device)
+    o = torch.empty((B, H, Nq, Dv), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if Dv != D:
+        none = ctypes.c_void_p(0)
+        _check(lib.attn_fwd_dv(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), none, none, none, _s4(q), _s4(k), _s4(v),
+                               _ptr(o), none, _s4(o), _ptr(lse), none, B, H, Nq, Nkv, D, Dv,
+                               float(sm_scale), int(bool(causal)), _stream(q)))
+        return o, lse
     _check(lib.attn_fwd(_dtype_code(q), _ptr(q), _s4(q), _ptr(k), _s4(k), _ptr(v), _s4(v),
                         _ptr(o), _s4(o), _ptr(lse), B, H, Nq, Nkv, D,
                         float(sm_scale), int(bool(causal)), _stream(q)))
@@ -180,16 +190,21 @@ def fwd_jvp(q, k, v, tq, tk, tv, causal=False, sm_scale=None, return_tlse=False)
         if t.shape != p.shape or t.stride() != p.stride():
             raise AttnError("tangents must match their primals in shape and strides")
     B, H, Nq, D = q.shape
-    Nkv = k.shape[2]
+    Nkv, Dv = k.shape[2], v.shape[3]
     if sm_scale is None:
         sm_scale = D ** -0.5
-    o = torch.empty((B, H, Nq, D), dtype=q.dtype, device=q.device)
+    o = torch.empty((B, H, Nq, Dv), dtype=q.dtype, device=q.device)
     to = torch.empty_like(o)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     tlse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if return_tlse else None
-    _check(lib.attn_fwd_jvp(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
-                            _s4(q), _s4(k), _s4(v), _ptr(o), _ptr(to), _s4(o), _ptr(lse), _ptr(tlse),
-                            B, H, Nq, Nkv, D, float(sm_scale), int(bool(causal)), _stream(q)))
+    if Dv != D:
+        _check(lib.attn_fwd_dv(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                               _s4(q), _s4(k), _s4(v), _ptr(o), _ptr(to), _s4(o), _ptr(lse), _ptr(tlse),
+                               B, H, Nq, Nkv, D, Dv, float(sm_scale), int(bool(causal)), _stream(q)))
+    else:
+        _check(lib.attn_fwd_jvp(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                                _s4(q), _s4(k), _s4(v), _ptr(o), _ptr(to), _s4(o), _ptr(lse), _ptr(tlse),
+                                B, H, Nq, Nkv, D, float(sm_scale), int(bool(causal)), _stream(q)))
     return (o, to, lse, tlse) if return_tlse else (o, to, lse)
 
 

@@ -2,9 +2,11 @@
 
     python -m attention_forward_online_attn_amd.build
 
-Compiles every time it is called.  Flags: -O3, gfx950 only, packed fp32 vector
-instructions disabled (-packed-fp32-ops), hidden visibility with the C ABI of
-include/attn.h exported.
+Compiles every time it is called: each csrc/*.hip translation unit (the host
+code and one file per kernel family) to an object, in parallel, then one link.
+Flags: -O3, gfx950 only, packed fp32 vector instructions disabled
+(-packed-fp32-ops), hidden visibility with the C ABI of include/attn.h
+exported.
 """
 
 from __future__ import annotations
@@ -12,39 +14,64 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = [os.path.join(PKG, "csrc", "attn_abi.hip")]
+CSRC = os.path.join(PKG, "csrc")
+# host code (attn_abi.hip) and one translation unit per kernel family (inst_*.hip)
+SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 OUTPUT = os.path.join(PKG, "libattn_mi355x.so")
 
-FLAGS = [
+COMPILE_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
+# one-step build of a single source (used by tools that compile one file)
+FLAGS = [*COMPILE_FLAGS, "-shared"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = OUTPUT + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def _noise(stderr: str):
     # hipcc's host pass does not know the packed-fp32 feature; drop that warning only
-    noise = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()
-             and not ln.startswith("1 warning generated") and not ln.endswith("warnings generated.")]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stderr)
-    if noise and verbose:
-        print("\n".join(noise), file=sys.stderr)
+    return [ln for ln in stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()
+            and not ln.startswith("1 warning generated") and not ln.endswith("warnings generated.")]
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every csrc/*.hip to an object in parallel, then link the
+    shared library (replaced atomically)."""
+    jobs = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1))
+    with tempfile.TemporaryDirectory(prefix="attn_build_") as tmpdir:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = [HIPCC, *COMPILE_FLAGS, "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(compile_one, SOURCES))
+        for (obj, res), src in zip(results, SOURCES):
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n" + res.stderr)
+            if verbose and _noise(res.stderr):
+                print("\n".join(_noise(res.stderr)), file=sys.stderr)
+        tmp = OUTPUT + ".tmp"
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fvisibility=hidden",
+               *[obj for obj, _ in results], "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n" + res.stderr)
     os.replace(tmp, OUTPUT)
     return OUTPUT
 

@@ -13,17 +13,12 @@
 
 #include "../../include/attn.h"
 #include "attn_common.h"
-#include "attn_bwd_bf16.h"
-#include "attn_fwd_bf16.h"
-#include "attn_fwd_f32.h"
+#include "attn_dispatch.h"
 #include "jagged_plan.h"
 
 namespace attn {
 namespace {
 
-// Tile shapes of the bf16 kernel (query tile 128 rows = 4 waves x 32).
-constexpr int kBnDense = 64;    // keys per tile, plain forward
-constexpr int kBnJvp = 32;      // keys per tile, JVP (four streamed tensors)
 constexpr int kPlanBmMin = 64;  // smallest query tile of any kernel (workspace bound)
 
 bool debug_sync() {
@@ -69,34 +64,6 @@ int check_s3(const attn_strides3& s, int64_t H, int64_t T, int64_t vec) {
   return ATTN_OK;
 }
 
-// Calls f(std::integral_constant<int, D>) for a supported head dim (checked
-// before: 32, 64 or 128).
-template <class F>
-auto by_dim(int64_t D, F&& f) {
-  if (D == 32) return f(std::integral_constant<int, 32>{});
-  if (D == 64) return f(std::integral_constant<int, 64>{});
-  return f(std::integral_constant<int, 128>{});
-}
-
-// One compiled forward kernel with its tile shape.
-struct KernelChoice {
-  void (*fn)(FwdArgs);
-  int BM;       // query rows per workgroup
-  int BN;       // keys per tile
-  int lds;      // dynamic LDS bytes
-  int threads;  // workgroup size
-};
-
-template <int D, int BN, bool JVP, int NW = 4, bool F16 = false, int BIAS = kNoBias>
-KernelChoice r32() {
-  using C = Bf16Cfg<D, BN, JVP, NW>;
-  return {attn_fwd_bf16_kernel<D, BN, JVP, NW, F16, BIAS>, C::BM, BN, C::LDS, C::THREADS};
-}
-template <int D, bool JVP, int BIAS = kNoBias>
-KernelChoice f32k() {
-  return {attn_fwd_f32_kernel<D, JVP, BIAS>, F32Cfg<D, JVP>::BM, F32Cfg<D, JVP>::BN, F32Cfg<D, JVP>::LDS, 256};
-}
-
 // Compute units of the current device (queried once per device).
 int cu_count() {
   static std::atomic<int> cache[64];
@@ -120,35 +87,13 @@ bool use_pairs(int dtype, int D, bool jvp, bool dense_causal, int64_t unpaired_g
   return dtype != ATTN_FP32 && dense_causal && !(jvp && D == 128) && unpaired_grid <= 4 * (int64_t)cu_count();
 }
 
-template <bool F16>
-KernelChoice choose16(int D, bool jvp, bool paired) {
-  return by_dim(D, [&](auto d) {
-    constexpr int Dc = decltype(d)::value;
-    if (paired) return !jvp ? r32<Dc, kBnDense, false, 8, F16>() : r32<Dc == 128 ? 64 : Dc, kBnJvp, true, 8, F16>();
-    return !jvp ? r32<Dc, kBnDense, false, 4, F16>() : r32<Dc, kBnJvp, true, 4, F16>();
-  });
-}
-
-// Biased forward (no JVP, never paired): one instance per dtype, D and kind.
-template <int BIAS>
-KernelChoice choose_bias(int dtype, int D) {
-  return by_dim(D, [&](auto d) {
-    constexpr int Dc = decltype(d)::value;
-    if (dtype == ATTN_BF16) return r32<Dc, kBnDense, false, 4, false, BIAS>();
-    if (dtype == ATTN_FP16) return r32<Dc, kBnDense, false, 4, true, BIAS>();
-    return f32k<Dc, false, BIAS>();
-  });
-}
-
-KernelChoice choose(int dtype, int D, bool jvp, bool paired, int bias_kind) {
-  if (bias_kind == kAddBias) return choose_bias<kAddBias>(dtype, D);
-  if (bias_kind == kMaskBias) return choose_bias<kMaskBias>(dtype, D);
-  if (dtype == ATTN_BF16) return choose16<false>(D, jvp, paired);
-  if (dtype == ATTN_FP16) return choose16<true>(D, jvp, paired);
-  return by_dim(D, [&](auto d) {
-    constexpr int Dc = decltype(d)::value;
-    return jvp ? f32k<Dc, true>() : f32k<Dc, false>();
-  });
+// Forward kernel for a dtype, head dims and variant (instance tables in the
+// inst_*.hip translation units).
+KernelChoice choose(int dtype, int D, bool jvp, bool paired, int bias_kind, int Dv) {
+  if (bias_kind != kNoBias) return fwd_bias(dtype, bias_kind, D);
+  if (dtype == ATTN_FP32) return fwd_f32(D, Dv, jvp);
+  if (Dv != D) return dtype == ATTN_BF16 ? fwd_mixed_bf16(D, Dv, jvp) : fwd_mixed_fp16(D, Dv, jvp);
+  return dtype == ATTN_BF16 ? fwd_bf16(D, jvp, paired) : fwd_fp16(D, jvp, paired);
 }
 
 int launch(const KernelChoice& k, int grid, hipStream_t stream, const FwdArgs& a) {
@@ -169,9 +114,11 @@ struct BiasOperand {
 int dense(int dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk, const void* tv,
           attn_strides4 sq, attn_strides4 sk, attn_strides4 sv, void* o, void* to, attn_strides4 so, float* lse,
           float* tlse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal,
-          void* stream, bool jvp, const BiasOperand& bias = BiasOperand()) {
+          void* stream, bool jvp, const BiasOperand& bias = BiasOperand(), int64_t Dv = 0) {
   int rc = check_common(dtype, D, sm_scale);
   if (rc) return rc;
+  if (Dv == 0) Dv = D;
+  if (Dv != 32 && Dv != 64 && Dv != 128) return Dv < 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
   if (causal && Nq != Nkv) return ATTN_ERR_CAUSAL_SHAPE;
   if (B * H * Nq == 0) return ATTN_OK;
@@ -195,8 +142,9 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   const int bias_kind = Nkv > 0 ? bias.kind : kNoBias;  // no key: nothing to read
 
   const int64_t n_qtiles = (Nq + 127) / 128;  // every bf16 instance uses 128-row q-tiles
-  const bool paired = bias_kind == kNoBias && use_pairs(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
-  const KernelChoice kc = choose(dtype, (int)D, jvp, paired, bias_kind);
+  const bool paired =
+      bias_kind == kNoBias && Dv == D && use_pairs(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
+  const KernelChoice kc = choose(dtype, (int)D, jvp, paired, bias_kind, (int)Dv);
   const int BM = kc.BM;
   const int64_t n_qtiles_k = (Nq + BM - 1) / BM;
   const int64_t grid = B * H * (paired ? (n_qtiles_k + 1) / 2 : n_qtiles_k);
@@ -228,40 +176,6 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   return finish(st);
 }
 
-template <class F>
-int launch_fn(F* fn, int grid, int threads, int lds, hipStream_t stream, const BwdArgs& a) {
-  if (grid <= 0) return ATTN_OK;
-  if (lds > 65536 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-    return ATTN_ERR_HIP;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), lds, stream, a);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
-// Key tiles of the dQ kernel (keys streamed per step).
-constexpr int kBnBwdDq = 32;
-
-// Dense: B*H*Nq rows, grids over (batch, head, tile).  Jagged (a.offsets
-// set): the prep kernel sees H*total_len rows as one batch (B = 1,
-// Nq = total_len, batch strides 0) and both gradient kernels cover `items`
-// plan items per head.
-template <int D, bool F16>
-int bwd_launch(hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t items = 0) {
-  const int64_t rows = B * H * Nq;
-  constexpr int rpb = 256 / (D / 8);
-  int rc = launch_fn(attn_bwd_prep_kernel<D, F16>, (int)((rows + rpb - 1) / rpb), 256, 0, st, a);
-  if (rc) return rc;
-  using Cq = BwdDqCfg<D, kBnBwdDq>;
-  using Ck = BwdDkdvCfg<D>;
-  static_assert(Cq::BM == 128 && Ck::BN == 128, "the jagged plan's tiles are 128 rows");
-  a.n_tiles = (int)((Nq + Cq::BM - 1) / Cq::BM);
-  const int64_t gq = a.offsets ? items * H : B * H * a.n_tiles;
-  rc = launch_fn(attn_bwd_dq_kernel<D, kBnBwdDq, F16>, (int)gq, Cq::THREADS, Cq::LDS, st, a);
-  if (rc) return rc;
-  a.n_tiles = (int)((Nkv + Ck::BN - 1) / Ck::BN);
-  const int64_t gk = a.offsets ? items * H : B * H * a.n_tiles;
-  return launch_fn(attn_bwd_dkdv_kernel<D, F16>, (int)gk, Ck::THREADS, Ck::LDS, st, a);
-}
 
 int64_t plan_capacity(int64_t num_seqs, int64_t total_len, int BM) {
   // sum_s ceil(len_s / BM) <= floor((total_len + num_seqs (BM - 1)) / BM)
@@ -293,6 +207,17 @@ int attn_fwd_bias(attn_dtype dtype, const void* q, attn_strides4 q_strides, cons
   b.strides = bias_strides;
   return dense((int)dtype, q, k, v, nullptr, nullptr, nullptr, q_strides, k_strides, v_strides, o, nullptr,
                o_strides, lse, nullptr, B, H, Nq, Nkv, D, sm_scale, causal, stream, false, b);
+}
+
+int attn_fwd_dv(attn_dtype dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk,
+                const void* tv, attn_strides4 q_strides, attn_strides4 k_strides, attn_strides4 v_strides, void* o,
+                void* to, attn_strides4 o_strides, float* lse, float* tlse, int64_t B, int64_t H, int64_t Nq,
+                int64_t Nkv, int64_t Dqk, int64_t Dv, float sm_scale, int causal, void* stream) {
+  if (Dv <= 0) return ATTN_ERR_INVALID;
+  const bool jvp = tq != nullptr;
+  if (!jvp && (tk || tv || to || tlse)) return ATTN_ERR_INVALID;
+  return dense((int)dtype, q, k, v, tq, tk, tv, q_strides, k_strides, v_strides, o, to, o_strides, lse, tlse, B, H,
+               Nq, Nkv, Dqk, sm_scale, causal, stream, jvp, BiasOperand(), Dv);
 }
 
 int attn_fwd_jvp(attn_dtype dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk,
@@ -327,7 +252,7 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   const void* ptrs[] = {q, k, v, o};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
-  const KernelChoice kc = choose((int)dtype, (int)D, false, false, kNoBias);
+  const KernelChoice kc = choose((int)dtype, (int)D, false, false, kNoBias, (int)D);
   const int BM = kc.BM;
   const int64_t cap = plan_capacity(num_seqs, total_len, BM);
   if (!workspace || workspace_bytes < (size_t)(16 + 8 * cap) || ((uintptr_t)workspace & 15u)) return ATTN_ERR_WORKSPACE;
@@ -425,11 +350,7 @@ int jagged_attn_bwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   a.plan = plan;
   a.total_len = (int)total_len;
   a.max_seq_len = mlen;
-  rc = by_dim(D, [&](auto d) {
-    constexpr int Dc = decltype(d)::value;
-    return dtype == ATTN_FP16 ? bwd_launch<Dc, true>(st, a, 1, H, total_len, total_len, cap)
-                              : bwd_launch<Dc, false>(st, a, 1, H, total_len, total_len, cap);
-  });
+  rc = bwd_run(dtype == ATTN_FP16, (int)D, st, a, 1, H, total_len, total_len, cap);
   if (rc) return rc;
   return finish(st);
 }
@@ -490,10 +411,7 @@ int attn_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const voi
   a.causal = causal ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
-  rc = by_dim(D, [&](auto d) {
-    constexpr int Dc = decltype(d)::value;
-    return dtype == ATTN_FP16 ? bwd_launch<Dc, true>(st, a, B, H, Nq, Nkv) : bwd_launch<Dc, false>(st, a, B, H, Nq, Nkv);
-  });
+  rc = bwd_run(dtype == ATTN_FP16, (int)D, st, a, B, H, Nq, Nkv, 0);
   if (rc) return rc;
   return finish(st);
 }

@@ -27,39 +27,6 @@
 
 namespace attn {
 
-struct BwdArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* o;
-  const void* dout;
-  const float* lse;  // [B, H, Nq] natural log, as attn_fwd writes it
-  void* dq;
-  void* dk;
-  void* dv;
-  float* delta;  // workspace [B * H * Nq]: rowsum(O dO)
-  float* lse2;   // workspace [B * H * Nq]: LSE log2(e); rows without keys +inf
-  int64_t q_sb, q_sh, q_sn;
-  int64_t k_sb, k_sh, k_sn;
-  int64_t v_sb, v_sh, v_sn;
-  int64_t o_sb, o_sh, o_sn;
-  int64_t do_sb, do_sh, do_sn;
-  int64_t dq_sb, dq_sh, dq_sn;
-  int64_t dk_sb, dk_sh, dk_sn;
-  int64_t dv_sb, dv_sh, dv_sn;
-  int32_t B, H, Nq, Nkv;
-  int32_t n_tiles;  // q-tiles (dQ kernel) or key tiles (dK/dV kernel) per (batch, head)
-  float c;          // sm_scale * log2(e)
-  float sm_scale;
-  int32_t causal;
-  // jagged layout (offsets != nullptr): tensors are [H, total_len, D], the
-  // LSE and the workspace rows [H, total_len]; workgroups follow the plan
-  const int64_t* offsets;
-  const int32_t* plan;  // [0] item count, items (seq, 128-row tile) from index 4
-  int32_t total_len;
-  int32_t max_seq_len;
-};
-
 // One workgroup's share: element offsets of row 0 of its (batch|sequence,
 // head) in every tensor, and the extents of that slice.
 struct BwdTile {

@@ -5,7 +5,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace attn {
+
+// Compile-time unrolled loop: f(std::integral_constant<int, i>) for i < N,
+// so that i can feed immediate operands of inline assembly and index
+// compile-time tables.
+template <int... Is, class F>
+__device__ __forceinline__ void static_for_seq(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(std::make_integer_sequence<int, N>{}, f);
+}
+
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -57,6 +73,40 @@ struct FwdArgs {
   // jagged layout (offsets != nullptr): q/k/v/o are [H, total_len, D]
   const int64_t* offsets;
   const int32_t* plan;  // [0] item count, items (seq, q-tile) from index 4
+  int32_t total_len;
+  int32_t max_seq_len;
+};
+
+// Arguments of the backward kernels (passed by value).  Strides in elements.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // [B, H, Nq] natural log, as attn_fwd writes it
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace [B * H * Nq]: rowsum(O dO)
+  float* lse2;   // workspace [B * H * Nq]: LSE log2(e); rows without keys +inf
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t do_sb, do_sh, do_sn;
+  int64_t dq_sb, dq_sh, dq_sn;
+  int64_t dk_sb, dk_sh, dk_sn;
+  int64_t dv_sb, dv_sh, dv_sn;
+  int32_t B, H, Nq, Nkv;
+  int32_t n_tiles;  // q-tiles (dQ kernel) or key tiles (dK/dV kernel) per (batch, head)
+  float c;          // sm_scale * log2(e)
+  float sm_scale;
+  int32_t causal;
+  // jagged layout (offsets != nullptr): tensors are [H, total_len, D], the
+  // LSE and the workspace rows [H, total_len]; workgroups follow the plan
+  const int64_t* offsets;
+  const int32_t* plan;  // [0] item count, items (seq, 128-row tile) from index 4
   int32_t total_len;
   int32_t max_seq_len;
 };

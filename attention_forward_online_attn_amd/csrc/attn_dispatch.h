@@ -1,0 +1,54 @@
+// Kernel selection shared by the host code (attn_abi.hip) and the
+// translation units that instantiate the kernels (inst_*.hip): every
+// instance table below is compiled in a source file of its own, so the
+// library builds in parallel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn_common.h"
+
+namespace attn {
+
+// Tile shapes of the 16-bit kernels (query tile 128 rows = 4 waves x 32).
+constexpr int kBnDense = 64;  // keys per tile, plain forward
+constexpr int kBnJvp = 32;    // keys per tile, JVP (four streamed tensors)
+constexpr int kBnBwdDq = 32;  // keys per tile of the backward's dQ kernel
+
+// One compiled forward kernel with its tile shape.
+struct KernelChoice {
+  void (*fn)(FwdArgs);
+  int BM;       // query rows per workgroup
+  int BN;       // keys per tile
+  int lds;      // dynamic LDS bytes
+  int threads;  // workgroup size
+};
+
+// Calls f(std::integral_constant<int, D>) for a supported head dim (checked
+// before: 32, 64 or 128).
+template <class F>
+auto by_dim(int64_t D, F&& f) {
+  if (D == 32) return f(std::integral_constant<int, 32>{});
+  if (D == 64) return f(std::integral_constant<int, 64>{});
+  return f(std::integral_constant<int, 128>{});
+}
+
+// Forward instance tables (dtype codes of include/attn.h).
+KernelChoice fwd_bf16(int D, bool jvp, bool paired);            // inst_fwd_bf16.hip
+KernelChoice fwd_fp16(int D, bool jvp, bool paired);            // inst_fwd_fp16.hip
+KernelChoice fwd_f32(int D, int Dv, bool jvp);                  // inst_fwd_f32.hip
+KernelChoice fwd_bias(int dtype, int kind, int D);              // inst_fwd_bias.hip
+KernelChoice fwd_mixed_bf16(int D, int Dv, bool jvp);           // inst_fwd_mixed_bf16.hip
+KernelChoice fwd_mixed_fp16(int D, int Dv, bool jvp);           // inst_fwd_mixed_fp16.hip
+
+// Backward: enqueues the prep, dQ and dK/dV kernels (inst_bwd.hip).  Dense:
+// B*H*Nq rows, grids over (batch, head, tile).  Jagged (a.offsets set): the
+// prep kernel sees H*total_len rows as one batch and both gradient kernels
+// cover `items` plan items per head.
+int bwd_run(bool f16, int D, hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
+            int64_t items);
+
+}  // namespace attn

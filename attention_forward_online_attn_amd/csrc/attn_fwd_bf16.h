@@ -157,17 +157,6 @@ __device__ __forceinline__ bf16x8 v_frag(const lds_t* vt, int key0, int lo, int 
   return __builtin_bit_cast(bf16x8, v8);
 }
 
-// Compile-time unrolled loop: f(std::integral_constant<int, i>) for i < N,
-// so that i can feed immediate operands of inline assembly.
-template <int... Is, class F>
-__device__ __forceinline__ void static_for_seq(std::integer_sequence<int, Is...>, F&& f) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_seq(std::make_integer_sequence<int, N>{}, f);
-}
-
 // V^T fragment read for the main PV product, as inline assembly.  The
 // compiler treats the transposing-read builtin as possibly aliasing every
 // global->LDS tile copy in flight and waits for all of them (vmcnt(0)) before
@@ -321,32 +310,47 @@ __device__ __forceinline__ void pv_lo_block(const lds_t* vt, const int (&vlo)[D 
   }
 }
 
-template <int D, int BN, bool JVP, int NW_ = 4>
+// D is the query/key head dim; DV_ (0: the same) the value head dim, which
+// sets the width of V, tV, O and tO (JVP page: _attention.forward takes
+// d_v != d_qk).
+template <int D, int BN, bool JVP, int NW_ = 4, int DV_ = 0>
 struct Bf16Cfg {
+  static constexpr int DQK = D, DV = DV_ ? DV_ : D;
   static constexpr int NW = NW_;            // waves per workgroup (32 query rows each)
   static constexpr int THREADS = 64 * NW;
   static constexpr int BM = 128;            // query rows per q-tile (4 waves); 8 waves take two q-tiles
-  static constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
-  static constexpr int TILE = BN * D * 2;   // bytes of one K (or V, tK, tV) tile
+  static constexpr int TILE_K = BN * DQK * 2;  // bytes of one K (or tK) tile
+  static constexpr int TILE_V = BN * DV * 2;   // bytes of one V (or tV) tile
+  // tile offsets in a stage: K, V, then tK, tV
+  static constexpr int OFF_V = TILE_K, OFF_TK = TILE_K + TILE_V, OFF_TV = 2 * TILE_K + TILE_V;
   static constexpr int NTEN = JVP ? 4 : 2;  // tensors streamed per key tile
-  static constexpr int STAGE = NTEN * TILE; // bytes of one pipeline stage
-  static constexpr bool DMA = !(JVP && D == 128);  // direct global -> LDS tile loads
+  static constexpr int STAGE = (JVP ? 2 : 1) * (TILE_K + TILE_V);  // bytes of one pipeline stage
+  static constexpr bool WIDE = JVP && (DQK == 128 || DV == 128);  // one wave per SIMD
+  static constexpr bool DMA = !WIDE;        // direct global -> LDS tile loads
   static constexpr int LDS = 2 * STAGE;     // double-buffered key tiles
-  static constexpr int LOADS = (BN * CPR + THREADS - 1) / THREADS;
-  static constexpr int WAVES_PER_EU = (JVP && D == 128) ? 1 : 2;
-  static_assert((BN * CPR) % THREADS == 0 || BN * CPR < THREADS, "tile must split evenly over the workgroup");
-  static_assert(BN % 32 == 0 && (D == 32 || D == 64 || D == 128), "unsupported tile");
+  static constexpr int CPR_K = DQK / 8, CPR_V = DV / 8;  // 16-byte chunks per row
+  static constexpr int LOADS_K = (BN * CPR_K + THREADS - 1) / THREADS;
+  static constexpr int LOADS_V = (BN * CPR_V + THREADS - 1) / THREADS;
+  static constexpr int WAVES_PER_EU = WIDE ? 1 : 2;
+  static_assert((BN * CPR_K) % THREADS == 0 || BN * CPR_K < THREADS, "tile must split evenly over the workgroup");
+  static_assert((BN * CPR_V) % THREADS == 0 || BN * CPR_V < THREADS, "tile must split evenly over the workgroup");
+  static_assert(BN % 32 == 0, "unsupported tile");
+  static_assert(DQK == 32 || DQK == 64 || DQK == 128, "unsupported head dim");
+  static_assert(DV == 32 || DV == 64 || DV == 128, "unsupported head dim");
 };
 
-template <int D, int BN, bool JVP, int NW_ = 4, bool F16 = false, int BIAS = kNoBias>
-__global__ void __launch_bounds__((Bf16Cfg<D, BN, JVP, NW_>::THREADS), (Bf16Cfg<D, BN, JVP, NW_>::WAVES_PER_EU))
+template <int D, int BN, bool JVP, int NW_ = 4, bool F16 = false, int BIAS = kNoBias, int DV_ = 0>
+__global__ void __launch_bounds__((Bf16Cfg<D, BN, JVP, NW_, DV_>::THREADS), (Bf16Cfg<D, BN, JVP, NW_, DV_>::WAVES_PER_EU))
 attn_fwd_bf16_kernel(FwdArgs a) {
-  using C = Bf16Cfg<D, BN, JVP, NW_>;
-  constexpr int BM = C::BM, CPR = C::CPR, TILE = C::TILE, NTEN = C::NTEN, STAGE = C::STAGE;
-  constexpr int LOADS = C::LOADS, THREADS = C::THREADS, NW = C::NW;
-  constexpr int NB = BN / 32;  // 32-key blocks per tile
-  constexpr int KD = D / 16;   // MFMA steps over the head dim
-  constexpr int DB = D / 32;   // 32-column output blocks
+  using C = Bf16Cfg<D, BN, JVP, NW_, DV_>;
+  constexpr int DQK = C::DQK, DV = C::DV;
+  constexpr int BM = C::BM, NTEN = C::NTEN, STAGE = C::STAGE, TILE_K = C::TILE_K, TILE_V = C::TILE_V;
+  constexpr int OFF_V = C::OFF_V, OFF_TK = C::OFF_TK, OFF_TV = C::OFF_TV;
+  constexpr int CPR_K = C::CPR_K, CPR_V = C::CPR_V, LOADS_K = C::LOADS_K, LOADS_V = C::LOADS_V;
+  constexpr int THREADS = C::THREADS, NW = C::NW;
+  constexpr int NB = BN / 32;    // 32-key blocks per tile
+  constexpr int KD = DQK / 16;   // MFMA steps over the query/key head dim
+  constexpr int DB = DV / 32;    // 32-column output blocks
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   lds_t* smem = (lds_t*)smem_raw;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
@@ -398,24 +402,31 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   }
 
   // ---- global -> register staging of one key tile, register -> LDS stores.
-  // Thread `tid` moves chunks id = tid + 256 it (row id / CPR, 16-byte chunk
-  // id % CPR).  Full tiles use a uniform tile base plus loop-invariant 32-bit
-  // byte offsets; only a ragged last tile clamps rows to the last valid key
-  // (those rows are masked).
-  uint32_t goff_k[LOADS], goff_v[LOADS];
-  int lds_off[LOADS];
+  // Thread `tid` moves chunks id = tid + 256 it of each tensor (row id / CPR,
+  // 16-byte chunk id % CPR; CPR of the K side or of the V side).  Full tiles
+  // use a uniform tile base plus loop-invariant 32-bit byte offsets; only a
+  // ragged last tile clamps rows to the last valid key (those rows are masked).
+  uint32_t goff_k[LOADS_K], goff_v[LOADS_V];
+  int lds_k[LOADS_K], lds_v[LOADS_V];
 #pragma unroll
-  for (int it = 0; it < LOADS; ++it) {
+  for (int it = 0; it < LOADS_K; ++it) {
     const int id = tid + THREADS * it;
-    const int row = id / CPR, ch = id % CPR;
+    const int row = id / CPR_K, ch = id % CPR_K;
     goff_k[it] = (uint32_t)((row * a.k_sn + ch * 8) * 2);
-    goff_v[it] = (uint32_t)((row * a.v_sn + ch * 8) * 2);
-    lds_off[it] = swz_off<D>(row, ch);
+    lds_k[it] = swz_off<DQK>(row, ch);
   }
-  const bool stager = BN * CPR >= THREADS || tid < BN * CPR;  // threads that move tile chunks
-  u32x4 stg[NTEN][LOADS];
+#pragma unroll
+  for (int it = 0; it < LOADS_V; ++it) {
+    const int id = tid + THREADS * it;
+    const int row = id / CPR_V, ch = id % CPR_V;
+    goff_v[it] = (uint32_t)((row * a.v_sn + ch * 8) * 2);
+    lds_v[it] = swz_off<DV>(row, ch);
+  }
+  const bool stager_k = BN * CPR_K >= THREADS || tid < BN * CPR_K;  // threads that move tile chunks
+  const bool stager_v = BN * CPR_V >= THREADS || tid < BN * CPR_V;
+  u32x4 stg_k[JVP ? 2 : 1][LOADS_K], stg_v[JVP ? 2 : 1][LOADS_V];
+  constexpr int LOADS_M = LOADS_K > LOADS_V ? LOADS_K : LOADS_V;
   auto load_tile = [&](int j) {
-    if (!stager) return;
     const int64_t k0 = (int64_t)j * BN;
     const char* kb = (const char*)K + k0 * a.k_sn * 2;
     const char* vb = (const char*)V + k0 * a.v_sn * 2;
@@ -423,39 +434,45 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     const char* tvb = JVP ? (const char*)TV + k0 * a.v_sn * 2 : nullptr;
     if (k0 + BN <= t.Lkv) {
 #pragma unroll
-      for (int it = 0; it < LOADS; ++it) {
-        stg[0][it] = *(const u32x4*)(kb + goff_k[it]);
-        stg[1][it] = *(const u32x4*)(vb + goff_v[it]);
+      for (int it = 0; it < LOADS_M; ++it) {
+        const bool lk = it < LOADS_K && stager_k, lv = it < LOADS_V && stager_v;
+        if (lk) stg_k[0][it % LOADS_K] = *(const u32x4*)(kb + goff_k[it % LOADS_K]);
+        if (lv) stg_v[0][it % LOADS_V] = *(const u32x4*)(vb + goff_v[it % LOADS_V]);
         if constexpr (JVP) {
-          stg[2][it] = *(const u32x4*)(tkb + goff_k[it]);
-          stg[3][it] = *(const u32x4*)(tvb + goff_v[it]);
+          if (lk) stg_k[1][it % LOADS_K] = *(const u32x4*)(tkb + goff_k[it % LOADS_K]);
+          if (lv) stg_v[1][it % LOADS_V] = *(const u32x4*)(tvb + goff_v[it % LOADS_V]);
         }
       }
     } else {
       const int last = t.Lkv - 1 - (int)k0;  // last valid row of this tile
 #pragma unroll
-      for (int it = 0; it < LOADS; ++it) {
+      for (int it = 0; it < LOADS_M; ++it) {
         const int id = tid + THREADS * it;
-        int row = id / CPR;
-        row = row < last ? row : last;
-        const int ch = id % CPR;
-        const uint32_t ok = (uint32_t)((row * a.k_sn + ch * 8) * 2);
-        const uint32_t ov = (uint32_t)((row * a.v_sn + ch * 8) * 2);
-        stg[0][it] = *(const u32x4*)(kb + ok);
-        stg[1][it] = *(const u32x4*)(vb + ov);
+        const bool lk = it < LOADS_K && stager_k, lv = it < LOADS_V && stager_v;
+        const int row_k = min(id / CPR_K, last), row_v = min(id / CPR_V, last);
+        const uint32_t ok = (uint32_t)((row_k * a.k_sn + (id % CPR_K) * 8) * 2);
+        const uint32_t ov = (uint32_t)((row_v * a.v_sn + (id % CPR_V) * 8) * 2);
+        if (lk) stg_k[0][it % LOADS_K] = *(const u32x4*)(kb + ok);
+        if (lv) stg_v[0][it % LOADS_V] = *(const u32x4*)(vb + ov);
         if constexpr (JVP) {
-          stg[2][it] = *(const u32x4*)(tkb + ok);
-          stg[3][it] = *(const u32x4*)(tvb + ov);
+          if (lk) stg_k[1][it % LOADS_K] = *(const u32x4*)(tkb + ok);
+          if (lv) stg_v[1][it % LOADS_V] = *(const u32x4*)(tvb + ov);
         }
       }
     }
   };
   auto store_tile = [&](lds_t* base) {
-    if (!stager) return;
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it)
-#pragma unroll
-      for (int x = 0; x < NTEN; ++x) *(__attribute__((address_space(3))) u32x4*)(base + x * TILE + lds_off[it]) = stg[x][it];
+    for (int it = 0; it < LOADS_M; ++it) {
+      const bool lk = it < LOADS_K && stager_k, lv = it < LOADS_V && stager_v;
+      if (lk) *(lds_u32x4*)(base + lds_k[it % LOADS_K]) = stg_k[0][it % LOADS_K];
+      if (lv) *(lds_u32x4*)(base + OFF_V + lds_v[it % LOADS_V]) = stg_v[0][it % LOADS_V];
+      if constexpr (JVP) {
+        if (lk) *(lds_u32x4*)(base + OFF_TK + lds_k[it % LOADS_K]) = stg_k[1][it % LOADS_K];
+        if (lv) *(lds_u32x4*)(base + OFF_TV + lds_v[it % LOADS_V]) = stg_v[1][it % LOADS_V];
+      }
+    }
   };
 
   // Direct global -> LDS tile loads (global_load_lds_dwordx4): instruction i
@@ -469,52 +486,67 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   // The D=128 JVP instance (1 wave per SIMD, which spills) keeps register
   // staging: with DMA it produced wrong scores on ragged last tiles in the
   // parity suite, a cause not isolated.
+  // K-side tensors (K, tK) and V-side tensors (V, tV) each have their own
+  // row width, hence their own block mapping; with equal head dims the two
+  // coincide and the instructions interleave as K, V, tK, tV.
   constexpr bool DMA = C::DMA;
-  constexpr int NBLK = TILE / 1024;                    // 1 KiB blocks per tile
-  constexpr int NI = NBLK >= NW ? NBLK / NW : 1;       // DMA instructions per wave per tensor
-  constexpr int RPB = 1024 / (2 * D);                  // rows per block
-  constexpr int RSTEP = NW * RPB;                      // rows between a wave's blocks
-  static_assert(!DMA || NBLK % NW == 0 || NBLK < NW, "DMA tiles are whole 1 KiB blocks per wave");
-  static_assert(!DMA || NI == 1 || RSTEP % 16 == 0, "per-lane swizzle must repeat every RSTEP rows");
-  const bool dma_wave = NBLK >= NW || wave < NBLK;    // waves past the tile's blocks fetch nothing
-  const int drow = RPB * wave + (lane * 16) / (2 * D);             // row of instruction 0
-  const int dch = (lane % (D / 8)) ^ swz_f<D>(drow);                // source chunk of that row
-  const uint32_t dk0 = (uint32_t)((drow * a.k_sn + dch * 8) * 2);  // byte offsets, instruction 0
-  const uint32_t dv0 = (uint32_t)((drow * a.v_sn + dch * 8) * 2);
+  constexpr int NBLK_K = TILE_K / 1024, NBLK_V = TILE_V / 1024;  // 1 KiB blocks per tile
+  constexpr int NI_K = NBLK_K >= NW ? NBLK_K / NW : 1;            // DMA instructions per wave per tensor
+  constexpr int NI_V = NBLK_V >= NW ? NBLK_V / NW : 1;
+  constexpr int NIM = NI_K > NI_V ? NI_K : NI_V;
+  constexpr int RPB_K = 1024 / (2 * DQK), RPB_V = 1024 / (2 * DV);  // rows per block
+  constexpr int RSTEP_K = NW * RPB_K, RSTEP_V = NW * RPB_V;         // rows between a wave's blocks
+  static_assert(!DMA || ((NBLK_K % NW == 0 || NBLK_K < NW) && (NBLK_V % NW == 0 || NBLK_V < NW)),
+                "DMA tiles are whole 1 KiB blocks per wave");
+  static_assert(!DMA || ((NI_K == 1 || RSTEP_K % 16 == 0) && (NI_V == 1 || RSTEP_V % 16 == 0)),
+                "per-lane swizzle must repeat every RSTEP rows");
+  const bool dma_k = NBLK_K >= NW || wave < NBLK_K;  // waves past the tile's blocks fetch nothing
+  const bool dma_v = NBLK_V >= NW || wave < NBLK_V;
+  const int drow_k = RPB_K * wave + (lane * 16) / (2 * DQK);          // row of instruction 0
+  const int drow_v = RPB_V * wave + (lane * 16) / (2 * DV);
+  const int dch_k = (lane % CPR_K) ^ swz_f<DQK>(drow_k);              // source chunk of that row
+  const int dch_v = (lane % CPR_V) ^ swz_f<DV>(drow_v);
+  const uint32_t dk0 = (uint32_t)((drow_k * a.k_sn + dch_k * 8) * 2);  // byte offsets, instruction 0
+  const uint32_t dv0 = (uint32_t)((drow_v * a.v_sn + dch_v * 8) * 2);
   auto dma_tile = [&](int j, lds_t* base) {
-    if (!dma_wave) return;
     const int64_t k0 = (int64_t)j * BN;
     const char* src[4] = {(const char*)K + k0 * a.k_sn * 2, (const char*)V + k0 * a.v_sn * 2,
                           JVP ? (const char*)TK + k0 * a.k_sn * 2 : nullptr,
                           JVP ? (const char*)TV + k0 * a.v_sn * 2 : nullptr};
-    const int64_t step_b[2] = {(int64_t)RSTEP * a.k_sn * 2, (int64_t)RSTEP * a.v_sn * 2};
+    const int toff[4] = {0, OFF_V, OFF_TK, OFF_TV};
+    const int64_t step_b[2] = {(int64_t)RSTEP_K * a.k_sn * 2, (int64_t)RSTEP_V * a.v_sn * 2};
     if (k0 + BN <= t.Lkv) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < NIM; ++i)
 #pragma unroll
         for (int x = 0; x < NTEN; ++x) {
+          const bool vs = x & 1;
+          if (i >= (vs ? NI_V : NI_K) || !(vs ? dma_v : dma_k)) continue;
           // the uniform part of the address stays an SGPR pair (saddr form:
           // scalar base + 32-bit lane offset); with several instructions per
           // tensor the compiler would otherwise fold it into per-lane 64-bit
           // addresses held across the loop
-          const char* b = src[x] + i * step_b[x & 1];
-          if constexpr (NI > 1) asm("" : "+s"(b));
-          __builtin_amdgcn_global_load_lds((const void*)(b + ((x & 1) ? dv0 : dk0)),
-                                           (__attribute__((address_space(3))) void*)(base + (NW * i + wave) * 1024 + x * TILE),
+          const char* b = src[x] + i * step_b[vs];
+          if constexpr (NIM > 1) asm("" : "+s"(b));
+          __builtin_amdgcn_global_load_lds((const void*)(b + (vs ? dv0 : dk0)),
+                                           (__attribute__((address_space(3))) void*)(base + (NW * i + wave) * 1024 + toff[x]),
                                            16, 0, 0);
         }
     } else {  // ragged last tile: rows past the keys re-read the last key (masked)
       const int last = t.Lkv - 1 - (int)k0;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int row = min(drow + RSTEP * i, last);
-        const uint32_t ok = (uint32_t)((row * a.k_sn + dch * 8) * 2);
-        const uint32_t ov = (uint32_t)((row * a.v_sn + dch * 8) * 2);
+      for (int i = 0; i < NIM; ++i) {
+        const int row_k = min(drow_k + RSTEP_K * i, last), row_v = min(drow_v + RSTEP_V * i, last);
+        const uint32_t ok = (uint32_t)((row_k * a.k_sn + dch_k * 8) * 2);
+        const uint32_t ov = (uint32_t)((row_v * a.v_sn + dch_v * 8) * 2);
 #pragma unroll
-        for (int x = 0; x < NTEN; ++x)
-          __builtin_amdgcn_global_load_lds((const void*)(src[x] + ((x & 1) ? ov : ok)),
-                                           (__attribute__((address_space(3))) void*)(base + (NW * i + wave) * 1024 + x * TILE),
+        for (int x = 0; x < NTEN; ++x) {
+          const bool vs = x & 1;
+          if (i >= (vs ? NI_V : NI_K) || !(vs ? dma_v : dma_k)) continue;
+          __builtin_amdgcn_global_load_lds((const void*)(src[x] + (vs ? ov : ok)),
+                                           (__attribute__((address_space(3))) void*)(base + (NW * i + wave) * 1024 + toff[x]),
                                            16, 0, 0);
+        }
       }
     }
   };
@@ -593,10 +625,10 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   const int krow = kperm(n32);
   uint32_t kaddr[KD];
 #pragma unroll
-  for (int kk = 0; kk < KD; ++kk) kaddr[kk] = lds_base + swz_off<D>(krow, 2 * kk + h32);
+  for (int kk = 0; kk < KD; ++kk) kaddr[kk] = lds_base + swz_off<DQK>(krow, 2 * kk + h32);
   int vlo[DB], vhi[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) v_frag_offsets<D>(lane, db, vlo[db], vhi[db]);
+  for (int db = 0; db < DB; ++db) v_frag_offsets<DV>(lane, db, vlo[db], vhi[db]);
 
   // One key tile on LDS stage S = j % 2: fetch tile j + 1 into the other
   // stage (freed by the barrier that ended the previous tile), compute, then
@@ -613,12 +645,12 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     }
 
     if (j * BN < wave_max) {  // wave-uniform: skip tiles this wave cannot see
-      const lds_t* vt = smem + S * STAGE + TILE;  // V tile (the cold residual pass reads it)
+      const lds_t* vt = smem + S * STAGE + OFF_V;  // V tile (the cold residual pass reads it)
 
       // S^T = K Q^T (and the tangent scores tQ K^T + Q tK^T)
       f32x16 s[NB];
       f32x16 ts[JVP ? NB : 1];
-      scores_section<D, NB, JVP, S * STAGE, S * STAGE + 2 * TILE, F16>(kaddr, qf, tqf, s, ts);
+      scores_section<DQK, NB, JVP, S * STAGE, S * STAGE + OFF_TK, F16>(kaddr, qf, tqf, s, ts);
 
       // mask keys past this row's limit (ragged tail, causal diagonal,
       // jagged truncation) -- only on tiles that reach some row's limit
@@ -691,7 +723,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], cs, nm));
             plo[r >> 3][r & 7] = to16<F16>(p - from16<F16>(to16<F16>(p)));
           }
-          pv_lo_block<D, F16>(vt, vlo, vhi, b, plo, acc);
+          pv_lo_block<DV, F16>(vt, vlo, vhi, b, plo, acc);
         }
       }
 
@@ -715,7 +747,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       constexpr int EPS = 8 / DB;  // elements of the next chunk per PV step
       static_for<8>(soft);
       // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
-      pv_section<D, NB, JVP, S * STAGE + TILE, S * STAGE + 3 * TILE, F16>(
+      pv_section<DV, NB, JVP, S * STAGE + OFF_V, S * STAGE + OFF_TV, F16>(
           lds_base, vlo, vhi, pf, hf, acc, accA, accB, [&](auto i_tag) {
             constexpr int i = decltype(i_tag)::value, c = i / DB;
             if constexpr (c + 1 < 2 * NB) {

@@ -20,21 +20,23 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
-template <int D, bool JVP>
+// D: query/key head dim; DV_ (0: the same): value head dim.
+template <int D, bool JVP, int DV_ = 0>
 struct F32Cfg {
+  static constexpr int DQK = D, DV = DV_ ? DV_ : D;
   static constexpr int BM = 64;   // query rows per workgroup (256 threads, 4 per row)
   static constexpr int BN = 32;   // keys per tile
   static constexpr int NTEN = JVP ? 4 : 2;
-  static constexpr int LDS = NTEN * BN * D * 4;
+  static constexpr int LDS = (JVP ? 2 : 1) * BN * (DQK + DV) * 4;
 };
 
-template <int D, bool JVP, int BIAS = kNoBias>
+template <int D, bool JVP, int BIAS = kNoBias, int DV_ = 0>
 __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
-  using C = F32Cfg<D, JVP>;
-  constexpr int BM = C::BM, BN = C::BN, NTEN = C::NTEN;
-  constexpr int DQ = D / 4;               // columns owned by each lane of a quad
-  constexpr int F4 = BN * D / 4;          // float4 per tensor tile
-  static_assert(F4 % 256 == 0, "tile must split evenly over 256 threads");
+  using C = F32Cfg<D, JVP, DV_>;
+  constexpr int BM = C::BM, BN = C::BN, NTEN = C::NTEN, DQK = C::DQK, DV = C::DV;
+  constexpr int DQ = DQK / 4;             // query/key columns owned by each lane of a quad
+  constexpr int DO_ = DV / 4;             // value / output columns owned by each lane
+  static_assert((BN * DQK / 4) % 256 == 0 && (BN * DV / 4) % 256 == 0, "tile must split evenly over 256 threads");
   extern __shared__ __attribute__((aligned(16))) float fsm[];
 
   const Tile t = resolve_tile<BM>(a, blockIdx.x);
@@ -56,15 +58,21 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
   const float* TV = JVP ? (const float*)a.tv + t.v_off : nullptr;
   const float* srcs[4] = {K, V, TK, TV};
   const int64_t sns[4] = {a.k_sn, a.v_sn, a.k_sn, a.v_sn};
+  // tiles in LDS: K, V, tK, tV (widths DQK, DV, DQK, DV)
+  constexpr int toff[4] = {0, BN * DQK, BN * (DQK + DV), BN * (2 * DQK + DV)};
+  constexpr int width[4] = {DQK, DV, DQK, DV};
 
   float qr[DQ], tqr[JVP ? DQ : 1];
-  float acc[DQ], accA[JVP ? DQ : 1], accB[JVP ? DQ : 1];
+  float acc[DO_], accA[JVP ? DO_ : 1], accB[JVP ? DO_ : 1];
 #pragma unroll
   for (int i = 0; i < DQ; ++i) {
     qr[i] = Q[rr * a.q_sn + 4 * i + u];
+    if constexpr (JVP) tqr[i] = TQ[rr * a.q_sn + 4 * i + u];
+  }
+#pragma unroll
+  for (int i = 0; i < DO_; ++i) {
     acc[i] = 0.f;
     if constexpr (JVP) {
-      tqr[i] = TQ[rr * a.q_sn + 4 * i + u];
       accA[i] = 0.f;
       accB[i] = 0.f;
     }
@@ -79,21 +87,22 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
 
   for (int j = 0; j < n_tiles; ++j) {
     __syncthreads();  // the previous tile is no longer being read
+    static_for<NTEN>([&](auto x_tag) {
+      constexpr int x = decltype(x_tag)::value, W = width[x];
 #pragma unroll
-    for (int x = 0; x < NTEN; ++x)
-#pragma unroll
-      for (int it = 0; it < F4 / 256; ++it) {
+      for (int it = 0; it < BN * W / 4 / 256; ++it) {
         const int id = tid + 256 * it;
-        const int row = id / (D / 4), c4 = id % (D / 4);
+        const int row = id / (W / 4), c4 = id % (W / 4);
         int key = j * BN + row;
         key = key < t.Lkv ? key : t.Lkv - 1;
-        *(f32x4*)(fsm + x * BN * D + row * D + 4 * c4) = *(const f32x4*)(srcs[x] + key * sns[x] + 4 * c4);
+        *(f32x4*)(fsm + toff[x] + row * W + 4 * c4) = *(const f32x4*)(srcs[x] + key * sns[x] + 4 * c4);
       }
+    });
     __syncthreads();
-    const float* kt = fsm;
-    const float* vt = fsm + BN * D;
-    const float* tkt = fsm + 2 * BN * D;
-    const float* tvt = fsm + 3 * BN * D;
+    const float* kt = fsm + toff[0];
+    const float* vt = fsm + toff[1];
+    const float* tkt = fsm + toff[2];
+    const float* tvt = fsm + toff[3];
 
     float s[BN], ts[JVP ? BN : 1];
 #pragma unroll
@@ -101,9 +110,9 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
       float part = 0.f, tpart = 0.f;
 #pragma unroll
       for (int i = 0; i < DQ; ++i) {
-        const float kv = kt[jj * D + 4 * i + u];
+        const float kv = kt[jj * DQK + 4 * i + u];
         part = __builtin_fmaf(qr[i], kv, part);
-        if constexpr (JVP) tpart = __builtin_fmaf(tqr[i], kv, __builtin_fmaf(qr[i], tkt[jj * D + 4 * i + u], tpart));
+        if constexpr (JVP) tpart = __builtin_fmaf(tqr[i], kv, __builtin_fmaf(qr[i], tkt[jj * DQK + 4 * i + u], tpart));
       }
       s[jj] = quad_sum(part);
       if constexpr (JVP) ts[jj] = quad_sum(tpart);
@@ -151,7 +160,7 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
     l_run *= alpha;
     r_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < DQ; ++i) {
+    for (int i = 0; i < DO_; ++i) {
       acc[i] *= alpha;
       if constexpr (JVP) { accA[i] *= alpha; accB[i] *= alpha; }
     }
@@ -162,12 +171,12 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
       const float hv = JVP ? p * ts[jj] : 0.f;
       r_run += hv;
 #pragma unroll
-      for (int i = 0; i < DQ; ++i) {
-        const float vv = vt[jj * D + 4 * i + u];
+      for (int i = 0; i < DO_; ++i) {
+        const float vv = vt[jj * DV + 4 * i + u];
         acc[i] = __builtin_fmaf(p, vv, acc[i]);
         if constexpr (JVP) {
           accB[i] = __builtin_fmaf(hv, vv, accB[i]);
-          accA[i] = __builtin_fmaf(p, tvt[jj * D + 4 * i + u], accA[i]);
+          accA[i] = __builtin_fmaf(p, tvt[jj * DV + 4 * i + u], accA[i]);
         }
       }
     }
@@ -181,7 +190,7 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
     float* torow = JVP ? (float*)a.to + t.o_off + my_row * a.o_sn : nullptr;
     const float r_tot = r_run * a.sm_scale;
 #pragma unroll
-    for (int i = 0; i < DQ; ++i) {
+    for (int i = 0; i < DO_; ++i) {
       const float o = acc[i] * inv;
       orow[4 * i + u] = o;
       if constexpr (JVP) torow[4 * i + u] = (accA[i] + a.sm_scale * accB[i] - r_tot * o) * inv;

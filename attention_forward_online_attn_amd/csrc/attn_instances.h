@@ -1,0 +1,46 @@
+// Instance builders for the forward kernels, included by the inst_*.hip
+// translation units only.
+#pragma once
+
+#include "attn_dispatch.h"
+#include "attn_fwd_bf16.h"
+#include "attn_fwd_f32.h"
+
+namespace attn {
+
+template <int D, int BN, bool JVP, int NW = 4, bool F16 = false, int BIAS = kNoBias, int DV = 0>
+KernelChoice r32() {
+  using C = Bf16Cfg<D, BN, JVP, NW, DV>;
+  return {attn_fwd_bf16_kernel<D, BN, JVP, NW, F16, BIAS, DV>, C::BM, BN, C::LDS, C::THREADS};
+}
+
+template <int D, bool JVP, int BIAS = kNoBias, int DV = 0>
+KernelChoice f32k() {
+  using C = F32Cfg<D, JVP, DV>;
+  return {attn_fwd_f32_kernel<D, JVP, BIAS, DV>, C::BM, C::BN, C::LDS, 256};
+}
+
+// 16-bit forward with equal head dims; `paired`: 8-wave workgroups that take
+// q-tiles p and n-1-p (never the D=128 JVP instance, one wave per SIMD).
+template <bool F16>
+KernelChoice choose16(int D, bool jvp, bool paired) {
+  return by_dim(D, [&](auto d) {
+    constexpr int Dc = decltype(d)::value;
+    if (paired) return !jvp ? r32<Dc, kBnDense, false, 8, F16>() : r32<Dc == 128 ? 64 : Dc, kBnJvp, true, 8, F16>();
+    return !jvp ? r32<Dc, kBnDense, false, 4, F16>() : r32<Dc, kBnJvp, true, 4, F16>();
+  });
+}
+
+// 16-bit forward whose value head dim differs from the query/key one (JVP
+// page: d_v != d_qk): 4-wave workgroups, never paired, no bias.
+template <bool F16>
+KernelChoice choose_mixed16(int D, int Dv, bool jvp) {
+  return by_dim(D, [&](auto dq) {
+    return by_dim(Dv, [&](auto dv) {
+      constexpr int A = decltype(dq)::value, V = decltype(dv)::value, DVp = A == V ? 0 : V;
+      return jvp ? r32<A, kBnJvp, true, 4, F16, kNoBias, DVp>() : r32<A, kBnDense, false, 4, F16, kNoBias, DVp>();
+    });
+  });
+}
+
+}  // namespace attn

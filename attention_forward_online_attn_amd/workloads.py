@@ -27,23 +27,25 @@ import torch
 DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 
-def _normal(shape, seed, dtype):
+def _normal(shape, seed, dtype, std=1.0):
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
-    return torch.randn(*shape, generator=g, dtype=torch.float32).to(dtype)
+    return (torch.randn(*shape, generator=g, dtype=torch.float32) * std).to(dtype)
 
 
-def dense_inputs(B, H, Nq, Nkv, D, dtype="bf16", seed_base=0, tangents=False):
-    """Q [B,H,Nq,D], K/V [B,H,Nkv,D] (and tQ/tK/tV when tangents) on the CPU."""
+def dense_inputs(B, H, Nq, Nkv, D, dtype="bf16", seed_base=0, tangents=False, Dv=None, std=1.0):
+    """Q [B,H,Nq,D], K [B,H,Nkv,D], V [B,H,Nkv,Dv] (Dv defaults to D; and
+    tQ/tK/tV when tangents) on the CPU, i.i.d. N(0, std^2)."""
     dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
-    q = _normal((B, H, Nq, D), seed_base + 0, dt)
-    k = _normal((B, H, Nkv, D), seed_base + 1, dt)
-    v = _normal((B, H, Nkv, D), seed_base + 2, dt)
+    Dv = D if Dv is None else Dv
+    q = _normal((B, H, Nq, D), seed_base + 0, dt, std)
+    k = _normal((B, H, Nkv, D), seed_base + 1, dt, std)
+    v = _normal((B, H, Nkv, Dv), seed_base + 2, dt, std)
     if not tangents:
         return q, k, v
-    tq = _normal((B, H, Nq, D), seed_base + 3, dt)
-    tk = _normal((B, H, Nkv, D), seed_base + 4, dt)
-    tv = _normal((B, H, Nkv, D), seed_base + 5, dt)
+    tq = _normal((B, H, Nq, D), seed_base + 3, dt, std)
+    tk = _normal((B, H, Nkv, D), seed_base + 4, dt, std)
+    tv = _normal((B, H, Nkv, Dv), seed_base + 5, dt, std)
     return q, k, v, tq, tk, tv
 
 

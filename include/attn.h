@@ -158,6 +158,27 @@ ATTN_API int attn_fwd_jvp(attn_dtype dtype,
                  float sm_scale, int causal, void* stream);
 
 /*
+ * Dense forward (and, with tangents, its JVP) whose values have their own
+ * head dim (JVP page: _attention.forward takes d_v != d_qk, and _test_jvp_ca
+ * checks it):
+ *   q, tq [B, H, Nq, Dqk]   k, tk [B, H, Nkv, Dqk]   v, tv [B, H, Nkv, Dv]
+ *   o, to [B, H, Nq, Dv]    lse, tlse [B, H, Nq]
+ * tq == NULL: the plain forward of attn_fwd (tk, tv, to and tlse must be
+ * NULL too); otherwise the fused JVP of attn_fwd_jvp (tlse optional).
+ * Dqk and Dv each in {32, 64, 128}; with Dqk == Dv this is exactly attn_fwd /
+ * attn_fwd_jvp.  sm_scale is the caller's (the page's default is
+ * Dqk^-0.5).  Other arguments, checks and errors as attn_fwd_jvp.
+ */
+ATTN_API int attn_fwd_dv(attn_dtype dtype,
+                const void* q, const void* k, const void* v,
+                const void* tq, const void* tk, const void* tv,
+                attn_strides4 q_strides, attn_strides4 k_strides, attn_strides4 v_strides,
+                void* o, void* to, attn_strides4 o_strides,
+                float* lse, float* tlse,
+                int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t Dqk, int64_t Dv,
+                float sm_scale, int causal, void* stream);
+
+/*
  * Bytes of device workspace jagged_attn_fwd needs (host function, no GPU
  * access).  Returns 0 for invalid sizes.
  */

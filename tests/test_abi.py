@@ -32,7 +32,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(
-        ["attn_fwd", "attn_fwd_bias", "attn_fwd_jvp", "jagged_attn_workspace_bytes", "jagged_attn_fwd",
+        ["attn_fwd", "attn_fwd_bias", "attn_fwd_dv", "attn_fwd_jvp", "jagged_attn_workspace_bytes", "jagged_attn_fwd",
          "attn_bwd_workspace_bytes", "attn_bwd", "jagged_attn_bwd_workspace_bytes", "jagged_attn_bwd",
          "attn_status_string"])
 
@@ -199,3 +199,20 @@ def test_jagged_bwd_validation(lib):
     assert call(lse=0) == INVALID
     assert call(dq=0) == INVALID
     assert call(H=0) == OK
+
+
+def test_dv_validation(lib):
+    B, H, N = 1, 2, 128
+    sq = dense_strides(B, H, N, 64)
+    sv = dense_strides(B, H, N, 128)
+
+    def call(Dqk=64, Dv=128, tq=0, tk=0, tv=0, to=0, tlse=0, B=B):
+        return lib.attn_fwd_dv(BF16, P, P, P, tq, tk, tv, sq, sq, sv, P, to, sv, P, tlse,
+                               B, H, N, N, Dqk, Dv, 0.125, 0, None)
+    assert call(Dv=96) == UNSUPPORTED
+    assert call(Dv=0) == INVALID
+    assert call(Dqk=48) == UNSUPPORTED
+    assert call(tk=P) == INVALID          # tangents without tq: not a JVP call
+    assert call(to=P) == INVALID
+    assert call(tq=P, tk=P, tv=P) == INVALID  # JVP without to
+    assert call(B=0) == OK

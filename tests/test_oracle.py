@@ -338,3 +338,28 @@ def test_golden_causal_equal_scores():
     np.testing.assert_allclose(o[0, 0], g["O"], atol=1e-15)
     np.testing.assert_allclose(lse[0, 0], [math.log(i + 1) for i in range(N)], atol=1e-15)
     np.testing.assert_allclose(lse[0, 0], g["LSE"], atol=1e-12)
+
+
+@pytest.mark.parametrize("Dqk,Dv,causal", [(8, 16, False), (16, 4, True), (4, 12, True)])
+def test_value_head_dim_differs(Dqk, Dv, causal):
+    """JVP page, _attention.forward and _test_jvp_ca: v (and tv, o, to) carry
+    their own head dim.  O against torch's attention (math backend, fp64) and
+    tO against torch forward-mode autodiff of the plain definition."""
+    N, scale = 9, Dqk ** -0.5
+    q, k = rnd((2, 2, N, Dqk), 60), rnd((2, 2, N, Dqk), 61)
+    v = rnd((2, 2, N, Dv), 62)
+    tq, tk, tv = rnd(q.shape, 63), rnd(k.shape, 64), rnd(v.shape, 65)
+    o, to, lse = oracle.attention_jvp(q, k, v, tq, tk, tv, scale, causal)
+    assert o.shape == (2, 2, N, Dv) and to.shape == (2, 2, N, Dv) and lse.shape == (2, 2, N)
+    t = torch.from_numpy
+    with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+        ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal, scale=scale)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+
+    def f(a, b, c):
+        s = scale * a @ b.transpose(-1, -2)
+        if causal:
+            s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+        return torch.softmax(s, dim=-1) @ c
+    _, rto = torch.func.jvp(f, (t(q), t(k), t(v)), (t(tq), t(tk), t(tv)))
+    np.testing.assert_allclose(to, rto.numpy(), rtol=0, atol=1e-12)
