@@ -10,6 +10,7 @@ current stream.
 from .binding import (  # noqa: F401
     AttnError,
     bwd,
+    bwd_bias,
     bwd_workspace_bytes,
     fwd,
     fwd_bias,

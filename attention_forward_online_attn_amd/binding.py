@@ -82,6 +82,9 @@ def load_library():
     lib.jagged_attn_bwd.argtypes = [i32, vp, S3, vp, S3, vp, S3, vp, S3, vp, S3, vp, vp, S3, vp, S3, vp, S3,
                                     vp, i64, i64, i64, i64, i64, f32, i32, vp, ctypes.c_size_t, vp]
     lib.jagged_attn_bwd.restype = i32
+    lib.attn_bwd_bias.argtypes = [i32, vp, S4, vp, S4, vp, S4, vp, S4, vp, S4, vp, vp, i32, S4, vp, S4,
+                                  vp, S4, vp, S4, vp, S4, i64, i64, i64, i64, i64, f32, i32, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd_bias.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -294,3 +297,44 @@ def jagged_bwd(q, k, v, o, do, lse, offsets, max_seq_len, causal=False, sm_scale
                                _ptr(offsets), S, H, T, D, int(max_seq_len), float(sm_scale), int(bool(causal)),
                                _ptr(workspace), workspace.numel(), _stream(q)))
     return dq, dk, dv
+
+
+def bwd_bias(q, k, v, o, do, lse, bias=None, mask=None, causal=False, sm_scale=None, workspace=None,
+             return_dbias=False):
+    """Dense backward with the score operand of fwd_bias (pass the same bias
+    or mask, and the lse fwd_bias returned) -> (dq, dk, dv), or
+    (dq, dk, dv, dbias) with return_dbias (additive bias only; dbias is the
+    full [B,H,Nq,Nkv] dS, a view of rows padded to 16 bytes: sum it over the
+    dimensions the bias broadcasts)."""
+    lib = load_library()
+    _same(q, k, v, o, do)
+    if (bias is None) == (mask is None):
+        raise AttnError("pass exactly one of bias and mask")
+    B, H, Nq, D = q.shape
+    Nkv = k.shape[2]
+    if lse.dtype != torch.float32 or lse.shape != (B, H, Nq) or not lse.is_contiguous():
+        raise AttnError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if bias is not None:
+        if bias.dtype != q.dtype or bias.device != q.device:
+            raise AttnError("bias must have the dtype and device of q")
+        op, kind = bias.expand(B, H, Nq, Nkv), ATTN_BIAS_ADD
+    else:
+        if mask.dtype not in (torch.bool, torch.uint8) or mask.device != q.device:
+            raise AttnError("mask must be a bool or uint8 tensor on the device of q")
+        if return_dbias:
+            raise AttnError("a mask has no gradient")
+        op, kind = mask.expand(B, H, Nq, Nkv), ATTN_BIAS_MASK
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(B, H, Nq), 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbias = None
+    if return_dbias:  # rows padded to a multiple of 8 elements (16 bytes), returned as the [.., :Nkv] view
+        dbias = torch.empty((B, H, Nq, (Nkv + 7) // 8 * 8), dtype=q.dtype, device=q.device)[..., :Nkv]
+    db_strides = _s4(dbias) if dbias is not None else Strides4(0, 0, 0, 1)
+    _check(lib.attn_bwd_bias(_dtype_code(q), _ptr(q), _s4(q), _ptr(k), _s4(k), _ptr(v), _s4(v), _ptr(o), _s4(o),
+                             _ptr(do), _s4(do), _ptr(lse), _ptr(op), kind, _s4(op), _ptr(dbias), db_strides,
+                             _ptr(dq), _s4(dq), _ptr(dk), _s4(dk), _ptr(dv), _s4(dv), B, H, Nq, Nkv, D,
+                             float(sm_scale), int(bool(causal)), _ptr(workspace), workspace.numel(), _stream(q)))
+    return (dq, dk, dv, dbias) if return_dbias else (dq, dk, dv)

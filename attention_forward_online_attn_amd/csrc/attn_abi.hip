@@ -350,7 +350,7 @@ int jagged_attn_bwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   a.plan = plan;
   a.total_len = (int)total_len;
   a.max_seq_len = mlen;
-  rc = bwd_run(dtype == ATTN_FP16, (int)D, st, a, 1, H, total_len, total_len, cap);
+  rc = bwd_run(dtype == ATTN_FP16, (int)D, kNoBias, st, a, 1, H, total_len, total_len, cap);
   if (rc) return rc;
   return finish(st);
 }
@@ -362,12 +362,18 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
   return (size_t)(8 * rows);
 }
 
-int attn_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const void* k, attn_strides4 k_strides,
-             const void* v, attn_strides4 v_strides, const void* o, attn_strides4 o_strides, const void* d_o,
-             attn_strides4 do_strides, const float* lse, void* dq, attn_strides4 dq_strides, void* dk,
-             attn_strides4 dk_strides, void* dv, attn_strides4 dv_strides, int64_t B, int64_t H, int64_t Nq,
-             int64_t Nkv, int64_t D, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
-             void* stream) {
+}  // extern "C"
+
+namespace attn {
+namespace {
+
+// Dense backward, optionally with a score operand and its gradient.
+int dense_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const void* k, attn_strides4 k_strides,
+              const void* v, attn_strides4 v_strides, const void* o, attn_strides4 o_strides, const void* d_o,
+              attn_strides4 do_strides, const float* lse, void* dq, attn_strides4 dq_strides, void* dk,
+              attn_strides4 dk_strides, void* dv, attn_strides4 dv_strides, int64_t B, int64_t H, int64_t Nq,
+              int64_t Nkv, int64_t D, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
+              void* stream, const BiasOperand& bias, void* dbias, attn_strides4 dbias_strides) {
   int rc = check_common((int)dtype, D, sm_scale);
   if (rc) return rc;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
@@ -387,6 +393,21 @@ int attn_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const voi
   const void* ptrs[] = {q, k, v, o, d_o, dq, dk, dv};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  const int bias_kind = Nq > 0 && Nkv > 0 ? bias.kind : kNoBias;  // nothing to read otherwise
+  if (bias_kind != kNoBias) {
+    if (!bias.ptr) return ATTN_ERR_INVALID;
+    const int64_t bvec = 8;  // 16-bit bias: 16-byte chunks; mask: 8-byte chunks
+    if ((rc = check_s4(bias.strides, B, H, Nq, bvec))) return rc;
+    if ((reinterpret_cast<uintptr_t>(bias.ptr) & (bias_kind == kAddBias ? 15u : 7u)) != 0) return ATTN_ERR_UNSUPPORTED;
+  }
+  if (dbias != nullptr && bias_kind != kNoBias) {
+    if (bias_kind != kAddBias) return ATTN_ERR_INVALID;  // a mask has no gradient
+    if ((rc = check_s4(dbias_strides, B, H, Nq, 8))) return rc;
+    // every element is written by one lane: broadcast (stride 0) would race
+    if ((B > 1 && dbias_strides.b == 0) || (H > 1 && dbias_strides.h == 0) || (Nq > 1 && dbias_strides.n == 0))
+      return ATTN_ERR_INVALID;
+    if (!aligned16(dbias)) return ATTN_ERR_UNSUPPORTED;
+  }
   const int64_t rows = B * H * Nq;
   if (rows > 0 && (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, Nq) || ((uintptr_t)workspace & 15u)))
     return ATTN_ERR_WORKSPACE;
@@ -405,15 +426,57 @@ int attn_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const voi
   a.dq_sb = dq_strides.b; a.dq_sh = dq_strides.h; a.dq_sn = dq_strides.n;
   a.dk_sb = dk_strides.b; a.dk_sh = dk_strides.h; a.dk_sn = dk_strides.n;
   a.dv_sb = dv_strides.b; a.dv_sh = dv_strides.h; a.dv_sn = dv_strides.n;
+  if (bias_kind != kNoBias) {
+    a.bias = bias.ptr;
+    a.bias_sb = bias.strides.b; a.bias_sh = bias.strides.h; a.bias_sn = bias.strides.n;
+    if (dbias != nullptr) {
+      a.dbias = dbias;
+      a.dbias_sb = dbias_strides.b; a.dbias_sh = dbias_strides.h; a.dbias_sn = dbias_strides.n;
+    }
+  }
   a.B = (int)B; a.H = (int)H; a.Nq = (int)Nq; a.Nkv = (int)Nkv;
   a.sm_scale = sm_scale;
   a.c = sm_scale * kLog2e;
+  if (a.c == 0.f) a.c = 1.17549435e-38f;  // sm_scale == 0: masked scores stay -inf (no 0 * inf)
   a.causal = causal ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
-  rc = bwd_run(dtype == ATTN_FP16, (int)D, st, a, B, H, Nq, Nkv, 0);
+  rc = bwd_run(dtype == ATTN_FP16, (int)D, bias_kind, st, a, B, H, Nq, Nkv, 0);
   if (rc) return rc;
   return finish(st);
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" {
+
+int attn_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const void* k, attn_strides4 k_strides,
+             const void* v, attn_strides4 v_strides, const void* o, attn_strides4 o_strides, const void* d_o,
+             attn_strides4 do_strides, const float* lse, void* dq, attn_strides4 dq_strides, void* dk,
+             attn_strides4 dk_strides, void* dv, attn_strides4 dv_strides, int64_t B, int64_t H, int64_t Nq,
+             int64_t Nkv, int64_t D, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  return dense_bwd(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, d_o, do_strides, lse, dq, dq_strides,
+                   dk, dk_strides, dv, dv_strides, B, H, Nq, Nkv, D, sm_scale, causal, workspace, workspace_bytes,
+                   stream, BiasOperand(), nullptr, attn_strides4{0, 0, 0, 1});
+}
+
+int attn_bwd_bias(attn_dtype dtype, const void* q, attn_strides4 q_strides, const void* k, attn_strides4 k_strides,
+                  const void* v, attn_strides4 v_strides, const void* o, attn_strides4 o_strides, const void* d_o,
+                  attn_strides4 do_strides, const float* lse, const void* bias, attn_bias_kind bias_kind,
+                  attn_strides4 bias_strides, void* dbias, attn_strides4 dbias_strides, void* dq,
+                  attn_strides4 dq_strides, void* dk, attn_strides4 dk_strides, void* dv, attn_strides4 dv_strides,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (bias_kind != ATTN_BIAS_ADD && bias_kind != ATTN_BIAS_MASK) return ATTN_ERR_UNSUPPORTED;
+  BiasOperand b;
+  b.ptr = bias;
+  b.kind = bias_kind == ATTN_BIAS_ADD ? kAddBias : kMaskBias;
+  b.strides = bias_strides;
+  return dense_bwd(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, d_o, do_strides, lse, dq, dq_strides,
+                   dk, dk_strides, dv, dv_strides, B, H, Nq, Nkv, D, sm_scale, causal, workspace, workspace_bytes,
+                   stream, b, dbias, dbias_strides);
 }
 
 const char* attn_status_string(int status) {

@@ -32,6 +32,7 @@ namespace attn {
 struct BwdTile {
   int64_t q_off, k_off, v_off, do_off, dq_off, dk_off, dv_off;
   int64_t row_base;  // index of row 0 in the LSE and workspace rows
+  int64_t bias_off, dbias_off;  // element offsets of row 0 in the bias and its gradient (dense)
   int t;             // query tile (dQ kernel) or key tile (dK/dV kernel)
   int Lstore;        // rows / keys [0, Lstore) exist and are written
   int Lq;            // queries [0, Lq) take part
@@ -92,6 +93,8 @@ __device__ __forceinline__ BwdTile bwd_tile(const BwdArgs& a, int bid, bool stor
     t.dk_off = b * a.dk_sb + h * a.dk_sh;
     t.dv_off = b * a.dv_sb + h * a.dv_sh;
     t.row_base = (int64_t)bh * a.Nq;
+    t.bias_off = b * a.bias_sb + h * a.bias_sh;
+    t.dbias_off = b * a.dbias_sb + h * a.dbias_sh;
     t.Lq = a.Nq;
     t.Lkv = a.Nkv;
     t.Lstore = store_rows_are_keys ? a.Nkv : a.Nq;
@@ -116,6 +119,8 @@ __device__ __forceinline__ BwdTile bwd_tile(const BwdArgs& a, int bid, bool stor
     t.dk_off = h * a.dk_sh + begin * a.dk_sn;
     t.dv_off = h * a.dv_sh + begin * a.dv_sn;
     t.row_base = (int64_t)h * T + begin;
+    t.bias_off = 0;
+    t.dbias_off = 0;
     t.Lq = used;
     t.Lkv = used;
     t.Lstore = len;
@@ -157,7 +162,7 @@ struct BwdDqCfg {
   static constexpr int LDS = 2 * STAGE;
 };
 
-template <int D, int BN, bool F16 = false>
+template <int D, int BN, bool F16 = false, int BIAS = kNoBias>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   using C = BwdDqCfg<D, BN>;
   constexpr int BM = C::BM, TILE = C::TILE, STAGE = C::STAGE, NW = C::NW;
@@ -218,6 +223,42 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   bf16x8 dummy_t[1];
   f32x16 dummy_ts[1];
 
+  // bias / mask of this lane's row, loaded one key tile ahead as in the
+  // forward; with a bias gradient requested, dS of the row (as rounded for
+  // the dQ product) is written for every key, 0 where the row sees none
+  constexpr int BCH = 2 * NB;
+  constexpr int BEL = BIAS == kAddBias ? 2 : 1;
+  unsigned bsl[BIAS ? 2 : 1][BIAS ? BCH : 1][bias_dwords<BIAS>()];
+  const char* brow = nullptr;
+  bf16* dbrow = nullptr;
+  if constexpr (BIAS != kNoBias) {
+    brow = (const char*)a.bias + (t.bias_off + (int64_t)r_cl * a.bias_sn) * BEL;
+    if (a.dbias != nullptr && my_row < t.Lstore) dbrow = (bf16*)a.dbias + t.dbias_off + (int64_t)my_row * a.dbias_sn;
+  }
+  const float cs = BIAS == kAddBias ? 1.f : a.c;  // the bias moves the scores to the exp2 domain
+  auto bias_load = [&](int j, auto slot_tag) {
+    if constexpr (BIAS != kNoBias)
+      bias_chunks<BIAS, BCH>(brow, j * BN + 8 * h32, j * BN + BN <= t.Lkv, t.Lkv, bsl[decltype(slot_tag)::value]);
+  };
+  auto dbias_chunk = [&](int key0, bf16x8 val) {  // keys key0 .. key0 + 7 of this lane's row
+    if (key0 + 8 <= t.Lkv) {
+      *(bf16x8*)(dbrow + key0) = val;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (key0 + e < t.Lkv) dbrow[key0 + e] = val[e];
+    }
+  };
+  auto dbias_zero_tile = [&](int j) {
+    if constexpr (BIAS != kNoBias) {
+      if (dbrow != nullptr) {
+        const bf16x8 z = {};
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) dbias_chunk(j * BN + 16 * c + 8 * h32, z);
+      }
+    }
+  };
+
   auto fetch = [&](int j, int stage) {
     bwd_dma_rows<D, BN, NW>(K + (int64_t)j * BN * a.k_sn, a.k_sn, 0, t.Lkv - j * BN, smem + stage * STAGE, wave, lane);
     bwd_dma_rows<D, BN, NW>(V + (int64_t)j * BN * a.v_sn, a.v_sn, 0, t.Lkv - j * BN, smem + stage * STAGE + TILE, wave,
@@ -226,7 +267,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 
   auto step = [&](int j, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
-    if (j + 1 < n_tiles) fetch(j + 1, S ^ 1);
+    if (j + 1 < n_tiles) {
+      bias_load(j + 1, std::integral_constant<int, S ^ 1>{});
+      fetch(j + 1, S ^ 1);
+    }
     if (j * BN < wave_max) {
       f32x16 s[NB], dp[NB];
       scores_section<D, NB, false, S * STAGE, 0, F16>(kaddr, qf, dummy_t, s, dummy_ts);          // S^T = K Q^T
@@ -240,13 +284,14 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
             if (key >= my_lim) s[bb][r] = -INFINITY;
           }
       }
+      if constexpr (BIAS != kNoBias) apply_bias<BIAS, F16, NB>(s, bsl[S], a.c);
       // dS^T = P^T (dP^T - delta) as the bf16 B operand (keys 8 per register
       // group = key chunk e / 8); chunk 0 first, chunk c+1 computed after the
       // MFMAs of chunk c of the product below
       bf16x8 dsf[NB][2];
       auto dsel = [&](auto e_tag) {
         constexpr int e = decltype(e_tag)::value, bb = e / 16, r = e % 16;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], a.c, -lse2));
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], cs, -lse2));
         dsf[bb][r >> 3][r & 7] = to16<F16>(p * (dp[bb][r] - delta));
       };
       static_for<8>(dsel);
@@ -258,11 +303,20 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
             dsel(std::integral_constant<int, 8 * (c + 1) + (i % DB) * EPS + decltype(k_tag)::value>{});
           });
       });
+      if constexpr (BIAS != kNoBias) {
+        if (dbrow != nullptr) {
+#pragma unroll
+          for (int c = 0; c < BCH; ++c) dbias_chunk(j * BN + 16 * c + 8 * h32, dsf[c >> 1][c & 1]);
+        }
+      }
+    } else {
+      dbias_zero_tile(j);  // no key of this tile is seen by the wave's rows
     }
     __syncthreads();
   };
 
   if (n_tiles > 0) {
+    bias_load(0, std::integral_constant<int, 0>{});
     fetch(0, 0);
     __syncthreads();
     int j = 0;
@@ -272,6 +326,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     }
     if (j < n_tiles) step(j, std::integral_constant<int, 0>{});
   }
+  for (int j = n_tiles; j * BN < t.Lkv; ++j) dbias_zero_tile(j);  // key tiles no row of the workgroup sees
 
   if (my_row < t.Lstore) {
     bf16* orow = (bf16*)a.dq + t.dq_off + my_row * a.dq_sn;
@@ -299,7 +354,7 @@ struct BwdDkdvCfg {
   static constexpr int WAVES_PER_EU = D == 128 ? 1 : 2;  // D=128 holds K, V, dK, dV: 1 wave per SIMD
 };
 
-template <int D, bool F16 = false>
+template <int D, bool F16 = false, int BIAS = kNoBias>
 __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_dkdv_kernel(BwdArgs a) {
   using C = BwdDkdvCfg<D>;
   constexpr int BN = C::BN, BMQ = C::BMQ, TILE = C::TILE, STAGE = C::STAGE, NW = C::NW;
@@ -359,6 +414,30 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
   bf16x8 dummy_t[1];
   f32x16 dummy_ts[1];
 
+  // bias / mask for this lane's key and the 16 queries of its registers
+  // (register r: query q0 + 16 (r / 8) + 8 h32 + r % 8), element loads one
+  // query tile ahead; 32 lanes read 64 consecutive bytes of a bias row
+  constexpr int BEL = BIAS == kAddBias ? 2 : 1;
+  unsigned bq[BIAS ? 2 : 1][BIAS ? 16 : 1];
+  const char* bcol = nullptr;
+  if constexpr (BIAS != kNoBias) {
+    const int kc = my_key < t.Lkv ? my_key : t.Lkv - 1;
+    bcol = (const char*)a.bias + (t.bias_off + kc) * BEL;
+  }
+  const float cs = BIAS == kAddBias ? 1.f : a.c;  // the bias moves the scores to the exp2 domain
+  auto bias_load = [&](int jq, auto slot_tag) {
+    if constexpr (BIAS != kNoBias) {
+      constexpr int SL = decltype(slot_tag)::value;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = min(jq * BMQ + 16 * (r >> 3) + 8 * h32 + (r & 7), t.Lq - 1);
+        const char* src = bcol + (int64_t)qi * a.bias_sn * BEL;
+        if constexpr (BIAS == kAddBias) bq[SL][r] = *(const unsigned short*)src;
+        else bq[SL][r] = *(const unsigned char*)src;
+      }
+    }
+  };
+
   // tile jq: Q and dO rows, then 32 lse2 and 32 delta values (4 bytes per
   // lane of wave 0: lanes 0-31 lse2, lanes 32-63 delta)
   auto fetch = [&](int jq, int stage) {
@@ -376,7 +455,10 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
 
   auto step = [&](int jq, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
-    if (jq + 1 < n_qt) fetch(jq + 1, S ^ 1);
+    if (jq + 1 < n_qt) {
+      bias_load(jq + 1, std::integral_constant<int, S ^ 1>{});
+      fetch(jq + 1, S ^ 1);
+    }
     const int q0 = jq * BMQ;
     if (wave_keys && q0 + BMQ > wave_q_first) {  // wave-uniform: some key of the wave sees some query
       f32x16 s[1], dp[1];
@@ -390,6 +472,15 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
           const int qi = q0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
           if (qi >= t.Lq || my_key >= t.Lkv || (a.causal && my_key > qi)) s[0][r] = -INFINITY;
         }
+      }
+      if constexpr (BIAS == kAddBias) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[0][r] = __builtin_fmaf(s[0][r], a.c, from16<F16>(__builtin_bit_cast(bf16, (unsigned short)bq[S][r])) * kLog2e);
+      } else if constexpr (BIAS == kMaskBias) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (bq[S][r] == 0u) s[0][r] = -INFINITY;
       }
       // register r holds query q0 + 16 (r / 8) + 8 h32 + r % 8; chunk c (the
       // 8 registers 8c..8c+7) needs the lse2 and delta of 8 consecutive queries
@@ -406,7 +497,7 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
         for (int e = 0; e < 8; ++e) {
           const float l2 = e < 4 ? a0[e & 3] : a1[e & 3];
           const float dl = e < 4 ? d0[e & 3] : d1[e & 3];
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][8 * c + e], a.c, -l2));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][8 * c + e], cs, -l2));
           pf[0][c][e] = to16<F16>(p);
           dsf[0][c][e] = to16<F16>(p * (dp[0][8 * c + e] - dl));
         }
@@ -422,6 +513,7 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
   };
 
   if (jq0 < n_qt && kt * BN < t.Lkv) {  // a tile of keys past Lkv only writes zeros
+    bias_load(jq0, std::integral_constant<int, 0>{});
     fetch(jq0, 0);
     __syncthreads();
     int jq = jq0;

@@ -90,6 +90,13 @@ struct BwdArgs {
   void* dv;
   float* delta;  // workspace [B * H * Nq]: rowsum(O dO)
   float* lse2;   // workspace [B * H * Nq]: LSE log2(e); rows without keys +inf
+  // dense only: optional [B, H, Nq, Nkv] bias (input element type) or uint8
+  // mask (key stride 1), and the bias gradient dS (input element type;
+  // nullptr: not written)
+  const void* bias;
+  int64_t bias_sb, bias_sh, bias_sn;
+  void* dbias;
+  int64_t dbias_sb, dbias_sh, dbias_sn;
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
   int64_t v_sb, v_sh, v_sn;

@@ -47,8 +47,12 @@ KernelChoice fwd_mixed_fp16(int D, int Dv, bool jvp);           // inst_fwd_mixe
 // Backward: enqueues the prep, dQ and dK/dV kernels (inst_bwd.hip).  Dense:
 // B*H*Nq rows, grids over (batch, head, tile).  Jagged (a.offsets set): the
 // prep kernel sees H*total_len rows as one batch and both gradient kernels
-// cover `items` plan items per head.
-int bwd_run(bool f16, int D, hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
+// cover `items` plan items per head.  With a bias kind (dense only) it hands
+// the gradient kernels over to the biased instances (bwd_run_bias,
+// inst_bwd_bias.hip).
+int bwd_run(bool f16, int D, int bias_kind, hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
             int64_t items);
+int bwd_run_bias(bool f16, int D, int bias_kind, hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq,
+                 int64_t Nkv);
 
 }  // namespace attn

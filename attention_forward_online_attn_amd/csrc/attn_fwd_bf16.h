@@ -310,6 +310,74 @@ __device__ __forceinline__ void pv_lo_block(const lds_t* vt, const int (&vlo)[D 
   }
 }
 
+// ---- bias / mask operand (flash attention with bias page, _attn_fwd_inner).
+// A lane whose scores sit in accumulator registers s[b][r] (key 32 b +
+// 16 (r / 8) + 8 h + r % 8 of a tile, h the lane's half) needs, of its own
+// row, the 8-key chunks c = 0 .. 2 NB - 1 at keys kb + 16 c (kb = tile start
+// + 8 h): 16 bytes of a 16-bit bias or 8 bytes of a uint8 mask each; chunk c
+// is registers 8 (c % 2) .. 8 (c % 2) + 7 of s[c / 2].
+template <int BIAS>
+constexpr int bias_dwords() { return BIAS == kAddBias ? 4 : 2; }
+
+// Loads the chunks of one row into registers; `full`: every key of the
+// chunks exists (vector loads), else element loads of the keys below Lkv.
+template <int BIAS, int NCH>
+__device__ __forceinline__ void bias_chunks(const char* brow, int kb, bool full, int Lkv,
+                                            unsigned (&dst)[NCH][bias_dwords<BIAS>()]) {
+  constexpr int BEL = BIAS == kAddBias ? 2 : 1;
+  if (full) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const char* src = brow + (int64_t)(kb + 16 * c) * BEL;
+      if constexpr (BIAS == kAddBias) {
+        const u32x4 w = *(const u32x4*)src;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dst[c][x] = w[x];
+      } else {
+        const u32x2 w = *(const u32x2*)src;
+        dst[c][0] = w[0];
+        dst[c][1] = w[1];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int x = 0; x < bias_dwords<BIAS>(); ++x) dst[c][x] = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kb + 16 * c + e;
+        if (key < Lkv) {
+          if constexpr (BIAS == kAddBias)
+            dst[c][e >> 1] |= (unsigned)(*(const unsigned short*)(brow + 2 * (int64_t)key)) << (16 * (e & 1));
+          else
+            dst[c][e >> 2] |= (unsigned)(*(const unsigned char*)(brow + key)) << (8 * (e & 3));
+        }
+      }
+    }
+  }
+}
+
+// Applies the chunks to the scores: additive bias -> s c + bias log2(e) (the
+// exp2 domain, after which the softmax scale is 1); mask -> -inf where 0.
+template <int BIAS, bool F16, int NB>
+__device__ __forceinline__ void apply_bias(f32x16 (&s)[NB], const unsigned (&src)[2 * NB][bias_dwords<BIAS>()],
+                                           float c) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (BIAS == kAddBias) {
+        const unsigned w = src[2 * b + (r >> 3)][(r & 7) >> 1];
+        const unsigned short h = (unsigned short)((r & 1) ? (w >> 16) : (w & 0xffffu));
+        s[b][r] = __builtin_fmaf(s[b][r], c, from16<F16>(__builtin_bit_cast(bf16, h)) * kLog2e);
+      } else {
+        const unsigned w = src[2 * b + (r >> 3)][(r & 7) >> 2];
+        if (((w >> (8 * (r & 3))) & 0xffu) == 0u) s[b][r] = -INFINITY;
+      }
+    }
+}
+
 // D is the query/key head dim; DV_ (0: the same) the value head dim, which
 // sets the width of V, tV, O and tO (JVP page: _attention.forward takes
 // d_v != d_qk).
@@ -566,50 +634,16 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   // has also completed them.  With an additive bias the scores are moved to
   // the exp2 domain once (s c + bias log2 e) and the scale below becomes 1.
   constexpr int BCH = 2 * NB;                      // chunks per lane per tile
-  constexpr int BWD = BIAS == kAddBias ? 4 : 2;    // dwords per chunk: 8 x 16-bit, or 8 bytes
   constexpr int BEL = BIAS == kAddBias ? 2 : 1;    // bytes per element
-  unsigned bsl[BIAS ? 2 : 1][BIAS ? BCH : 1][BWD];
+  unsigned bsl[BIAS ? 2 : 1][BIAS ? BCH : 1][bias_dwords<BIAS>()];
   const char* brow = nullptr;
   if constexpr (BIAS != kNoBias) {
     const int r = my_row < t.Lstore ? my_row : t.Lstore - 1;
     brow = (const char*)a.bias + (t.bias_off + (int64_t)r * a.bias_sn) * BEL;
   }
   auto bias_load = [&](int j, auto slot_tag) {
-    if constexpr (BIAS != kNoBias) {
-      constexpr int SL = decltype(slot_tag)::value;
-      const int kb = j * BN + 8 * h32;
-      if (j * BN + BN <= t.Lkv) {
-#pragma unroll
-        for (int c = 0; c < BCH; ++c) {
-          const char* src = brow + (int64_t)(kb + 16 * c) * BEL;
-          if constexpr (BIAS == kAddBias) {
-            const u32x4 w = *(const u32x4*)src;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) bsl[SL][c][x] = w[x];
-          } else {
-            const u32x2 w = *(const u32x2*)src;
-            bsl[SL][c][0] = w[0];
-            bsl[SL][c][1] = w[1];
-          }
-        }
-      } else {  // ragged last tile: element loads of the keys that exist
-#pragma unroll
-        for (int c = 0; c < BCH; ++c) {
-#pragma unroll
-          for (int x = 0; x < BWD; ++x) bsl[SL][c][x] = 0u;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = kb + 16 * c + e;
-            if (key < t.Lkv) {
-              if constexpr (BIAS == kAddBias)
-                bsl[SL][c][e >> 1] |= (unsigned)(*(const unsigned short*)(brow + 2 * (int64_t)key)) << (16 * (e & 1));
-              else
-                bsl[SL][c][e >> 2] |= (unsigned)(*(const unsigned char*)(brow + key)) << (8 * (e & 3));
-            }
-          }
-        }
-      }
-    }
+    if constexpr (BIAS != kNoBias)
+      bias_chunks<BIAS, BCH>(brow, j * BN + 8 * h32, j * BN + BN <= t.Lkv, t.Lkv, bsl[decltype(slot_tag)::value]);
   };
   // scale of the scores into the exp2 domain at the softmax (1 once an
   // additive bias has been applied)
@@ -663,24 +697,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
             if (key >= my_lim) s[b][r] = -INFINITY;
           }
       }
-      if constexpr (BIAS == kAddBias) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const unsigned w = bsl[S][2 * b + (r >> 3)][(r & 7) >> 1];
-            const unsigned short h = (unsigned short)((r & 1) ? (w >> 16) : (w & 0xffffu));
-            s[b][r] = __builtin_fmaf(s[b][r], a.c, from16<F16>(__builtin_bit_cast(bf16, h)) * kLog2e);
-          }
-      } else if constexpr (BIAS == kMaskBias) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const unsigned w = bsl[S][2 * b + (r >> 3)][(r & 7) >> 2];
-            if (((w >> (8 * (r & 3))) & 0xffu) == 0u) s[b][r] = -INFINITY;
-          }
-      }
+      if constexpr (BIAS != kNoBias) apply_bias<BIAS, F16, NB>(s, bsl[S], a.c);
 
       // online softmax: tile row max (in-lane, then the other half-wave)
       float mx = s[0][0];

@@ -37,8 +37,10 @@ template <bool F16>
 KernelChoice choose_mixed16(int D, int Dv, bool jvp) {
   return by_dim(D, [&](auto dq) {
     return by_dim(Dv, [&](auto dv) {
-      constexpr int A = decltype(dq)::value, V = decltype(dv)::value, DVp = A == V ? 0 : V;
-      return jvp ? r32<A, kBnJvp, true, 4, F16, kNoBias, DVp>() : r32<A, kBnDense, false, 4, F16, kNoBias, DVp>();
+      constexpr int A = decltype(dq)::value, V = decltype(dv)::value;
+      // equal dims never come here (they take choose16; no instance twice in the library)
+      if constexpr (A == V) return KernelChoice{};
+      else return jvp ? r32<A, kBnJvp, true, 4, F16, kNoBias, V>() : r32<A, kBnDense, false, 4, F16, kNoBias, V>();
     });
   });
 }

@@ -258,6 +258,39 @@ ATTN_API int attn_bwd(attn_dtype dtype,
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Dense attention backward with the score operand of attn_fwd_bias (flash
+ * attention with bias page: _attn_bwd_dkdv, _attn_bwd_dq and
+ * _flash_attn_bwd): P is recomputed as exp(sm_scale q k^T + bias - lse)
+ * (ATTN_BIAS_ADD) or with the masked keys removed (ATTN_BIAS_MASK), and the
+ * gradients are those of attn_bwd.  bias, bias_kind and bias_strides as for
+ * attn_fwd_bias, and lse must be what attn_fwd_bias wrote with that operand.
+ *   dbias   optional (NULL: not written) gradient of the bias, dS =
+ *           P * (dP - delta), [B, H, Nq, Nkv] in the input element type
+ *           through dbias_strides = {b, h, n, d}: d must be 1, no stride may be
+ *           0 where its extent exceeds 1 and distinct elements must not
+ *           overlap; base 16-byte aligned, b/h/n strides multiples of 16
+ *           bytes.  Every element is written, 0 for masked pairs.  With a
+ *           broadcast bias the caller sums dbias over the broadcast dims.
+ *           Only with ATTN_BIAS_ADD (a mask has no gradient).
+ * bf16 or fp16; other arguments, checks and errors as attn_bwd.
+ */
+ATTN_API int attn_bwd_bias(attn_dtype dtype,
+                  const void* q, attn_strides4 q_strides,
+                  const void* k, attn_strides4 k_strides,
+                  const void* v, attn_strides4 v_strides,
+                  const void* o, attn_strides4 o_strides,
+                  const void* d_o, attn_strides4 do_strides,
+                  const float* lse,
+                  const void* bias, attn_bias_kind bias_kind, attn_strides4 bias_strides,
+                  void* dbias, attn_strides4 dbias_strides,
+                  void* dq, attn_strides4 dq_strides,
+                  void* dk, attn_strides4 dk_strides,
+                  void* dv, attn_strides4 dv_strides,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D,
+                  float sm_scale, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace jagged_attn_bwd needs (host function, no GPU
  * access): the tile plan plus two fp32 values per row of every head.
  * Returns 0 for invalid sizes.

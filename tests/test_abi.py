@@ -33,7 +33,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(
         ["attn_fwd", "attn_fwd_bias", "attn_fwd_dv", "attn_fwd_jvp", "jagged_attn_workspace_bytes", "jagged_attn_fwd",
-         "attn_bwd_workspace_bytes", "attn_bwd", "jagged_attn_bwd_workspace_bytes", "jagged_attn_bwd",
+         "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_bias", "jagged_attn_bwd_workspace_bytes", "jagged_attn_bwd",
          "attn_status_string"])
 
 
@@ -215,4 +215,26 @@ def test_dv_validation(lib):
     assert call(tk=P) == INVALID          # tangents without tq: not a JVP call
     assert call(to=P) == INVALID
     assert call(tq=P, tk=P, tv=P) == INVALID  # JVP without to
+    assert call(B=0) == OK
+
+
+def test_bwd_bias_validation(lib):
+    B, H, N, D = 1, 2, 128, 64
+    st = dense_strides(B, H, N, D)
+    full = Strides4(H * N * N, N * N, N, 1)
+    need = lib.attn_bwd_workspace_bytes(B, H, N)
+    ADD, MASK = 1, 2
+
+    def call(kind=ADD, bias=P, bs=full, dbias=0, dbs=full, dtype=BF16, B=B):
+        return lib.attn_bwd_bias(dtype, P, st, P, st, P, st, P, st, P, st, P, bias, kind, bs, dbias, dbs,
+                                 P, st, P, st, P, st, B, H, N, N, D, 0.125, 0, P, need, None)
+    assert call(kind=0) == UNSUPPORTED
+    assert call(dtype=FP32) == UNSUPPORTED
+    assert call(bias=0) == INVALID
+    assert call(bs=Strides4(0, 0, N, 2)) == INVALID                      # key stride must be 1
+    assert call(bias=P + 2) == UNSUPPORTED
+    assert call(kind=MASK, dbias=P) == INVALID                           # a mask has no gradient
+    assert call(dbias=P, dbs=Strides4(H * N * N, 0, N, 1)) == INVALID    # heads would share (race)
+    assert call(dbias=P, dbs=Strides4(H * N * N, N * N, 0, 1)) == INVALID
+    assert call(dbias=P + 8) == UNSUPPORTED
     assert call(B=0) == OK
