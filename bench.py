@@ -19,7 +19,7 @@ launch, outside the events, which evicts L2 and the Infinity Cache).  `cpu_basel
 sample of the same workload (a few heads) on this host's cores.
 
 Profiling modes (for rocprofv3 runs): --only {fwd,fwd_causal,jvp,jvp_causal,
-causal_d64,jagged,bwd,bwd_causal,fwd_fp16,fwd_bias,fwd_mask,jagged_bwd} runs just that workload K times; --copy-calibration runs a
+causal_d64,jagged,bwd,bwd_causal,fwd_fp16,fwd_bias,fwd_mask,bwd_bias,jagged_bwd} runs just that workload K times; --copy-calibration runs a
 plain device copy of known size (the scale for FETCH_SIZE / WRITE_SIZE).
 """
 
@@ -130,6 +130,14 @@ def make_cases(torch, attn, wl):
                              q, k, v, o_f, do, lse_f, causal=c, sm_scale=w.sm_scale, workspace=ws_b)),
                          2.5 * dense_flops(w.B, w.H, w.N, w.N, w.D, causal), bwd_io,
                          f"{w.name} backward: B={w.B} H={w.H} N={w.N} D={w.D} bf16 causal={causal} (dQ, dK, dV)")
+
+    # backward of the per-head bias workload (the bias as a fixed operand)
+    o_b, lse_b = attn.fwd_bias(q, k, v, bias=bias, sm_scale=w.sm_scale)
+    ws_bb = torch.empty(attn.bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+    cases["bwd_bias"] = Case("bwd_bias", lambda: attn.bwd_bias(q, k, v, o_b, do, lse_b, bias=bias, sm_scale=w.sm_scale,
+                                                               workspace=ws_bb),
+                             2.5 * dense_flops(w.B, w.H, w.N, w.N, w.D, False), bwd_io + bias.numel() * 2,
+                             f"{w.name} backward: B={w.B} H={w.H} N={w.N} D={w.D} bf16 + bias [1,{w.H},{w.N},{w.N}] bf16 (dQ, dK, dV)")
 
     w5 = wl.WORKLOADS["jagged_d128"]
     lengths = wl.jagged_lengths(w5.num_seqs, w5.max_len, 0)
@@ -293,7 +301,7 @@ def main():
 
     extra = {"fwd": summary(head, durs, time_launches(torch, head, n_cold, 2, flush)[0])}
     for name in ("fwd_causal", "fwd_fp16", "fwd_bias", "fwd_mask", "jvp", "jvp_causal", "causal_d64", "jagged", "bwd",
-                 "bwd_causal", "jagged_bwd"):
+                 "bwd_causal", "bwd_bias", "jagged_bwd"):
         c = cases[name]
         dw, _ = time_launches(torch, c, max(5, args.steps // 2), 10)
         dc, _ = time_launches(torch, c, n_cold, 2, flush)
