@@ -74,87 +74,122 @@ class Case:
         self.name, self.run, self.flops, self.bytes, self.desc = name, run, flops, bytes_, desc
 
 
-def make_cases(torch, attn, wl):
+def make_cases(torch, attn, wl, only=None):
+    """Workloads bound to resident device inputs.  With `only`, just that
+    case is built, and nothing but what it needs (its inputs, and the forward
+    pass that produces a backward's O and LSE) is launched before it runs, so
+    a profile of `--only X` holds X's kernels alone."""
     dev = torch.device("cuda:0")
-    cases = {}
+    memo = {}
 
-    w = wl.WORKLOADS["long_d128"]
-    q, k, v = (t.to(dev) for t in wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "bf16", 0))
-    io_bytes = 4 * q.numel() * 2 + w.B * w.H * w.N * 4
-    for causal in (False, True):
-        nm = "fwd_causal" if causal else "fwd"
-        cases[nm] = Case(nm, (lambda c=causal: attn.fwd(q, k, v, causal=c, sm_scale=w.sm_scale)),
-                         dense_flops(w.B, w.H, w.N, w.N, w.D, causal), io_bytes,
-                         f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} bf16 causal={causal}")
+    def shared(key, fn):  # inputs several cases use, built once
+        if key not in memo:
+            memo[key] = fn()
+        return memo[key]
 
-    # the headline shape with fp16 inputs (same 16-bit MFMA peak)
-    qh, kh, vh = (t.to(dev) for t in wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "fp16", 0))
-    cases["fwd_fp16"] = Case("fwd_fp16", lambda: attn.fwd(qh, kh, vh, causal=False, sm_scale=w.sm_scale),
-                             dense_flops(w.B, w.H, w.N, w.N, w.D, False), io_bytes,
-                             f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} fp16 causal=False")
-
+    w, w2, w4, w5 = (wl.WORKLOADS[n] for n in ("long_d128", "causal_d64", "jvp_d64", "jagged_d128"))
+    head = lambda: shared("head", lambda: [t.to(dev) for t in wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "bf16", 0)])
+    io_bytes = 4 * w.B * w.H * w.N * w.D * 2 + w.B * w.H * w.N * 4
+    bwd_io = 8 * w.B * w.H * w.N * w.D * 2 + w.B * w.H * w.N * 4
     # the headline shape with a score operand (bias page): a per-head additive
     # bias shared by the batch, and a per-batch boolean mask shared by the heads
-    bias = wl.score_bias((1, w.H, w.N, w.N), "bf16", 0).to(dev)
-    cases["fwd_bias"] = Case("fwd_bias", lambda: attn.fwd_bias(q, k, v, bias=bias, sm_scale=w.sm_scale),
-                             dense_flops(w.B, w.H, w.N, w.N, w.D, False), io_bytes + bias.numel() * 2,
-                             f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} bf16 + bias [1,{w.H},{w.N},{w.N}] bf16")
-    mask = wl.score_mask((w.B, 1, w.N, w.N), 0.75, 0).to(dev)
-    cases["fwd_mask"] = Case("fwd_mask", lambda: attn.fwd_bias(q, k, v, mask=mask, sm_scale=w.sm_scale),
-                             dense_flops(w.B, w.H, w.N, w.N, w.D, False), io_bytes + mask.numel(),
-                             f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} bf16 + mask [{w.B},1,{w.N},{w.N}] bool")
+    bias = lambda: shared("bias", lambda: wl.score_bias((1, w.H, w.N, w.N), "bf16", 0).to(dev))
+    mask = lambda: shared("mask", lambda: wl.score_mask((w.B, 1, w.N, w.N), 0.75, 0).to(dev))
+    grad = lambda: shared("do", lambda: wl.grad_output((w.B, w.H, w.N, w.D), "bf16", 0).to(dev))
+    lengths = wl.jagged_lengths(w5.num_seqs, w5.max_len, 0)
+    jag = lambda: shared("jag", lambda: [t.to(dev) for t in wl.jagged_inputs(lengths, w5.H, w5.D, "bf16", 0)])
 
-    w4 = wl.WORKLOADS["jvp_d64"]
-    ts = [t.to(dev) for t in wl.dense_inputs(w4.B, w4.H, w4.N, w4.N, w4.D, "bf16", 0, tangents=True)]
-    io4 = 8 * ts[0].numel() * 2 + w4.B * w4.H * w4.N * 4
-    for causal in (False, True):
-        nm = "jvp_causal" if causal else "jvp"
-        cases[nm] = Case(nm, (lambda c=causal: attn.fwd_jvp(*ts, causal=c, sm_scale=w4.sm_scale)),
-                         dense_flops(w4.B, w4.H, w4.N, w4.N, w4.D, causal, jvp=True), io4,
-                         f"{w4.name}: B={w4.B} H={w4.H} N={w4.N} D={w4.D} bf16 causal={causal} (O, tO, LSE)")
+    def fwd_case(causal):
+        q, k, v = head()
+        return Case("fwd_causal" if causal else "fwd", lambda: attn.fwd(q, k, v, causal=causal, sm_scale=w.sm_scale),
+                    dense_flops(w.B, w.H, w.N, w.N, w.D, causal), io_bytes,
+                    f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} bf16 causal={causal}")
 
-    w2 = wl.WORKLOADS["causal_d64"]
-    q2, k2, v2 = (t.to(dev) for t in wl.dense_inputs(w2.B, w2.H, w2.N, w2.N, w2.D, "bf16", 0))
-    cases["causal_d64"] = Case("causal_d64", lambda: attn.fwd(q2, k2, v2, causal=True, sm_scale=w2.sm_scale),
-                               dense_flops(w2.B, w2.H, w2.N, w2.N, w2.D, True), 4 * q2.numel() * 2 + w2.B * w2.H * w2.N * 4,
-                               f"{w2.name}: B={w2.B} H={w2.H} N={w2.N} D={w2.D} bf16 causal")
+    def fp16_case():  # the headline shape with fp16 inputs (same 16-bit MFMA peak)
+        qh, kh, vh = (t.to(dev) for t in wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "fp16", 0))
+        return Case("fwd_fp16", lambda: attn.fwd(qh, kh, vh, causal=False, sm_scale=w.sm_scale),
+                    dense_flops(w.B, w.H, w.N, w.N, w.D, False), io_bytes,
+                    f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} fp16 causal=False")
 
-    # backward over the headline shape: the forward's O and LSE, a seeded dO
-    do = wl.grad_output(q.shape, "bf16", 0).to(dev)
-    bwd_io = 8 * q.numel() * 2 + w.B * w.H * w.N * 4
-    for causal in (False, True):
-        nm = "bwd_causal" if causal else "bwd"
+    def bias_case():
+        q, k, v = head()
+        b = bias()
+        return Case("fwd_bias", lambda: attn.fwd_bias(q, k, v, bias=b, sm_scale=w.sm_scale),
+                    dense_flops(w.B, w.H, w.N, w.N, w.D, False), io_bytes + b.numel() * 2,
+                    f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} bf16 + bias [1,{w.H},{w.N},{w.N}] bf16")
+
+    def mask_case():
+        q, k, v = head()
+        m = mask()
+        return Case("fwd_mask", lambda: attn.fwd_bias(q, k, v, mask=m, sm_scale=w.sm_scale),
+                    dense_flops(w.B, w.H, w.N, w.N, w.D, False), io_bytes + m.numel(),
+                    f"{w.name}: B={w.B} H={w.H} N={w.N} D={w.D} bf16 + mask [{w.B},1,{w.N},{w.N}] bool")
+
+    def jvp_case(causal):
+        ts = shared("jvp", lambda: [t.to(dev) for t in wl.dense_inputs(w4.B, w4.H, w4.N, w4.N, w4.D, "bf16", 0,
+                                                                        tangents=True)])
+        return Case("jvp_causal" if causal else "jvp", lambda: attn.fwd_jvp(*ts, causal=causal, sm_scale=w4.sm_scale),
+                    dense_flops(w4.B, w4.H, w4.N, w4.N, w4.D, causal, jvp=True),
+                    8 * w4.B * w4.H * w4.N * w4.D * 2 + w4.B * w4.H * w4.N * 4,
+                    f"{w4.name}: B={w4.B} H={w4.H} N={w4.N} D={w4.D} bf16 causal={causal} (O, tO, LSE)")
+
+    def causal_d64_case():
+        q2, k2, v2 = (t.to(dev) for t in wl.dense_inputs(w2.B, w2.H, w2.N, w2.N, w2.D, "bf16", 0))
+        return Case("causal_d64", lambda: attn.fwd(q2, k2, v2, causal=True, sm_scale=w2.sm_scale),
+                    dense_flops(w2.B, w2.H, w2.N, w2.N, w2.D, True), 4 * q2.numel() * 2 + w2.B * w2.H * w2.N * 4,
+                    f"{w2.name}: B={w2.B} H={w2.H} N={w2.N} D={w2.D} bf16 causal")
+
+    def bwd_case(causal):  # backward over the headline shape: the forward's O and LSE, a seeded dO
+        q, k, v = head()
+        do = grad()
         o_f, lse_f = attn.fwd(q, k, v, causal=causal, sm_scale=w.sm_scale)
         ws_b = torch.empty(attn.bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
-        cases[nm] = Case(nm, (lambda c=causal, o_f=o_f, lse_f=lse_f, ws_b=ws_b: attn.bwd(
-                             q, k, v, o_f, do, lse_f, causal=c, sm_scale=w.sm_scale, workspace=ws_b)),
-                         2.5 * dense_flops(w.B, w.H, w.N, w.N, w.D, causal), bwd_io,
-                         f"{w.name} backward: B={w.B} H={w.H} N={w.N} D={w.D} bf16 causal={causal} (dQ, dK, dV)")
+        return Case("bwd_causal" if causal else "bwd",
+                    lambda: attn.bwd(q, k, v, o_f, do, lse_f, causal=causal, sm_scale=w.sm_scale, workspace=ws_b),
+                    2.5 * dense_flops(w.B, w.H, w.N, w.N, w.D, causal), bwd_io,
+                    f"{w.name} backward: B={w.B} H={w.H} N={w.N} D={w.D} bf16 causal={causal} (dQ, dK, dV)")
 
-    # backward of the per-head bias workload (the bias as a fixed operand)
-    o_b, lse_b = attn.fwd_bias(q, k, v, bias=bias, sm_scale=w.sm_scale)
-    ws_bb = torch.empty(attn.bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
-    cases["bwd_bias"] = Case("bwd_bias", lambda: attn.bwd_bias(q, k, v, o_b, do, lse_b, bias=bias, sm_scale=w.sm_scale,
-                                                               workspace=ws_bb),
-                             2.5 * dense_flops(w.B, w.H, w.N, w.N, w.D, False), bwd_io + bias.numel() * 2,
-                             f"{w.name} backward: B={w.B} H={w.H} N={w.N} D={w.D} bf16 + bias [1,{w.H},{w.N},{w.N}] bf16 (dQ, dK, dV)")
+    def bwd_bias_case():  # backward of the per-head bias workload (the bias as a fixed operand)
+        q, k, v = head()
+        b, do = bias(), grad()
+        o_b, lse_b = attn.fwd_bias(q, k, v, bias=b, sm_scale=w.sm_scale)
+        ws_bb = torch.empty(attn.bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+        return Case("bwd_bias", lambda: attn.bwd_bias(q, k, v, o_b, do, lse_b, bias=b, sm_scale=w.sm_scale,
+                                                      workspace=ws_bb),
+                    2.5 * dense_flops(w.B, w.H, w.N, w.N, w.D, False), bwd_io + b.numel() * 2,
+                    f"{w.name} backward: B={w.B} H={w.H} N={w.N} D={w.D} bf16 + bias [1,{w.H},{w.N},{w.N}] bf16 (dQ, dK, dV)")
 
-    w5 = wl.WORKLOADS["jagged_d128"]
-    lengths = wl.jagged_lengths(w5.num_seqs, w5.max_len, 0)
-    jq, jk, jv, off = (t.to(dev) for t in wl.jagged_inputs(lengths, w5.H, w5.D, "bf16", 0))
-    ws = torch.empty(attn.jagged_workspace_bytes(w5.num_seqs, jq.shape[1]), dtype=torch.uint8, device=dev)
-    cases["jagged"] = Case("jagged", lambda: attn.jagged_fwd(jq, jk, jv, off, w5.max_len, sm_scale=w5.sm_scale, workspace=ws),
-                           jagged_flops(lengths.tolist(), w5.H, w5.D), 4 * jq.numel() * 2 + jq.shape[0] * jq.shape[1] * 4,
-                           f"{w5.name}: 256 sequences U[1,1024], H=8 D=128 bf16, total_len={jq.shape[1]}")
-    # jagged backward over the same sequences, from the forward's O and LSE
-    jo, jl = attn.jagged_fwd(jq, jk, jv, off, w5.max_len, sm_scale=w5.sm_scale, workspace=ws)
-    jdo = wl.grad_output(jq.shape, "bf16", 0).to(dev)
-    jws = torch.empty(attn.jagged_bwd_workspace_bytes(w5.num_seqs, w5.H, jq.shape[1]), dtype=torch.uint8, device=dev)
-    cases["jagged_bwd"] = Case("jagged_bwd", lambda: attn.jagged_bwd(jq, jk, jv, jo, jdo, jl, off, w5.max_len,
-                                                                     sm_scale=w5.sm_scale, workspace=jws),
-                               2.5 * jagged_flops(lengths.tolist(), w5.H, w5.D), 8 * jq.numel() * 2 + jq.shape[0] * jq.shape[1] * 4,
-                               f"{w5.name} backward: 256 sequences U[1,1024], H=8 D=128 bf16 (dQ, dK, dV)")
-    return cases
+    def jagged_ws():
+        jq = jag()[0]
+        return shared("jws", lambda: torch.empty(attn.jagged_workspace_bytes(w5.num_seqs, jq.shape[1]),
+                                                 dtype=torch.uint8, device=dev))
+
+    def jagged_case():
+        jq, jk, jv, off = jag()
+        ws = jagged_ws()
+        return Case("jagged", lambda: attn.jagged_fwd(jq, jk, jv, off, w5.max_len, sm_scale=w5.sm_scale, workspace=ws),
+                    jagged_flops(lengths.tolist(), w5.H, w5.D), 4 * jq.numel() * 2 + jq.shape[0] * jq.shape[1] * 4,
+                    f"{w5.name}: 256 sequences U[1,1024], H=8 D=128 bf16, total_len={jq.shape[1]}")
+
+    def jagged_bwd_case():  # jagged backward over the same sequences, from the forward's O and LSE
+        jq, jk, jv, off = jag()
+        jo, jl = attn.jagged_fwd(jq, jk, jv, off, w5.max_len, sm_scale=w5.sm_scale, workspace=jagged_ws())
+        jdo = wl.grad_output(jq.shape, "bf16", 0).to(dev)
+        jws = torch.empty(attn.jagged_bwd_workspace_bytes(w5.num_seqs, w5.H, jq.shape[1]), dtype=torch.uint8, device=dev)
+        return Case("jagged_bwd", lambda: attn.jagged_bwd(jq, jk, jv, jo, jdo, jl, off, w5.max_len,
+                                                          sm_scale=w5.sm_scale, workspace=jws),
+                    2.5 * jagged_flops(lengths.tolist(), w5.H, w5.D), 8 * jq.numel() * 2 + jq.shape[0] * jq.shape[1] * 4,
+                    f"{w5.name} backward: 256 sequences U[1,1024], H=8 D=128 bf16 (dQ, dK, dV)")
+
+    builders = {
+        "fwd": lambda: fwd_case(False), "fwd_causal": lambda: fwd_case(True), "fwd_fp16": fp16_case,
+        "fwd_bias": bias_case, "fwd_mask": mask_case, "jvp": lambda: jvp_case(False),
+        "jvp_causal": lambda: jvp_case(True), "causal_d64": causal_d64_case, "jagged": jagged_case,
+        "bwd": lambda: bwd_case(False), "bwd_causal": lambda: bwd_case(True), "bwd_bias": bwd_bias_case,
+        "jagged_bwd": jagged_bwd_case,
+    }
+    names = [only] if only else list(builders)
+    return {n: builders[n]() for n in names}
 
 
 def time_case(torch, case, steps, warmup):
@@ -270,7 +305,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, args.steps)
         return
-    cases = make_cases(torch, attn, wl)
+    cases = make_cases(torch, attn, wl, args.only)
     if args.only:
         c = cases[args.only]
         avg, mn, _ = time_case(torch, c, args.steps, args.warmup)
@@ -331,7 +366,7 @@ def main():
         "jvp_value": extra["jvp"]["tflops"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128,64,false,4,false>",
+                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128,64,false,4,false,0,0>",
                      "avg_launch_ms": round(avg, 4), "min_launch_ms": round(mn, 4)},
         "extra": extra,
     }
