@@ -43,10 +43,11 @@ bool stride_ok(int64_t stride, int64_t extent, int64_t vec) {
   return extent <= 1 || stride % vec == 0;
 }
 
-int check_common(int dtype, int64_t D, float sm_scale) {
+// qk16: the query/key head dim may also be 16 (value-dim variants only).
+int check_common(int dtype, int64_t D, float sm_scale, bool qk16 = false) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP32 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale) || sm_scale < 0.f) return ATTN_ERR_INVALID;
-  if (D != 32 && D != 64 && D != 128) return D <= 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 128 && !(qk16 && D == 16)) return D <= 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -115,7 +116,7 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
           attn_strides4 sq, attn_strides4 sk, attn_strides4 sv, void* o, void* to, attn_strides4 so, float* lse,
           float* tlse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal,
           void* stream, bool jvp, const BiasOperand& bias = BiasOperand(), int64_t Dv = 0) {
-  int rc = check_common(dtype, D, sm_scale);
+  int rc = check_common(dtype, D, sm_scale, Dv != 0 && Dv != D);
   if (rc) return rc;
   if (Dv == 0) Dv = D;
   if (Dv != 32 && Dv != 64 && Dv != 128) return Dv < 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
@@ -214,6 +215,7 @@ int attn_fwd_dv(attn_dtype dtype, const void* q, const void* k, const void* v, c
                 void* to, attn_strides4 o_strides, float* lse, float* tlse, int64_t B, int64_t H, int64_t Nq,
                 int64_t Nkv, int64_t Dqk, int64_t Dv, float sm_scale, int causal, void* stream) {
   if (Dv <= 0) return ATTN_ERR_INVALID;
+  if (Dqk == 16 && Dv == 16) return ATTN_ERR_UNSUPPORTED;  // a 16-wide value tile: half an MFMA block
   const bool jvp = tq != nullptr;
   if (!jvp && (tk || tv || to || tlse)) return ATTN_ERR_INVALID;
   return dense((int)dtype, q, k, v, tq, tk, tv, q_strides, k_strides, v_strides, o, to, o_strides, lse, tlse, B, H,

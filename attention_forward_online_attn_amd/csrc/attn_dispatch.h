@@ -36,6 +36,14 @@ auto by_dim(int64_t D, F&& f) {
   return f(std::integral_constant<int, 128>{});
 }
 
+// The query/key head dim of the value-dim variants, which also takes 16
+// (the JVP page's cross-attention test pairs d_qk = 16 with d_v = 32).
+template <class F>
+auto by_dim_qk(int64_t D, F&& f) {
+  if (D == 16) return f(std::integral_constant<int, 16>{});
+  return by_dim(D, f);
+}
+
 // Forward instance tables (dtype codes of include/attn.h).
 KernelChoice fwd_bf16(int D, bool jvp, bool paired);            // inst_fwd_bf16.hip
 KernelChoice fwd_fp16(int D, bool jvp, bool paired);            // inst_fwd_fp16.hip

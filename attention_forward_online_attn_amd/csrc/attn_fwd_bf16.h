@@ -92,7 +92,9 @@ __device__ __forceinline__ float from16(bf16 x) {
 // 16 lanes writing consecutive chunks (tile stores).  The 64 banks span 256
 // bytes: a row of D = 128 fills them (the chunk is XORed with a bijection of
 // row % 16), D = 64 rows share them in pairs (bijection of (row / 2) % 8),
-// D = 32 rows in fours (row 4a + b, chunk c lands in slot 4 b + (c ^ a)).
+// D = 32 rows in fours (row 4a + b, chunk c lands in slot 4 b + (c ^ a)),
+// D = 16 (K tiles only) rows in eights (rows r and r + 8 swap their two
+// chunks).
 template <int D>
 __device__ __forceinline__ int swz_f(int row) {
   if constexpr (D == 128) {
@@ -101,8 +103,10 @@ __device__ __forceinline__ int swz_f(int row) {
   } else if constexpr (D == 64) {
     const int u = (row >> 1) & 7;
     return ((u & 1) << 2) | (u >> 1);
-  } else {
+  } else if constexpr (D == 32) {
     return (row >> 2) & 3;
+  } else {
+    return (row >> 3) & 1;
   }
 }
 
@@ -403,7 +407,7 @@ struct Bf16Cfg {
   static_assert((BN * CPR_K) % THREADS == 0 || BN * CPR_K < THREADS, "tile must split evenly over the workgroup");
   static_assert((BN * CPR_V) % THREADS == 0 || BN * CPR_V < THREADS, "tile must split evenly over the workgroup");
   static_assert(BN % 32 == 0, "unsupported tile");
-  static_assert(DQK == 32 || DQK == 64 || DQK == 128, "unsupported head dim");
+  static_assert(DQK == 16 || DQK == 32 || DQK == 64 || DQK == 128, "unsupported head dim");
   static_assert(DV == 32 || DV == 64 || DV == 128, "unsupported head dim");
 };
 

@@ -36,7 +36,8 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
   constexpr int BM = C::BM, BN = C::BN, NTEN = C::NTEN, DQK = C::DQK, DV = C::DV;
   constexpr int DQ = DQK / 4;             // query/key columns owned by each lane of a quad
   constexpr int DO_ = DV / 4;             // value / output columns owned by each lane
-  static_assert((BN * DQK / 4) % 256 == 0 && (BN * DV / 4) % 256 == 0, "tile must split evenly over 256 threads");
+  static_assert(((BN * DQK / 4) % 256 == 0 || BN * DQK / 4 < 256) && (BN * DV / 4) % 256 == 0,
+                "tile must split evenly over 256 threads");
   extern __shared__ __attribute__((aligned(16))) float fsm[];
 
   const Tile t = resolve_tile<BM>(a, blockIdx.x);
@@ -89,9 +90,11 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
     __syncthreads();  // the previous tile is no longer being read
     static_for<NTEN>([&](auto x_tag) {
       constexpr int x = decltype(x_tag)::value, W = width[x];
+      constexpr int F4 = BN * W / 4;  // float4 per tile
 #pragma unroll
-      for (int it = 0; it < BN * W / 4 / 256; ++it) {
+      for (int it = 0; it < (F4 + 255) / 256; ++it) {
         const int id = tid + 256 * it;
+        if (F4 < 256 && id >= F4) break;
         const int row = id / (W / 4), c4 = id % (W / 4);
         int key = j * BN + row;
         key = key < t.Lkv ? key : t.Lkv - 1;

@@ -35,7 +35,7 @@ KernelChoice choose16(int D, bool jvp, bool paired) {
 // page: d_v != d_qk): 4-wave workgroups, never paired, no bias.
 template <bool F16>
 KernelChoice choose_mixed16(int D, int Dv, bool jvp) {
-  return by_dim(D, [&](auto dq) {
+  return by_dim_qk(D, [&](auto dq) {
     return by_dim(Dv, [&](auto dv) {
       constexpr int A = decltype(dq)::value, V = decltype(dv)::value;
       // equal dims never come here (they take choose16; no instance twice in the library)

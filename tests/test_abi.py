@@ -212,6 +212,8 @@ def test_dv_validation(lib):
     assert call(Dv=96) == UNSUPPORTED
     assert call(Dv=0) == INVALID
     assert call(Dqk=48) == UNSUPPORTED
+    assert call(Dqk=16, Dv=16) == UNSUPPORTED  # a 16-wide value tile is not built
+    assert call(Dqk=16, Dv=32, B=0) == OK
     assert call(tk=P) == INVALID          # tangents without tq: not a JVP call
     assert call(to=P) == INVALID
     assert call(tq=P, tk=P, tv=P) == INVALID  # JVP without to

@@ -1,7 +1,8 @@
 """GPU parity of the forward and JVP whose value head dim differs from the
 query/key one (attn_fwd_dv through the C ABI; JVP page: _attention.forward
 and _test_jvp_ca) against the fp64 oracle, for every pair of distinct head
-dims in {32, 64, 128}, bf16, fp16 and fp32, causal and not, including the
+dims in {32, 64, 128} and a query/key dim of 16 with every value dim, bf16,
+fp16 and fp32, causal and not, including the
 JVP page's own cross-attention shapes (Nq != Nkv, Nkv < one key tile)."""
 
 import pytest
@@ -15,7 +16,7 @@ from parity import assert_close, host64
 pytestmark = pytest.mark.gpu
 
 DT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
-PAIRS = [(64, 128), (128, 64), (128, 32), (32, 128), (32, 64), (64, 32)]
+PAIRS = [(64, 128), (128, 64), (128, 32), (32, 128), (32, 64), (64, 32), (16, 32), (16, 64), (16, 128)]
 
 
 def dv_case(B, H, Nq, Nkv, Dqk, Dv, dtype, causal, jvp, seed=0, scale=None, std=1.0):
@@ -56,3 +57,5 @@ def test_dv_jvp_page_shapes(gpu_lib, dtype):
     bf16 alone can exceed 1e-2)."""
     dv_case(1, 2, 256, 1024, 64, 128, dtype, False, True, seed=104, scale=0.5, std=0.5)
     dv_case(1, 2, 1000, 15, 128, 32, dtype, False, True, seed=105, scale=0.5, std=0.5)
+    dv_case(1, 2, 512, 512, 16, 32, dtype, False, True, seed=106, scale=0.5, std=0.5)
+    dv_case(1, 2, 515, 999, 16, 32, dtype, False, True, seed=107, scale=0.5, std=0.5)
