@@ -43,11 +43,13 @@ bool stride_ok(int64_t stride, int64_t extent, int64_t vec) {
   return extent <= 1 || stride % vec == 0;
 }
 
-// qk16: the query/key head dim may also be 16 (value-dim variants only).
-int check_common(int dtype, int64_t D, float sm_scale, bool qk16 = false) {
+// qk16: the query/key head dim may also be 16 (value-dim variants only);
+// d256: head dim 256 is allowed (the plain forward only).
+int check_common(int dtype, int64_t D, float sm_scale, bool qk16 = false, bool d256 = false) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP32 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale) || sm_scale < 0.f) return ATTN_ERR_INVALID;
-  if (D != 32 && D != 64 && D != 128 && !(qk16 && D == 16)) return D <= 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 128 && !(qk16 && D == 16) && !(d256 && D == 256))
+    return D <= 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -91,6 +93,7 @@ bool use_pairs(int dtype, int D, bool jvp, bool dense_causal, int64_t unpaired_g
 // Forward kernel for a dtype, head dims and variant (instance tables in the
 // inst_*.hip translation units).
 KernelChoice choose(int dtype, int D, bool jvp, bool paired, int bias_kind, int Dv) {
+  if (D == 256) return fwd_d256(dtype);  // plain forward only (checked by the caller)
   if (bias_kind != kNoBias) return fwd_bias(dtype, bias_kind, D);
   if (dtype == ATTN_FP32) return fwd_f32(D, Dv, jvp);
   if (Dv != D) return dtype == ATTN_BF16 ? fwd_mixed_bf16(D, Dv, jvp) : fwd_mixed_fp16(D, Dv, jvp);
@@ -116,10 +119,12 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
           attn_strides4 sq, attn_strides4 sk, attn_strides4 sv, void* o, void* to, attn_strides4 so, float* lse,
           float* tlse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal,
           void* stream, bool jvp, const BiasOperand& bias = BiasOperand(), int64_t Dv = 0) {
-  int rc = check_common(dtype, D, sm_scale, Dv != 0 && Dv != D);
+  const bool plain = !jvp && bias.kind == kNoBias && (Dv == 0 || Dv == D);
+  int rc = check_common(dtype, D, sm_scale, Dv != 0 && Dv != D, plain);
   if (rc) return rc;
   if (Dv == 0) Dv = D;
-  if (Dv != 32 && Dv != 64 && Dv != 128) return Dv < 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
+  if (Dv != 32 && Dv != 64 && Dv != 128 && !(Dv == 256 && D == 256))
+    return Dv < 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
   if (causal && Nq != Nkv) return ATTN_ERR_CAUSAL_SHAPE;
   if (B * H * Nq == 0) return ATTN_OK;
@@ -144,7 +149,7 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
 
   const int64_t n_qtiles = (Nq + 127) / 128;  // every bf16 instance uses 128-row q-tiles
   const bool paired =
-      bias_kind == kNoBias && Dv == D && use_pairs(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
+      bias_kind == kNoBias && Dv == D && D != 256 && use_pairs(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
   const KernelChoice kc = choose(dtype, (int)D, jvp, paired, bias_kind, (int)Dv);
   const int BM = kc.BM;
   const int64_t n_qtiles_k = (Nq + BM - 1) / BM;
@@ -241,7 +246,7 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
                     const int64_t* offsets, int64_t num_seqs, int64_t H, int64_t total_len, int64_t D,
                     int64_t max_seq_len, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  int rc = check_common((int)dtype, D, sm_scale);
+  int rc = check_common((int)dtype, D, sm_scale, false, true);
   if (rc) return rc;
   if (num_seqs < 0 || H < 0 || total_len < 0 || max_seq_len < 1) return ATTN_ERR_INVALID;
   if (num_seqs > INT_MAX - 1 || H > INT_MAX || total_len > INT_MAX) return ATTN_ERR_INVALID;

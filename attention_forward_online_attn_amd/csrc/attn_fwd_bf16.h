@@ -97,7 +97,7 @@ __device__ __forceinline__ float from16(bf16 x) {
 // chunks).
 template <int D>
 __device__ __forceinline__ int swz_f(int row) {
-  if constexpr (D == 128) {
+  if constexpr (D == 128 || D == 256) {  // D = 256: a row spans the banks twice; XOR on the low 4 chunk bits
     const int u = row & 15;
     return ((u & 3) << 2) | (u >> 2);
   } else if constexpr (D == 64) {
@@ -397,8 +397,8 @@ struct Bf16Cfg {
   static constexpr int OFF_V = TILE_K, OFF_TK = TILE_K + TILE_V, OFF_TV = 2 * TILE_K + TILE_V;
   static constexpr int NTEN = JVP ? 4 : 2;  // tensors streamed per key tile
   static constexpr int STAGE = (JVP ? 2 : 1) * (TILE_K + TILE_V);  // bytes of one pipeline stage
-  static constexpr bool WIDE = JVP && (DQK == 128 || DV == 128);  // one wave per SIMD
-  static constexpr bool DMA = !WIDE;        // direct global -> LDS tile loads
+  static constexpr bool WIDE = (JVP && (DQK == 128 || DV == 128)) || DQK == 256;  // one wave per SIMD
+  static constexpr bool DMA = !(JVP && WIDE);  // direct global -> LDS tile loads
   static constexpr int LDS = 2 * STAGE;     // double-buffered key tiles
   static constexpr int CPR_K = DQK / 8, CPR_V = DV / 8;  // 16-byte chunks per row
   static constexpr int LOADS_K = (BN * CPR_K + THREADS - 1) / THREADS;
@@ -407,8 +407,9 @@ struct Bf16Cfg {
   static_assert((BN * CPR_K) % THREADS == 0 || BN * CPR_K < THREADS, "tile must split evenly over the workgroup");
   static_assert((BN * CPR_V) % THREADS == 0 || BN * CPR_V < THREADS, "tile must split evenly over the workgroup");
   static_assert(BN % 32 == 0, "unsupported tile");
-  static_assert(DQK == 16 || DQK == 32 || DQK == 64 || DQK == 128, "unsupported head dim");
-  static_assert(DV == 32 || DV == 64 || DV == 128, "unsupported head dim");
+  static_assert(DQK == 16 || DQK == 32 || DQK == 64 || DQK == 128 || (DQK == 256 && DV == 256 && !JVP),
+                "unsupported head dim");
+  static_assert(DV == 32 || DV == 64 || DV == 128 || DV == 256, "unsupported head dim");
 };
 
 template <int D, int BN, bool JVP, int NW_ = 4, bool F16 = false, int BIAS = kNoBias, int DV_ = 0>
@@ -570,16 +571,32 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int RSTEP_K = NW * RPB_K, RSTEP_V = NW * RPB_V;         // rows between a wave's blocks
   static_assert(!DMA || ((NBLK_K % NW == 0 || NBLK_K < NW) && (NBLK_V % NW == 0 || NBLK_V < NW)),
                 "DMA tiles are whole 1 KiB blocks per wave");
-  static_assert(!DMA || ((NI_K == 1 || RSTEP_K % 16 == 0) && (NI_V == 1 || RSTEP_V % 16 == 0)),
-                "per-lane swizzle must repeat every RSTEP rows");
+  // The swizzle depends on the row modulo 16.  When a wave's blocks lie a
+  // multiple of 16 rows apart one per-lane offset serves every instruction;
+  // with fewer rows per block (D = 256: 2 rows, blocks 8 rows apart) the
+  // swizzle of instruction i repeats with period NPH = 16 / RSTEP, and each
+  // phase has its own per-lane offset.
+  static_assert(!DMA || ((NI_K == 1 || RSTEP_K % 16 == 0 || 16 % RSTEP_K == 0) &&
+                         (NI_V == 1 || RSTEP_V % 16 == 0 || 16 % RSTEP_V == 0)),
+                "per-lane swizzle must repeat with the block step");
+  constexpr int NPH_K = (NI_K == 1 || RSTEP_K % 16 == 0) ? 1 : 16 / RSTEP_K;
+  constexpr int NPH_V = (NI_V == 1 || RSTEP_V % 16 == 0) ? 1 : 16 / RSTEP_V;
   const bool dma_k = NBLK_K >= NW || wave < NBLK_K;  // waves past the tile's blocks fetch nothing
   const bool dma_v = NBLK_V >= NW || wave < NBLK_V;
   const int drow_k = RPB_K * wave + (lane * 16) / (2 * DQK);          // row of instruction 0
   const int drow_v = RPB_V * wave + (lane * 16) / (2 * DV);
-  const int dch_k = (lane % CPR_K) ^ swz_f<DQK>(drow_k);              // source chunk of that row
-  const int dch_v = (lane % CPR_V) ^ swz_f<DV>(drow_v);
-  const uint32_t dk0 = (uint32_t)((drow_k * a.k_sn + dch_k * 8) * 2);  // byte offsets, instruction 0
-  const uint32_t dv0 = (uint32_t)((drow_v * a.v_sn + dch_v * 8) * 2);
+  int dch_k[NPH_K], dch_v[NPH_V];                                     // source chunk per phase
+  uint32_t dk0[NPH_K], dv0[NPH_V];                                    // byte offsets per phase
+#pragma unroll
+  for (int ph = 0; ph < NPH_K; ++ph) {
+    dch_k[ph] = (lane % CPR_K) ^ swz_f<DQK>(drow_k + RSTEP_K * ph);
+    dk0[ph] = (uint32_t)((drow_k * a.k_sn + dch_k[ph] * 8) * 2);
+  }
+#pragma unroll
+  for (int ph = 0; ph < NPH_V; ++ph) {
+    dch_v[ph] = (lane % CPR_V) ^ swz_f<DV>(drow_v + RSTEP_V * ph);
+    dv0[ph] = (uint32_t)((drow_v * a.v_sn + dch_v[ph] * 8) * 2);
+  }
   auto dma_tile = [&](int j, lds_t* base) {
     const int64_t k0 = (int64_t)j * BN;
     const char* src[4] = {(const char*)K + k0 * a.k_sn * 2, (const char*)V + k0 * a.v_sn * 2,
@@ -600,7 +617,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
           // addresses held across the loop
           const char* b = src[x] + i * step_b[vs];
           if constexpr (NIM > 1) asm("" : "+s"(b));
-          __builtin_amdgcn_global_load_lds((const void*)(b + (vs ? dv0 : dk0)),
+          __builtin_amdgcn_global_load_lds((const void*)(b + (vs ? dv0[i % NPH_V] : dk0[i % NPH_K])),
                                            (__attribute__((address_space(3))) void*)(base + (NW * i + wave) * 1024 + toff[x]),
                                            16, 0, 0);
         }
@@ -609,8 +626,8 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < NIM; ++i) {
         const int row_k = min(drow_k + RSTEP_K * i, last), row_v = min(drow_v + RSTEP_V * i, last);
-        const uint32_t ok = (uint32_t)((row_k * a.k_sn + dch_k * 8) * 2);
-        const uint32_t ov = (uint32_t)((row_v * a.v_sn + dch_v * 8) * 2);
+        const uint32_t ok = (uint32_t)((row_k * a.k_sn + dch_k[i % NPH_K] * 8) * 2);
+        const uint32_t ov = (uint32_t)((row_v * a.v_sn + dch_v[i % NPH_V] * 8) * 2);
 #pragma unroll
         for (int x = 0; x < NTEN; ++x) {
           const bool vs = x & 1;
