@@ -43,12 +43,12 @@ bool stride_ok(int64_t stride, int64_t extent, int64_t vec) {
   return extent <= 1 || stride % vec == 0;
 }
 
-// qk16: the query/key head dim may also be 16 (value-dim variants only);
-// d256: head dim 256 is allowed (the plain forward only).
-int check_common(int dtype, int64_t D, float sm_scale, bool qk16 = false, bool d256 = false) {
+// d16: head dim 16 is allowed (the unbiased forward and JVP); d256: head
+// dim 256 is allowed (the plain forward only).
+int check_common(int dtype, int64_t D, float sm_scale, bool d16 = false, bool d256 = false) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP32 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale) || sm_scale < 0.f) return ATTN_ERR_INVALID;
-  if (D != 32 && D != 64 && D != 128 && !(qk16 && D == 16) && !(d256 && D == 256))
+  if (D != 32 && D != 64 && D != 128 && !(d16 && D == 16) && !(d256 && D == 256))
     return D <= 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
@@ -96,7 +96,7 @@ KernelChoice choose(int dtype, int D, bool jvp, bool paired, int bias_kind, int 
   if (D == 256) return fwd_d256(dtype);  // plain forward only (checked by the caller)
   if (bias_kind != kNoBias) return fwd_bias(dtype, bias_kind, D);
   if (dtype == ATTN_FP32) return fwd_f32(D, Dv, jvp);
-  if (Dv != D) return dtype == ATTN_BF16 ? fwd_mixed_bf16(D, Dv, jvp) : fwd_mixed_fp16(D, Dv, jvp);
+  if (Dv != D || D == 16) return dtype == ATTN_BF16 ? fwd_mixed_bf16(D, Dv, jvp) : fwd_mixed_fp16(D, Dv, jvp);
   return dtype == ATTN_BF16 ? fwd_bf16(D, jvp, paired) : fwd_fp16(D, jvp, paired);
 }
 
@@ -120,10 +120,12 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
           float* tlse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal,
           void* stream, bool jvp, const BiasOperand& bias = BiasOperand(), int64_t Dv = 0) {
   const bool plain = !jvp && bias.kind == kNoBias && (Dv == 0 || Dv == D);
-  int rc = check_common(dtype, D, sm_scale, Dv != 0 && Dv != D, plain);
+  int rc = check_common(dtype, D, sm_scale, bias.kind == kNoBias, plain);
   if (rc) return rc;
   if (Dv == 0) Dv = D;
-  if (Dv != 32 && Dv != 64 && Dv != 128 && !(Dv == 256 && D == 256))
+  // a 16-wide value tile: unbiased, and not with the one-wave 128-wide JVP
+  const bool v16 = Dv == 16 && bias.kind == kNoBias && !(jvp && D == 128 && dtype != ATTN_FP32);
+  if (Dv != 32 && Dv != 64 && Dv != 128 && !(Dv == 256 && D == 256) && !v16)
     return Dv < 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
   if (causal && Nq != Nkv) return ATTN_ERR_CAUSAL_SHAPE;
@@ -149,7 +151,7 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
 
   const int64_t n_qtiles = (Nq + 127) / 128;  // every bf16 instance uses 128-row q-tiles
   const bool paired =
-      bias_kind == kNoBias && Dv == D && D != 256 && use_pairs(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
+      bias_kind == kNoBias && Dv == D && D != 256 && D != 16 && use_pairs(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
   const KernelChoice kc = choose(dtype, (int)D, jvp, paired, bias_kind, (int)Dv);
   const int BM = kc.BM;
   const int64_t n_qtiles_k = (Nq + BM - 1) / BM;
@@ -220,7 +222,6 @@ int attn_fwd_dv(attn_dtype dtype, const void* q, const void* k, const void* v, c
                 void* to, attn_strides4 o_strides, float* lse, float* tlse, int64_t B, int64_t H, int64_t Nq,
                 int64_t Nkv, int64_t Dqk, int64_t Dv, float sm_scale, int causal, void* stream) {
   if (Dv <= 0) return ATTN_ERR_INVALID;
-  if (Dqk == 16 && Dv == 16) return ATTN_ERR_UNSUPPORTED;  // a 16-wide value tile: half an MFMA block
   const bool jvp = tq != nullptr;
   if (!jvp && (tk || tv || to || tlse)) return ATTN_ERR_INVALID;
   return dense((int)dtype, q, k, v, tq, tk, tv, q_strides, k_strides, v_strides, o, to, o_strides, lse, tlse, B, H,
@@ -246,7 +247,7 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
                     const int64_t* offsets, int64_t num_seqs, int64_t H, int64_t total_len, int64_t D,
                     int64_t max_seq_len, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  int rc = check_common((int)dtype, D, sm_scale, false, true);
+  int rc = check_common((int)dtype, D, sm_scale, true, true);
   if (rc) return rc;
   if (num_seqs < 0 || H < 0 || total_len < 0 || max_seq_len < 1) return ATTN_ERR_INVALID;
   if (num_seqs > INT_MAX - 1 || H > INT_MAX || total_len > INT_MAX) return ATTN_ERR_INVALID;

@@ -388,11 +388,14 @@ __device__ __forceinline__ void apply_bias(f32x16 (&s)[NB], const unsigned (&src
 template <int D, int BN, bool JVP, int NW_ = 4, int DV_ = 0>
 struct Bf16Cfg {
   static constexpr int DQK = D, DV = DV_ ? DV_ : D;
+  // value width in LDS: a 16-wide value tile is laid out 32 wide, its upper
+  // half zero, so that the PV product keeps whole 32-row MFMA blocks
+  static constexpr int DVL = DV < 32 ? 32 : DV;
   static constexpr int NW = NW_;            // waves per workgroup (32 query rows each)
   static constexpr int THREADS = 64 * NW;
   static constexpr int BM = 128;            // query rows per q-tile (4 waves); 8 waves take two q-tiles
   static constexpr int TILE_K = BN * DQK * 2;  // bytes of one K (or tK) tile
-  static constexpr int TILE_V = BN * DV * 2;   // bytes of one V (or tV) tile
+  static constexpr int TILE_V = BN * DVL * 2;  // bytes of one V (or tV) tile
   // tile offsets in a stage: K, V, then tK, tV
   static constexpr int OFF_V = TILE_K, OFF_TK = TILE_K + TILE_V, OFF_TV = 2 * TILE_K + TILE_V;
   static constexpr int NTEN = JVP ? 4 : 2;  // tensors streamed per key tile
@@ -400,7 +403,8 @@ struct Bf16Cfg {
   static constexpr bool WIDE = (JVP && (DQK == 128 || DV == 128)) || DQK == 256;  // one wave per SIMD
   static constexpr bool DMA = !(JVP && WIDE);  // direct global -> LDS tile loads
   static constexpr int LDS = 2 * STAGE;     // double-buffered key tiles
-  static constexpr int CPR_K = DQK / 8, CPR_V = DV / 8;  // 16-byte chunks per row
+  static constexpr int CPR_K = DQK / 8, CPR_V = DVL / 8;  // 16-byte chunks per row (in LDS)
+  static constexpr int CPR_VS = DV / 8;                   // of those, chunks that hold data
   static constexpr int LOADS_K = (BN * CPR_K + THREADS - 1) / THREADS;
   static constexpr int LOADS_V = (BN * CPR_V + THREADS - 1) / THREADS;
   static constexpr int WAVES_PER_EU = WIDE ? 1 : 2;
@@ -409,21 +413,22 @@ struct Bf16Cfg {
   static_assert(BN % 32 == 0, "unsupported tile");
   static_assert(DQK == 16 || DQK == 32 || DQK == 64 || DQK == 128 || (DQK == 256 && DV == 256 && !JVP),
                 "unsupported head dim");
-  static_assert(DV == 32 || DV == 64 || DV == 128 || DV == 256, "unsupported head dim");
+  static_assert(DV == 16 || DV == 32 || DV == 64 || DV == 128 || DV == 256, "unsupported head dim");
+  static_assert(DV >= 32 || !(JVP && WIDE), "a 16-wide value tile needs the DMA path");
 };
 
 template <int D, int BN, bool JVP, int NW_ = 4, bool F16 = false, int BIAS = kNoBias, int DV_ = 0>
 __global__ void __launch_bounds__((Bf16Cfg<D, BN, JVP, NW_, DV_>::THREADS), (Bf16Cfg<D, BN, JVP, NW_, DV_>::WAVES_PER_EU))
 attn_fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BN, JVP, NW_, DV_>;
-  constexpr int DQK = C::DQK, DV = C::DV;
+  constexpr int DQK = C::DQK, DV = C::DV, DVL = C::DVL, CPR_VS = C::CPR_VS;
   constexpr int BM = C::BM, NTEN = C::NTEN, STAGE = C::STAGE, TILE_K = C::TILE_K, TILE_V = C::TILE_V;
   constexpr int OFF_V = C::OFF_V, OFF_TK = C::OFF_TK, OFF_TV = C::OFF_TV;
   constexpr int CPR_K = C::CPR_K, CPR_V = C::CPR_V, LOADS_K = C::LOADS_K, LOADS_V = C::LOADS_V;
   constexpr int THREADS = C::THREADS, NW = C::NW;
   constexpr int NB = BN / 32;    // 32-key blocks per tile
   constexpr int KD = DQK / 16;   // MFMA steps over the query/key head dim
-  constexpr int DB = DV / 32;    // 32-column output blocks
+  constexpr int DB = DVL / 32;   // 32-column output blocks
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   lds_t* smem = (lds_t*)smem_raw;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
@@ -493,7 +498,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     const int id = tid + THREADS * it;
     const int row = id / CPR_V, ch = id % CPR_V;
     goff_v[it] = (uint32_t)((row * a.v_sn + ch * 8) * 2);
-    lds_v[it] = swz_off<DV>(row, ch);
+    lds_v[it] = swz_off<DVL>(row, ch);
   }
   const bool stager_k = BN * CPR_K >= THREADS || tid < BN * CPR_K;  // threads that move tile chunks
   const bool stager_v = BN * CPR_V >= THREADS || tid < BN * CPR_V;
@@ -567,7 +572,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int NI_K = NBLK_K >= NW ? NBLK_K / NW : 1;            // DMA instructions per wave per tensor
   constexpr int NI_V = NBLK_V >= NW ? NBLK_V / NW : 1;
   constexpr int NIM = NI_K > NI_V ? NI_K : NI_V;
-  constexpr int RPB_K = 1024 / (2 * DQK), RPB_V = 1024 / (2 * DV);  // rows per block
+  constexpr int RPB_K = 1024 / (2 * DQK), RPB_V = 1024 / (2 * DVL);  // rows per block
   constexpr int RSTEP_K = NW * RPB_K, RSTEP_V = NW * RPB_V;         // rows between a wave's blocks
   static_assert(!DMA || ((NBLK_K % NW == 0 || NBLK_K < NW) && (NBLK_V % NW == 0 || NBLK_V < NW)),
                 "DMA tiles are whole 1 KiB blocks per wave");
@@ -584,7 +589,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   const bool dma_k = NBLK_K >= NW || wave < NBLK_K;  // waves past the tile's blocks fetch nothing
   const bool dma_v = NBLK_V >= NW || wave < NBLK_V;
   const int drow_k = RPB_K * wave + (lane * 16) / (2 * DQK);          // row of instruction 0
-  const int drow_v = RPB_V * wave + (lane * 16) / (2 * DV);
+  const int drow_v = RPB_V * wave + (lane * 16) / (2 * DVL);
   int dch_k[NPH_K], dch_v[NPH_V];                                     // source chunk per phase
   uint32_t dk0[NPH_K], dv0[NPH_V];                                    // byte offsets per phase
 #pragma unroll
@@ -594,7 +599,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   }
 #pragma unroll
   for (int ph = 0; ph < NPH_V; ++ph) {
-    dch_v[ph] = (lane % CPR_V) ^ swz_f<DV>(drow_v + RSTEP_V * ph);
+    dch_v[ph] = (lane % CPR_V) ^ swz_f<DVL>(drow_v + RSTEP_V * ph);
     dv0[ph] = (uint32_t)((drow_v * a.v_sn + dch_v[ph] * 8) * 2);
   }
   auto dma_tile = [&](int j, lds_t* base) {
@@ -611,6 +616,8 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         for (int x = 0; x < NTEN; ++x) {
           const bool vs = x & 1;
           if (i >= (vs ? NI_V : NI_K) || !(vs ? dma_v : dma_k)) continue;
+          // a padded value tile: lanes whose slot is padding stay inactive
+          if (vs && DV < DVL && dch_v[i % NPH_V] >= CPR_VS) continue;
           // the uniform part of the address stays an SGPR pair (saddr form:
           // scalar base + 32-bit lane offset); with several instructions per
           // tensor the compiler would otherwise fold it into per-lane 64-bit
@@ -632,6 +639,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         for (int x = 0; x < NTEN; ++x) {
           const bool vs = x & 1;
           if (i >= (vs ? NI_V : NI_K) || !(vs ? dma_v : dma_k)) continue;
+          if (vs && DV < DVL && dch_v[i % NPH_V] >= CPR_VS) continue;
           __builtin_amdgcn_global_load_lds((const void*)(src[x] + (vs ? ov : ok)),
                                            (__attribute__((address_space(3))) void*)(base + (NW * i + wave) * 1024 + toff[x]),
                                            16, 0, 0);
@@ -683,7 +691,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   for (int kk = 0; kk < KD; ++kk) kaddr[kk] = lds_base + swz_off<DQK>(krow, 2 * kk + h32);
   int vlo[DB], vhi[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) v_frag_offsets<DV>(lane, db, vlo[db], vhi[db]);
+  for (int db = 0; db < DB; ++db) v_frag_offsets<DVL>(lane, db, vlo[db], vhi[db]);
 
   // One key tile on LDS stage S = j % 2: fetch tile j + 1 into the other
   // stage (freed by the barrier that ended the previous tile), compute, then
@@ -761,7 +769,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], cs, nm));
             plo[r >> 3][r & 7] = to16<F16>(p - from16<F16>(to16<F16>(p)));
           }
-          pv_lo_block<DV, F16>(vt, vlo, vhi, b, plo, acc);
+          pv_lo_block<DVL, F16>(vt, vlo, vhi, b, plo, acc);
         }
       }
 
@@ -785,7 +793,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       constexpr int EPS = 8 / DB;  // elements of the next chunk per PV step
       static_for<8>(soft);
       // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
-      pv_section<DV, NB, JVP, S * STAGE + OFF_V, S * STAGE + OFF_TV, F16>(
+      pv_section<DVL, NB, JVP, S * STAGE + OFF_V, S * STAGE + OFF_TV, F16>(
           lds_base, vlo, vhi, pf, hf, acc, accA, accB, [&](auto i_tag) {
             constexpr int i = decltype(i_tag)::value, c = i / DB;
             if constexpr (c + 1 < 2 * NB) {
@@ -803,6 +811,18 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   // The loop sits inside the prologue's branch: on every path into it the
   // Q-fragment loads have completed, so no wait for the next tile's prefetch
   // is needed inside the loop.
+  if constexpr (DV < DVL) {
+    // the padding chunks of every value tile (both stages, V and tV) are
+    // zeroed once: the tile copies never write them, and the barrier after
+    // the prologue orders these stores before any fragment read
+    constexpr int NVT = JVP ? 2 : 1, PADC = CPR_V - CPR_VS;
+    for (int id = tid; id < 2 * NVT * BN * PADC; id += THREADS) {
+      const int c = CPR_VS + id % PADC, row = (id / PADC) % BN, st = id / (PADC * BN);
+      const int off = (st >> 1) * STAGE + ((st & 1) ? OFF_TV : OFF_V) + swz_off<DVL>(row, c);
+      *(__attribute__((address_space(3))) u32x4*)(smem + off) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
   if (n_tiles > 0) {
     bias_load(0, std::integral_constant<int, 0>{});
     if constexpr (DMA) {
@@ -834,6 +854,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        if (32 * db + 8 * g >= DV) continue;  // padding columns of a 16-wide value tile
         const int d = 32 * db + 8 * g + 4 * h32;  // registers 4g..4g+3 are columns d..d+3
         bf16x4 ov;
         bf16x4 tov;

@@ -36,7 +36,7 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
   constexpr int BM = C::BM, BN = C::BN, NTEN = C::NTEN, DQK = C::DQK, DV = C::DV;
   constexpr int DQ = DQK / 4;             // query/key columns owned by each lane of a quad
   constexpr int DO_ = DV / 4;             // value / output columns owned by each lane
-  static_assert(((BN * DQK / 4) % 256 == 0 || BN * DQK / 4 < 256) && (BN * DV / 4) % 256 == 0,
+  static_assert(((BN * DQK / 4) % 256 == 0 || BN * DQK / 4 < 256) && ((BN * DV / 4) % 256 == 0 || BN * DV / 4 < 256),
                 "tile must split evenly over 256 threads");
   extern __shared__ __attribute__((aligned(16))) float fsm[];
 

@@ -4,7 +4,7 @@
 namespace attn {
 KernelChoice fwd_f32(int D, int Dv, bool jvp) {
   return by_dim_qk(D, [&](auto dq) {
-    return by_dim(Dv, [&](auto dv) {
+    return by_dim_qk(Dv, [&](auto dv) {
       constexpr int A = decltype(dq)::value, V = decltype(dv)::value, DVp = A == V ? 0 : V;
       return jvp ? f32k<A, true, kNoBias, DVp>() : f32k<A, false, kNoBias, DVp>();
     });

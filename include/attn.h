@@ -27,9 +27,10 @@
  *   tensors satisfy this.  Anything else is ATTN_ERR_UNSUPPORTED.
  * - Tangent tensors (JVP) share the strides of their primals, and tO shares
  *   the strides of O (as the JVP page's wrapper requires).
- * - Supported head dims: 32, 64 and 128 everywhere; 256 for the plain forward
- *   (attn_fwd, jagged_attn_fwd, attn_fwd_dv with Dqk = Dv = 256); a query/key
- *   head dim of 16 for attn_fwd_dv.  dtype ATTN_BF16 (ATTN_FP16) computes
+ * - Supported head dims: 32, 64 and 128 everywhere; 16 on the unbiased
+ *   forward and JVP (dense and jagged, and either side of attn_fwd_dv, except
+ *   a 16-bit JVP with Dqk = 128 and Dv = 16); 256 for the plain forward
+ *   (attn_fwd, jagged_attn_fwd, attn_fwd_dv with Dqk = Dv = 256).  dtype ATTN_BF16 (ATTN_FP16) computes
  *   the products on bf16 (fp16) MFMA with fp32 accumulation and rounds O/tO to
  *   the input format (RNE); ATTN_FP32 computes everything in fp32.  LSE is
  *   always fp32.

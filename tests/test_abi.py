@@ -212,8 +212,9 @@ def test_dv_validation(lib):
     assert call(Dv=96) == UNSUPPORTED
     assert call(Dv=0) == INVALID
     assert call(Dqk=48) == UNSUPPORTED
-    assert call(Dqk=16, Dv=16) == UNSUPPORTED  # a 16-wide value tile is not built
+    assert call(Dqk=16, Dv=16, B=0) == OK
     assert call(Dqk=16, Dv=32, B=0) == OK
+    assert call(Dqk=128, Dv=16, tq=P, tk=P, tv=P, to=P) == UNSUPPORTED  # one-wave 128-wide JVP: no 16-wide values
     assert call(tk=P) == INVALID          # tangents without tq: not a JVP call
     assert call(to=P) == INVALID
     assert call(tq=P, tk=P, tv=P) == INVALID  # JVP without to
@@ -258,3 +259,17 @@ def test_d256_only_for_the_plain_forward(lib):
                         P, need, None) == UNSUPPORTED
     assert lib.attn_fwd_dv(BF16, P, P, P, 0, 0, 0, st, st, st, P, 0, st, P, 0, 1, H, N, N, 256, 128, 0.1, 0, None) \
         == UNSUPPORTED
+
+
+def test_d16_paths(lib):
+    """Head dim 16 runs the unbiased forward and JVP; bias and backward at
+    16 are not built."""
+    H, N = 2, 128
+    st = dense_strides(1, H, N, 16)
+    assert call_fwd(lib, D=16, B=0) == OK
+    full = Strides4(H * N * N, N * N, N, 1)
+    assert lib.attn_fwd_bias(BF16, P, st, P, st, P, st, P, st, P, P, 1, full, 1, H, N, N, 16, 0.1, 0, None) \
+        == UNSUPPORTED
+    need = lib.attn_bwd_workspace_bytes(1, H, N)
+    assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st, 1, H, N, N, 16, 0.1, 0,
+                        P, need, None) == UNSUPPORTED

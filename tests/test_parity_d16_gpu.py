@@ -1,0 +1,33 @@
+"""GPU parity at head dim 16 against the fp64 oracle: equal dims 16 on the
+dense, causal, JVP and jagged forward (bf16, fp16, fp32), and a value dim of
+16 under wider query/key dims.  A 16-wide value tile is laid out 32 wide in
+LDS with a zero upper half, so the PV product keeps whole MFMA blocks."""
+
+import pytest
+
+from test_parity_gpu import dense_case, jvp_case, jagged_case
+from test_parity_dv_gpu import dv_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d16_dense_and_jvp(gpu_lib, dtype, causal):
+    dense_case(2, 3, 300, 300, 16, dtype, causal, seed=130)
+    dense_case(1, 2, 1, 1, 16, dtype, causal, seed=131)
+    jvp_case(2, 2, 300, 300, 16, dtype, causal, seed=132)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_d16_jagged(gpu_lib, causal):
+    jagged_case([5, 0, 300, 64, 129], 2, 16, "bf16", 256, causal, seed=133)
+
+
+@pytest.mark.parametrize("Dqk", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_value_dim_16(gpu_lib, Dqk, dtype):
+    dv_case(2, 2, 300, 300, Dqk, 16, dtype, False, False, seed=134)
+    dv_case(1, 2, 200, 200, Dqk, 16, dtype, True, False, seed=135)
+    if Dqk != 128 or dtype == "fp32":  # the one-wave 128-wide 16-bit JVP has no 16-wide value tile
+        dv_case(1, 2, 200, 200, Dqk, 16, dtype, True, True, seed=136)
