@@ -53,6 +53,12 @@ int check_common(int dtype, int64_t D, float sm_scale, bool d16 = false, bool d2
   return ATTN_OK;
 }
 
+// The forward kernels address the rows of a key tile (at most 128 rows) with
+// 32-bit per-lane byte offsets from a uniform tile base: K and V row strides
+// must keep 128 rows of 4-byte elements within 2^31 bytes.
+constexpr int64_t kMaxKvRowStride = (int64_t)1 << 22;
+bool kv_row_stride_ok(int64_t n_stride) { return n_stride <= kMaxKvRowStride; }
+
 int check_s4(const attn_strides4& s, int64_t B, int64_t H, int64_t N, int64_t vec) {
   if (s.d != 1) return ATTN_ERR_INVALID;
   if (s.b < 0 || s.h < 0 || s.n < 0) return ATTN_ERR_INVALID;
@@ -137,6 +143,7 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   if (jvp && (!to || !tq || (Nkv > 0 && (!tk || !tv)))) return ATTN_ERR_INVALID;
   if ((rc = check_s4(sq, B, H, Nq, vec)) || (rc = check_s4(so, B, H, Nq, vec))) return rc;
   if (Nkv > 0 && ((rc = check_s4(sk, B, H, Nkv, vec)) || (rc = check_s4(sv, B, H, Nkv, vec)))) return rc;
+  if (Nkv > 1 && (!kv_row_stride_ok(sk.n) || !kv_row_stride_ok(sv.n))) return ATTN_ERR_UNSUPPORTED;
   const void* ptrs[] = {q, k, v, o, tq, tk, tv, to};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return ATTN_ERR_UNSUPPORTED;
@@ -257,6 +264,7 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   if ((rc = check_s3(q_strides, H, total_len, vec)) || (rc = check_s3(k_strides, H, total_len, vec)) ||
       (rc = check_s3(v_strides, H, total_len, vec)) || (rc = check_s3(o_strides, H, total_len, vec)))
     return rc;
+  if (total_len > 1 && (!kv_row_stride_ok(k_strides.t) || !kv_row_stride_ok(v_strides.t))) return ATTN_ERR_UNSUPPORTED;
   const void* ptrs[] = {q, k, v, o};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;

@@ -23,8 +23,9 @@
  *   default stream).  Calls are asynchronous: nothing synchronises the host.
  * - Strides are in ELEMENTS.  The innermost (head-dim) stride must be 1.
  *   Base pointers must be 16-byte aligned and every other stride a multiple of
- *   16 bytes (8 bf16 or fp16 elements, 4 fp32 elements); contiguous torch
- *   tensors satisfy this.  Anything else is ATTN_ERR_UNSUPPORTED.
+ *   16 bytes (8 bf16 or fp16 elements, 4 fp32 elements), and the row (n)
+ *   stride of K and V at most 2^22 elements; contiguous torch tensors
+ *   satisfy this.  Anything else is ATTN_ERR_UNSUPPORTED.
  * - Tangent tensors (JVP) share the strides of their primals, and tO shares
  *   the strides of O (as the JVP page's wrapper requires).
  * - Supported head dims: 32, 64 and 128 everywhere; 16 on the unbiased

@@ -82,6 +82,9 @@ def test_dense_validation(lib):
     assert call_fwd(lib, q=P + 2) == UNSUPPORTED                      # misaligned base
     assert call_fwd(lib, sq=Strides4(2 * 128 * 64, 128 * 64, 64, 2)) == INVALID  # head dim not unit stride
     assert call_fwd(lib, sq=Strides4(2 * 128 * 64, 128 * 64, 65, 1)) == UNSUPPORTED  # row stride not 16 B
+    big = Strides4(0, 0, (1 << 22) + 8, 1)                                # K row stride beyond the 32-bit lane offsets
+    assert lib.attn_fwd(BF16, P, dense_strides(1, 2, 128, 64), P, big, P, dense_strides(1, 2, 128, 64), P,
+                        dense_strides(1, 2, 128, 64), P, 1, 2, 128, 128, 64, 0.125, 0, None) == UNSUPPORTED
     # no work: nothing is enqueued, null data pointers are fine
     assert call_fwd(lib, B=0, q=0, k=0, v=0, o=0, lse=0) == OK
     assert call_fwd(lib, Nq=0, q=0, k=0, v=0, o=0, lse=0) == OK
