@@ -10,7 +10,8 @@
 // offsets on the device (no host sync), counting-sorts the non-empty items by
 // cost and writes the list; the forward kernel's grid covers an upper bound
 // of the item count and maps workgroup i to item i / H, head i % H, so the
-// heaviest tiles are dispatched first.
+// heaviest tiles are dispatched first, and a sequence's tiles of equal cost
+// are dispatched back to back.
 #pragma once
 
 #include "attn_common.h"
@@ -74,7 +75,12 @@ jagged_plan_kernel(const int64_t* offsets, int num_seqs, int64_t total_len, int 
   }
   __syncthreads();
 
-  // pass 2: scatter the items to their bucket's range
+  // pass 2: scatter the items to their bucket's range.  A sequence's
+  // consecutive tiles of equal cost (all its tiles without causal masking)
+  // take one contiguous run of positions, so they are dispatched back to
+  // back: with H a multiple of 8, workgroup (item H + h) of every tile of a
+  // (sequence, head) lands on the same XCD, and those tiles read the
+  // sequence's K/V through one L2 instead of each fetching it from HBM.
   for (int s = tid; s < num_seqs; s += kPlanThreads) {
     int64_t b = offsets[s], e = offsets[s + 1];
     b = b < 0 ? 0 : (b > total_len ? total_len : b);
@@ -82,13 +88,17 @@ jagged_plan_kernel(const int64_t* offsets, int num_seqs, int64_t total_len, int 
     const int len = (int)(e - b);
     const int used = len < max_seq_len ? len : max_seq_len;
     const int nq = (len + BM - 1) / BM;
-    for (int qt = 0; qt < nq; ++qt) {
+    for (int qt = 0; qt < nq;) {
       const int c = min(item_cost(qt, used, causal, BM, BN), kPlanBuckets - 1);
-      const int pos = atomicAdd(&hist[c], 1);
-      if (pos < capacity) {
-        plan[4 + 2 * pos] = s;
-        plan[5 + 2 * pos] = qt;
-      }
+      int run = 1;
+      while (qt + run < nq && min(item_cost(qt + run, used, causal, BM, BN), kPlanBuckets - 1) == c) ++run;
+      const int pos = atomicAdd(&hist[c], run);
+      for (int r = 0; r < run; ++r)
+        if (pos + r < capacity) {
+          plan[4 + 2 * (pos + r)] = s;
+          plan[5 + 2 * (pos + r)] = qt + r;
+        }
+      qt += run;
     }
   }
 }

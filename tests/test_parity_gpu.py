@@ -262,6 +262,54 @@ def test_jagged_repeatable_and_workspace_independent(gpu_lib):
     assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
+def _plan_cost(qt, used, causal, BM=128, BN=64):
+    """Key tiles a (sequence, 128-row query tile) item visits: none past
+    max_seq_len, else up to the last key any of its rows sees."""
+    r0 = qt * BM
+    if r0 >= used:
+        return 0
+    lim = min(r0 + BM, used) if causal else used
+    return -(-lim // BN)
+
+
+@pytest.mark.parametrize("case", ["uniform_1_1024", "empty_and_truncated", "causal"])
+def test_jagged_plan_order(gpu_lib, case):
+    """The on-device tile plan in the caller's workspace (int32: [0] item
+    count, then (sequence, query tile) pairs from index 4) for the D=128 bf16
+    kernel (128-row query tiles, 64-key tiles) lists every item exactly once,
+    most key tiles first, and gives each sequence's run of equal-cost tiles
+    consecutive positions in ascending tile order (what keeps a sequence's
+    tiles on one XCD, sharing its K/V through L2)."""
+    causal = case == "causal"
+    if case == "uniform_1_1024":
+        lengths, msl = wl.jagged_lengths(256, 1024, 0), 1024
+    else:
+        g = torch.Generator().manual_seed(21)
+        lengths = torch.randint(0, 900, (300,), generator=g)
+        lengths[::7] = 0
+        msl = 300
+    q, k, v, off = cuda(*wl.jagged_inputs(lengths, 8, 128, "bf16", 21))
+    S, T = len(lengths), q.shape[1]
+    ws = torch.empty(attn.jagged_workspace_bytes(S, T), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)
+    attn.jagged_fwd(q, k, v, off, msl, causal=causal, workspace=ws)
+    torch.cuda.synchronize()
+    plan = ws.cpu().view(torch.int32)
+    lens = lengths.tolist()
+    expect = {(s, qt) for s, L in enumerate(lens) for qt in range(-(-L // 128))}
+    n = int(plan[0])
+    assert n == len(expect)
+    items = plan[4:4 + 2 * n].view(-1, 2).tolist()
+    assert len({tuple(x) for x in items}) == n and {tuple(x) for x in items} == expect
+    costs = [_plan_cost(qt, min(lens[s], msl), causal) for s, qt in items]
+    assert all(a >= b for a, b in zip(costs, costs[1:])), "items not in descending cost order"
+    pos = {tuple(x): i for i, x in enumerate(items)}
+    for s, L in enumerate(lens):
+        for qt in range(1, -(-L // 128)):
+            if _plan_cost(qt, min(L, msl), causal) == _plan_cost(qt - 1, min(L, msl), causal):
+                assert pos[(s, qt)] == pos[(s, qt - 1)] + 1, f"sequence {s}: tiles {qt - 1}, {qt} not adjacent"
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_jagged_many_short_sequences(gpu_lib, D):
     """Thousands of short sequences (the plan kernel loops over them in
