@@ -178,6 +178,7 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   a.B = (int)B; a.H = (int)H; a.Nq = (int)Nq; a.Nkv = (int)Nkv;
   a.n_qtiles = (int)n_qtiles_k;
   a.paired = paired ? 1 : 0;
+  a.batch_inner = bias_kind != kNoBias && bias.strides.b == 0 && B > 1 ? 1 : 0;
   a.sm_scale = sm_scale;
   a.c = sm_scale * kLog2e;
   if (a.c == 0.f) a.c = 1.17549435e-38f;  // sm_scale == 0: keep exp2 arguments exactly 0 and -inf masks -inf
@@ -451,6 +452,7 @@ int dense_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const vo
     }
   }
   a.B = (int)B; a.H = (int)H; a.Nq = (int)Nq; a.Nkv = (int)Nkv;
+  a.batch_inner = bias_kind != kNoBias && bias.strides.b == 0 && B > 1 ? 1 : 0;
   a.sm_scale = sm_scale;
   a.c = sm_scale * kLog2e;
   if (a.c == 0.f) a.c = 1.17549435e-38f;  // sm_scale == 0: masked scores stay -inf (no 0 * inf)

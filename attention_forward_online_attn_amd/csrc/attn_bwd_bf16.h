@@ -71,7 +71,8 @@ __global__ void __launch_bounds__(256) attn_bwd_prep_kernel(BwdArgs a) {
 
 // Workgroup -> tile.  Dense: (batch, head, tile), XCD-aware like the forward
 // (a run of consecutive work items per XCD shares that XCD's L2 copy of a
-// head).  Jagged: item bid / H of the device-built plan, head bid % H; a
+// head); with a bias shared by the batch, (head, tile, batch) as in the
+// forward.  Jagged: item bid / H of the device-built plan, head bid % H; a
 // sequence's first min(len, max_seq_len) rows take part as queries and keys,
 // its later rows get zero gradients (SLL jagged page, backward).
 // `store_rows_are_keys` selects which extent Lstore describes (dK/dV: keys).
@@ -82,9 +83,19 @@ __device__ __forceinline__ BwdTile bwd_tile(const BwdArgs& a, int bid, bool stor
     const int total = a.B * a.H * per_head;
     int logical = bid;
     if ((total & 7) == 0) logical = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int bh = logical / per_head;
-    t.t = logical - bh * per_head;
-    const int b = bh / a.H, h = bh - b * a.H;
+    int b, h;
+    if (a.batch_inner) {  // (head, tile, batch)-major: the batches of a tile share its bias through one L2
+      b = logical % a.B;
+      const int r = logical / a.B;
+      h = r / per_head;
+      t.t = r - h * per_head;
+    } else {
+      const int bh0 = logical / per_head;
+      t.t = logical - bh0 * per_head;
+      b = bh0 / a.H;
+      h = bh0 - b * a.H;
+    }
+    const int bh = b * a.H + h;
     t.q_off = b * a.q_sb + h * a.q_sh;
     t.k_off = b * a.k_sb + h * a.k_sh;
     t.v_off = b * a.v_sb + h * a.v_sh;

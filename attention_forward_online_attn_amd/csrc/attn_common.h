@@ -67,6 +67,7 @@ struct FwdArgs {
   int32_t B, H, Nq, Nkv;
   int32_t n_qtiles;  // dense: number of query tiles per (batch, head)
   int32_t paired;    // dense causal: one workgroup takes q-tiles p and n_qtiles-1-p
+  int32_t batch_inner;  // dense: the batch is the fastest work index (a bias shared by the batch)
   float c;           // sm_scale * log2(e): scores go to the exp2 domain
   float sm_scale;
   int32_t causal;
@@ -107,6 +108,7 @@ struct BwdArgs {
   int64_t dv_sb, dv_sh, dv_sn;
   int32_t B, H, Nq, Nkv;
   int32_t n_tiles;  // q-tiles (dQ kernel) or key tiles (dK/dV kernel) per (batch, head)
+  int32_t batch_inner;  // dense: the batch is the fastest work index (a bias shared by the batch)
   float c;          // sm_scale * log2(e)
   float sm_scale;
   int32_t causal;
@@ -134,7 +136,11 @@ struct Tile {
 // Workgroup -> tile.  Dense: the hardware hands workgroup i to XCD i % 8, so
 // each XCD is given a contiguous run of the (batch, head)-major work list:
 // the query tiles of a head then run on one XCD and share its L2 copy of
-// that head's K and V.  Causal: with pairing, workgroup p of a head takes
+// that head's K and V.  With an operand shared by the batch (bias batch
+// stride 0) the list is (head, query tile, batch)-major instead: the batches
+// of one query tile run together on one XCD and read each bias row through
+// one L2, where the bias (N^2 elements per head) would otherwise be fetched
+// from HBM once per batch.  Causal: with pairing, workgroup p of a head takes
 // query tiles p and n-1-p (equal work for every workgroup; the shorter key
 // range is a prefix of the longer one, so both share the K/V tiles);
 // without it, tiles run heaviest first within a head.
@@ -149,15 +155,25 @@ __device__ __forceinline__ Tile resolve_tile(const FwdArgs& a, int bid) {
     const int total = a.B * a.H * per_head;
     int logical = bid;
     if ((total & 7) == 0) logical = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int bh = logical / per_head;
-    int qt = logical - bh * per_head;
+    int b, h, qt;
+    if (a.batch_inner) {
+      b = logical % a.B;
+      const int r = logical / a.B;
+      h = r / per_head;
+      qt = r - h * per_head;
+    } else {
+      const int bh0 = logical / per_head;
+      qt = logical - bh0 * per_head;
+      b = bh0 / a.H;
+      h = bh0 - b * a.H;
+    }
+    const int bh = b * a.H + h;
     if (a.paired) {
       const int other = a.n_qtiles - 1 - qt;
       t.qt2 = other != qt ? other : -1;
     } else if (a.causal) {
       qt = a.n_qtiles - 1 - qt;
     }
-    const int b = bh / a.H, h = bh - b * a.H;
     t.q_off = b * a.q_sb + h * a.q_sh;
     t.k_off = b * a.k_sb + h * a.k_sh;
     t.v_off = b * a.v_sb + h * a.v_sh;

@@ -88,6 +88,9 @@ def test_bias_bwd_broadcast(gpu_lib):
     for shape in [(1, H, N, N), (B, 1, N, N), (B, 1, 1, N)]:
         bias_bwd_case(B, H, N, N, 64, "bf16", False, "add", bshape=shape, seed=114)
     bias_bwd_case(B, H, N, N, 64, "bf16", True, "mask", bshape=(B, 1, 1, N), seed=115)
+    # operands shared by the batch put the batch innermost in the work order
+    bias_bwd_case(3, H, N, N, 128, "bf16", True, "add", bshape=(1, H, N, N), seed=116)
+    bias_bwd_case(4, 2, N, N, 64, "fp16", False, "mask", bshape=(1, 1, N, N), seed=117)
 
 
 def test_bias_bwd_empty_rows_and_zero_scale(gpu_lib):

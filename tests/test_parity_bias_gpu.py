@@ -77,6 +77,9 @@ def test_broadcast_operands(gpu_lib, kind):
     for shape in [(1, H, N, N), (B, 1, N, N), (B, 1, 1, N), (N, N), (1, 1, 1, N)]:
         bias_case(B, H, N, N, 128, "bf16", False, kind, bshape=shape, seed=64)
     bias_case(B, H, N, N, 64, "bf16", True, kind, bshape=(1, H, N, N), seed=65)
+    # shared by the batch (the batch is then the fastest work index): odd batch counts, causal
+    bias_case(3, 2, 300, 300, 128, "fp16", True, kind, bshape=(1, 2, 300, 300), seed=72)
+    bias_case(5, 3, 200, 200, 64, "fp32", False, kind, bshape=(1, 1, 200, 200), seed=73)
 
 
 def test_mask_rows_without_keys(gpu_lib):
