@@ -86,24 +86,26 @@ int cu_count() {
   return n;
 }
 
-// Dense causal work is paired (an 8-wave workgroup takes q-tiles p and
-// n-1-p) when the unpaired grid is small -- at most four workgroups per CU,
-// where the heaviest q-tiles would otherwise set the finish time; larger
+// Dense causal work on a small grid (at most four query tiles per CU) runs
+// paired key-split workgroups: 8 waves take q-tiles p and n-1-p of a head in
+// turn (equal work for every workgroup), and the two 4-wave groups split
+// each tile's key range in halves merged at the end, so that both waves of
+// a SIMD stay busy and the heaviest tiles take half as many steps.  Larger
 // grids balance well enough by heaviest-first dispatch and keep 4-wave
 // workgroups.  The D=128 JVP instance runs one wave per SIMD and is never
-// paired.
-bool use_pairs(int dtype, int D, bool jvp, bool dense_causal, int64_t unpaired_grid) {
-  return dtype != ATTN_FP32 && dense_causal && !(jvp && D == 128) && unpaired_grid <= 4 * (int64_t)cu_count();
+// split.
+bool use_split(int dtype, int D, bool jvp, bool dense_causal, int64_t grid) {
+  return dtype != ATTN_FP32 && dense_causal && !(jvp && D == 128) && grid <= 4 * (int64_t)cu_count();
 }
 
 // Forward kernel for a dtype, head dims and variant (instance tables in the
 // inst_*.hip translation units).
-KernelChoice choose(int dtype, int D, bool jvp, bool paired, int bias_kind, int Dv) {
+KernelChoice choose(int dtype, int D, bool jvp, bool split, int bias_kind, int Dv) {
   if (D == 256) return fwd_d256(dtype);  // plain forward only (checked by the caller)
   if (bias_kind != kNoBias) return fwd_bias(dtype, bias_kind, D);
   if (dtype == ATTN_FP32) return fwd_f32(D, Dv, jvp);
   if (Dv != D || D == 16) return dtype == ATTN_BF16 ? fwd_mixed_bf16(D, Dv, jvp) : fwd_mixed_fp16(D, Dv, jvp);
-  return dtype == ATTN_BF16 ? fwd_bf16(D, jvp, paired) : fwd_fp16(D, jvp, paired);
+  return dtype == ATTN_BF16 ? fwd_bf16(D, jvp, split) : fwd_fp16(D, jvp, split);
 }
 
 int launch(const KernelChoice& k, int grid, hipStream_t stream, const FwdArgs& a) {
@@ -157,12 +159,12 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   const int bias_kind = Nkv > 0 ? bias.kind : kNoBias;  // no key: nothing to read
 
   const int64_t n_qtiles = (Nq + 127) / 128;  // every bf16 instance uses 128-row q-tiles
-  const bool paired =
-      bias_kind == kNoBias && Dv == D && D != 256 && D != 16 && use_pairs(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
-  const KernelChoice kc = choose(dtype, (int)D, jvp, paired, bias_kind, (int)Dv);
+  const bool split =
+      bias_kind == kNoBias && Dv == D && D != 256 && D != 16 && use_split(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
+  const KernelChoice kc = choose(dtype, (int)D, jvp, split, bias_kind, (int)Dv);
   const int BM = kc.BM;
   const int64_t n_qtiles_k = (Nq + BM - 1) / BM;
-  const int64_t grid = B * H * (paired ? (n_qtiles_k + 1) / 2 : n_qtiles_k);
+  const int64_t grid = B * H * (split ? (n_qtiles_k + 1) / 2 : n_qtiles_k);
   if (grid > INT_MAX) return ATTN_ERR_INVALID;
 
   FwdArgs a = {};
@@ -177,7 +179,7 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   }
   a.B = (int)B; a.H = (int)H; a.Nq = (int)Nq; a.Nkv = (int)Nkv;
   a.n_qtiles = (int)n_qtiles_k;
-  a.paired = paired ? 1 : 0;
+  a.paired = split ? 1 : 0;
   a.batch_inner = bias_kind != kNoBias && bias.strides.b == 0 && B > 1 ? 1 : 0;
   a.sm_scale = sm_scale;
   a.c = sm_scale * kLog2e;

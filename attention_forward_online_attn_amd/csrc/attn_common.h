@@ -66,7 +66,7 @@ struct FwdArgs {
   int64_t o_sb, o_sh, o_sn;
   int32_t B, H, Nq, Nkv;
   int32_t n_qtiles;  // dense: number of query tiles per (batch, head)
-  int32_t paired;    // dense causal: one workgroup takes q-tiles p and n_qtiles-1-p
+  int32_t paired;    // dense (8-wave key-split instances): a workgroup takes q-tiles p and n_qtiles-1-p
   int32_t batch_inner;  // dense: the batch is the fastest work index (a bias shared by the batch)
   float c;           // sm_scale * log2(e): scores go to the exp2 domain
   float sm_scale;
@@ -140,10 +140,9 @@ struct Tile {
 // stride 0) the list is (head, query tile, batch)-major instead: the batches
 // of one query tile run together on one XCD and read each bias row through
 // one L2, where the bias (N^2 elements per head) would otherwise be fetched
-// from HBM once per batch.  Causal: with pairing, workgroup p of a head takes
-// query tiles p and n-1-p (equal work for every workgroup; the shorter key
-// range is a prefix of the longer one, so both share the K/V tiles);
-// without it, tiles run heaviest first within a head.
+// from HBM once per batch.  Paired (small causal grids): workgroup p of a
+// head takes query tiles p and n-1-p, which hold the same number of key
+// tiles in all.  Otherwise, causal tiles run heaviest first within a head.
 // Jagged: the device-built plan lists (sequence, query tile) items, most
 // key tiles first; the head is the fastest index.
 template <int BM>

@@ -46,8 +46,8 @@ auto by_dim_qk(int64_t D, F&& f) {
 }
 
 // Forward instance tables (dtype codes of include/attn.h).
-KernelChoice fwd_bf16(int D, bool jvp, bool paired);            // inst_fwd_bf16.hip
-KernelChoice fwd_fp16(int D, bool jvp, bool paired);            // inst_fwd_fp16.hip
+KernelChoice fwd_bf16(int D, bool jvp, bool split);             // inst_fwd_bf16.hip
+KernelChoice fwd_fp16(int D, bool jvp, bool split);             // inst_fwd_fp16.hip
 KernelChoice fwd_f32(int D, int Dv, bool jvp);                  // inst_fwd_f32.hip
 KernelChoice fwd_bias(int dtype, int kind, int D);              // inst_fwd_bias.hip
 KernelChoice fwd_mixed_bf16(int D, int Dv, bool jvp);           // inst_fwd_mixed_bf16.hip

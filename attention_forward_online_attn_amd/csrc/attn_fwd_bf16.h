@@ -393,7 +393,11 @@ struct Bf16Cfg {
   static constexpr int DVL = DV < 32 ? 32 : DV;
   static constexpr int NW = NW_;            // waves per workgroup (32 query rows each)
   static constexpr int THREADS = 64 * NW;
-  static constexpr int BM = 128;            // query rows per q-tile (4 waves); 8 waves take two q-tiles
+  static constexpr int BM = 128;            // query rows per q-tile (4 waves)
+  // 8 waves: two groups of 4 take the same 128 query rows and split the key
+  // range in two halves, each streaming its own tiles; the halves' partial
+  // (m, l, O) are merged through LDS at the end
+  static constexpr bool SPLIT = NW == 8;
   static constexpr int TILE_K = BN * DQK * 2;  // bytes of one K (or tK) tile
   static constexpr int TILE_V = BN * DVL * 2;  // bytes of one V (or tV) tile
   // tile offsets in a stage: K, V, then tK, tV
@@ -402,7 +406,11 @@ struct Bf16Cfg {
   static constexpr int STAGE = (JVP ? 2 : 1) * (TILE_K + TILE_V);  // bytes of one pipeline stage
   static constexpr bool WIDE = (JVP && (DQK == 128 || DV == 128)) || DQK == 256;  // one wave per SIMD
   static constexpr bool DMA = !(JVP && WIDE);  // direct global -> LDS tile loads
-  static constexpr int LDS = 2 * STAGE;     // double-buffered key tiles
+  // floats per lane handed from group 1 to group 0 at the merge: m, l (r),
+  // the O accumulator (and accA, accB)
+  static constexpr int NVM = (JVP ? 3 : 2) + (DVL / 32) * 16 * (JVP ? 3 : 1);
+  // double-buffered key tiles (per group when split); the merge reuses them
+  static constexpr int LDS = SPLIT ? (4 * STAGE > NVM * 1024 ? 4 * STAGE : NVM * 1024) : 2 * STAGE;
   static constexpr int CPR_K = DQK / 8, CPR_V = DVL / 8;  // 16-byte chunks per row (in LDS)
   static constexpr int CPR_VS = DV / 8;                   // of those, chunks that hold data
   static constexpr int LOADS_K = (BN * CPR_K + THREADS - 1) / THREADS;
@@ -415,6 +423,7 @@ struct Bf16Cfg {
                 "unsupported head dim");
   static_assert(DV == 16 || DV == 32 || DV == 64 || DV == 128 || DV == 256, "unsupported head dim");
   static_assert(DV >= 32 || !(JVP && WIDE), "a 16-wide value tile needs the DMA path");
+  static_assert(NW == 4 || (NW == 8 && DMA && DV == DVL), "8 waves: key-split workgroups with DMA tiles");
 };
 
 template <int D, int BN, bool JVP, int NW_ = 4, bool F16 = false, int BIAS = kNoBias, int DV_ = 0>
@@ -426,6 +435,10 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int OFF_V = C::OFF_V, OFF_TK = C::OFF_TK, OFF_TV = C::OFF_TV;
   constexpr int CPR_K = C::CPR_K, CPR_V = C::CPR_V, LOADS_K = C::LOADS_K, LOADS_V = C::LOADS_V;
   constexpr int THREADS = C::THREADS, NW = C::NW;
+  constexpr bool SPLIT = C::SPLIT;
+  constexpr int NWD = SPLIT ? 4 : NW;              // waves that fill one tile (a group's)
+  constexpr int SSTR = STAGE;  // bytes from one pipeline stage to the next (a group's two stages are adjacent)
+  static_assert(!SPLIT || BIAS == kNoBias, "no score operand with key-split workgroups");
   constexpr int NB = BN / 32;    // 32-key blocks per tile
   constexpr int KD = DQK / 16;   // MFMA steps over the query/key head dim
   constexpr int DB = DVL / 32;   // 32-column output blocks
@@ -439,45 +452,19 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: per-wave branches stay scalar
   const int n32 = lane & 31, h32 = lane >> 5;
+  // key-range group of this wave (always 0 with 4 waves), its wave index
+  // within the group, and the group's two LDS stages (the stage offset stays
+  // an immediate of the LDS reads, which hold 16 bits)
+  const int grp = SPLIT ? wave >> 2 : 0;
+  const int wd = SPLIT ? wave & 3 : wave;
+  lds_t* const smem_g = smem + grp * 2 * STAGE;
+  const uint32_t lds_g = lds_base + grp * 2 * STAGE;
   const bf16* Q = (const bf16*)a.q + t.q_off;
   const bf16* K = (const bf16*)a.k + t.k_off;
   const bf16* V = (const bf16*)a.v + t.v_off;
   const bf16* TQ = JVP ? (const bf16*)a.tq + t.q_off : nullptr;
   const bf16* TK = JVP ? (const bf16*)a.tk + t.k_off : nullptr;
   const bf16* TV = JVP ? (const bf16*)a.tv + t.v_off : nullptr;
-
-  // ---- row bookkeeping (lane % 32 is this lane's query row)
-  // waves 0-3 take q-tile t.qt; with 8 waves, waves 4-7 take q-tile t.qt2
-  // (none when it is -1: those waves only help stage K/V)
-  const int my_qt = (NW == 8 && wave >= 4) ? t.qt2 : t.qt;
-  const int row0 = my_qt * BM;
-  const int w0 = my_qt < 0 ? t.Lstore : row0 + (wave & 3) * 32;
-  const int my_row = w0 + n32;
-  const int my_lim = kv_limit(t, a.causal, my_row < t.Lstore ? my_row : t.Lstore - 1);
-  const int w1 = min(w0 + 31, t.Lstore - 1);
-  int wave_max = 0, wave_min = 0;  // max / min key limit over the wave's rows
-  if (w0 <= w1) {
-    wave_max = w0 < t.Lattend ? kv_limit(t, a.causal, min(w1, t.Lattend - 1)) : 0;
-    wave_min = w1 >= t.Lattend ? 0 : kv_limit(t, a.causal, w0);
-  }
-  const int last_qt = t.qt2 > t.qt ? t.qt2 : t.qt;  // the workgroup's later q-tile
-  const int b1 = min(last_qt * BM + BM, t.Lattend) - 1;
-  const int blk_max = last_qt * BM <= b1 ? kv_limit(t, a.causal, b1) : 0;
-  const int n_tiles = (blk_max + BN - 1) / BN;
-
-  // ---- Q (and tQ) fragments, resident for the whole key loop: the B operand
-  // of S^T = K Q^T, lane (query n32, half h32) holds Q[row][16 kk + 8 h32 + 0..7]
-  bf16x8 qf[KD];
-  bf16x8 tqf[JVP ? KD : 1];
-  {
-    const int r = my_row < t.Lstore ? my_row : t.Lstore - 1;
-#pragma unroll
-    for (int kk = 0; kk < KD; ++kk) qf[kk] = *(const bf16x8*)(Q + r * a.q_sn + 16 * kk + 8 * h32);
-    if constexpr (JVP) {
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk) tqf[kk] = *(const bf16x8*)(TQ + r * a.q_sn + 16 * kk + 8 * h32);
-    }
-  }
 
   // ---- global -> register staging of one key tile, register -> LDS stores.
   // Thread `tid` moves chunks id = tid + 256 it of each tensor (row id / CPR,
@@ -554,7 +541,9 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   };
 
   // Direct global -> LDS tile loads (global_load_lds_dwordx4): instruction i
-  // of this wave fills the 1 KiB block NW * i + wave of a tile (RPB rows), lane
+  // of this wave fills the 1 KiB block NWD * i + wd of a tile (RPB rows; the
+  // NWD waves of a group fill that group's tiles, wd is the wave's index in
+  // it), lane
   // l the 16 bytes at l * 16 of it, so lane l fetches the chunk whose swizzled
   // home is that spot (the swizzle is an XOR, its own inverse).  A wave's
   // consecutive blocks lie RSTEP rows apart, a multiple of 16, and the
@@ -569,12 +558,12 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   // coincide and the instructions interleave as K, V, tK, tV.
   constexpr bool DMA = C::DMA;
   constexpr int NBLK_K = TILE_K / 1024, NBLK_V = TILE_V / 1024;  // 1 KiB blocks per tile
-  constexpr int NI_K = NBLK_K >= NW ? NBLK_K / NW : 1;            // DMA instructions per wave per tensor
-  constexpr int NI_V = NBLK_V >= NW ? NBLK_V / NW : 1;
+  constexpr int NI_K = NBLK_K >= NWD ? NBLK_K / NWD : 1;          // DMA instructions per wave per tensor
+  constexpr int NI_V = NBLK_V >= NWD ? NBLK_V / NWD : 1;
   constexpr int NIM = NI_K > NI_V ? NI_K : NI_V;
   constexpr int RPB_K = 1024 / (2 * DQK), RPB_V = 1024 / (2 * DVL);  // rows per block
-  constexpr int RSTEP_K = NW * RPB_K, RSTEP_V = NW * RPB_V;         // rows between a wave's blocks
-  static_assert(!DMA || ((NBLK_K % NW == 0 || NBLK_K < NW) && (NBLK_V % NW == 0 || NBLK_V < NW)),
+  constexpr int RSTEP_K = NWD * RPB_K, RSTEP_V = NWD * RPB_V;       // rows between a wave's blocks
+  static_assert(!DMA || ((NBLK_K % NWD == 0 || NBLK_K < NWD) && (NBLK_V % NWD == 0 || NBLK_V < NWD)),
                 "DMA tiles are whole 1 KiB blocks per wave");
   // The swizzle depends on the row modulo 16.  When a wave's blocks lie a
   // multiple of 16 rows apart one per-lane offset serves every instruction;
@@ -586,10 +575,10 @@ attn_fwd_bf16_kernel(FwdArgs a) {
                 "per-lane swizzle must repeat with the block step");
   constexpr int NPH_K = (NI_K == 1 || RSTEP_K % 16 == 0) ? 1 : 16 / RSTEP_K;
   constexpr int NPH_V = (NI_V == 1 || RSTEP_V % 16 == 0) ? 1 : 16 / RSTEP_V;
-  const bool dma_k = NBLK_K >= NW || wave < NBLK_K;  // waves past the tile's blocks fetch nothing
-  const bool dma_v = NBLK_V >= NW || wave < NBLK_V;
-  const int drow_k = RPB_K * wave + (lane * 16) / (2 * DQK);          // row of instruction 0
-  const int drow_v = RPB_V * wave + (lane * 16) / (2 * DVL);
+  const bool dma_k = NBLK_K >= NWD || wd < NBLK_K;  // waves past the tile's blocks fetch nothing
+  const bool dma_v = NBLK_V >= NWD || wd < NBLK_V;
+  const int drow_k = RPB_K * wd + (lane * 16) / (2 * DQK);            // row of instruction 0
+  const int drow_v = RPB_V * wd + (lane * 16) / (2 * DVL);
   int dch_k[NPH_K], dch_v[NPH_V];                                     // source chunk per phase
   uint32_t dk0[NPH_K], dv0[NPH_V];                                    // byte offsets per phase
 #pragma unroll
@@ -625,7 +614,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
           const char* b = src[x] + i * step_b[vs];
           if constexpr (NIM > 1) asm("" : "+s"(b));
           __builtin_amdgcn_global_load_lds((const void*)(b + (vs ? dv0[i % NPH_V] : dk0[i % NPH_K])),
-                                           (__attribute__((address_space(3))) void*)(base + (NW * i + wave) * 1024 + toff[x]),
+                                           (__attribute__((address_space(3))) void*)(base + (NWD * i + wd) * 1024 + toff[x]),
                                            16, 0, 0);
         }
     } else {  // ragged last tile: rows past the keys re-read the last key (masked)
@@ -641,238 +630,336 @@ attn_fwd_bf16_kernel(FwdArgs a) {
           if (i >= (vs ? NI_V : NI_K) || !(vs ? dma_v : dma_k)) continue;
           if (vs && DV < DVL && dch_v[i % NPH_V] >= CPR_VS) continue;
           __builtin_amdgcn_global_load_lds((const void*)(src[x] + (vs ? ov : ok)),
-                                           (__attribute__((address_space(3))) void*)(base + (NW * i + wave) * 1024 + toff[x]),
+                                           (__attribute__((address_space(3))) void*)(base + (NWD * i + wd) * 1024 + toff[x]),
                                            16, 0, 0);
         }
       }
     }
   };
 
-  f32x16 acc[DB];
-  f32x16 accA[JVP ? DB : 1], accB[JVP ? DB : 1];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    acc[i] = f32x16{};
-    if constexpr (JVP) { accA[i] = f32x16{}; accB[i] = f32x16{}; }
-  }
-  // ---- bias / mask: lane (query n32, half h32) needs, of each tile, the
-  // 8-key chunks c = 0 .. 2 NB - 1 at keys 16 c + 8 h32 of its own row: chunk
-  // c is accumulator registers 8 (c % 2) .. 8 (c % 2) + 7 of s[c / 2].  The
-  // chunks of tile j + 1 are loaded into register slot (j + 1) % 2 at the start
-  // of tile j, ahead of that tile's K/V fetch, so the barrier that ends tile j
-  // has also completed them.  With an additive bias the scores are moved to
-  // the exp2 domain once (s c + bias log2 e) and the scale below becomes 1.
-  constexpr int BCH = 2 * NB;                      // chunks per lane per tile
-  constexpr int BEL = BIAS == kAddBias ? 2 : 1;    // bytes per element
-  unsigned bsl[BIAS ? 2 : 1][BIAS ? BCH : 1][bias_dwords<BIAS>()];
-  const char* brow = nullptr;
-  if constexpr (BIAS != kNoBias) {
-    const int r = my_row < t.Lstore ? my_row : t.Lstore - 1;
-    brow = (const char*)a.bias + (t.bias_off + (int64_t)r * a.bias_sn) * BEL;
-  }
-  auto bias_load = [&](int j, auto slot_tag) {
-    if constexpr (BIAS != kNoBias)
-      bias_chunks<BIAS, BCH>(brow, j * BN + 8 * h32, j * BN + BN <= t.Lkv, t.Lkv, bsl[decltype(slot_tag)::value]);
-  };
-  // scale of the scores into the exp2 domain at the softmax (1 once an
-  // additive bias has been applied)
-  const float cs = BIAS == kAddBias ? 1.f : a.c;
+  // ---- one query tile per pass: with 8 waves a workgroup takes q-tiles p
+  // and n-1-p of a head one after the other (every pair holds the same
+  // number of key tiles in all, and each is split between the two groups)
+  const int n_pass = SPLIT && t.qt2 >= 0 ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    const int qt = pass == 0 ? t.qt : t.qt2;
 
-  float m_run = -INFINITY;  // running max, exp2 domain (scores times c)
-  float l_run = 0.f;        // this lane's partial row sum (its 16 of every 32 keys)
-  float r_run = 0.f;        // JVP: partial rowsum of p * (tQ K^T + Q tK^T)
-  // lane-dependent LDS offsets of the K fragments (per head-dim step) and of
-  // the V^T fragments (per output column block); tile, block and stage
-  // positions are added as immediates.  The swizzle depends on the row mod 16,
-  // which 32-key blocks do not change.
-  const int krow = kperm(n32);
-  uint32_t kaddr[KD];
-#pragma unroll
-  for (int kk = 0; kk < KD; ++kk) kaddr[kk] = lds_base + swz_off<DQK>(krow, 2 * kk + h32);
-  int vlo[DB], vhi[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) v_frag_offsets<DVL>(lane, db, vlo[db], vhi[db]);
+    // ---- row bookkeeping (lane % 32 is this lane's query row; with 8 waves
+    // both groups take the same rows)
+    const int row0 = qt * BM;
+    const int w0 = row0 + (wave & 3) * 32;
+    const int my_row = w0 + n32;
+    const int my_lim = kv_limit(t, a.causal, my_row < t.Lstore ? my_row : t.Lstore - 1);
+    const int w1 = min(w0 + 31, t.Lstore - 1);
+    int wave_max = 0, wave_min = 0;  // max / min key limit over the wave's rows
+    if (w0 <= w1) {
+      wave_max = w0 < t.Lattend ? kv_limit(t, a.causal, min(w1, t.Lattend - 1)) : 0;
+      wave_min = w1 >= t.Lattend ? 0 : kv_limit(t, a.causal, w0);
+    }
+    const int b1 = min(row0 + BM, t.Lattend) - 1;
+    const int blk_max = row0 <= b1 ? kv_limit(t, a.causal, b1) : 0;
+    const int n_tiles = (blk_max + BN - 1) / BN;
+    // key tiles of this wave's group: all of them, or with 8 waves group g
+    // takes tiles [g n0, min((g + 1) n0, n_tiles)); every wave runs n0 steps
+    const int n0 = SPLIT ? (n_tiles + 1) >> 1 : n_tiles;
+    const int jbase = grp * n0;
+    const int n_mine = SPLIT ? min(n0, n_tiles - jbase) : n_tiles;
 
-  // One key tile on LDS stage S = j % 2: fetch tile j + 1 into the other
-  // stage (freed by the barrier that ended the previous tile), compute, then
-  // one barrier makes tile j + 1 complete and visible.  S is a compile-time
-  // constant so every LDS address is a hoisted register plus an immediate.
-  auto step = [&](int j, auto stage_tag) {
-    constexpr int S = decltype(stage_tag)::value;
-    constexpr int SN = S ^ 1;
-    const bool ahead = j + 1 < n_tiles;
-    if (ahead) {  // in flight while this tile computes
-      bias_load(j + 1, std::integral_constant<int, SN>{});
-      if constexpr (DMA) dma_tile(j + 1, smem + SN * STAGE);
-      else load_tile(j + 1);
+    // ---- Q (and tQ) fragments, resident for the whole key loop: the B operand
+    // of S^T = K Q^T, lane (query n32, half h32) holds Q[row][16 kk + 8 h32 + 0..7]
+    bf16x8 qf[KD];
+    bf16x8 tqf[JVP ? KD : 1];
+    {
+      const int r = my_row < t.Lstore ? my_row : t.Lstore - 1;
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) qf[kk] = *(const bf16x8*)(Q + r * a.q_sn + 16 * kk + 8 * h32);
+      if constexpr (JVP) {
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) tqf[kk] = *(const bf16x8*)(TQ + r * a.q_sn + 16 * kk + 8 * h32);
+      }
     }
 
-    if (j * BN < wave_max) {  // wave-uniform: skip tiles this wave cannot see
-      const lds_t* vt = smem + S * STAGE + OFF_V;  // V tile (the cold residual pass reads it)
+    f32x16 acc[DB];
+    f32x16 accA[JVP ? DB : 1], accB[JVP ? DB : 1];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      acc[i] = f32x16{};
+      if constexpr (JVP) { accA[i] = f32x16{}; accB[i] = f32x16{}; }
+    }
+    // ---- bias / mask: lane (query n32, half h32) needs, of each tile, the
+    // 8-key chunks c = 0 .. 2 NB - 1 at keys 16 c + 8 h32 of its own row: chunk
+    // c is accumulator registers 8 (c % 2) .. 8 (c % 2) + 7 of s[c / 2].  The
+    // chunks of tile j + 1 are loaded into register slot (j + 1) % 2 at the start
+    // of tile j, ahead of that tile's K/V fetch, so the barrier that ends tile j
+    // has also completed them.  With an additive bias the scores are moved to
+    // the exp2 domain once (s c + bias log2 e) and the scale below becomes 1.
+    constexpr int BCH = 2 * NB;                      // chunks per lane per tile
+    constexpr int BEL = BIAS == kAddBias ? 2 : 1;    // bytes per element
+    unsigned bsl[BIAS ? 2 : 1][BIAS ? BCH : 1][bias_dwords<BIAS>()];
+    const char* brow = nullptr;
+    if constexpr (BIAS != kNoBias) {
+      const int r = my_row < t.Lstore ? my_row : t.Lstore - 1;
+      brow = (const char*)a.bias + (t.bias_off + (int64_t)r * a.bias_sn) * BEL;
+    }
+    auto bias_load = [&](int j, auto slot_tag) {
+      if constexpr (BIAS != kNoBias)
+        bias_chunks<BIAS, BCH>(brow, j * BN + 8 * h32, j * BN + BN <= t.Lkv, t.Lkv, bsl[decltype(slot_tag)::value]);
+    };
+    // scale of the scores into the exp2 domain at the softmax (1 once an
+    // additive bias has been applied)
+    const float cs = BIAS == kAddBias ? 1.f : a.c;
 
-      // S^T = K Q^T (and the tangent scores tQ K^T + Q tK^T)
-      f32x16 s[NB];
-      f32x16 ts[JVP ? NB : 1];
-      scores_section<DQK, NB, JVP, S * STAGE, S * STAGE + OFF_TK, F16>(kaddr, qf, tqf, s, ts);
+    float m_run = -INFINITY;  // running max, exp2 domain (scores times c)
+    float l_run = 0.f;        // this lane's partial row sum (its 16 of every 32 keys)
+    float r_run = 0.f;        // JVP: partial rowsum of p * (tQ K^T + Q tK^T)
+    // lane-dependent LDS offsets of the K fragments (per head-dim step) and of
+    // the V^T fragments (per output column block); tile, block and stage
+    // positions are added as immediates.  The swizzle depends on the row mod 16,
+    // which 32-key blocks do not change.
+    const int krow = kperm(n32);
+    uint32_t kaddr[KD];
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) kaddr[kk] = lds_g + swz_off<DQK>(krow, 2 * kk + h32);
+    int vlo[DB], vhi[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) v_frag_offsets<DVL>(lane, db, vlo[db], vhi[db]);
 
-      // mask keys past this row's limit (ragged tail, causal diagonal,
-      // jagged truncation) -- only on tiles that reach some row's limit
-      if ((j + 1) * BN > wave_min) {
+    // One key tile on LDS stage S = j % 2: fetch tile j + 1 into the other
+    // stage (freed by the barrier that ended the previous tile), compute, then
+    // one barrier makes tile j + 1 complete and visible.  S is a compile-time
+    // constant so every LDS address is a hoisted register plus an immediate.
+    auto step = [&](int j, auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;
+      constexpr int SN = S ^ 1;
+      const int jt = jbase + j;  // this group's key tile
+      const bool ahead = j + 1 < n_mine;
+      if (ahead) {  // in flight while this tile computes
+        bias_load(jt + 1, std::integral_constant<int, SN>{});
+        if constexpr (DMA) dma_tile(jt + 1, smem_g + SN * SSTR);
+        else load_tile(jt + 1);
+      }
+
+      if (j < n_mine && jt * BN < wave_max) {  // wave-uniform: skip tiles this wave cannot see
+        const lds_t* vt = smem_g + S * SSTR + OFF_V;  // V tile (the cold residual pass reads it)
+
+        // S^T = K Q^T (and the tangent scores tQ K^T + Q tK^T)
+        f32x16 s[NB];
+        f32x16 ts[JVP ? NB : 1];
+        scores_section<DQK, NB, JVP, S * SSTR, S * SSTR + OFF_TK, F16>(kaddr, qf, tqf, s, ts);
+
+        // mask keys past this row's limit (ragged tail, causal diagonal,
+        // jagged truncation) -- only on tiles that reach some row's limit
+        if ((jt + 1) * BN > wave_min) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = jt * BN + 32 * b + 16 * (r >> 3) + 8 * h32 + (r & 7);
+              if (key >= my_lim) s[b][r] = -INFINITY;
+            }
+        }
+        if constexpr (BIAS != kNoBias) apply_bias<BIAS, F16, NB>(s, bsl[S], a.c);
+
+        // online softmax: tile row max (in-lane, then the other half-wave)
+        float mx = s[0][0];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j * BN + 32 * b + 16 * (r >> 3) + 8 * h32 + (r & 7);
-            if (key >= my_lim) s[b][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+        mx = xhalf_max(mx);
+        const float m_new = mx * cs;
+        const bool upd = m_new > m_run + (BIAS != kNoBias ? kTauBias : kTau);
+        if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+          const float m_next = upd ? m_new : m_run;
+          const float alpha = m_next == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_next);
+#pragma unroll
+          for (int i = 0; i < DB; ++i) {
+            acc[i] *= alpha;
+            if constexpr (JVP) { accA[i] *= alpha; accB[i] *= alpha; }
           }
-      }
-      if constexpr (BIAS != kNoBias) apply_bias<BIAS, F16, NB>(s, bsl[S], a.c);
-
-      // online softmax: tile row max (in-lane, then the other half-wave)
-      float mx = s[0][0];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-      mx = xhalf_max(mx);
-      const float m_new = mx * cs;
-      const bool upd = m_new > m_run + (BIAS != kNoBias ? kTauBias : kTau);
-      if (__builtin_amdgcn_ballot_w64(upd) != 0) {
-        const float m_next = upd ? m_new : m_run;
-        const float alpha = m_next == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_next);
-#pragma unroll
-        for (int i = 0; i < DB; ++i) {
-          acc[i] *= alpha;
-          if constexpr (JVP) { accA[i] *= alpha; accB[i] *= alpha; }
+          l_run *= alpha;
+          r_run *= alpha;
+          m_run = m_next;
         }
-        l_run *= alpha;
-        r_run *= alpha;
-        m_run = m_next;
-      }
-      const float msub = m_run == -INFINITY ? 0.f : m_run;
+        const float msub = m_run == -INFINITY ? 0.f : m_run;
 
-      // Rows that attend at most kSplitKeys keys (short jagged sequences, the
-      // first causal rows) follow few keys closely, so |O| can reach max|v|
-      // and P's bf16 rounding (2^-9 relative) shows in O: these waves first
-      // add V^T Plo^T, Plo = p - bf16(p) being that rounding's residual.  p
-      // is recomputed below bit for bit; this pass stays apart from the main
-      // product so the latter's code is the same for every wave.
-      if (__builtin_expect(wave_max <= kSplitKeys, 0)) {
-        float nm = -msub;
-        asm volatile("" : "+v"(nm));  // opaque copy: no value here is shared with the main path
+        // Rows that attend at most kSplitKeys keys (short jagged sequences, the
+        // first causal rows) follow few keys closely, so |O| can reach max|v|
+        // and P's bf16 rounding (2^-9 relative) shows in O: these waves first
+        // add V^T Plo^T, Plo = p - bf16(p) being that rounding's residual.  p
+        // is recomputed below bit for bit; this pass stays apart from the main
+        // product so the latter's code is the same for every wave.
+        if (__builtin_expect(wave_max <= kSplitKeys, 0)) {
+          float nm = -msub;
+          asm volatile("" : "+v"(nm));  // opaque copy: no value here is shared with the main path
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          if (j * BN + 32 * b >= wave_max) break;  // no row of the wave sees this block
-          bf16x8 plo[2];
+          for (int b = 0; b < NB; ++b) {
+            if (jt * BN + 32 * b >= wave_max) break;  // no row of the wave sees this block
+            bf16x8 plo[2];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], cs, nm));
-            plo[r >> 3][r & 7] = to16<F16>(p - from16<F16>(to16<F16>(p)));
-          }
-          pv_lo_block<DVL, F16>(vt, vlo, vhi, b, plo, acc);
-        }
-      }
-
-      // p = exp2(s c - m); P (and H = p tS) as bf16 B operands: registers
-      // 8 c16 .. 8 c16 + 7 of block b are keys 32 b + 16 c16 + 8 h32 + 0..7,
-      // i.e. key chunk 2 b + c16 of the PV product.  Chunk 0 is computed
-      // first; chunk c+1 is computed in slices after the MFMAs of chunk c.
-      bf16x8 pf[NB][2];
-      bf16x8 hf[JVP ? NB : 1][2];
-      auto soft = [&](auto e_tag) {  // one element e of this lane's 16 NB scores
-        constexpr int e = decltype(e_tag)::value, b = e / 16, r = e % 16;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], cs, -msub));
-        l_run += p;
-        pf[b][r >> 3][r & 7] = to16<F16>(p);
-        if constexpr (JVP) {
-          const float hv = p * ts[b][r];
-          r_run += hv;
-          hf[b][r >> 3][r & 7] = to16<F16>(hv);
-        }
-      };
-      constexpr int EPS = 8 / DB;  // elements of the next chunk per PV step
-      static_for<8>(soft);
-      // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
-      pv_section<DVL, NB, JVP, S * STAGE + OFF_V, S * STAGE + OFF_TV, F16>(
-          lds_base, vlo, vhi, pf, hf, acc, accA, accB, [&](auto i_tag) {
-            constexpr int i = decltype(i_tag)::value, c = i / DB;
-            if constexpr (c + 1 < 2 * NB) {
-              static_for<EPS>([&](auto k_tag) {
-                soft(std::integral_constant<int, 8 * (c + 1) + (i % DB) * EPS + decltype(k_tag)::value>{});
-              });
+            for (int r = 0; r < 16; ++r) {
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], cs, nm));
+              plo[r >> 3][r & 7] = to16<F16>(p - from16<F16>(to16<F16>(p)));
             }
-          });
-    }
-
-    if (!DMA && ahead) store_tile(smem + SN * STAGE);
-    __syncthreads();
-  };
-
-  // The loop sits inside the prologue's branch: on every path into it the
-  // Q-fragment loads have completed, so no wait for the next tile's prefetch
-  // is needed inside the loop.
-  if constexpr (DV < DVL) {
-    // the padding chunks of every value tile (both stages, V and tV) are
-    // zeroed once: the tile copies never write them, and the barrier after
-    // the prologue orders these stores before any fragment read
-    constexpr int NVT = JVP ? 2 : 1, PADC = CPR_V - CPR_VS;
-    for (int id = tid; id < 2 * NVT * BN * PADC; id += THREADS) {
-      const int c = CPR_VS + id % PADC, row = (id / PADC) % BN, st = id / (PADC * BN);
-      const int off = (st >> 1) * STAGE + ((st & 1) ? OFF_TV : OFF_V) + swz_off<DVL>(row, c);
-      *(__attribute__((address_space(3))) u32x4*)(smem + off) = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  if (n_tiles > 0) {
-    bias_load(0, std::integral_constant<int, 0>{});
-    if constexpr (DMA) {
-      dma_tile(0, smem);
-    } else {
-      load_tile(0);
-      store_tile(smem);
-    }
-    __syncthreads();
-    int j = 0;
-    for (; j + 2 <= n_tiles; j += 2) {
-      step(j, std::integral_constant<int, 0>{});
-      step(j + 1, std::integral_constant<int, 1>{});
-    }
-    if (j < n_tiles) step(j, std::integral_constant<int, 0>{});
-  }
-
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln2, tO = (accA + accB - r O) / l,
-  // tLSE = r / l
-  const float l_tot = xhalf_sum(l_run);
-  const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
-  const float lse = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
-  const float r_tot = JVP ? xhalf_sum(r_run) * a.sm_scale : 0.f;
-  if (my_row < t.Lstore) {
-    bf16* orow = (bf16*)a.o + t.o_off + my_row * a.o_sn;
-    bf16* torow = JVP ? (bf16*)a.to + t.o_off + my_row * a.o_sn : nullptr;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (32 * db + 8 * g >= DV) continue;  // padding columns of a 16-wide value tile
-        const int d = 32 * db + 8 * g + 4 * h32;  // registers 4g..4g+3 are columns d..d+3
-        bf16x4 ov;
-        bf16x4 tov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float o = acc[db][4 * g + e] * inv;
-          ov[e] = to16<F16>(o);
-          if constexpr (JVP)
-            tov[e] = to16<F16>((accA[db][4 * g + e] + a.sm_scale * accB[db][4 * g + e] - r_tot * o) * inv);
+            pv_lo_block<DVL, F16>(vt, vlo, vhi, b, plo, acc);
+          }
         }
-        *(bf16x4*)(orow + d) = ov;
-        if constexpr (JVP) *(bf16x4*)(torow + d) = tov;
+
+        // p = exp2(s c - m); P (and H = p tS) as bf16 B operands: registers
+        // 8 c16 .. 8 c16 + 7 of block b are keys 32 b + 16 c16 + 8 h32 + 0..7,
+        // i.e. key chunk 2 b + c16 of the PV product.  Chunk 0 is computed
+        // first; chunk c+1 is computed in slices after the MFMAs of chunk c.
+        bf16x8 pf[NB][2];
+        bf16x8 hf[JVP ? NB : 1][2];
+        auto soft = [&](auto e_tag) {  // one element e of this lane's 16 NB scores
+          constexpr int e = decltype(e_tag)::value, b = e / 16, r = e % 16;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], cs, -msub));
+          l_run += p;
+          pf[b][r >> 3][r & 7] = to16<F16>(p);
+          if constexpr (JVP) {
+            const float hv = p * ts[b][r];
+            r_run += hv;
+            hf[b][r >> 3][r & 7] = to16<F16>(hv);
+          }
+        };
+        constexpr int EPS = 8 / DB;  // elements of the next chunk per PV step
+        static_for<8>(soft);
+        // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
+        pv_section<DVL, NB, JVP, S * SSTR + OFF_V, S * SSTR + OFF_TV, F16>(
+            lds_g, vlo, vhi, pf, hf, acc, accA, accB, [&](auto i_tag) {
+              constexpr int i = decltype(i_tag)::value, c = i / DB;
+              if constexpr (c + 1 < 2 * NB) {
+                static_for<EPS>([&](auto k_tag) {
+                  soft(std::integral_constant<int, 8 * (c + 1) + (i % DB) * EPS + decltype(k_tag)::value>{});
+                });
+              }
+            });
       }
-    if (h32 == 0) a.lse[t.lse_off + my_row] = lse;
-    // tangent of LSE: rowsum(P tS) = r / l (0 for a row without keys)
-    if constexpr (JVP)
-      if (h32 == 0 && a.tlse != nullptr) a.tlse[t.lse_off + my_row] = r_tot * inv;
-  }
+
+      if (!DMA && ahead) store_tile(smem_g + SN * SSTR);
+      __syncthreads();
+    };
+
+    // The loop sits inside the prologue's branch: on every path into it the
+    // Q-fragment loads have completed, so no wait for the next tile's prefetch
+    // is needed inside the loop.
+    if constexpr (DV < DVL) {
+      // the padding chunks of every value tile (both stages, V and tV) are
+      // zeroed once: the tile copies never write them, and the barrier after
+      // the prologue orders these stores before any fragment read
+      constexpr int NVT = JVP ? 2 : 1, PADC = CPR_V - CPR_VS;
+      for (int id = tid; id < 2 * NVT * BN * PADC; id += THREADS) {
+        const int c = CPR_VS + id % PADC, row = (id / PADC) % BN, st = id / (PADC * BN);
+        const int off = (st >> 1) * STAGE + ((st & 1) ? OFF_TV : OFF_V) + swz_off<DVL>(row, c);
+        *(__attribute__((address_space(3))) u32x4*)(smem + off) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+
+    if (n0 > 0) {
+      bias_load(0, std::integral_constant<int, 0>{});
+      if constexpr (DMA) {
+        if (n_mine > 0) dma_tile(jbase, smem_g);
+      } else {
+        load_tile(0);
+        store_tile(smem);
+      }
+      __syncthreads();
+      int j = 0;
+      for (; j + 2 <= n0; j += 2) {
+        step(j, std::integral_constant<int, 0>{});
+        step(j + 1, std::integral_constant<int, 1>{});
+      }
+      if (j < n0) step(j, std::integral_constant<int, 0>{});
+    }
+
+    // ---- key-split merge: group 1 hands its partial row state (running max,
+    // partial sums, accumulators, all relative to its own max) to group 0
+    // through LDS, which the loop's last barrier has freed; lane value e sits
+    // at float index (e * 4 + wave % 4) * 64 + lane.  Group 0 rescales both
+    // parts to the larger max and adds them (the online-softmax merge of two
+    // key ranges), then writes the rows.
+    if constexpr (SPLIT) {
+      typedef __attribute__((address_space(3))) float lds_f;
+      lds_f* X = (lds_f*)smem;
+      const int sl = (wave & 3) * 64 + lane;
+      constexpr int E0 = JVP ? 3 : 2;  // m, l (, r), then the accumulators
+      if (grp == 1) {
+        X[sl] = m_run;
+        X[256 + sl] = l_run;
+        if constexpr (JVP) X[512 + sl] = r_run;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            X[(E0 + 16 * db + r) * 256 + sl] = acc[db][r];
+            if constexpr (JVP) {
+              X[(E0 + 16 * (DB + db) + r) * 256 + sl] = accA[db][r];
+              X[(E0 + 16 * (2 * DB + db) + r) * 256 + sl] = accB[db][r];
+            }
+          }
+      }
+      __syncthreads();
+      if (grp == 0) {
+        const float m1 = X[sl];
+        const float mm = fmaxf(m_run, m1);
+        const float s0 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+        const float s1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+        l_run = l_run * s0 + X[256 + sl] * s1;
+        if constexpr (JVP) r_run = r_run * s0 + X[512 + sl] * s1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc[db][r] = acc[db][r] * s0 + X[(E0 + 16 * db + r) * 256 + sl] * s1;
+            if constexpr (JVP) {
+              accA[db][r] = accA[db][r] * s0 + X[(E0 + 16 * (DB + db) + r) * 256 + sl] * s1;
+              accB[db][r] = accB[db][r] * s0 + X[(E0 + 16 * (2 * DB + db) + r) * 256 + sl] * s1;
+            }
+          }
+        m_run = mm;
+      }
+    }
+
+    // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln2, tO = (accA + accB - r O) / l,
+    // tLSE = r / l
+    // (with 8 waves, by group 0)
+    if (!SPLIT || grp == 0) {
+      const float l_tot = xhalf_sum(l_run);
+      const bool empty = !(l_tot > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_tot;
+      const float lse = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
+      const float r_tot = JVP ? xhalf_sum(r_run) * a.sm_scale : 0.f;
+      if (my_row < t.Lstore) {
+        bf16* orow = (bf16*)a.o + t.o_off + my_row * a.o_sn;
+        bf16* torow = JVP ? (bf16*)a.to + t.o_off + my_row * a.o_sn : nullptr;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            if (32 * db + 8 * g >= DV) continue;  // padding columns of a 16-wide value tile
+            const int d = 32 * db + 8 * g + 4 * h32;  // registers 4g..4g+3 are columns d..d+3
+            bf16x4 ov;
+            bf16x4 tov;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float o = acc[db][4 * g + e] * inv;
+              ov[e] = to16<F16>(o);
+              if constexpr (JVP)
+                tov[e] = to16<F16>((accA[db][4 * g + e] + a.sm_scale * accB[db][4 * g + e] - r_tot * o) * inv);
+            }
+            *(bf16x4*)(orow + d) = ov;
+            if constexpr (JVP) *(bf16x4*)(torow + d) = tov;
+          }
+        if (h32 == 0) a.lse[t.lse_off + my_row] = lse;
+        // tangent of LSE: rowsum(P tS) = r / l (0 for a row without keys)
+        if constexpr (JVP)
+          if (h32 == 0 && a.tlse != nullptr) a.tlse[t.lse_off + my_row] = r_tot * inv;
+      }
+    }
+    // a second query tile's first copies would overwrite the merge area that
+    // group 0 has just read
+    if (SPLIT && pass + 1 < n_pass) __syncthreads();
+  }  // query tile pass
 }
 
 }  // namespace attn

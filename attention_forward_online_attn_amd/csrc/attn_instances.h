@@ -20,19 +20,20 @@ KernelChoice f32k() {
   return {attn_fwd_f32_kernel<D, JVP, BIAS, DV>, C::BM, C::BN, C::LDS, 256};
 }
 
-// 16-bit forward with equal head dims; `paired`: 8-wave workgroups that take
-// q-tiles p and n-1-p (never the D=128 JVP instance, one wave per SIMD).
+// 16-bit forward with equal head dims; `split`: 8-wave workgroups whose two
+// halves split a query tile's key range (never the D=128 JVP instance, one
+// wave per SIMD).
 template <bool F16>
-KernelChoice choose16(int D, bool jvp, bool paired) {
+KernelChoice choose16(int D, bool jvp, bool split) {
   return by_dim(D, [&](auto d) {
     constexpr int Dc = decltype(d)::value;
-    if (paired) return !jvp ? r32<Dc, kBnDense, false, 8, F16>() : r32<Dc == 128 ? 64 : Dc, kBnJvp, true, 8, F16>();
+    if (split) return !jvp ? r32<Dc, kBnDense, false, 8, F16>() : r32<Dc == 128 ? 64 : Dc, kBnJvp, true, 8, F16>();
     return !jvp ? r32<Dc, kBnDense, false, 4, F16>() : r32<Dc, kBnJvp, true, 4, F16>();
   });
 }
 
 // 16-bit forward whose value head dim differs from the query/key one (JVP
-// page: d_v != d_qk): 4-wave workgroups, never paired, no bias.
+// page: d_v != d_qk): 4-wave workgroups, never split, no bias.
 template <bool F16>
 KernelChoice choose_mixed16(int D, int Dv, bool jvp) {
   return by_dim_qk(D, [&](auto dq) {

@@ -2,5 +2,5 @@
 #include "attn_instances.h"
 
 namespace attn {
-KernelChoice fwd_bf16(int D, bool jvp, bool paired) { return choose16<false>(D, jvp, paired); }
+KernelChoice fwd_bf16(int D, bool jvp, bool split) { return choose16<false>(D, jvp, split); }
 }  // namespace attn

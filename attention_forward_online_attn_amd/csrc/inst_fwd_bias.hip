@@ -1,5 +1,5 @@
 // Forward instances with an additive bias or a boolean mask (no JVP, never
-// paired): one per dtype, head dim and kind.
+// split): one per dtype, head dim and kind.
 #include "../../include/attn.h"
 #include "attn_instances.h"
 

@@ -2,5 +2,5 @@
 #include "attn_instances.h"
 
 namespace attn {
-KernelChoice fwd_fp16(int D, bool jvp, bool paired) { return choose16<true>(D, jvp, paired); }
+KernelChoice fwd_fp16(int D, bool jvp, bool split) { return choose16<true>(D, jvp, split); }
 }  // namespace attn

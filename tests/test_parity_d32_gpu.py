@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 def test_d32_dense(gpu_lib, dtype, causal):
     dense_case(2, 3, 300, 300, 32, dtype, causal, seed=90)
     dense_case(1, 2, 1, 1, 32, dtype, causal, seed=91)
-    dense_case(2, 2, 640, 640, 32, dtype, causal, seed=92)  # small causal grid: paired instances
+    dense_case(2, 2, 640, 640, 32, dtype, causal, seed=92)  # small causal grid: paired key-split instances
 
 
 def test_d32_cross_attention(gpu_lib):

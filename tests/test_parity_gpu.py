@@ -349,8 +349,10 @@ def test_jagged_strided_layout(gpu_lib):
 
 @pytest.mark.parametrize("N", [300, 640])
 def test_causal_pairing_odd_and_even_tile_counts(gpu_lib, N):
-    """Causal grids small enough to be paired: 3 q-tiles (the middle one runs
-    alone) and 5 q-tiles, for the forward and the JVP."""
+    """Causal grids small enough for paired key-split workgroups: 3 q-tiles
+    (the middle one runs alone) and 5 q-tiles, for the forward and the JVP;
+    with D=128 the first tile's 2 key tiles split one per group, and the
+    JVP's 32-key tiles leave the second group one tile short on odd counts."""
     dense_case(2, 3, N, N, 128, "bf16", True, seed=N)
     jvp_case(2, 3, N, N, 64, "bf16", True, seed=N + 1)
 
@@ -405,6 +407,6 @@ def test_fp16_jagged(gpu_lib):
 
 
 def test_fp16_paired_causal_grid(gpu_lib):
-    """A small causal grid takes the paired 8-wave instances."""
+    """A small causal grid takes the paired key-split 8-wave instances."""
     dense_case(2, 2, 640, 640, 64, "fp16", True, seed=49)
     dense_case(2, 2, 640, 640, 128, "fp16", True, seed=50)
