@@ -37,6 +37,9 @@ int finish(hipStream_t stream) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// a * b <= limit for non-negative a, b, without forming the product first
+bool mul_within(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
+
 // A stride is usable when its dimension is trivial or it keeps 16-byte rows.
 bool stride_ok(int64_t stride, int64_t extent, int64_t vec) {
   if (stride < 0) return false;
@@ -137,8 +140,9 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
     return Dv < 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
   if (causal && Nq != Nkv) return ATTN_ERR_CAUSAL_SHAPE;
-  if (B * H * Nq == 0) return ATTN_OK;
-  if (Nq > INT_MAX || Nkv > INT_MAX || B > INT_MAX || H > INT_MAX) return ATTN_ERR_INVALID;
+  if (B == 0 || H == 0 || Nq == 0) return ATTN_OK;
+  // (batch, head) indices are 32-bit on the device
+  if (Nq > INT_MAX || Nkv > INT_MAX || !mul_within(B, H, INT_MAX)) return ATTN_ERR_INVALID;
   const int64_t vec = dtype == ATTN_FP32 ? 4 : 8;
   if (!q || !o || !lse) return ATTN_ERR_INVALID;
   if (Nkv > 0 && (!k || !v)) return ATTN_ERR_INVALID;
@@ -309,6 +313,7 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
 size_t jagged_attn_bwd_workspace_bytes(int64_t num_seqs, int64_t H, int64_t total_len) {
   if (num_seqs < 0 || H < 0 || total_len < 0 || num_seqs > INT_MAX - 1 || total_len > INT_MAX || H > INT_MAX)
     return 0;
+  if (!mul_within(H, total_len, (int64_t)1 << 40)) return 0;
   const int64_t plan = (16 + 8 * plan_capacity(num_seqs, total_len, 128) + 15) / 16 * 16;
   return (size_t)(plan + 8 * H * total_len);
 }
@@ -335,9 +340,10 @@ int jagged_attn_bwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
   if (((uintptr_t)lse & 3u) != 0) return ATTN_ERR_UNSUPPORTED;
   const int64_t cap = plan_capacity(num_seqs, total_len, 128);
-  const size_t need = jagged_attn_bwd_workspace_bytes(num_seqs, H, total_len);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u)) return ATTN_ERR_WORKSPACE;
   if (cap * H > INT_MAX) return ATTN_ERR_INVALID;
+  const size_t need = jagged_attn_bwd_workspace_bytes(num_seqs, H, total_len);
+  if (need == 0) return ATTN_ERR_INVALID;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u)) return ATTN_ERR_WORKSPACE;
   const int mlen = (int)(max_seq_len < INT_MAX ? max_seq_len : INT_MAX);
 
   hipStream_t st = (hipStream_t)stream;
@@ -376,9 +382,8 @@ int jagged_attn_bwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
   if (B < 0 || H < 0 || Nq < 0) return 0;
-  const int64_t rows = B * H * Nq;
-  if (rows > ((int64_t)1 << 40)) return 0;
-  return (size_t)(8 * rows);
+  if (!mul_within(B, H, (int64_t)1 << 40) || !mul_within(B * H, Nq, (int64_t)1 << 40)) return 0;
+  return (size_t)(8 * B * H * Nq);
 }
 
 }  // extern "C"
@@ -398,8 +403,8 @@ int dense_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const vo
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
   if (causal && Nq != Nkv) return ATTN_ERR_CAUSAL_SHAPE;
-  if (B * H * (Nq + Nkv) == 0) return ATTN_OK;
-  if (Nq > INT_MAX || Nkv > INT_MAX || B > INT_MAX || H > INT_MAX) return ATTN_ERR_INVALID;
+  if (B == 0 || H == 0 || (Nq == 0 && Nkv == 0)) return ATTN_OK;
+  if (Nq > INT_MAX || Nkv > INT_MAX || !mul_within(B, H, INT_MAX)) return ATTN_ERR_INVALID;
   if (Nq > 0 && (!q || !o || !d_o || !lse || !dq)) return ATTN_ERR_INVALID;
   if (Nkv > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVALID;
   const int64_t vec = 8;
@@ -427,11 +432,11 @@ int dense_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const vo
       return ATTN_ERR_INVALID;
     if (!aligned16(dbias)) return ATTN_ERR_UNSUPPORTED;
   }
-  const int64_t rows = B * H * Nq;
-  if (rows > 0 && (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, Nq) || ((uintptr_t)workspace & 15u)))
-    return ATTN_ERR_WORKSPACE;
+  const int64_t rows = B * H * Nq;  // B H <= INT_MAX, Nq <= INT_MAX: no overflow
   if (B * H * ((Nq + 127) / 128) > INT_MAX || B * H * ((Nkv + 127) / 128) > INT_MAX || rows / 16 > INT_MAX)
     return ATTN_ERR_INVALID;
+  if (rows > 0 && (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, Nq) || ((uintptr_t)workspace & 15u)))
+    return ATTN_ERR_WORKSPACE;
 
   BwdArgs a = {};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = d_o; a.lse = lse; a.dq = dq; a.dk = dk; a.dv = dv;

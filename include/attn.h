@@ -37,6 +37,10 @@
  *   always fp32.
  * - sm_scale must be finite and >= 0 (every page uses a positive scale,
  *   by default D^-0.5).
+ * - Sizes: Nq, Nkv, total_len and num_seqs + 1 at most 2^31 - 1, and
+ *   B * H at most 2^31 - 1 (the device indexes rows, tiles and (batch, head)
+ *   pairs with 32-bit integers); larger extents are ATTN_ERR_INVALID, and the
+ *   workspace-size functions return 0 for extents they cannot serve.
  * - A query row with no key to attend (Nkv == 0, or a jagged row beyond
  *   max_seq_len inside its sequence) gets O = 0, tO = 0 and LSE = -inf.
  * - All argument checks happen on the host before anything is enqueued; a
@@ -60,7 +64,7 @@ extern "C" {
 /* Status codes (every entry point returns one). */
 enum {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID = -1,      /* null pointer with work to do, negative size, bad stride, bad scale */
+  ATTN_ERR_INVALID = -1,      /* null pointer with work to do, negative or oversized size, bad stride, bad scale */
   ATTN_ERR_UNSUPPORTED = -2,  /* head dim not in {32,64,128}, unknown dtype, misaligned pointer/stride */
   ATTN_ERR_CAUSAL_SHAPE = -3, /* causal with Nq != Nkv (the mask is top-left aligned) */
   ATTN_ERR_WORKSPACE = -4,    /* jagged workspace missing or too small */

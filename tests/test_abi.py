@@ -58,6 +58,23 @@ def call_fwd(lib, dtype=BF16, B=1, H=2, Nq=128, Nkv=128, D=64, scale=0.125, caus
     return lib.attn_fwd(dtype, q, sq, k, sk, v, sk, o, so, lse, B, H, Nq, Nkv, D, scale, causal, None)
 
 
+def test_oversized_extents_are_rejected(lib):
+    """Extents whose products would overflow 64-bit integers, or whose
+    (batch, head) count exceeds the 32-bit device indices, are rejected on
+    the host before any product is formed; the workspace sizes report 0."""
+    huge = 1 << 40
+    assert call_fwd(lib, B=huge, H=huge) == INVALID
+    assert call_fwd(lib, B=(1 << 31) - 1, H=2) == INVALID
+    assert call_fwd(lib, Nq=1 << 31, Nkv=1 << 31) == INVALID
+    st = dense_strides(1, 2, 128, 64)
+    assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st,
+                        huge, huge, 128, 128, 64, 0.125, 0, P, 1 << 20, None) == INVALID
+    assert lib.attn_bwd_workspace_bytes(huge, huge, huge) == 0
+    assert lib.attn_bwd_workspace_bytes(1 << 20, 1 << 20, 2) == 0
+    assert lib.attn_bwd_workspace_bytes(1 << 10, 1 << 10, 1 << 10) == 8 << 30
+    assert lib.jagged_attn_bwd_workspace_bytes(4, (1 << 31) - 1, (1 << 31) - 1) == 0
+
+
 def test_status_strings(lib):
     assert lib.attn_status_string(0) == b"ok"
     for rc in (INVALID, UNSUPPORTED, CAUSAL, WORKSPACE, -5):
