@@ -113,3 +113,60 @@ def test_random_backward(gpu_lib, case):
     got = attn.bwd(qc, kc, vc, o, doc, lse, causal=causal, sm_scale=scale)
     ref = oracle.attention_bwd(q, k, v, do, oracle.scale_as_passed(scale), causal)
     check_grads(got, ref, f"random backward case {case}", dtype)
+
+
+def draw_jagged_cases(n, seed):
+    """(case id, lengths, H, D, dtype, max_seq_len, causal, backward): lengths
+    from a mix of distributions (empty sequences included), max_seq_len at or
+    below the longest sequence."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        S = int(rng.integers(1, 40))
+        kind = int(rng.integers(0, 3))
+        if kind == 0:
+            lengths = rng.integers(0, 600, S)
+        elif kind == 1:
+            lengths = rng.integers(0, 70, S)
+        else:
+            lengths = np.where(rng.random(S) < 0.3, 0, rng.integers(100, 400, S))
+        if lengths.sum() == 0:
+            lengths[0] = 1
+        longest = max(int(lengths.max()), 1)
+        msl = longest if rng.random() < 0.5 else int(rng.integers(1, longest + 1))
+        backward = bool(rng.integers(0, 2))
+        dtype = ["bf16", "fp16"][int(rng.integers(0, 2))] if backward else ["bf16", "fp16", "fp32"][int(rng.integers(0, 3))]
+        D = int(rng.choice([32, 64, 128] if backward else [16, 32, 64, 128]))
+        out.append((i, [int(x) for x in lengths], int(rng.integers(1, 5)), D, dtype, msl, bool(rng.integers(0, 2)),
+                    backward))
+    return out
+
+
+JAGGED_CASES = draw_jagged_cases(24, seed=2028)
+
+
+@pytest.mark.parametrize("case", JAGGED_CASES, ids=lambda c: "j{}-S{}-H{}-D{}-{}-msl{}{}{}".format(
+    c[0], len(c[1]), c[2], c[3], c[4], c[5], "-causal" if c[6] else "", "-bwd" if c[7] else ""))
+def test_random_jagged(gpu_lib, case):
+    """Jagged forward (and, for the backward cases, dQ, dK, dV from the
+    forward's own O and LSE) against the oracle."""
+    i, lengths, H, D, dtype, msl, causal, backward = case
+    lengths = torch.as_tensor(lengths, dtype=torch.int64)
+    q, k, v, off = wl.jagged_inputs(lengths, H, D, dtype, 900 + 10 * i)
+    scale = D ** -0.5
+    qc, kc, vc, oc = (t.cuda() for t in (q, k, v, off))
+    o, lse = attn.jagged_fwd(qc, kc, vc, oc, max_seq_len=msl, causal=causal, sm_scale=scale)
+    ro, rl = oracle.jagged_attention(q, k, v, off.numpy(), msl, oracle.scale_as_passed(scale), causal)
+    assert_close(DT[dtype], host64(o), host64(lse), ro, rl, label=f"random jagged case {case}")
+    if backward:
+        do = wl.grad_output(q.shape, dtype, 900 + 10 * i)
+        got = attn.jagged_bwd(qc, kc, vc, o, do.cuda(), lse, oc, msl, causal=causal, sm_scale=scale)
+        ref = oracle.jagged_attention_bwd(q, k, v, do, off.numpy(), msl, oracle.scale_as_passed(scale), causal)
+        check_grads(got, ref, f"random jagged backward case {case}", dtype)
+        # rows past max_seq_len inside a sequence get exactly zero gradients
+        offs = off.numpy()
+        for g in got:
+            g = host64(g)
+            for s_ in range(len(lengths)):
+                a, b = int(offs[s_]), int(offs[s_ + 1])
+                assert np.all(g[:, a + min(b - a, msl):b] == 0), f"rows past max_seq_len in case {case}"
