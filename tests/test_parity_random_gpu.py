@@ -1,5 +1,6 @@
-"""Seeded random sweeps of the dense forward and JVP, and of the backward,
-over the supported configuration space, each case against the fp64 oracle on
+"""Seeded random sweeps over the supported configuration space -- the dense
+forward and JVP, the backward, the jagged forward and backward, and the
+biased / masked forward and backward -- each case against the fp64 oracle on
 the same seeded inputs.
 
 The hand-picked cases elsewhere cover each edge on its own; this sweep draws
@@ -170,3 +171,41 @@ def test_random_jagged(gpu_lib, case):
             for s_ in range(len(lengths)):
                 a, b = int(offs[s_]), int(offs[s_ + 1])
                 assert np.all(g[:, a + min(b - a, msl):b] == 0), f"rows past max_seq_len in case {case}"
+
+
+def draw_bias_cases(n, seed):
+    """(case id, B, H, Nq, Nkv, D, dtype, causal, kind, operand shape,
+    backward): additive bias or boolean mask, each of the batch, head and
+    query dims of the operand either full or broadcast (1)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        backward = bool(rng.integers(0, 2))
+        kind = ["add", "mask"][int(rng.integers(0, 2))]
+        dtype = ["bf16", "fp16"][int(rng.integers(0, 2))] if backward else ["bf16", "fp16", "fp32"][int(rng.integers(0, 3))]
+        D = int(rng.choice([32, 64, 128]))
+        causal = bool(rng.integers(0, 2))
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        Nq = int(rng.integers(1, 400))
+        Nkv = Nq if causal else int(rng.integers(1, 400))
+        shape = tuple(d if rng.random() < 0.5 else 1 for d in (B, H, Nq)) + (Nkv,)
+        out.append((i, B, H, Nq, Nkv, D, dtype, causal, kind, shape, backward))
+    return out
+
+
+BIAS_CASES = draw_bias_cases(24, seed=2029)
+
+
+@pytest.mark.parametrize("case", BIAS_CASES, ids=lambda c: "x{}-B{}H{}-{}x{}-D{}-{}-{}-op{}{}{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[8], "x".join(map(str, c[9])), "-causal" if c[7] else "",
+    "-bwd" if c[10] else ""))
+def test_random_bias(gpu_lib, case):
+    """Biased or masked forward, or backward (with the bias gradient for an
+    additive bias), against the oracle."""
+    from test_parity_bias_gpu import bias_case
+    from test_parity_bias_bwd_gpu import bias_bwd_case
+    i, B, H, Nq, Nkv, D, dtype, causal, kind, shape, backward = case
+    if backward:
+        bias_bwd_case(B, H, Nq, Nkv, D, dtype, causal, kind, bshape=shape, seed=1100 + 10 * i)
+    else:
+        bias_case(B, H, Nq, Nkv, D, dtype, causal, kind, bshape=shape, seed=1100 + 10 * i)
