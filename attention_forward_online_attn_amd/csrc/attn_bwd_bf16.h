@@ -355,20 +355,28 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------- dK/dV kernel
-template <int D>
+template <int D, int BIAS = kNoBias>
 struct BwdDkdvCfg {
   static constexpr int NW = 4, THREADS = 256, BN = 128;  // keys per workgroup, 32 per wave
-  static constexpr int BMQ = 32;                         // query rows per streamed tile
-  static constexpr int TILE = BMQ * D * 2;               // one Q or dO tile
-  static constexpr int STAGE = 2 * TILE + 2 * BMQ * 4;   // Q, dO, then lse2 and delta of those rows
-  static constexpr int LDS = 2 * STAGE;
   static constexpr int WAVES_PER_EU = D == 128 ? 1 : 2;  // D=128 holds K, V, dK, dV: 1 wave per SIMD
+  // query rows per streamed tile: the one-wave D=128 kernel takes 64 (two
+  // independent 32-query blocks per step, half the steps and barriers)
+  static constexpr int BMQ = D == 128 && BIAS == kNoBias ? 64 : 32;
+  static constexpr int NBQ = BMQ / 32;                   // 32-query blocks per tile
+  static constexpr int TILE = BMQ * D * 2;               // one Q or dO tile
+  // LDS: the two Q stages, the two dO stages, then each stage's lse2 and
+  // delta rows (per 32-query block: 32 lse2 then 32 delta) -- grouped by
+  // tensor so that every fragment read's offset fits the 16-bit immediate
+  static constexpr int OFF_DO = 2 * TILE, OFF_ROWS = 4 * TILE, ROWS = NBQ * 256;
+  static constexpr int LDS = 4 * TILE + 2 * ROWS;
 };
 
 template <int D, bool F16 = false, int BIAS = kNoBias>
-__global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_dkdv_kernel(BwdArgs a) {
-  using C = BwdDkdvCfg<D>;
-  constexpr int BN = C::BN, BMQ = C::BMQ, TILE = C::TILE, STAGE = C::STAGE, NW = C::NW;
+__global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn_bwd_dkdv_kernel(BwdArgs a) {
+  using C = BwdDkdvCfg<D, BIAS>;
+  constexpr int BN = C::BN, BMQ = C::BMQ, NBQ = C::NBQ, TILE = C::TILE, NW = C::NW;
+  constexpr int OFF_DO = C::OFF_DO, OFF_ROWS = C::OFF_ROWS, ROWS = C::ROWS;
+  static_assert(BIAS == kNoBias || NBQ == 1, "bias operands are loaded per 32-query tile");
   constexpr int KD = D / 16, DB = D / 32;
   extern __shared__ __attribute__((aligned(256))) char smem_raw[];
   lds_t* smem = (lds_t*)smem_raw;
@@ -449,17 +457,17 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
     }
   };
 
-  // tile jq: Q and dO rows, then 32 lse2 and 32 delta values (4 bytes per
-  // lane of wave 0: lanes 0-31 lse2, lanes 32-63 delta)
+  // tile jq: Q and dO rows, then per 32-query block b 32 lse2 and 32 delta
+  // values (4 bytes per lane of wave b: lanes 0-31 lse2, lanes 32-63 delta)
   auto fetch = [&](int jq, int stage) {
     const int q0 = jq * BMQ;
-    lds_t* base = smem + stage * STAGE;
-    bwd_dma_rows<D, BMQ, NW>(Q, a.q_sn, q0, t.Lq, base, wave, lane);
-    bwd_dma_rows<D, BMQ, NW>(DO, a.do_sn, q0, t.Lq, base + TILE, wave, lane);
-    if (wave == 0) {
-      const int qi = min(q0 + n32, t.Lq - 1);
+    bwd_dma_rows<D, BMQ, NW>(Q, a.q_sn, q0, t.Lq, smem + stage * TILE, wave, lane);
+    bwd_dma_rows<D, BMQ, NW>(DO, a.do_sn, q0, t.Lq, smem + OFF_DO + stage * TILE, wave, lane);
+    if (wave < NBQ) {
+      const int qi = min(q0 + 32 * wave + n32, t.Lq - 1);
       const float* src = (h32 ? a.delta : a.lse2) + row_base + qi;
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(base + 2 * TILE),
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)(smem + OFF_ROWS + stage * ROWS + 256 * wave),
                                        4, 0, 0);
     }
   };
@@ -472,17 +480,19 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
     }
     const int q0 = jq * BMQ;
     if (wave_keys && q0 + BMQ > wave_q_first) {  // wave-uniform: some key of the wave sees some query
-      f32x16 s[1], dp[1];
-      scores_section<D, 1, false, S * STAGE, 0, F16>(qaddr, kf, dummy_t, s, dummy_ts);          // S = Q K^T
-      scores_section<D, 1, false, S * STAGE + TILE, 0, F16>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
+      f32x16 s[NBQ], dp[NBQ];
+      scores_section<D, NBQ, false, S * TILE, 0, F16>(qaddr, kf, dummy_t, s, dummy_ts);            // S = Q K^T
+      scores_section<D, NBQ, false, OFF_DO + S * TILE, 0, F16>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
       // masked pairs (query past Lq, key past Lkv; causal: key after query) get P = 0
       const bool edge = q0 + BMQ > t.Lq || k0 + 32 > t.Lkv || (a.causal && q0 < k0 + 32);
       if (edge) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = q0 + 16 * (r >> 3) + 8 * h32 + (r & 7);
-          if (qi >= t.Lq || my_key >= t.Lkv || (a.causal && my_key > qi)) s[0][r] = -INFINITY;
-        }
+        for (int b = 0; b < NBQ; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = q0 + 32 * b + 16 * (r >> 3) + 8 * h32 + (r & 7);
+            if (qi >= t.Lq || my_key >= t.Lkv || (a.causal && my_key > qi)) s[b][r] = -INFINITY;
+          }
       }
       if constexpr (BIAS == kAddBias) {
 #pragma unroll
@@ -493,32 +503,36 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D>::WAVES_PER_EU)) attn_bwd_d
         for (int r = 0; r < 16; ++r)
           if (bq[S][r] == 0u) s[0][r] = -INFINITY;
       }
-      // register r holds query q0 + 16 (r / 8) + 8 h32 + r % 8; chunk c (the
-      // 8 registers 8c..8c+7) needs the lse2 and delta of 8 consecutive queries
-      const lds_t* st = smem + S * STAGE + 2 * TILE;
-      bf16x8 pf[1][2], dsf[1][2];
+      // register r of block b holds query q0 + 32 b + 16 (r / 8) + 8 h32 + r % 8;
+      // chunk c (block c / 2, registers 8 (c % 2) .. + 7) needs the lse2 and
+      // delta of 8 consecutive queries
+      const lds_t* st = smem + OFF_ROWS + S * ROWS;
+      bf16x8 pf[NBQ][2], dsf[NBQ][2];
       auto chunk = [&](auto c_tag) {
-        constexpr int c = decltype(c_tag)::value;
-        constexpr int qo = 16 * c * 4;
+        constexpr int c = decltype(c_tag)::value, b = c / 2, h = c % 2;
+        constexpr int qo = 256 * b + 64 * h;
         const f32x4 a0 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 32 * h32);
         const f32x4 a1 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 32 * h32 + 16);
-        const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(st + BMQ * 4 + qo + 32 * h32);
-        const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(st + BMQ * 4 + qo + 32 * h32 + 16);
+        const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 128 + 32 * h32);
+        const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 128 + 32 * h32 + 16);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float l2 = e < 4 ? a0[e & 3] : a1[e & 3];
           const float dl = e < 4 ? d0[e & 3] : d1[e & 3];
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][8 * c + e], cs, -l2));
-          pf[0][c][e] = to16<F16>(p);
-          dsf[0][c][e] = to16<F16>(p * (dp[0][8 * c + e] - dl));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * h + e], cs, -l2));
+          pf[b][h][e] = to16<F16>(p);
+          dsf[b][h][e] = to16<F16>(p * (dp[b][8 * h + e] - dl));
         }
       };
       chunk(std::integral_constant<int, 0>{});
-      // dV^T += dO^T P and dK^T += Q^T dS (transposing reads of the dO and Q tiles)
-      pv_section<D, 1, false, S * STAGE + TILE, 0, F16>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b, [&](auto i_tag) {
-        if constexpr (decltype(i_tag)::value == 0) chunk(std::integral_constant<int, 1>{});  // after the first MFMA
+      // dV^T += dO^T P and dK^T += Q^T dS (transposing reads of the dO and Q
+      // tiles); chunk c + 1 is formed after the first MFMA that consumes chunk c
+      pv_section<D, NBQ, false, OFF_DO + S * TILE, 0, F16>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b,
+                                                          [&](auto i_tag) {
+        constexpr int i = decltype(i_tag)::value;
+        if constexpr (i % DB == 0 && i / DB + 1 < 2 * NBQ) chunk(std::integral_constant<int, i / DB + 1>{});
       });
-      pv_section<D, 1, false, S * STAGE, 0, F16>(lds_base, vlo, vhi, dsf, dummy_h, dk, dummy_a, dummy_b, [](auto) {});
+      pv_section<D, NBQ, false, S * TILE, 0, F16>(lds_base, vlo, vhi, dsf, dummy_h, dk, dummy_a, dummy_b, [](auto) {});
     }
     __syncthreads();
   };

@@ -23,7 +23,7 @@ template <int D, bool F16, int BIAS>
 int bwd_launch_grads(hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t items) {
   int rc = ATTN_OK;
   using Cq = BwdDqCfg<D, kBnBwdDq>;
-  using Ck = BwdDkdvCfg<D>;
+  using Ck = BwdDkdvCfg<D, BIAS>;
   static_assert(Cq::BM == 128 && Ck::BN == 128, "the jagged plan's tiles are 128 rows");
   a.n_tiles = (int)((Nq + Cq::BM - 1) / Cq::BM);
   const int64_t gq = a.offsets ? items * H : B * H * a.n_tiles;
