@@ -361,7 +361,7 @@ struct BwdDkdvCfg {
   static constexpr int WAVES_PER_EU = D == 128 ? 1 : 2;  // D=128 holds K, V, dK, dV: 1 wave per SIMD
   // query rows per streamed tile: the one-wave D=128 kernel takes 64 (two
   // independent 32-query blocks per step, half the steps and barriers)
-  static constexpr int BMQ = D == 128 && BIAS == kNoBias ? 64 : 32;
+  static constexpr int BMQ = D == 128 ? 64 : 32;
   static constexpr int NBQ = BMQ / 32;                   // 32-query blocks per tile
   static constexpr int TILE = BMQ * D * 2;               // one Q or dO tile
   // LDS: the two Q stages, the two dO stages, then each stage's lse2 and
@@ -376,7 +376,6 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
   using C = BwdDkdvCfg<D, BIAS>;
   constexpr int BN = C::BN, BMQ = C::BMQ, NBQ = C::NBQ, TILE = C::TILE, NW = C::NW;
   constexpr int OFF_DO = C::OFF_DO, OFF_ROWS = C::OFF_ROWS, ROWS = C::ROWS;
-  static_assert(BIAS == kNoBias || NBQ == 1, "bias operands are loaded per 32-query tile");
   constexpr int KD = D / 16, DB = D / 32;
   extern __shared__ __attribute__((aligned(256))) char smem_raw[];
   lds_t* smem = (lds_t*)smem_raw;
@@ -433,11 +432,12 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
   bf16x8 dummy_t[1];
   f32x16 dummy_ts[1];
 
-  // bias / mask for this lane's key and the 16 queries of its registers
-  // (register r: query q0 + 16 (r / 8) + 8 h32 + r % 8), element loads one
-  // query tile ahead; 32 lanes read 64 consecutive bytes of a bias row
+  // bias / mask for this lane's key and the 16 queries of each block's
+  // registers (register r of block b: query q0 + 32 b + 16 (r / 8) + 8 h32 +
+  // r % 8), element loads one query tile ahead; 32 lanes read 64 consecutive
+  // bytes of a bias row
   constexpr int BEL = BIAS == kAddBias ? 2 : 1;
-  unsigned bq[BIAS ? 2 : 1][BIAS ? 16 : 1];
+  unsigned bq[BIAS ? 2 : 1][BIAS ? 16 * NBQ : 1];  // register r of block b at 16 b + r
   const char* bcol = nullptr;
   if constexpr (BIAS != kNoBias) {
     const int kc = my_key < t.Lkv ? my_key : t.Lkv - 1;
@@ -448,8 +448,8 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
     if constexpr (BIAS != kNoBias) {
       constexpr int SL = decltype(slot_tag)::value;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = min(jq * BMQ + 16 * (r >> 3) + 8 * h32 + (r & 7), t.Lq - 1);
+      for (int r = 0; r < 16 * NBQ; ++r) {
+        const int qi = min(jq * BMQ + 32 * (r >> 4) + 16 * ((r >> 3) & 1) + 8 * h32 + (r & 7), t.Lq - 1);
         const char* src = bcol + (int64_t)qi * a.bias_sn * BEL;
         if constexpr (BIAS == kAddBias) bq[SL][r] = *(const unsigned short*)src;
         else bq[SL][r] = *(const unsigned char*)src;
@@ -496,12 +496,17 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
       }
       if constexpr (BIAS == kAddBias) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[0][r] = __builtin_fmaf(s[0][r], a.c, from16<F16>(__builtin_bit_cast(bf16, (unsigned short)bq[S][r])) * kLog2e);
+        for (int b = 0; b < NBQ; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[b][r] = __builtin_fmaf(s[b][r], a.c,
+                                     from16<F16>(__builtin_bit_cast(bf16, (unsigned short)bq[S][16 * b + r])) * kLog2e);
       } else if constexpr (BIAS == kMaskBias) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (bq[S][r] == 0u) s[0][r] = -INFINITY;
+        for (int b = 0; b < NBQ; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (bq[S][16 * b + r] == 0u) s[b][r] = -INFINITY;
       }
       // register r of block b holds query q0 + 32 b + 16 (r / 8) + 8 h32 + r % 8;
       // chunk c (block c / 2, registers 8 (c % 2) .. + 7) needs the lse2 and
