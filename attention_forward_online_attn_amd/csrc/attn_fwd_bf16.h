@@ -405,7 +405,6 @@ struct Bf16Cfg {
   static constexpr int NTEN = JVP ? 4 : 2;  // tensors streamed per key tile
   static constexpr int STAGE = (JVP ? 2 : 1) * (TILE_K + TILE_V);  // bytes of one pipeline stage
   static constexpr bool WIDE = (JVP && (DQK == 128 || DV == 128)) || DQK == 256;  // one wave per SIMD
-  static constexpr bool DMA = !(JVP && WIDE);  // direct global -> LDS tile loads
   // floats per lane handed from group 1 to group 0 at the merge: m, l (r),
   // the O accumulator (and accA, accB)
   static constexpr int NVM = (JVP ? 3 : 2) + (DVL / 32) * 16 * (JVP ? 3 : 1);
@@ -413,17 +412,12 @@ struct Bf16Cfg {
   static constexpr int LDS = SPLIT ? (4 * STAGE > NVM * 1024 ? 4 * STAGE : NVM * 1024) : 2 * STAGE;
   static constexpr int CPR_K = DQK / 8, CPR_V = DVL / 8;  // 16-byte chunks per row (in LDS)
   static constexpr int CPR_VS = DV / 8;                   // of those, chunks that hold data
-  static constexpr int LOADS_K = (BN * CPR_K + THREADS - 1) / THREADS;
-  static constexpr int LOADS_V = (BN * CPR_V + THREADS - 1) / THREADS;
   static constexpr int WAVES_PER_EU = WIDE ? 1 : 2;
-  static_assert((BN * CPR_K) % THREADS == 0 || BN * CPR_K < THREADS, "tile must split evenly over the workgroup");
-  static_assert((BN * CPR_V) % THREADS == 0 || BN * CPR_V < THREADS, "tile must split evenly over the workgroup");
   static_assert(BN % 32 == 0, "unsupported tile");
   static_assert(DQK == 16 || DQK == 32 || DQK == 64 || DQK == 128 || (DQK == 256 && DV == 256 && !JVP),
                 "unsupported head dim");
   static_assert(DV == 16 || DV == 32 || DV == 64 || DV == 128 || DV == 256, "unsupported head dim");
-  static_assert(DV >= 32 || !(JVP && WIDE), "a 16-wide value tile needs the DMA path");
-  static_assert(NW == 4 || (NW == 8 && DMA && DV == DVL), "8 waves: key-split workgroups with DMA tiles");
+  static_assert(NW == 4 || (NW == 8 && DV == DVL), "8 waves: key-split workgroups of full-width value tiles");
 };
 
 template <int D, int BN, bool JVP, int NW_ = 4, bool F16 = false, int BIAS = kNoBias, int DV_ = 0>
@@ -433,7 +427,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int DQK = C::DQK, DV = C::DV, DVL = C::DVL, CPR_VS = C::CPR_VS;
   constexpr int BM = C::BM, NTEN = C::NTEN, STAGE = C::STAGE, TILE_K = C::TILE_K, TILE_V = C::TILE_V;
   constexpr int OFF_V = C::OFF_V, OFF_TK = C::OFF_TK, OFF_TV = C::OFF_TV;
-  constexpr int CPR_K = C::CPR_K, CPR_V = C::CPR_V, LOADS_K = C::LOADS_K, LOADS_V = C::LOADS_V;
+  constexpr int CPR_K = C::CPR_K, CPR_V = C::CPR_V;
   constexpr int THREADS = C::THREADS, NW = C::NW;
   constexpr bool SPLIT = C::SPLIT;
   constexpr int NWD = SPLIT ? 4 : NW;              // waves that fill one tile (a group's)
@@ -466,80 +460,6 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   const bf16* TK = JVP ? (const bf16*)a.tk + t.k_off : nullptr;
   const bf16* TV = JVP ? (const bf16*)a.tv + t.v_off : nullptr;
 
-  // ---- global -> register staging of one key tile, register -> LDS stores.
-  // Thread `tid` moves chunks id = tid + 256 it of each tensor (row id / CPR,
-  // 16-byte chunk id % CPR; CPR of the K side or of the V side).  Full tiles
-  // use a uniform tile base plus loop-invariant 32-bit byte offsets; only a
-  // ragged last tile clamps rows to the last valid key (those rows are masked).
-  uint32_t goff_k[LOADS_K], goff_v[LOADS_V];
-  int lds_k[LOADS_K], lds_v[LOADS_V];
-#pragma unroll
-  for (int it = 0; it < LOADS_K; ++it) {
-    const int id = tid + THREADS * it;
-    const int row = id / CPR_K, ch = id % CPR_K;
-    goff_k[it] = (uint32_t)((row * a.k_sn + ch * 8) * 2);
-    lds_k[it] = swz_off<DQK>(row, ch);
-  }
-#pragma unroll
-  for (int it = 0; it < LOADS_V; ++it) {
-    const int id = tid + THREADS * it;
-    const int row = id / CPR_V, ch = id % CPR_V;
-    goff_v[it] = (uint32_t)((row * a.v_sn + ch * 8) * 2);
-    lds_v[it] = swz_off<DVL>(row, ch);
-  }
-  const bool stager_k = BN * CPR_K >= THREADS || tid < BN * CPR_K;  // threads that move tile chunks
-  const bool stager_v = BN * CPR_V >= THREADS || tid < BN * CPR_V;
-  u32x4 stg_k[JVP ? 2 : 1][LOADS_K], stg_v[JVP ? 2 : 1][LOADS_V];
-  constexpr int LOADS_M = LOADS_K > LOADS_V ? LOADS_K : LOADS_V;
-  auto load_tile = [&](int j) {
-    const int64_t k0 = (int64_t)j * BN;
-    const char* kb = (const char*)K + k0 * a.k_sn * 2;
-    const char* vb = (const char*)V + k0 * a.v_sn * 2;
-    const char* tkb = JVP ? (const char*)TK + k0 * a.k_sn * 2 : nullptr;
-    const char* tvb = JVP ? (const char*)TV + k0 * a.v_sn * 2 : nullptr;
-    if (k0 + BN <= t.Lkv) {
-#pragma unroll
-      for (int it = 0; it < LOADS_M; ++it) {
-        const bool lk = it < LOADS_K && stager_k, lv = it < LOADS_V && stager_v;
-        if (lk) stg_k[0][it % LOADS_K] = *(const u32x4*)(kb + goff_k[it % LOADS_K]);
-        if (lv) stg_v[0][it % LOADS_V] = *(const u32x4*)(vb + goff_v[it % LOADS_V]);
-        if constexpr (JVP) {
-          if (lk) stg_k[1][it % LOADS_K] = *(const u32x4*)(tkb + goff_k[it % LOADS_K]);
-          if (lv) stg_v[1][it % LOADS_V] = *(const u32x4*)(tvb + goff_v[it % LOADS_V]);
-        }
-      }
-    } else {
-      const int last = t.Lkv - 1 - (int)k0;  // last valid row of this tile
-#pragma unroll
-      for (int it = 0; it < LOADS_M; ++it) {
-        const int id = tid + THREADS * it;
-        const bool lk = it < LOADS_K && stager_k, lv = it < LOADS_V && stager_v;
-        const int row_k = min(id / CPR_K, last), row_v = min(id / CPR_V, last);
-        const uint32_t ok = (uint32_t)((row_k * a.k_sn + (id % CPR_K) * 8) * 2);
-        const uint32_t ov = (uint32_t)((row_v * a.v_sn + (id % CPR_V) * 8) * 2);
-        if (lk) stg_k[0][it % LOADS_K] = *(const u32x4*)(kb + ok);
-        if (lv) stg_v[0][it % LOADS_V] = *(const u32x4*)(vb + ov);
-        if constexpr (JVP) {
-          if (lk) stg_k[1][it % LOADS_K] = *(const u32x4*)(tkb + ok);
-          if (lv) stg_v[1][it % LOADS_V] = *(const u32x4*)(tvb + ov);
-        }
-      }
-    }
-  };
-  auto store_tile = [&](lds_t* base) {
-    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-#pragma unroll
-    for (int it = 0; it < LOADS_M; ++it) {
-      const bool lk = it < LOADS_K && stager_k, lv = it < LOADS_V && stager_v;
-      if (lk) *(lds_u32x4*)(base + lds_k[it % LOADS_K]) = stg_k[0][it % LOADS_K];
-      if (lv) *(lds_u32x4*)(base + OFF_V + lds_v[it % LOADS_V]) = stg_v[0][it % LOADS_V];
-      if constexpr (JVP) {
-        if (lk) *(lds_u32x4*)(base + OFF_TK + lds_k[it % LOADS_K]) = stg_k[1][it % LOADS_K];
-        if (lv) *(lds_u32x4*)(base + OFF_TV + lds_v[it % LOADS_V]) = stg_v[1][it % LOADS_V];
-      }
-    }
-  };
-
   // Direct global -> LDS tile loads (global_load_lds_dwordx4): instruction i
   // of this wave fills the 1 KiB block NWD * i + wd of a tile (RPB rows; the
   // NWD waves of a group fill that group's tiles, wd is the wave's index in
@@ -550,27 +470,23 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   // swizzle depends on the row modulo 16 only: one per-lane byte offset
   // serves every instruction, which adds a uniform i * RSTEP rows.  No
   // registers or ds_write instructions are spent on staging.
-  // The D=128 JVP instance (1 wave per SIMD, which spills) keeps register
-  // staging: with DMA it produced wrong scores on ragged last tiles in the
-  // parity suite, a cause not isolated.
   // K-side tensors (K, tK) and V-side tensors (V, tV) each have their own
   // row width, hence their own block mapping; with equal head dims the two
   // coincide and the instructions interleave as K, V, tK, tV.
-  constexpr bool DMA = C::DMA;
   constexpr int NBLK_K = TILE_K / 1024, NBLK_V = TILE_V / 1024;  // 1 KiB blocks per tile
   constexpr int NI_K = NBLK_K >= NWD ? NBLK_K / NWD : 1;          // DMA instructions per wave per tensor
   constexpr int NI_V = NBLK_V >= NWD ? NBLK_V / NWD : 1;
   constexpr int NIM = NI_K > NI_V ? NI_K : NI_V;
   constexpr int RPB_K = 1024 / (2 * DQK), RPB_V = 1024 / (2 * DVL);  // rows per block
   constexpr int RSTEP_K = NWD * RPB_K, RSTEP_V = NWD * RPB_V;       // rows between a wave's blocks
-  static_assert(!DMA || ((NBLK_K % NWD == 0 || NBLK_K < NWD) && (NBLK_V % NWD == 0 || NBLK_V < NWD)),
+  static_assert((NBLK_K % NWD == 0 || NBLK_K < NWD) && (NBLK_V % NWD == 0 || NBLK_V < NWD),
                 "DMA tiles are whole 1 KiB blocks per wave");
   // The swizzle depends on the row modulo 16.  When a wave's blocks lie a
   // multiple of 16 rows apart one per-lane offset serves every instruction;
   // with fewer rows per block (D = 256: 2 rows, blocks 8 rows apart) the
   // swizzle of instruction i repeats with period NPH = 16 / RSTEP, and each
   // phase has its own per-lane offset.
-  static_assert(!DMA || ((NI_K == 1 || RSTEP_K % 16 == 0 || 16 % RSTEP_K == 0) &&
+  static_assert(((NI_K == 1 || RSTEP_K % 16 == 0 || 16 % RSTEP_K == 0) &&
                          (NI_V == 1 || RSTEP_V % 16 == 0 || 16 % RSTEP_V == 0)),
                 "per-lane swizzle must repeat with the block step");
   constexpr int NPH_K = (NI_K == 1 || RSTEP_K % 16 == 0) ? 1 : 16 / RSTEP_K;
@@ -735,8 +651,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       const bool ahead = j + 1 < n_mine;
       if (ahead) {  // in flight while this tile computes
         bias_load(jt + 1, std::integral_constant<int, SN>{});
-        if constexpr (DMA) dma_tile(jt + 1, smem_g + SN * SSTR);
-        else load_tile(jt + 1);
+        dma_tile(jt + 1, smem_g + SN * SSTR);
       }
 
       if (j < n_mine && jt * BN < wave_max) {  // wave-uniform: skip tiles this wave cannot see
@@ -836,7 +751,6 @@ attn_fwd_bf16_kernel(FwdArgs a) {
             });
       }
 
-      if (!DMA && ahead) store_tile(smem_g + SN * SSTR);
       __syncthreads();
     };
 
@@ -857,12 +771,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 
     if (n0 > 0) {
       bias_load(0, std::integral_constant<int, 0>{});
-      if constexpr (DMA) {
-        if (n_mine > 0) dma_tile(jbase, smem_g);
-      } else {
-        load_tile(0);
-        store_tile(smem);
-      }
+      if (n_mine > 0) dma_tile(jbase, smem_g);
       __syncthreads();
       int j = 0;
       for (; j + 2 <= n0; j += 2) {
