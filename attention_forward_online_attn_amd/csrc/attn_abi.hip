@@ -134,8 +134,8 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   int rc = check_common(dtype, D, sm_scale, bias.kind == kNoBias, plain);
   if (rc) return rc;
   if (Dv == 0) Dv = D;
-  // a 16-wide value tile: unbiased, and not with the one-wave 128-wide JVP
-  const bool v16 = Dv == 16 && bias.kind == kNoBias && !(jvp && D == 128 && dtype != ATTN_FP32);
+  // a 16-wide value tile: unbiased
+  const bool v16 = Dv == 16 && bias.kind == kNoBias;
   if (Dv != 32 && Dv != 64 && Dv != 128 && !(Dv == 256 && D == 256) && !v16)
     return Dv < 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;

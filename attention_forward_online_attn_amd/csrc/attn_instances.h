@@ -39,13 +39,9 @@ KernelChoice choose_mixed16(int D, int Dv, bool jvp) {
   return by_dim_qk(D, [&](auto dq) {
     return by_dim_qk(Dv, [&](auto dv) {
       constexpr int A = decltype(dq)::value, V = decltype(dv)::value;
-      // equal dims other than 16 take choose16 (no instance twice in the library);
-      // a 16-wide value tile with a 128-wide query/key side (a one-wave JVP
-      // with register staging) is not built
+      // equal dims other than 16 take choose16 (no instance twice in the library)
       if constexpr (A == V && A != 16) {
         return KernelChoice{};
-      } else if constexpr (V == 16 && A == 128) {
-        return jvp ? KernelChoice{} : r32<A, kBnDense, false, 4, F16, kNoBias, V>();
       } else {
         return jvp ? r32<A, kBnJvp, true, 4, F16, kNoBias, V>() : r32<A, kBnDense, false, 4, F16, kNoBias, V>();
       }

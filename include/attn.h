@@ -29,8 +29,8 @@
  * - Tangent tensors (JVP) share the strides of their primals, and tO shares
  *   the strides of O (as the JVP page's wrapper requires).
  * - Supported head dims: 32, 64 and 128 everywhere; 16 on the unbiased
- *   forward and JVP (dense and jagged, and either side of attn_fwd_dv, except
- *   a 16-bit JVP with Dqk = 128 and Dv = 16); 256 for the plain forward
+ *   forward and JVP (dense and jagged, and either side of attn_fwd_dv); 256
+ *   for the plain forward
  *   (attn_fwd, jagged_attn_fwd, attn_fwd_dv with Dqk = Dv = 256).  dtype ATTN_BF16 (ATTN_FP16) computes
  *   the products on bf16 (fp16) MFMA with fp32 accumulation and rounds O/tO to
  *   the input format (RNE); ATTN_FP32 computes everything in fp32.  LSE is
@@ -173,8 +173,8 @@ ATTN_API int attn_fwd_jvp(attn_dtype dtype,
  *   o, to [B, H, Nq, Dv]    lse, tlse [B, H, Nq]
  * tq == NULL: the plain forward of attn_fwd (tk, tv, to and tlse must be
  * NULL too); otherwise the fused JVP of attn_fwd_jvp (tlse optional).
- * Dqk and Dv each in {32, 64, 128}; with Dqk == Dv this is exactly attn_fwd /
- * attn_fwd_jvp.  sm_scale is the caller's (the page's default is
+ * Dqk and Dv each in {16, 32, 64, 128}, or both 256 on the plain forward;
+ * with Dqk == Dv this is exactly attn_fwd / attn_fwd_jvp.  sm_scale is the caller's (the page's default is
  * Dqk^-0.5).  Other arguments, checks and errors as attn_fwd_jvp.
  */
 ATTN_API int attn_fwd_dv(attn_dtype dtype,
