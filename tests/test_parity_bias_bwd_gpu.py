@@ -103,3 +103,25 @@ def test_bias_bwd_empty_rows_and_zero_scale(gpu_lib):
 
 def test_bias_bwd_without_dbias(gpu_lib):
     bias_bwd_case(2, 2, 300, 300, 128, "bf16", True, "add", seed=118, dbias=False)
+
+
+def test_bias_bwd_full_size_sampled_heads(gpu_lib):
+    """The benchmark's biased backward: B=4 H=32 N=4096 D=128 with a per-head
+    bias [1, 32, 4096, 4096] shared by the batch (batch-inner work order,
+    64-query dK/dV tiles), gradients and the bias gradient dS checked on whole
+    sampled (batch, head) slices against the oracle."""
+    B, H, N, D = 4, 32, 4096, 128
+    q, k, v = wl.dense_inputs(B, H, N, N, D, "bf16", 0)
+    do = wl.grad_output((B, H, N, D), "bf16", 0)
+    bias = wl.score_bias((1, H, N, N), "bf16", 0)
+    qc, kc, vc, doc, bc = (t.cuda() for t in (q, k, v, do, bias))
+    o, lse = attn.fwd_bias(qc, kc, vc, bias=bc)
+    dq, dk, dv, db = attn.bwd_bias(qc, kc, vc, o, doc, lse, bias=bc, return_dbias=True)
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for b, h in ((0, 5), (3, 30)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.attention_bwd(q[sl], k[sl], v[sl], do[sl], oracle.scale_as_passed(D ** -0.5),
+                                   bias=bias[:, h:h + 1], with_dbias=True)
+        got_db = db[b:b + 1, h:h + 1].cpu()
+        check([dq[sl], dk[sl], dv[sl], got_db], list(ref[:3]) + [ref[3]], ["dq", "dk", "dv", "dbias"], "bf16",
+              f"bias bwd [4,32,4096,128] operand [1,32,4096,4096] slice (b={b}, h={h})")

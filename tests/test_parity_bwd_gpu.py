@@ -139,3 +139,22 @@ def test_bwd_fp16(gpu_lib, D, causal):
 def test_bwd_fp16_odd_shapes(gpu_lib):
     bwd_case(1, 2, 1, 1, 64, True, seed=10, dtype="fp16")
     bwd_case(1, 2, 100, 333, 128, False, seed=11, dtype="fp16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_full_size_sampled_heads(gpu_lib, causal):
+    """The benchmark's backward, B=4 H=32 N=4096 D=128 (4096 workgroups per
+    gradient kernel, XCD-aware order), checked on whole (batch, head) slices:
+    heads are independent, so the oracle computes the gradients of a few
+    sampled slices exactly."""
+    B, H, N, D = 4, 32, 4096, 128
+    q, k, v = wl.dense_inputs(B, H, N, N, D, "bf16", 0)
+    do = wl.grad_output((B, H, N, D), "bf16", 0)
+    qc, kc, vc, doc = (t.cuda() for t in (q, k, v, do))
+    o, lse = attn.fwd(qc, kc, vc, causal=causal)
+    dq, dk, dv = (g.cpu() for g in attn.bwd(qc, kc, vc, o, doc, lse, causal=causal))
+    del qc, kc, vc, doc, o, lse
+    for b, h in ((0, 0), (3, 31), (1, 17)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.attention_bwd(q[sl], k[sl], v[sl], do[sl], oracle.scale_as_passed(D ** -0.5), causal)
+        check_grads((dq[sl], dk[sl], dv[sl]), ref, f"bwd [4,32,4096,128] causal={causal} slice (b={b}, h={h})")
