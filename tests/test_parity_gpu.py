@@ -66,17 +66,19 @@ def test_causal_d64_full(gpu_lib):
     dense_case(w.B, w.H, w.N, w.N, w.D, "bf16", True, label="causal bf16 [4,16,1024,64]")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_long_d128_sampled(gpu_lib, causal):
+def test_long_d128_sampled(gpu_lib, causal, dtype):
     w = wl.WORKLOADS["long_d128"]
-    q, k, v = wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "bf16", 0)
+    q, k, v = wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, dtype, 0)
     o, lse = attn.fwd(*cuda(q, k, v), causal=causal, sm_scale=w.sm_scale)
     rows = sampled_rows(w.B, w.H, w.N, 160)
     ro, rl = oracle.attention_sampled(q, k, v, oracle.scale_as_passed(w.sm_scale), causal, rows)
     oc, lc = host64(o), host64(lse)
     go = np.stack([oc[b, h, i] for b, h, i in rows])
     gl = np.array([lc[b, h, i] for b, h, i in rows])
-    assert_close(BF16, go, gl, ro, rl, label=f"long bf16 [4,32,4096,128] causal={causal}, {len(rows)} sampled rows")
+    assert_close(DT[dtype], go, gl, ro, rl,
+                 label=f"long {dtype} [4,32,4096,128] causal={causal}, {len(rows)} sampled rows")
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 

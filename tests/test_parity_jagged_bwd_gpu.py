@@ -65,3 +65,35 @@ def test_jagged_bwd_many_sequences(gpu_lib):
     lengths = wl.jagged_lengths(64, 300, seed_base=83)
     jagged_bwd_case(lengths.tolist(), 2, 128, "bf16", 200, False, seed=83)
     jagged_bwd_case(lengths.tolist(), 2, 64, "bf16", 300, True, seed=84)
+
+
+def test_jagged_bwd_full_size_sampled_sequences(gpu_lib):
+    """The benchmark's jagged backward (256 sequences of 1..1024 rows, H=8,
+    D=128), whole sampled sequences against the oracle: sequences are
+    independent, so the oracle runs on the sampled ones alone."""
+    w = wl.WORKLOADS["jagged_d128"]
+    lengths = wl.jagged_lengths(w.num_seqs, w.max_len, 0)
+    q, k, v, off = wl.jagged_inputs(lengths, w.H, w.D, "bf16", 0)
+    do = wl.grad_output(q.shape, "bf16", 0)
+    qc, kc, vc, oc_, doc = (t.cuda() for t in (q, k, v, off, do))
+    o, lse = attn.jagged_fwd(qc, kc, vc, oc_, max_seq_len=w.max_len, sm_scale=w.sm_scale)
+    grads = [host64(g) for g in attn.jagged_bwd(qc, kc, vc, o, doc, lse, oc_, w.max_len, sm_scale=w.sm_scale)]
+    L = lengths.numpy()
+    seqs = sorted(set([int(np.argmax(L)), int(np.argmin(L)), 0, len(L) - 1]) |
+                  set(int(x) for x in np.random.default_rng(2).integers(0, len(L), 12)))
+    offs = off.numpy()
+    parts = [slice(offs[s], offs[s + 1]) for s in seqs]
+    sub = lambda x: np.concatenate([host64(x)[:, p] for p in parts], axis=1)
+    sub_off = np.concatenate([[0], np.cumsum([L[s] for s in seqs])])
+    ref = oracle.jagged_attention_bwd(sub(q), sub(k), sub(v), sub(do), sub_off, w.max_len,
+                                      oracle.scale_as_passed(w.sm_scale))
+    msgs, ok = [], True
+    for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
+        g = np.concatenate([g[:, p] for p in parts], axis=1)
+        gmax = float(np.max(np.abs(r)))
+        diff = float(np.max(np.abs(g - r))) if np.all(np.isfinite(g)) else np.inf
+        ok = ok and diff <= REL["bf16"] * gmax + ABS
+        msgs.append(f"{name} {diff / gmax:.2e}")
+    msg = f"jagged bwd H=8 D=128, {len(seqs)} of 256 sequences: max|dg|/max|g| " + ", ".join(msgs)
+    print(msg, flush=True)
+    assert ok, msg
