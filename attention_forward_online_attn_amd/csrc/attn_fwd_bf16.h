@@ -33,12 +33,16 @@
 //   of a row is exp2(0) = 1, which the 16-bit P holds exactly, and a bias
 //   makes rows peaked enough that the rounding of that one term would
 //   otherwise show in O.
-// * Per key tile: the next tile's global loads are issued first and stay in
-//   flight through the tile's two MFMA sections (scores, then PV), whose LDS
-//   fragment reads run a fixed distance ahead of their MFMAs; the prefetched
-//   tile is stored to the other LDS stage and one barrier ends the tile.
-//   Two workgroups share each CU (two waves per SIMD), so one wave's softmax
-//   overlaps the other's MFMAs.
+// * Per key tile: the next tile is copied straight from global memory into
+//   the other LDS stage (global_load_lds_dwordx4, no staging registers); the
+//   copies stay in flight through the tile's two MFMA sections (scores, then
+//   PV), whose LDS fragment reads run a fixed distance ahead of their MFMAs,
+//   and one barrier ends the tile.  Two workgroups share each CU (two waves
+//   per SIMD), so one wave's softmax overlaps the other's MFMAs.
+// * Small causal grids use 8-wave workgroups: two 4-wave groups take the same
+//   query tile, split its key range in halves (each streaming its own tiles
+//   into its own LDS stages) and merge their partial (m, l, O) through LDS;
+//   such a workgroup takes q-tiles p and n-1-p of a head in turn.
 #pragma once
 
 #include <type_traits>
