@@ -131,11 +131,10 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
           float* tlse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal,
           void* stream, bool jvp, const BiasOperand& bias = BiasOperand(), int64_t Dv = 0) {
   const bool plain = !jvp && bias.kind == kNoBias && (Dv == 0 || Dv == D);
-  int rc = check_common(dtype, D, sm_scale, bias.kind == kNoBias, plain);
+  int rc = check_common(dtype, D, sm_scale, true, plain);
   if (rc) return rc;
   if (Dv == 0) Dv = D;
-  // a 16-wide value tile: unbiased
-  const bool v16 = Dv == 16 && bias.kind == kNoBias;
+  const bool v16 = Dv == 16;  // a 16-wide value tile (laid out 32 wide in LDS)
   if (Dv != 32 && Dv != 64 && Dv != 128 && !(Dv == 256 && D == 256) && !v16)
     return Dv < 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;

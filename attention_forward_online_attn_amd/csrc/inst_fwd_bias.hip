@@ -7,7 +7,7 @@ namespace attn {
 namespace {
 template <int BIAS>
 KernelChoice pick(int dtype, int D) {
-  return by_dim(D, [&](auto d) {
+  return by_dim_qk(D, [&](auto d) {
     constexpr int Dc = decltype(d)::value;
     if (dtype == ATTN_BF16) return r32<Dc, kBnDense, false, 4, false, BIAS>();
     if (dtype == ATTN_FP16) return r32<Dc, kBnDense, false, 4, true, BIAS>();

@@ -30,3 +30,17 @@ def test_value_dim_16(gpu_lib, Dqk, dtype):
     dv_case(2, 2, 300, 300, Dqk, 16, dtype, False, False, seed=134)
     dv_case(1, 2, 200, 200, Dqk, 16, dtype, True, False, seed=135)
     dv_case(1, 2, 200, 200, Dqk, 16, dtype, True, True, seed=136)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d16_bias_and_mask(gpu_lib, dtype, causal):
+    """Head dim 16 on the biased forward: additive bias and boolean mask,
+    full-shape and broadcast operands, ragged tiles."""
+    from test_parity_bias_gpu import bias_case
+    bias_case(2, 3, 300, 300, 16, dtype, causal, "add", seed=137)
+    bias_case(2, 3, 300, 300, 16, dtype, causal, "mask", seed=138)
+    bias_case(2, 2, 200, 200, 16, dtype, causal, "add", bshape=(1, 2, 200, 200), seed=139)
+    if not causal:
+        bias_case(1, 2, 77, 333, 16, dtype, False, "mask", seed=140, keep=0.3)
+
