@@ -53,6 +53,7 @@ KernelChoice fwd_bias(int dtype, int kind, int D);              // inst_fwd_bias
 KernelChoice fwd_mixed_bf16(int D, int Dv, bool jvp);           // inst_fwd_mixed_bf16.hip
 KernelChoice fwd_mixed_fp16(int D, int Dv, bool jvp);           // inst_fwd_mixed_fp16.hip
 KernelChoice fwd_d256(int dtype);                               // inst_fwd_d256.hip (plain forward)
+KernelChoice fwd_d256_bias(int dtype, int kind);                // inst_fwd_d256.hip (bias or mask)
 
 // Backward: enqueues the prep, dQ and dK/dV kernels (inst_bwd.hip).  Dense:
 // B*H*Nq rows, grids over (batch, head, tile).  Jagged (a.offsets set): the

@@ -30,8 +30,8 @@
  *   the strides of O (as the JVP page's wrapper requires).
  * - Supported head dims: 32, 64 and 128 everywhere; 16 on the forward
  *   (plain, biased, jagged, either side of attn_fwd_dv) and the JVP, not the
- *   backward; 256 for the plain forward
- *   (attn_fwd, jagged_attn_fwd, attn_fwd_dv with Dqk = Dv = 256).  dtype ATTN_BF16 (ATTN_FP16) computes
+ *   backward; 256 on the forward without tangents (attn_fwd, attn_fwd_bias,
+ *   jagged_attn_fwd, attn_fwd_dv with Dqk = Dv = 256).  dtype ATTN_BF16 (ATTN_FP16) computes
  *   the products on bf16 (fp16) MFMA with fp32 accumulation and rounds O/tO to
  *   the input format (RNE); ATTN_FP32 computes everything in fp32.  LSE is
  *   always fp32.

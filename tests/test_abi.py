@@ -264,16 +264,15 @@ def test_bwd_bias_validation(lib):
 
 
 def test_d256_only_for_the_plain_forward(lib):
-    """Head dim 256 runs the plain forward; the 16-bit JVP, bias and backward
-    kernels at 256 are not built."""
+    """Head dim 256 runs the forward (biased or not); the 16-bit JVP and the
+    backward kernels at 256 are not built."""
     B, H, N, D = 0, 2, 128, 256  # B = 0: nothing is enqueued when the call is accepted
     st = dense_strides(1, H, N, D)
     assert call_fwd(lib, D=256, B=0) == OK
     assert lib.attn_fwd_jvp(BF16, P, P, P, P, P, P, st, st, st, P, P, st, P, None, 1, H, N, N, D, 0.1, 0, None) \
         == UNSUPPORTED
     full = Strides4(H * N * N, N * N, N, 1)
-    assert lib.attn_fwd_bias(BF16, P, st, P, st, P, st, P, st, P, P, 1, full, 1, H, N, N, D, 0.1, 0, None) \
-        == UNSUPPORTED
+    assert lib.attn_fwd_bias(BF16, P, st, P, st, P, st, P, st, P, P, 1, full, 0, H, N, N, D, 0.1, 0, None) == OK
     need = lib.attn_bwd_workspace_bytes(1, H, N)
     assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st, 1, H, N, N, D, 0.1, 0,
                         P, need, None) == UNSUPPORTED

@@ -180,7 +180,7 @@ def draw_bias_cases(n, seed):
         backward = bool(rng.integers(0, 2))
         kind = ["add", "mask"][int(rng.integers(0, 2))]
         dtype = ["bf16", "fp16"][int(rng.integers(0, 2))] if backward else ["bf16", "fp16", "fp32"][int(rng.integers(0, 3))]
-        D = int(rng.choice([32, 64, 128] if backward else [16, 32, 64, 128]))
+        D = int(rng.choice([32, 64, 128] if backward else [16, 32, 64, 128, 256]))
         causal = bool(rng.integers(0, 2))
         B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
         Nq = int(rng.integers(1, 400))
