@@ -140,11 +140,13 @@ __device__ __forceinline__ BwdTile bwd_tile(const BwdArgs& a, int bid, bool stor
   return t;
 }
 
-// Direct global -> LDS copy of ROWS rows of D bf16 (row stride sn elements)
-// into the swizzled tile at byte `dst` of LDS: instruction i of wave w fills
-// 1 KiB block NW i + w, lane l the 16 bytes at l * 16; rows at or past
-// `valid` re-read the last valid row (their results are masked or dropped).
-template <int D, int ROWS, int NW>
+// Direct global -> LDS copy of ROWS rows of DA bf16 (row stride sn elements)
+// into the swizzled tile of D-element rows (D >= DA) at byte `dst` of LDS:
+// instruction i of wave w fills 1 KiB block NW i + w, lane l the 16 bytes at
+// l * 16; rows at or past `valid` re-read the last valid row (their results
+// are masked or dropped).  With DA < D the lanes whose chunk is padding stay
+// inactive: bwd_zero_pad clears those chunks once.
+template <int D, int ROWS, int NW, int DA = D>
 __device__ __forceinline__ void bwd_dma_rows(const bf16* base, int64_t sn, int row0, int valid, lds_t* dst, int wave,
                                              int lane) {
   constexpr int TILE = ROWS * D * 2, NBLK = TILE / 1024, NI = NBLK >= NW ? NBLK / NW : 1;
@@ -157,6 +159,7 @@ __device__ __forceinline__ void bwd_dma_rows(const bf16* base, int64_t sn, int r
     const int blk = NW * i + wave;
     const int r = RPB * blk + (lane * 16) / (2 * D);
     const int ch = (lane % (D / 8)) ^ swz_f<D>(r);
+    if (DA < D && ch >= DA / 8) continue;
     const int rr = r < last ? r : last;
     const char* src = (const char*)(base + (int64_t)(row0 + rr) * sn) + ch * 16;
     __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + blk * 1024),
@@ -164,11 +167,35 @@ __device__ __forceinline__ void bwd_dma_rows(const bf16* base, int64_t sn, int r
   }
 }
 
+// Zero the padding chunks (columns DA .. D-1 of every row) of NT consecutive
+// swizzled tiles of ROWS rows of D elements from byte `dst` of LDS: the tile
+// copies never write them, so a 16-wide head dim can run on the 32-wide
+// layout, its upper half zero (no effect on the scores; the output rows it
+// feeds are not stored).  The caller's barrier after its first tile copy
+// orders these stores before any read.
+template <int D, int DA, int ROWS, int NT>
+__device__ __forceinline__ void bwd_zero_pad(lds_t* dst, int tid) {
+  constexpr int TILE = ROWS * D * 2, PADC = (D - DA) / 8;
+  if constexpr (PADC > 0) {
+    for (int id = tid; id < NT * ROWS * PADC; id += 256) {
+      const int c = DA / 8 + id % PADC, row = (id / PADC) % ROWS, tl = id / (PADC * ROWS);
+      *(__attribute__((address_space(3))) u32x4*)(dst + tl * TILE + swz_off<D>(row, c)) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// Layout head dim of the gradient kernels: 16 runs on the 32-wide tiles.
+template <int D>
+constexpr int bwd_layout_dim() {
+  return D < 32 ? 32 : D;
+}
+
 // ---------------------------------------------------------------- dQ kernel
 template <int D, int BN>
 struct BwdDqCfg {
   static constexpr int NW = 4, THREADS = 256, BM = 128;
-  static constexpr int TILE = BN * D * 2;  // one K or V tile
+  static constexpr int DL = bwd_layout_dim<D>();
+  static constexpr int TILE = BN * DL * 2;  // one K or V tile
   static constexpr int STAGE = 2 * TILE;   // K then V
   static constexpr int LDS = 2 * STAGE;
 };
@@ -176,8 +203,8 @@ struct BwdDqCfg {
 template <int D, int BN, bool F16 = false, int BIAS = kNoBias>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   using C = BwdDqCfg<D, BN>;
-  constexpr int BM = C::BM, TILE = C::TILE, STAGE = C::STAGE, NW = C::NW;
-  constexpr int NB = BN / 32, KD = D / 16, DB = D / 32;
+  constexpr int BM = C::BM, TILE = C::TILE, STAGE = C::STAGE, NW = C::NW, DL = C::DL;
+  constexpr int NB = BN / 32, KD = DL / 16, DB = DL / 32;
   extern __shared__ __attribute__((aligned(256))) char smem_raw[];
   lds_t* smem = (lds_t*)smem_raw;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
@@ -212,8 +239,13 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   bf16x8 qf[KD], df[KD];
 #pragma unroll
   for (int kk = 0; kk < KD; ++kk) {
-    qf[kk] = *(const bf16x8*)(Q + r_cl * a.q_sn + 16 * kk + 8 * h32);
-    df[kk] = *(const bf16x8*)(DO + r_cl * a.do_sn + 16 * kk + 8 * h32);
+    if (16 * kk < D) {
+      qf[kk] = *(const bf16x8*)(Q + r_cl * a.q_sn + 16 * kk + 8 * h32);
+      df[kk] = *(const bf16x8*)(DO + r_cl * a.do_sn + 16 * kk + 8 * h32);
+    } else {  // padding columns of a 16-wide head
+      qf[kk] = bf16x8{};
+      df[kk] = bf16x8{};
+    }
   }
   const float lse2 = a.lse2[row_base + r_cl];
   const float delta = a.delta[row_base + r_cl];
@@ -221,10 +253,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   const int krow = kperm(n32);
   uint32_t kaddr[KD];
 #pragma unroll
-  for (int kk = 0; kk < KD; ++kk) kaddr[kk] = lds_base + swz_off<D>(krow, 2 * kk + h32);
+  for (int kk = 0; kk < KD; ++kk) kaddr[kk] = lds_base + swz_off<DL>(krow, 2 * kk + h32);
   int vlo[DB], vhi[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) v_frag_offsets<D>(lane, db, vlo[db], vhi[db]);
+  for (int db = 0; db < DB; ++db) v_frag_offsets<DL>(lane, db, vlo[db], vhi[db]);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -271,9 +303,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   };
 
   auto fetch = [&](int j, int stage) {
-    bwd_dma_rows<D, BN, NW>(K + (int64_t)j * BN * a.k_sn, a.k_sn, 0, t.Lkv - j * BN, smem + stage * STAGE, wave, lane);
-    bwd_dma_rows<D, BN, NW>(V + (int64_t)j * BN * a.v_sn, a.v_sn, 0, t.Lkv - j * BN, smem + stage * STAGE + TILE, wave,
-                            lane);
+    bwd_dma_rows<DL, BN, NW, D>(K + (int64_t)j * BN * a.k_sn, a.k_sn, 0, t.Lkv - j * BN, smem + stage * STAGE, wave,
+                                lane);
+    bwd_dma_rows<DL, BN, NW, D>(V + (int64_t)j * BN * a.v_sn, a.v_sn, 0, t.Lkv - j * BN, smem + stage * STAGE + TILE,
+                                wave, lane);
   };
 
   auto step = [&](int j, auto stage_tag) {
@@ -284,8 +317,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     }
     if (j * BN < wave_max) {
       f32x16 s[NB], dp[NB];
-      scores_section<D, NB, false, S * STAGE, 0, F16>(kaddr, qf, dummy_t, s, dummy_ts);          // S^T = K Q^T
-      scores_section<D, NB, false, S * STAGE + TILE, 0, F16>(kaddr, df, dummy_t, dp, dummy_ts);  // dP^T = V dO^T
+      scores_section<DL, NB, false, S * STAGE, 0, F16>(kaddr, qf, dummy_t, s, dummy_ts);          // S^T = K Q^T
+      scores_section<DL, NB, false, S * STAGE + TILE, 0, F16>(kaddr, df, dummy_t, dp, dummy_ts);  // dP^T = V dO^T
       if ((j + 1) * BN > wave_min) {  // keys past this row's limit: P = 0
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb)
@@ -307,7 +340,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
       };
       static_for<8>(dsel);
       // dQ^T += K^T dS^T (transposing reads of the K tile)
-      pv_section<D, NB, false, S * STAGE, 0, F16>(lds_base, vlo, vhi, dsf, dummy_h, acc, dummy_a, dummy_b, [&](auto i_tag) {
+      pv_section<DL, NB, false, S * STAGE, 0, F16>(lds_base, vlo, vhi, dsf, dummy_h, acc, dummy_a, dummy_b, [&](auto i_tag) {
         constexpr int i = decltype(i_tag)::value, c = i / DB, EPS = 8 / DB;
         if constexpr (c + 1 < 2 * NB)
           static_for<EPS>([&](auto k_tag) {
@@ -326,6 +359,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
   };
 
+  bwd_zero_pad<DL, D, BN, 4>(smem, tid);  // K, V of both stages
   if (n_tiles > 0) {
     bias_load(0, std::integral_constant<int, 0>{});
     fetch(0, 0);
@@ -345,6 +379,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        if (8 * g >= D) continue;  // padding rows of a 16-wide head
         const int d = 32 * db + 8 * g + 4 * h32;
         bf16x4 ov;
 #pragma unroll
@@ -363,7 +398,8 @@ struct BwdDkdvCfg {
   // independent 32-query blocks per step, half the steps and barriers)
   static constexpr int BMQ = D == 128 ? 64 : 32;
   static constexpr int NBQ = BMQ / 32;                   // 32-query blocks per tile
-  static constexpr int TILE = BMQ * D * 2;               // one Q or dO tile
+  static constexpr int DL = bwd_layout_dim<D>();
+  static constexpr int TILE = BMQ * DL * 2;              // one Q or dO tile
   // LDS: the two Q stages, the two dO stages, then each stage's lse2 and
   // delta rows (per 32-query block: 32 lse2 then 32 delta) -- grouped by
   // tensor so that every fragment read's offset fits the 16-bit immediate
@@ -376,7 +412,7 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
   using C = BwdDkdvCfg<D, BIAS>;
   constexpr int BN = C::BN, BMQ = C::BMQ, NBQ = C::NBQ, TILE = C::TILE, NW = C::NW;
   constexpr int OFF_DO = C::OFF_DO, OFF_ROWS = C::OFF_ROWS, ROWS = C::ROWS;
-  constexpr int KD = D / 16, DB = D / 32;
+  constexpr int DL = C::DL, KD = DL / 16, DB = DL / 32;
   extern __shared__ __attribute__((aligned(256))) char smem_raw[];
   lds_t* smem = (lds_t*)smem_raw;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
@@ -409,17 +445,22 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
   bf16x8 kf[KD], vf[KD];
 #pragma unroll
   for (int kk = 0; kk < KD; ++kk) {
-    kf[kk] = *(const bf16x8*)(K + k_cl * a.k_sn + 16 * kk + 8 * h32);
-    vf[kk] = *(const bf16x8*)(V + k_cl * a.v_sn + 16 * kk + 8 * h32);
+    if (16 * kk < D) {
+      kf[kk] = *(const bf16x8*)(K + k_cl * a.k_sn + 16 * kk + 8 * h32);
+      vf[kk] = *(const bf16x8*)(V + k_cl * a.v_sn + 16 * kk + 8 * h32);
+    } else {  // padding columns of a 16-wide head
+      kf[kk] = bf16x8{};
+      vf[kk] = bf16x8{};
+    }
   }
 
   const int qrow = kperm(n32);
   uint32_t qaddr[KD];
 #pragma unroll
-  for (int kk = 0; kk < KD; ++kk) qaddr[kk] = lds_base + swz_off<D>(qrow, 2 * kk + h32);
+  for (int kk = 0; kk < KD; ++kk) qaddr[kk] = lds_base + swz_off<DL>(qrow, 2 * kk + h32);
   int vlo[DB], vhi[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) v_frag_offsets<D>(lane, db, vlo[db], vhi[db]);
+  for (int db = 0; db < DB; ++db) v_frag_offsets<DL>(lane, db, vlo[db], vhi[db]);
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -461,8 +502,8 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
   // values (4 bytes per lane of wave b: lanes 0-31 lse2, lanes 32-63 delta)
   auto fetch = [&](int jq, int stage) {
     const int q0 = jq * BMQ;
-    bwd_dma_rows<D, BMQ, NW>(Q, a.q_sn, q0, t.Lq, smem + stage * TILE, wave, lane);
-    bwd_dma_rows<D, BMQ, NW>(DO, a.do_sn, q0, t.Lq, smem + OFF_DO + stage * TILE, wave, lane);
+    bwd_dma_rows<DL, BMQ, NW, D>(Q, a.q_sn, q0, t.Lq, smem + stage * TILE, wave, lane);
+    bwd_dma_rows<DL, BMQ, NW, D>(DO, a.do_sn, q0, t.Lq, smem + OFF_DO + stage * TILE, wave, lane);
     if (wave < NBQ) {
       const int qi = min(q0 + 32 * wave + n32, t.Lq - 1);
       const float* src = (h32 ? a.delta : a.lse2) + row_base + qi;
@@ -481,8 +522,8 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
     const int q0 = jq * BMQ;
     if (wave_keys && q0 + BMQ > wave_q_first) {  // wave-uniform: some key of the wave sees some query
       f32x16 s[NBQ], dp[NBQ];
-      scores_section<D, NBQ, false, S * TILE, 0, F16>(qaddr, kf, dummy_t, s, dummy_ts);            // S = Q K^T
-      scores_section<D, NBQ, false, OFF_DO + S * TILE, 0, F16>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
+      scores_section<DL, NBQ, false, S * TILE, 0, F16>(qaddr, kf, dummy_t, s, dummy_ts);            // S = Q K^T
+      scores_section<DL, NBQ, false, OFF_DO + S * TILE, 0, F16>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
       // masked pairs (query past Lq, key past Lkv; causal: key after query) get P = 0
       const bool edge = q0 + BMQ > t.Lq || k0 + 32 > t.Lkv || (a.causal && q0 < k0 + 32);
       if (edge) {
@@ -532,16 +573,17 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
       chunk(std::integral_constant<int, 0>{});
       // dV^T += dO^T P and dK^T += Q^T dS (transposing reads of the dO and Q
       // tiles); chunk c + 1 is formed after the first MFMA that consumes chunk c
-      pv_section<D, NBQ, false, OFF_DO + S * TILE, 0, F16>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b,
+      pv_section<DL, NBQ, false, OFF_DO + S * TILE, 0, F16>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b,
                                                           [&](auto i_tag) {
         constexpr int i = decltype(i_tag)::value;
         if constexpr (i % DB == 0 && i / DB + 1 < 2 * NBQ) chunk(std::integral_constant<int, i / DB + 1>{});
       });
-      pv_section<D, NBQ, false, S * TILE, 0, F16>(lds_base, vlo, vhi, dsf, dummy_h, dk, dummy_a, dummy_b, [](auto) {});
+      pv_section<DL, NBQ, false, S * TILE, 0, F16>(lds_base, vlo, vhi, dsf, dummy_h, dk, dummy_a, dummy_b, [](auto) {});
     }
     __syncthreads();
   };
 
+  bwd_zero_pad<DL, D, BMQ, 4>(smem, tid);  // Q, dO of both stages
   if (jq0 < n_qt && kt * BN < t.Lkv) {  // a tile of keys past Lkv only writes zeros
     bias_load(jq0, std::integral_constant<int, 0>{});
     fetch(jq0, 0);
@@ -561,6 +603,7 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        if (8 * g >= D) continue;  // padding rows of a 16-wide head
         const int d = 32 * db + 8 * g + 4 * h32;
         bf16x4 kv, vv;
 #pragma unroll

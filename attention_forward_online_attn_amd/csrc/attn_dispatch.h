@@ -36,9 +36,10 @@ auto by_dim(int64_t D, F&& f) {
   return f(std::integral_constant<int, 128>{});
 }
 
-// Head dims of the value-dim variants, which also take 16 (the JVP page's
+// Head dims that also take 16: the value-dim variants (the JVP page's
 // cross-attention test pairs d_qk = 16 with d_v = 32; a 16-wide value tile
-// is padded to 32 in LDS).
+// is padded to 32 in LDS), the biased forward and the backward (whose
+// gradient kernels run a 16-wide head on the 32-wide tiles).
 template <class F>
 auto by_dim_qk(int64_t D, F&& f) {
   if (D == 16) return f(std::integral_constant<int, 16>{});

@@ -6,7 +6,7 @@ namespace attn {
 
 int bwd_run(bool f16, int D, int bias_kind, hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
             int64_t items) {
-  int rc = by_dim(D, [&](auto d) {
+  int rc = by_dim_qk(D, [&](auto d) {
     constexpr int Dc = decltype(d)::value;
     constexpr int rpb = 256 / (Dc / 8);
     const int grid = (int)((B * H * Nq + rpb - 1) / rpb);
@@ -15,7 +15,7 @@ int bwd_run(bool f16, int D, int bias_kind, hipStream_t st, BwdArgs& a, int64_t 
   });
   if (rc) return rc;
   if (bias_kind != kNoBias) return bwd_run_bias(f16, D, bias_kind, st, a, B, H, Nq, Nkv);
-  return by_dim(D, [&](auto d) {
+  return by_dim_qk(D, [&](auto d) {
     constexpr int Dc = decltype(d)::value;
     return f16 ? bwd_launch_grads<Dc, true, kNoBias>(st, a, B, H, Nq, Nkv, items)
                : bwd_launch_grads<Dc, false, kNoBias>(st, a, B, H, Nq, Nkv, items);

@@ -8,7 +8,7 @@ namespace attn {
 
 int bwd_run_bias(bool f16, int D, int bias_kind, hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq,
                  int64_t Nkv) {
-  return by_dim(D, [&](auto d) {
+  return by_dim_qk(D, [&](auto d) {
     constexpr int Dc = decltype(d)::value;
     if (bias_kind == kAddBias)
       return f16 ? bwd_launch_grads<Dc, true, kAddBias>(st, a, B, H, Nq, Nkv, 0)

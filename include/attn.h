@@ -28,9 +28,9 @@
  *   satisfy this.  Anything else is ATTN_ERR_UNSUPPORTED.
  * - Tangent tensors (JVP) share the strides of their primals, and tO shares
  *   the strides of O (as the JVP page's wrapper requires).
- * - Supported head dims: 32, 64 and 128 everywhere; 16 on the forward
- *   (plain, biased, jagged, either side of attn_fwd_dv) and the JVP, not the
- *   backward; 256 on the forward without tangents (attn_fwd, attn_fwd_bias,
+ * - Supported head dims: 16, 32, 64 and 128 everywhere (the forward, plain,
+ *   biased or jagged, either side of attn_fwd_dv, the JVP and the backward);
+ *   256 on the forward without tangents (attn_fwd, attn_fwd_bias,
  *   jagged_attn_fwd, attn_fwd_dv with Dqk = Dv = 256).  dtype ATTN_BF16 (ATTN_FP16) computes
  *   the products on bf16 (fp16) MFMA with fp32 accumulation and rounds O/tO to
  *   the input format (RNE); ATTN_FP32 computes everything in fp32.  LSE is
@@ -65,7 +65,7 @@ extern "C" {
 enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID = -1,      /* null pointer with work to do, negative or oversized size, bad stride, bad scale */
-  ATTN_ERR_UNSUPPORTED = -2,  /* head dim not in {32,64,128}, unknown dtype, misaligned pointer/stride */
+  ATTN_ERR_UNSUPPORTED = -2,  /* head dim not supported by the call, unknown dtype, misaligned pointer/stride */
   ATTN_ERR_CAUSAL_SHAPE = -3, /* causal with Nq != Nkv (the mask is top-left aligned) */
   ATTN_ERR_WORKSPACE = -4,    /* jagged workspace missing or too small */
   ATTN_ERR_HIP = -5           /* the HIP runtime reported an error while enqueuing */
@@ -245,7 +245,7 @@ ATTN_API size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
  *   workspace      DEVICE scratch of at least attn_bwd_workspace_bytes(B, H, Nq)
  *                  bytes, 16-byte aligned; contents on entry are ignored.
  *                  Calls that share a workspace must not overlap.
- * Strides, alignment, sm_scale, causal (Nq == Nkv) and D in {32, 64, 128} as for
+ * Strides, alignment, sm_scale, causal (Nq == Nkv) and D in {16, 32, 64, 128} as for
  * attn_fwd.  P and dS are rounded to the input format for their products,
  * with fp32 accumulation.  Each output element is written by exactly one
  * thread: the result is deterministic.  ATTN_FP32 returns ATTN_ERR_UNSUPPORTED.  Three

@@ -281,13 +281,16 @@ def test_d256_only_for_the_plain_forward(lib):
 
 
 def test_d16_paths(lib):
-    """Head dim 16 runs the forward (biased or not) and the JVP; the backward
-    at 16 is not built."""
+    """Head dim 16 runs the forward (biased or not), the JVP and the
+    backward; other widths below 32 are not head dims."""
     H, N = 2, 128
     st = dense_strides(1, H, N, 16)
     assert call_fwd(lib, D=16, B=0) == OK
     full = Strides4(H * N * N, N * N, N, 1)
     assert lib.attn_fwd_bias(BF16, P, st, P, st, P, st, P, st, P, P, 1, full, 0, H, N, N, 16, 0.1, 0, None) == OK
     need = lib.attn_bwd_workspace_bytes(1, H, N)
-    assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st, 1, H, N, N, 16, 0.1, 0,
+    # B = 0: the head dim passes validation and nothing is launched
+    assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st, 0, H, N, N, 16, 0.1, 0,
+                        P, need, None) == OK
+    assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st, 1, H, N, N, 24, 0.1, 0,
                         P, need, None) == UNSUPPORTED
