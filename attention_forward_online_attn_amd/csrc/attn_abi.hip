@@ -47,7 +47,7 @@ bool stride_ok(int64_t stride, int64_t extent, int64_t vec) {
 }
 
 // d16: head dim 16 is allowed (the forward, JVP and backward); d256: head
-// dim 256 is allowed (the forward without tangents).
+// dim 256 is allowed (the forward without tangents and the backward).
 int check_common(int dtype, int64_t D, float sm_scale, bool d16 = false, bool d256 = false) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP32 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale) || sm_scale < 0.f) return ATTN_ERR_INVALID;
@@ -323,7 +323,7 @@ int jagged_attn_bwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
                     attn_strides3 dk_strides, void* dv, attn_strides3 dv_strides, const int64_t* offsets,
                     int64_t num_seqs, int64_t H, int64_t total_len, int64_t D, int64_t max_seq_len, float sm_scale,
                     int causal, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_common((int)dtype, D, sm_scale, true);
+  int rc = check_common((int)dtype, D, sm_scale, true, true);
   if (rc) return rc;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (num_seqs < 0 || H < 0 || total_len < 0 || max_seq_len < 1) return ATTN_ERR_INVALID;
@@ -397,7 +397,7 @@ int dense_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const vo
               attn_strides4 dk_strides, void* dv, attn_strides4 dv_strides, int64_t B, int64_t H, int64_t Nq,
               int64_t Nkv, int64_t D, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
               void* stream, const BiasOperand& bias, void* dbias, attn_strides4 dbias_strides) {
-  int rc = check_common((int)dtype, D, sm_scale, true);
+  int rc = check_common((int)dtype, D, sm_scale, true, true);
   if (rc) return rc;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;

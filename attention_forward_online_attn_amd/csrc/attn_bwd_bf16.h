@@ -194,6 +194,7 @@ constexpr int bwd_layout_dim() {
 template <int D, int BN>
 struct BwdDqCfg {
   static constexpr int NW = 4, THREADS = 256, BM = 128;
+  static constexpr int WAVES_PER_EU = D == 256 ? 1 : 2;  // D=256 holds Q, dO and dQ: 1 wave per SIMD
   static constexpr int DL = bwd_layout_dim<D>();
   static constexpr int TILE = BN * DL * 2;  // one K or V tile
   static constexpr int STAGE = 2 * TILE;   // K then V
@@ -201,7 +202,7 @@ struct BwdDqCfg {
 };
 
 template <int D, int BN, bool F16 = false, int BIAS = kNoBias>
-__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, (BwdDqCfg<D, BN>::WAVES_PER_EU)) attn_bwd_dq_kernel(BwdArgs a) {
   using C = BwdDqCfg<D, BN>;
   constexpr int BM = C::BM, TILE = C::TILE, STAGE = C::STAGE, NW = C::NW, DL = C::DL;
   constexpr int NB = BN / 32, KD = DL / 16, DB = DL / 32;
@@ -393,7 +394,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 template <int D, int BIAS = kNoBias>
 struct BwdDkdvCfg {
   static constexpr int NW = 4, THREADS = 256, BN = 128;  // keys per workgroup, 32 per wave
-  static constexpr int WAVES_PER_EU = D == 128 ? 1 : 2;  // D=128 holds K, V, dK, dV: 1 wave per SIMD
+  static constexpr int WAVES_PER_EU = D >= 128 ? 1 : 2;  // D>=128 holds K, V, dK, dV: 1 wave per SIMD
   // query rows per streamed tile: the one-wave D=128 kernel takes 64 (two
   // independent 32-query blocks per step, half the steps and barriers)
   static constexpr int BMQ = D == 128 ? 64 : 32;
@@ -407,12 +408,18 @@ struct BwdDkdvCfg {
   static constexpr int LDS = 4 * TILE + 2 * ROWS;
 };
 
-template <int D, bool F16 = false, int BIAS = kNoBias>
+// PART: kDkdvBoth computes dK and dV; at D = 256, where K, V and both
+// accumulators do not fit one wave's registers, kDkdvOnlyV (K and dV: S and
+// P only) and kDkdvOnlyK (K, V and dK) run as two launches.
+constexpr int kDkdvBoth = 0, kDkdvOnlyV = 1, kDkdvOnlyK = 2;
+
+template <int D, bool F16 = false, int BIAS = kNoBias, int PART = kDkdvBoth>
 __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn_bwd_dkdv_kernel(BwdArgs a) {
   using C = BwdDkdvCfg<D, BIAS>;
   constexpr int BN = C::BN, BMQ = C::BMQ, NBQ = C::NBQ, TILE = C::TILE, NW = C::NW;
   constexpr int OFF_DO = C::OFF_DO, OFF_ROWS = C::OFF_ROWS, ROWS = C::ROWS;
   constexpr int DL = C::DL, KD = DL / 16, DB = DL / 32;
+  constexpr bool DO_DV = PART != kDkdvOnlyK, DO_DK = PART != kDkdvOnlyV;
   extern __shared__ __attribute__((aligned(256))) char smem_raw[];
   lds_t* smem = (lds_t*)smem_raw;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
@@ -447,7 +454,7 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
   for (int kk = 0; kk < KD; ++kk) {
     if (16 * kk < D) {
       kf[kk] = *(const bf16x8*)(K + k_cl * a.k_sn + 16 * kk + 8 * h32);
-      vf[kk] = *(const bf16x8*)(V + k_cl * a.v_sn + 16 * kk + 8 * h32);
+      vf[kk] = DO_DK ? *(const bf16x8*)(V + k_cl * a.v_sn + 16 * kk + 8 * h32) : bf16x8{};
     } else {  // padding columns of a 16-wide head
       kf[kk] = bf16x8{};
       vf[kk] = bf16x8{};
@@ -523,7 +530,8 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
     if (wave_keys && q0 + BMQ > wave_q_first) {  // wave-uniform: some key of the wave sees some query
       f32x16 s[NBQ], dp[NBQ];
       scores_section<DL, NBQ, false, S * TILE, 0, F16>(qaddr, kf, dummy_t, s, dummy_ts);            // S = Q K^T
-      scores_section<DL, NBQ, false, OFF_DO + S * TILE, 0, F16>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
+      if constexpr (DO_DK)
+        scores_section<DL, NBQ, false, OFF_DO + S * TILE, 0, F16>(qaddr, vf, dummy_t, dp, dummy_ts);  // dP = dO V^T
       // masked pairs (query past Lq, key past Lkv; causal: key after query) get P = 0
       const bool edge = q0 + BMQ > t.Lq || k0 + 32 > t.Lkv || (a.causal && q0 < k0 + 32);
       if (edge) {
@@ -559,26 +567,35 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
         constexpr int qo = 256 * b + 64 * h;
         const f32x4 a0 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 32 * h32);
         const f32x4 a1 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 32 * h32 + 16);
-        const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 128 + 32 * h32);
-        const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 128 + 32 * h32 + 16);
+        f32x4 d0 = {}, d1 = {};
+        if constexpr (DO_DK) {
+          d0 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 128 + 32 * h32);
+          d1 = *(const __attribute__((address_space(3))) f32x4*)(st + qo + 128 + 32 * h32 + 16);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float l2 = e < 4 ? a0[e & 3] : a1[e & 3];
-          const float dl = e < 4 ? d0[e & 3] : d1[e & 3];
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * h + e], cs, -l2));
           pf[b][h][e] = to16<F16>(p);
-          dsf[b][h][e] = to16<F16>(p * (dp[b][8 * h + e] - dl));
+          if constexpr (DO_DK) {
+            const float dl = e < 4 ? d0[e & 3] : d1[e & 3];
+            dsf[b][h][e] = to16<F16>(p * (dp[b][8 * h + e] - dl));
+          }
         }
       };
       chunk(std::integral_constant<int, 0>{});
       // dV^T += dO^T P and dK^T += Q^T dS (transposing reads of the dO and Q
       // tiles); chunk c + 1 is formed after the first MFMA that consumes chunk c
-      pv_section<DL, NBQ, false, OFF_DO + S * TILE, 0, F16>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b,
-                                                          [&](auto i_tag) {
-        constexpr int i = decltype(i_tag)::value;
-        if constexpr (i % DB == 0 && i / DB + 1 < 2 * NBQ) chunk(std::integral_constant<int, i / DB + 1>{});
-      });
-      pv_section<DL, NBQ, false, S * TILE, 0, F16>(lds_base, vlo, vhi, dsf, dummy_h, dk, dummy_a, dummy_b, [](auto) {});
+      if constexpr (DO_DV)
+        pv_section<DL, NBQ, false, OFF_DO + S * TILE, 0, F16>(lds_base, vlo, vhi, pf, dummy_h, dv, dummy_a, dummy_b,
+                                                            [&](auto i_tag) {
+          constexpr int i = decltype(i_tag)::value;
+          if constexpr (i % DB == 0 && i / DB + 1 < 2 * NBQ) chunk(std::integral_constant<int, i / DB + 1>{});
+        });
+      else
+        static_for<2 * NBQ - 1>([&](auto c_tag) { chunk(std::integral_constant<int, decltype(c_tag)::value + 1>{}); });
+      if constexpr (DO_DK)
+        pv_section<DL, NBQ, false, S * TILE, 0, F16>(lds_base, vlo, vhi, dsf, dummy_h, dk, dummy_a, dummy_b, [](auto) {});
     }
     __syncthreads();
   };
@@ -611,8 +628,8 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
           kv[e] = to16<F16>(dk[db][4 * g + e] * a.sm_scale);
           vv[e] = to16<F16>(dv[db][4 * g + e]);
         }
-        *(bf16x4*)(krow_o + d) = kv;
-        *(bf16x4*)(vrow_o + d) = vv;
+        if constexpr (DO_DK) *(bf16x4*)(krow_o + d) = kv;
+        if constexpr (DO_DV) *(bf16x4*)(vrow_o + d) = vv;
       }
   }
 }

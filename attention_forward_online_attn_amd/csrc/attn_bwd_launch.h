@@ -31,7 +31,13 @@ int bwd_launch_grads(hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t N
   if (rc) return rc;
   a.n_tiles = (int)((Nkv + Ck::BN - 1) / Ck::BN);
   const int64_t gk = a.offsets ? items * H : B * H * a.n_tiles;
-  return bwd_launch_one(attn_bwd_dkdv_kernel<D, F16, BIAS>, (int)gk, Ck::THREADS, Ck::LDS, st, a);
+  if constexpr (D == 256) {  // dV, then dK: the two do not fit one wave's registers together
+    rc = bwd_launch_one(attn_bwd_dkdv_kernel<D, F16, BIAS, kDkdvOnlyV>, (int)gk, Ck::THREADS, Ck::LDS, st, a);
+    if (rc) return rc;
+    return bwd_launch_one(attn_bwd_dkdv_kernel<D, F16, BIAS, kDkdvOnlyK>, (int)gk, Ck::THREADS, Ck::LDS, st, a);
+  } else {
+    return bwd_launch_one(attn_bwd_dkdv_kernel<D, F16, BIAS>, (int)gk, Ck::THREADS, Ck::LDS, st, a);
+  }
 }
 
 }  // namespace attn

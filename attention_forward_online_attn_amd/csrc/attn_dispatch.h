@@ -46,6 +46,14 @@ auto by_dim_qk(int64_t D, F&& f) {
   return by_dim(D, f);
 }
 
+// Head dims of the backward's prep kernel: those of by_dim_qk and 256 (whose
+// gradient kernels live in inst_bwd_d256.hip).
+template <class F>
+auto by_dim_bwd(int64_t D, F&& f) {
+  if (D == 256) return f(std::integral_constant<int, 256>{});
+  return by_dim_qk(D, f);
+}
+
 // Forward instance tables (dtype codes of include/attn.h).
 KernelChoice fwd_bf16(int D, bool jvp, bool split);             // inst_fwd_bf16.hip
 KernelChoice fwd_fp16(int D, bool jvp, bool split);             // inst_fwd_fp16.hip
@@ -66,5 +74,8 @@ int bwd_run(bool f16, int D, int bias_kind, hipStream_t st, BwdArgs& a, int64_t 
             int64_t items);
 int bwd_run_bias(bool f16, int D, int bias_kind, hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq,
                  int64_t Nkv);
+// The gradient kernels at head dim 256, any score operand (inst_bwd_d256.hip).
+int bwd_run_d256(bool f16, int bias_kind, hipStream_t st, BwdArgs& a, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
+                 int64_t items);
 
 }  // namespace attn

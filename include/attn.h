@@ -30,8 +30,9 @@
  *   the strides of O (as the JVP page's wrapper requires).
  * - Supported head dims: 16, 32, 64 and 128 everywhere (the forward, plain,
  *   biased or jagged, either side of attn_fwd_dv, the JVP and the backward);
- *   256 on the forward without tangents (attn_fwd, attn_fwd_bias,
- *   jagged_attn_fwd, attn_fwd_dv with Dqk = Dv = 256).  dtype ATTN_BF16 (ATTN_FP16) computes
+ *   256 everywhere except the JVP and unequal value dims (attn_fwd,
+ *   attn_fwd_bias, jagged_attn_fwd, attn_fwd_dv with Dqk = Dv = 256, and the
+ *   three backward calls).  dtype ATTN_BF16 (ATTN_FP16) computes
  *   the products on bf16 (fp16) MFMA with fp32 accumulation and rounds O/tO to
  *   the input format (RNE); ATTN_FP32 computes everything in fp32.  LSE is
  *   always fp32.
@@ -245,7 +246,7 @@ ATTN_API size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
  *   workspace      DEVICE scratch of at least attn_bwd_workspace_bytes(B, H, Nq)
  *                  bytes, 16-byte aligned; contents on entry are ignored.
  *                  Calls that share a workspace must not overlap.
- * Strides, alignment, sm_scale, causal (Nq == Nkv) and D in {16, 32, 64, 128} as for
+ * Strides, alignment, sm_scale, causal (Nq == Nkv) and D in {16, 32, 64, 128, 256} as for
  * attn_fwd.  P and dS are rounded to the input format for their products,
  * with fp32 accumulation.  Each output element is written by exactly one
  * thread: the result is deterministic.  ATTN_FP32 returns ATTN_ERR_UNSUPPORTED.  Three

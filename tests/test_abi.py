@@ -263,9 +263,9 @@ def test_bwd_bias_validation(lib):
     assert call(B=0) == OK
 
 
-def test_d256_only_for_the_plain_forward(lib):
-    """Head dim 256 runs the forward (biased or not); the 16-bit JVP and the
-    backward kernels at 256 are not built."""
+def test_d256_paths(lib):
+    """Head dim 256 runs the forward (biased or not) and the backward; the
+    16-bit JVP and unequal value dims at 256 are not built."""
     B, H, N, D = 0, 2, 128, 256  # B = 0: nothing is enqueued when the call is accepted
     st = dense_strides(1, H, N, D)
     assert call_fwd(lib, D=256, B=0) == OK
@@ -274,7 +274,9 @@ def test_d256_only_for_the_plain_forward(lib):
     full = Strides4(H * N * N, N * N, N, 1)
     assert lib.attn_fwd_bias(BF16, P, st, P, st, P, st, P, st, P, P, 1, full, 0, H, N, N, D, 0.1, 0, None) == OK
     need = lib.attn_bwd_workspace_bytes(1, H, N)
-    assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st, 1, H, N, N, D, 0.1, 0,
+    assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st, 0, H, N, N, D, 0.1, 0,
+                        P, need, None) == OK
+    assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st, 1, H, N, N, 512, 0.1, 0,
                         P, need, None) == UNSUPPORTED
     assert lib.attn_fwd_dv(BF16, P, P, P, 0, 0, 0, st, st, st, P, 0, st, P, 0, 1, H, N, N, 256, 128, 0.1, 0, None) \
         == UNSUPPORTED

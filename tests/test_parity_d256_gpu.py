@@ -1,6 +1,7 @@
-"""GPU parity at head dim 256 (the plain forward: dense, causal, jagged;
-bf16, fp16, fp32) against the fp64 oracle, with the tolerances of each
-dtype.  The 256-wide kernels use 32-key tiles and one wave per SIMD."""
+"""GPU parity at head dim 256 against the fp64 oracle, with the tolerances
+of each dtype: the forward (dense, causal, jagged, biased; bf16, fp16,
+fp32) and the backward (dense, jagged, biased; bf16, fp16).  The 256-wide
+kernels use 32-key tiles and one wave per SIMD."""
 
 import pytest
 
@@ -36,3 +37,29 @@ def test_d256_bias_and_mask(gpu_lib, dtype, causal):
     bias_case(2, 2, 200, 200, 256, dtype, causal, "mask", seed=124)
     bias_case(2, 2, 130, 130, 256, dtype, causal, "add", bshape=(1, 2, 130, 130), seed=125)
 
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_backward(gpu_lib, dtype, causal):
+    """dQ, dK, dV at head dim 256 (dK and dV from two passes of the dK/dV
+    kernel): ragged 128-row tiles, one row, cross-attention, and the jagged
+    layout with empty, short and truncated sequences."""
+    from test_parity_bwd_gpu import bwd_case
+    from test_parity_jagged_bwd_gpu import jagged_bwd_case
+    bwd_case(2, 2, 300, 300, 256, causal, seed=241, dtype=dtype)
+    bwd_case(1, 2, 1, 1, 256, causal, seed=242, dtype=dtype)
+    if not causal:
+        bwd_case(1, 2, 77, 333, 256, False, seed=243, dtype=dtype)
+    jagged_bwd_case([5, 0, 300, 64, 129, 1], 2, 256, dtype, 256, causal, seed=244)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_bias_backward(gpu_lib, dtype, causal):
+    """The backward with an additive bias (and its gradient) or a boolean
+    mask at head dim 256, full-shape and broadcast operands."""
+    from test_parity_bias_bwd_gpu import bias_bwd_case
+    bias_bwd_case(2, 2, 300, 300, 256, dtype, causal, "add", seed=245)
+    bias_bwd_case(2, 2, 300, 300, 256, dtype, causal, "mask", seed=246)
+    bias_bwd_case(2, 2, 200, 200, 256, dtype, causal, "add", bshape=(1, 2, 200, 200), seed=247)

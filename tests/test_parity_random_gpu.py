@@ -80,12 +80,12 @@ def test_random_configuration(gpu_lib, case):
 
 def draw_bwd_cases(n, seed):
     """(case id, B, H, Nq, Nkv, D, dtype, causal, strided): the backward's
-    support is bf16 and fp16 at head dims 16, 32, 64 and 128."""
+    support is bf16 and fp16 at head dims 16, 32, 64, 128 and 256."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
         dtype = ["bf16", "fp16"][int(rng.integers(0, 2))]
-        D = int(rng.choice([16, 32, 64, 128]))
+        D = int(rng.choice([16, 32, 64, 128, 256]))
         causal = bool(rng.integers(0, 2))
         B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
         Nq = int(rng.integers(1, 500))
@@ -180,7 +180,7 @@ def draw_bias_cases(n, seed):
         backward = bool(rng.integers(0, 2))
         kind = ["add", "mask"][int(rng.integers(0, 2))]
         dtype = ["bf16", "fp16"][int(rng.integers(0, 2))] if backward else ["bf16", "fp16", "fp32"][int(rng.integers(0, 3))]
-        D = int(rng.choice([16, 32, 64, 128] if backward else [16, 32, 64, 128, 256]))
+        D = int(rng.choice([16, 32, 64, 128, 256]))
         causal = bool(rng.integers(0, 2))
         B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
         Nq = int(rng.integers(1, 400))
