@@ -47,7 +47,7 @@ bool stride_ok(int64_t stride, int64_t extent, int64_t vec) {
 }
 
 // d16: head dim 16 is allowed (the forward, JVP and backward); d256: head
-// dim 256 is allowed (the forward without tangents and the backward).
+// dim 256 is allowed (the forward, the 16-bit JVP and the backward).
 int check_common(int dtype, int64_t D, float sm_scale, bool d16 = false, bool d256 = false) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP32 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale) || sm_scale < 0.f) return ATTN_ERR_INVALID;
@@ -104,7 +104,7 @@ bool use_split(int dtype, int D, bool jvp, bool dense_causal, int64_t grid) {
 // Forward kernel for a dtype, head dims and variant (instance tables in the
 // inst_*.hip translation units).
 KernelChoice choose(int dtype, int D, bool jvp, bool split, int bias_kind, int Dv) {
-  if (D == 256) return bias_kind != kNoBias ? fwd_d256_bias(dtype, bias_kind) : fwd_d256(dtype);  // no JVP (checked by the caller)
+  if (D == 256) return bias_kind != kNoBias ? fwd_d256_bias(dtype, bias_kind) : fwd_d256(dtype, jvp);
   if (bias_kind != kNoBias) return fwd_bias(dtype, bias_kind, D);
   if (dtype == ATTN_FP32) return fwd_f32(D, Dv, jvp);
   if (Dv != D || D == 16) return dtype == ATTN_BF16 ? fwd_mixed_bf16(D, Dv, jvp) : fwd_mixed_fp16(D, Dv, jvp);
@@ -130,8 +130,9 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
           attn_strides4 sq, attn_strides4 sk, attn_strides4 sv, void* o, void* to, attn_strides4 so, float* lse,
           float* tlse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal,
           void* stream, bool jvp, const BiasOperand& bias = BiasOperand(), int64_t Dv = 0) {
-  const bool plain = !jvp && (Dv == 0 || Dv == D);  // head dim 256: no JVP, equal value dim
-  int rc = check_common(dtype, D, sm_scale, true, plain);
+  // head dim 256: equal value dim; the JVP only on the 16-bit kernels
+  const bool d256 = (Dv == 0 || Dv == D) && !(jvp && dtype == ATTN_FP32);
+  int rc = check_common(dtype, D, sm_scale, true, d256);
   if (rc) return rc;
   if (Dv == 0) Dv = D;
   const bool v16 = Dv == 16;  // a 16-wide value tile (laid out 32 wide in LDS)
@@ -194,6 +195,17 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   (void)hipGetLastError();  // clear a stale error so that finish() reports only ours
   rc = launch(kc, (int)grid, st, a);
   if (rc) return rc;
+  if (jvp && D == 256) {
+    // the 256-wide JVP runs as two launches over the halves of the value
+    // columns (the kernel takes 128 of them); both write the same LSE and tLSE
+    const int64_t half = 128 * 2;  // bytes of 128 16-bit elements
+    a.v = v ? (const char*)v + half : nullptr;  // no keys: V is never read
+    a.tv = tv ? (const char*)tv + half : nullptr;
+    a.o = (char*)o + half;
+    a.to = (char*)to + half;
+    rc = launch(kc, (int)grid, st, a);
+    if (rc) return rc;
+  }
   return finish(st);
 }
 

@@ -404,10 +404,21 @@ struct Bf16Cfg {
   static constexpr bool SPLIT = NW == 8;
   static constexpr int TILE_K = BN * DQK * 2;  // bytes of one K (or tK) tile
   static constexpr int TILE_V = BN * DVL * 2;  // bytes of one V (or tV) tile
-  // tile offsets in a stage: K, V, then tK, tV
-  static constexpr int OFF_V = TILE_K, OFF_TK = TILE_K + TILE_V, OFF_TV = 2 * TILE_K + TILE_V;
   static constexpr int NTEN = JVP ? 4 : 2;  // tensors streamed per key tile
   static constexpr int STAGE = (JVP ? 2 : 1) * (TILE_K + TILE_V);  // bytes of one pipeline stage
+  // Stage layout: K, V, then tK, tV, stage after stage.  When two stages
+  // pass the 16-bit offset of the LDS reads (the JVP with 256-wide queries
+  // and keys) both stages' K-side tiles come first and both stages' V-side
+  // tiles after them, and the V-side reads take that region's start as their
+  // base: VSPLIT.  KSTR / VSTR: bytes from one stage's K-side / V-side tiles
+  // to the next stage's; VBASE: start of the V-side region; OFF_*: a tile's
+  // offset from its side's stage start.
+  static constexpr bool VSPLIT = !SPLIT && 2 * STAGE > 65536;
+  static constexpr int KSTR = VSPLIT ? (JVP ? 2 : 1) * TILE_K : STAGE;
+  static constexpr int VSTR = VSPLIT ? (JVP ? 2 : 1) * TILE_V : STAGE;
+  static constexpr int VBASE = VSPLIT ? 2 * KSTR : 0;
+  static constexpr int OFF_V = VSPLIT ? 0 : TILE_K, OFF_TK = VSPLIT ? TILE_K : TILE_K + TILE_V;
+  static constexpr int OFF_TV = VSPLIT ? TILE_V : 2 * TILE_K + TILE_V;
   static constexpr bool WIDE = (JVP && (DQK == 128 || DV == 128)) || DQK == 256;  // one wave per SIMD
   // floats per lane handed from group 1 to group 0 at the merge: m, l (r),
   // the O accumulator (and accA, accB)
@@ -418,8 +429,11 @@ struct Bf16Cfg {
   static constexpr int CPR_VS = DV / 8;                   // of those, chunks that hold data
   static constexpr int WAVES_PER_EU = WIDE ? 1 : 2;
   static_assert(BN % 32 == 0, "unsupported tile");
-  static_assert(DQK == 16 || DQK == 32 || DQK == 64 || DQK == 128 || (DQK == 256 && DV == 256 && !JVP),
+  // 256-wide queries and keys: the plain forward with 256-wide values, or
+  // the JVP with 128-wide values (a 256-wide JVP runs as two such halves)
+  static_assert(DQK == 16 || DQK == 32 || DQK == 64 || DQK == 128 || (DQK == 256 && DV == (JVP ? 128 : 256)),
                 "unsupported head dim");
+  static_assert(!VSPLIT || (2 * KSTR <= 65536 && 2 * VSTR <= 65536), "each side's two stages within 16-bit offsets");
   static_assert(DV == 16 || DV == 32 || DV == 64 || DV == 128 || DV == 256, "unsupported head dim");
   static_assert(NW == 4 || (NW == 8 && DV == DVL), "8 waves: key-split workgroups of full-width value tiles");
 };
@@ -431,11 +445,11 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int DQK = C::DQK, DV = C::DV, DVL = C::DVL, CPR_VS = C::CPR_VS;
   constexpr int BM = C::BM, NTEN = C::NTEN, STAGE = C::STAGE, TILE_K = C::TILE_K, TILE_V = C::TILE_V;
   constexpr int OFF_V = C::OFF_V, OFF_TK = C::OFF_TK, OFF_TV = C::OFF_TV;
+  constexpr int KSTR = C::KSTR, VSTR = C::VSTR, VBASE = C::VBASE;
   constexpr int CPR_K = C::CPR_K, CPR_V = C::CPR_V;
   constexpr int THREADS = C::THREADS, NW = C::NW;
   constexpr bool SPLIT = C::SPLIT;
   constexpr int NWD = SPLIT ? 4 : NW;              // waves that fill one tile (a group's)
-  constexpr int SSTR = STAGE;  // bytes from one pipeline stage to the next (a group's two stages are adjacent)
   static_assert(!SPLIT || BIAS == kNoBias, "no score operand with key-split workgroups");
   constexpr int NB = BN / 32;    // 32-key blocks per tile
   constexpr int KD = DQK / 16;   // MFMA steps over the query/key head dim
@@ -511,12 +525,14 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     dch_v[ph] = (lane % CPR_V) ^ swz_f<DVL>(drow_v + RSTEP_V * ph);
     dv0[ph] = (uint32_t)((drow_v * a.v_sn + dch_v[ph] * 8) * 2);
   }
-  auto dma_tile = [&](int j, lds_t* base) {
+  auto dma_tile = [&](int j, int stage) {
     const int64_t k0 = (int64_t)j * BN;
     const char* src[4] = {(const char*)K + k0 * a.k_sn * 2, (const char*)V + k0 * a.v_sn * 2,
                           JVP ? (const char*)TK + k0 * a.k_sn * 2 : nullptr,
                           JVP ? (const char*)TV + k0 * a.v_sn * 2 : nullptr};
-    const int toff[4] = {0, OFF_V, OFF_TK, OFF_TV};
+    lds_t* const base = smem_g;
+    const int toff[4] = {stage * KSTR, VBASE + stage * VSTR + OFF_V, stage * KSTR + OFF_TK,
+                         VBASE + stage * VSTR + OFF_TV};
     const int64_t step_b[2] = {(int64_t)RSTEP_K * a.k_sn * 2, (int64_t)RSTEP_V * a.v_sn * 2};
     if (k0 + BN <= t.Lkv) {
 #pragma unroll
@@ -655,16 +671,16 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       const bool ahead = j + 1 < n_mine;
       if (ahead) {  // in flight while this tile computes
         bias_load(jt + 1, std::integral_constant<int, SN>{});
-        dma_tile(jt + 1, smem_g + SN * SSTR);
+        dma_tile(jt + 1, SN);
       }
 
       if (j < n_mine && jt * BN < wave_max) {  // wave-uniform: skip tiles this wave cannot see
-        const lds_t* vt = smem_g + S * SSTR + OFF_V;  // V tile (the cold residual pass reads it)
+        const lds_t* vt = smem_g + VBASE + S * VSTR + OFF_V;  // V tile (the cold residual pass reads it)
 
         // S^T = K Q^T (and the tangent scores tQ K^T + Q tK^T)
         f32x16 s[NB];
         f32x16 ts[JVP ? NB : 1];
-        scores_section<DQK, NB, JVP, S * SSTR, S * SSTR + OFF_TK, F16>(kaddr, qf, tqf, s, ts);
+        scores_section<DQK, NB, JVP, S * KSTR, S * KSTR + OFF_TK, F16>(kaddr, qf, tqf, s, ts);
 
         // mask keys past this row's limit (ragged tail, causal diagonal,
         // jagged truncation) -- only on tiles that reach some row's limit
@@ -744,8 +760,8 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         constexpr int EPS = 8 / DB;  // elements of the next chunk per PV step
         static_for<8>(soft);
         // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
-        pv_section<DVL, NB, JVP, S * SSTR + OFF_V, S * SSTR + OFF_TV, F16>(
-            lds_g, vlo, vhi, pf, hf, acc, accA, accB, [&](auto i_tag) {
+        pv_section<DVL, NB, JVP, S * VSTR + OFF_V, S * VSTR + OFF_TV, F16>(
+            lds_g + VBASE, vlo, vhi, pf, hf, acc, accA, accB, [&](auto i_tag) {
               constexpr int i = decltype(i_tag)::value, c = i / DB;
               if constexpr (c + 1 < 2 * NB) {
                 static_for<EPS>([&](auto k_tag) {
@@ -768,14 +784,14 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       constexpr int NVT = JVP ? 2 : 1, PADC = CPR_V - CPR_VS;
       for (int id = tid; id < 2 * NVT * BN * PADC; id += THREADS) {
         const int c = CPR_VS + id % PADC, row = (id / PADC) % BN, st = id / (PADC * BN);
-        const int off = (st >> 1) * STAGE + ((st & 1) ? OFF_TV : OFF_V) + swz_off<DVL>(row, c);
+        const int off = VBASE + (st >> 1) * VSTR + ((st & 1) ? OFF_TV : OFF_V) + swz_off<DVL>(row, c);
         *(__attribute__((address_space(3))) u32x4*)(smem + off) = u32x4{0u, 0u, 0u, 0u};
       }
     }
 
     if (n0 > 0) {
       bias_load(0, std::integral_constant<int, 0>{});
-      if (n_mine > 0) dma_tile(jbase, smem_g);
+      if (n_mine > 0) dma_tile(jbase, 0);
       __syncthreads();
       int j = 0;
       for (; j + 2 <= n0; j += 2) {

@@ -1,12 +1,16 @@
-// Head dim 256, forward without tangents (dense, causal, jagged, and with a
-// bias or mask): 32-key tiles and one wave per SIMD, so that the 256-column
-// accumulator (128 registers per lane) and the Q fragments fit; bf16, fp16
-// and fp32.
+// Head dim 256 (dense, causal, jagged, and with a bias or mask): 32-key
+// tiles and one wave per SIMD, so that the 256-column accumulator (128
+// registers per lane) and the Q fragments fit; bf16, fp16 and fp32.  The
+// 16-bit JVP takes 128 value columns per launch (the caller runs it once per
+// half): its three accumulators over 256 columns would not fit beside the Q
+// and tQ fragments.
 #include "../../include/attn.h"
 #include "attn_instances.h"
 
 namespace attn {
-KernelChoice fwd_d256(int dtype) {
+KernelChoice fwd_d256(int dtype, bool jvp) {
+  if (jvp) return dtype == ATTN_FP16 ? r32<256, 32, true, 4, true, kNoBias, 128>()
+                                     : r32<256, 32, true, 4, false, kNoBias, 128>();
   if (dtype == ATTN_BF16) return r32<256, 32, false, 4, false>();
   if (dtype == ATTN_FP16) return r32<256, 32, false, 4, true>();
   return f32k<256, false>();

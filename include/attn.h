@@ -30,9 +30,9 @@
  *   the strides of O (as the JVP page's wrapper requires).
  * - Supported head dims: 16, 32, 64 and 128 everywhere (the forward, plain,
  *   biased or jagged, either side of attn_fwd_dv, the JVP and the backward);
- *   256 everywhere except the JVP and unequal value dims (attn_fwd,
- *   attn_fwd_bias, jagged_attn_fwd, attn_fwd_dv with Dqk = Dv = 256, and the
- *   three backward calls).  dtype ATTN_BF16 (ATTN_FP16) computes
+ *   256 everywhere except the fp32 JVP and unequal value dims (attn_fwd,
+ *   attn_fwd_bias, jagged_attn_fwd, attn_fwd_jvp in bf16 and fp16,
+ *   attn_fwd_dv with Dqk = Dv = 256, and the three backward calls).  dtype ATTN_BF16 (ATTN_FP16) computes
  *   the products on bf16 (fp16) MFMA with fp32 accumulation and rounds O/tO to
  *   the input format (RNE); ATTN_FP32 computes everything in fp32.  LSE is
  *   always fp32.

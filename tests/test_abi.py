@@ -264,12 +264,14 @@ def test_bwd_bias_validation(lib):
 
 
 def test_d256_paths(lib):
-    """Head dim 256 runs the forward (biased or not) and the backward; the
-    16-bit JVP and unequal value dims at 256 are not built."""
+    """Head dim 256 runs the forward (biased or not), the 16-bit JVP and the
+    backward; the fp32 JVP and unequal value dims at 256 are not built."""
     B, H, N, D = 0, 2, 128, 256  # B = 0: nothing is enqueued when the call is accepted
     st = dense_strides(1, H, N, D)
     assert call_fwd(lib, D=256, B=0) == OK
-    assert lib.attn_fwd_jvp(BF16, P, P, P, P, P, P, st, st, st, P, P, st, P, None, 1, H, N, N, D, 0.1, 0, None) \
+    for dt in (BF16, FP16):
+        assert lib.attn_fwd_jvp(dt, P, P, P, P, P, P, st, st, st, P, P, st, P, None, 0, H, N, N, D, 0.1, 0, None) == OK
+    assert lib.attn_fwd_jvp(FP32, P, P, P, P, P, P, st, st, st, P, P, st, P, None, 1, H, N, N, D, 0.1, 0, None) \
         == UNSUPPORTED
     full = Strides4(H * N * N, N * N, N, 1)
     assert lib.attn_fwd_bias(BF16, P, st, P, st, P, st, P, st, P, P, 1, full, 0, H, N, N, D, 0.1, 0, None) == OK

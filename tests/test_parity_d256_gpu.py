@@ -1,7 +1,8 @@
 """GPU parity at head dim 256 against the fp64 oracle, with the tolerances
 of each dtype: the forward (dense, causal, jagged, biased; bf16, fp16,
-fp32) and the backward (dense, jagged, biased; bf16, fp16).  The 256-wide
-kernels use 32-key tiles and one wave per SIMD."""
+fp32), the JVP (bf16, fp16; two launches over the halves of the value
+columns) and the backward (dense, jagged, biased; bf16, fp16).  The
+256-wide kernels use 32-key tiles and one wave per SIMD."""
 
 import pytest
 
@@ -63,3 +64,16 @@ def test_d256_bias_backward(gpu_lib, dtype, causal):
     bias_bwd_case(2, 2, 300, 300, 256, dtype, causal, "add", seed=245)
     bias_bwd_case(2, 2, 300, 300, 256, dtype, causal, "mask", seed=246)
     bias_bwd_case(2, 2, 200, 200, 256, dtype, causal, "add", bshape=(1, 2, 200, 200), seed=247)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_jvp(gpu_lib, dtype, causal):
+    """O, tO, LSE at head dim 256: ragged tiles, one row and (non-causal)
+    cross-attention; each value half comes from its own launch, both write
+    the same LSE."""
+    from test_parity_gpu import jvp_case
+    jvp_case(2, 2, 300, 300, 256, dtype, causal, seed=251)
+    jvp_case(1, 2, 1, 1, 256, dtype, causal, seed=252)
+    if not causal:
+        jvp_case(1, 2, 77, 333, 256, dtype, False, seed=253)
