@@ -95,8 +95,8 @@ int cu_count() {
 // each tile's key range in halves merged at the end, so that both waves of
 // a SIMD stay busy and the heaviest tiles take half as many steps.  Larger
 // grids balance well enough by heaviest-first dispatch and keep 4-wave
-// workgroups.  The D=128 JVP instance runs one wave per SIMD and is never
-// split.
+// workgroups.  The JVP at D = 128 (two launches over the value halves) is
+// never split.
 bool use_split(int dtype, int D, bool jvp, bool dense_causal, int64_t grid) {
   return dtype != ATTN_FP32 && dense_causal && !(jvp && D == 128) && grid <= 4 * (int64_t)cu_count();
 }
@@ -112,6 +112,7 @@ KernelChoice choose(int dtype, int D, bool jvp, bool split, int bias_kind, int D
 }
 
 int launch(const KernelChoice& k, int grid, hipStream_t stream, const FwdArgs& a) {
+  if (k.fn == nullptr) return ATTN_ERR_UNSUPPORTED;  // no instance for this combination
   if (k.lds > 65536 &&
       hipFuncSetAttribute(reinterpret_cast<const void*>(k.fn), hipFuncAttributeMaxDynamicSharedMemorySize, k.lds) != hipSuccess)
     return ATTN_ERR_HIP;
@@ -165,7 +166,13 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   const int64_t n_qtiles = (Nq + 127) / 128;  // every bf16 instance uses 128-row q-tiles
   const bool split =
       bias_kind == kNoBias && Dv == D && D != 256 && D != 16 && use_split(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
-  const KernelChoice kc = choose(dtype, (int)D, jvp, split, bias_kind, (int)Dv);
+  // The 16-bit JVP at D = 128 and 256 runs as two launches over the halves of
+  // the value columns: its three value accumulators over all D columns hold
+  // a wave to one per SIMD (and spill at 256), over D / 2 columns two waves
+  // share a SIMD at 128.  Each launch recomputes the scores (1.5x the
+  // products); at 128 the pair still ran 1.35x faster, with identical bits.
+  const bool halves = jvp && dtype != ATTN_FP32 && bias_kind == kNoBias && Dv == D && (D == 128 || D == 256);
+  const KernelChoice kc = choose(dtype, (int)D, jvp, split, bias_kind, (int)(halves ? Dv / 2 : Dv));
   const int BM = kc.BM;
   const int64_t n_qtiles_k = (Nq + BM - 1) / BM;
   const int64_t grid = B * H * (split ? (n_qtiles_k + 1) / 2 : n_qtiles_k);
@@ -195,10 +202,8 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   (void)hipGetLastError();  // clear a stale error so that finish() reports only ours
   rc = launch(kc, (int)grid, st, a);
   if (rc) return rc;
-  if (jvp && D == 256) {
-    // the 256-wide JVP runs as two launches over the halves of the value
-    // columns (the kernel takes 128 of them); both write the same LSE and tLSE
-    const int64_t half = 128 * 2;  // bytes of 128 16-bit elements
+  if (halves) {  // the second half of the value columns; both launches write the same LSE and tLSE
+    const int64_t half = Dv / 2 * 2;  // bytes of Dv / 2 16-bit elements
     a.v = v ? (const char*)v + half : nullptr;  // no keys: V is never read
     a.tv = tv ? (const char*)tv + half : nullptr;
     a.o = (char*)o + half;

@@ -419,7 +419,10 @@ struct Bf16Cfg {
   static constexpr int VBASE = VSPLIT ? 2 * KSTR : 0;
   static constexpr int OFF_V = VSPLIT ? 0 : TILE_K, OFF_TK = VSPLIT ? TILE_K : TILE_K + TILE_V;
   static constexpr int OFF_TV = VSPLIT ? TILE_V : 2 * TILE_K + TILE_V;
-  static constexpr bool WIDE = (JVP && (DQK == 128 || DV == 128)) || DQK == 256;  // one wave per SIMD
+  // one wave per SIMD: 128-wide JVP accumulators (three of 64 registers) or
+  // 256-wide queries and keys; the JVP with 128-wide queries and keys and at
+  // most 64 value columns keeps two (at 64 with a 72-byte spill, still faster)
+  static constexpr bool WIDE = (JVP && DV == 128) || DQK == 256;
   // floats per lane handed from group 1 to group 0 at the merge: m, l (r),
   // the O accumulator (and accA, accB)
   static constexpr int NVM = (JVP ? 3 : 2) + (DVL / 32) * 16 * (JVP ? 3 : 1);

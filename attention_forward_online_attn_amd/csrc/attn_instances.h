@@ -21,14 +21,20 @@ KernelChoice f32k() {
 }
 
 // 16-bit forward with equal head dims; `split`: 8-wave workgroups whose two
-// halves split a query tile's key range (never the D=128 JVP instance, one
-// wave per SIMD).
+// halves split a query tile's key range.  The JVP at 128 has no instance
+// here: it runs as two launches of the (128, 64) value-dim instance over the
+// halves of the value columns.
 template <bool F16>
 KernelChoice choose16(int D, bool jvp, bool split) {
   return by_dim(D, [&](auto d) {
     constexpr int Dc = decltype(d)::value;
-    if (split) return !jvp ? r32<Dc, kBnDense, false, 8, F16>() : r32<Dc == 128 ? 64 : Dc, kBnJvp, true, 8, F16>();
-    return !jvp ? r32<Dc, kBnDense, false, 4, F16>() : r32<Dc, kBnJvp, true, 4, F16>();
+    if constexpr (Dc == 128) {
+      if (jvp) return KernelChoice{};
+      return split ? r32<Dc, kBnDense, false, 8, F16>() : r32<Dc, kBnDense, false, 4, F16>();
+    } else {
+      if (split) return !jvp ? r32<Dc, kBnDense, false, 8, F16>() : r32<Dc, kBnJvp, true, 8, F16>();
+      return !jvp ? r32<Dc, kBnDense, false, 4, F16>() : r32<Dc, kBnJvp, true, 4, F16>();
+    }
   });
 }
 
