@@ -166,12 +166,13 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   const int64_t n_qtiles = (Nq + 127) / 128;  // every bf16 instance uses 128-row q-tiles
   const bool split =
       bias_kind == kNoBias && Dv == D && D != 256 && D != 16 && use_split(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
-  // The 16-bit JVP at D = 128 and 256 runs as two launches over the halves of
-  // the value columns: its three value accumulators over all D columns hold
-  // a wave to one per SIMD (and spill at 256), over D / 2 columns two waves
-  // share a SIMD at 128.  Each launch recomputes the scores (1.5x the
-  // products); at 128 the pair still ran 1.35x faster, with identical bits.
-  const bool halves = jvp && dtype != ATTN_FP32 && bias_kind == kNoBias && Dv == D && (D == 128 || D == 256);
+  // The 16-bit JVP with 128 value columns (any query/key dim) or at
+  // D = Dv = 256 runs as two launches over the halves of the value columns:
+  // three value accumulators over 128 columns hold a wave to one per SIMD
+  // (at 256 they spill), over 64 columns two waves share a SIMD.  Each
+  // launch recomputes the scores, yet the pair ran 1.2x to 1.5x faster at
+  // Dv = 128, with identical bits (every column sees the same products).
+  const bool halves = jvp && dtype != ATTN_FP32 && bias_kind == kNoBias && (Dv == 128 || (D == 256 && Dv == 256));
   const KernelChoice kc = choose(dtype, (int)D, jvp, split, bias_kind, (int)(halves ? Dv / 2 : Dv));
   const int BM = kc.BM;
   const int64_t n_qtiles_k = (Nq + BM - 1) / BM;

@@ -48,6 +48,8 @@ KernelChoice choose_mixed16(int D, int Dv, bool jvp) {
       // equal dims other than 16 take choose16 (no instance twice in the library)
       if constexpr (A == V && A != 16) {
         return KernelChoice{};
+      } else if constexpr (V == 128) {  // the JVP with 128 value columns runs as two (A, 64) halves
+        return jvp ? KernelChoice{} : r32<A, kBnDense, false, 4, F16, kNoBias, V>();
       } else {
         return jvp ? r32<A, kBnJvp, true, 4, F16, kNoBias, V>() : r32<A, kBnDense, false, 4, F16, kNoBias, V>();
       }
