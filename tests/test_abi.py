@@ -234,7 +234,7 @@ def test_dv_validation(lib):
     assert call(Dqk=48) == UNSUPPORTED
     assert call(Dqk=16, Dv=16, B=0) == OK
     assert call(Dqk=16, Dv=32, B=0) == OK
-    assert call(Dqk=128, Dv=16, tq=P, tk=P, tv=P, to=P, B=0) == OK  # the one-wave 128-wide JVP with 16-wide values
+    assert call(Dqk=128, Dv=16, tq=P, tk=P, tv=P, to=P, B=0) == OK  # the 128-wide JVP with 16-wide values
     assert call(tk=P) == INVALID          # tangents without tq: not a JVP call
     assert call(to=P) == INVALID
     assert call(tq=P, tk=P, tv=P) == INVALID  # JVP without to
