@@ -1,6 +1,9 @@
-// Head dim 256 (dense, causal, jagged, and with a bias or mask): 32-key
-// tiles and one wave per SIMD, so that the 256-column accumulator (128
-// registers per lane) and the Q fragments fit; bf16, fp16 and fp32.  The
+// Head dim 256 (dense, causal, jagged, and with a bias or mask): one wave
+// per SIMD, so that the 256-column accumulator (128 registers per lane) and
+// the Q fragments fit; bf16, fp16 and fp32.  The plain 16-bit forward
+// streams 64-key tiles (two stages take 128 KB of LDS in the split K-side /
+// V-side layout; half the barriers per key of 32-key tiles, 4-11% faster);
+// with a bias or mask the 64-key instance would spill, so it keeps 32.  The
 // 16-bit JVP takes 128 value columns per launch (the caller runs it once per
 // half): its three accumulators over 256 columns would not fit beside the Q
 // and tQ fragments.
@@ -11,8 +14,8 @@ namespace attn {
 KernelChoice fwd_d256(int dtype, bool jvp) {
   if (jvp) return dtype == ATTN_FP16 ? r32<256, 32, true, 4, true, kNoBias, 128>()
                                      : r32<256, 32, true, 4, false, kNoBias, 128>();
-  if (dtype == ATTN_BF16) return r32<256, 32, false, 4, false>();
-  if (dtype == ATTN_FP16) return r32<256, 32, false, 4, true>();
+  if (dtype == ATTN_BF16) return r32<256, 64, false, 4, false>();
+  if (dtype == ATTN_FP16) return r32<256, 64, false, 4, true>();
   return f32k<256, false>();
 }
 
