@@ -20,7 +20,10 @@
 //   through LDS: S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
 //   dK^T += Q^T dS through the transposing Q and dO reads.
 // Each output element is written once by one lane: no atomics, and the
-// result does not depend on the order of the work.
+// result does not depend on the order of the work.  Head dim 16 runs on the
+// 32-wide tiles with a zero upper half; at head dim 256 the dK/dV kernel
+// runs twice over the same key tiles (dV, then dK), since K, V and both
+// accumulators exceed one wave's registers.
 #pragma once
 
 #include "attn_fwd_bf16.h"
