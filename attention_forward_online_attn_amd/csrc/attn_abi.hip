@@ -357,7 +357,10 @@ int jagged_attn_bwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
   if (((uintptr_t)lse & 3u) != 0) return ATTN_ERR_UNSUPPORTED;
   const int64_t cap = plan_capacity(num_seqs, total_len, 128);
-  if (cap * H > INT_MAX) return ATTN_ERR_INVALID;
+  // grids within an int (checked again by bwd_run, after the plan kernel has
+  // been enqueued): the gradient kernels' cap H items and the prep kernel's
+  // H total_len rows at 8 or more rows per block
+  if (cap * H > INT_MAX || H * total_len / 8 > INT_MAX) return ATTN_ERR_INVALID;
   const size_t need = jagged_attn_bwd_workspace_bytes(num_seqs, H, total_len);
   if (need == 0) return ATTN_ERR_INVALID;
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u)) return ATTN_ERR_WORKSPACE;
@@ -450,7 +453,7 @@ int dense_bwd(attn_dtype dtype, const void* q, attn_strides4 q_strides, const vo
     if (!aligned16(dbias)) return ATTN_ERR_UNSUPPORTED;
   }
   const int64_t rows = B * H * Nq;  // B H <= INT_MAX, Nq <= INT_MAX: no overflow
-  if (B * H * ((Nq + 127) / 128) > INT_MAX || B * H * ((Nkv + 127) / 128) > INT_MAX || rows / 16 > INT_MAX)
+  if (B * H * ((Nq + 127) / 128) > INT_MAX || B * H * ((Nkv + 127) / 128) > INT_MAX || rows / 8 > INT_MAX)
     return ATTN_ERR_INVALID;
   if (rows > 0 && (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, Nq) || ((uintptr_t)workspace & 15u)))
     return ATTN_ERR_WORKSPACE;

@@ -25,14 +25,19 @@
 // * K and V live in LDS in their natural [key][d] layout with a 16-byte chunk
 //   XOR swizzle; K fragments are ds_read_b128, V^T fragments come from the
 //   transposing ds_read_b64_tr_b16.  Both are bank-conflict free.
-// * Lazy rescaling: the running max used for p only moves when a row's max
-//   grows by more than kTau (in log2 units), so p <= 2^kTau and the O
-//   rescale is skipped on almost every tile; m, l and acc always share the
-//   same reference, so the result is the same identity up to rounding.  The
-//   biased kernels keep the exact running max instead: with it the largest p
-//   of a row is exp2(0) = 1, which the 16-bit P holds exactly, and a bias
-//   makes rows peaked enough that the rounding of that one term would
-//   otherwise show in O.
+// * Lagged rescaling: the running max used for p only moves when a row's
+//   max passes it by more than the row's lag (log2 units), so the O rescale
+//   is skipped on almost every tile; m, l and acc always share the same
+//   reference, so the result is the same identity up to rounding.  The lag
+//   is set after each rescale to log2(l) - 1 (row sum l relative to the new
+//   max), clamped to [0, kTau]: a term taken without a rescale then has
+//   p <= l / 2, i.e. at most a third of the row's final weight.  A row that
+//   one key dominates therefore has that key's p = exp2(0) = 1, exact in the
+//   16-bit P, as with the exact running max; spread rows, whose l grows fast,
+//   reach the full lag kTau after a tile or two.  The biased kernels and the
+//   fp16 JVP keep the exact running max (lag 0): the first because a bias
+//   makes rows peaked by construction, the second so that |p| <= 1 keeps the
+//   fp16 H = p * scale * tS within the range of the page's own formulation.
 // * Per key tile: the next tile is copied straight from global memory into
 //   the other LDS stage (global_load_lds_dwordx4, no staging registers); the
 //   copies stay in flight through the tile's two MFMA sections (scores, then
@@ -52,8 +57,7 @@
 
 namespace attn {
 
-constexpr float kTau = 8.0f;       // lazy rescale threshold (log2 units)
-constexpr float kTauBias = 0.0f;   // biased kernels: exact running max
+constexpr float kTau = 8.0f;  // largest lag of the running max (log2 units): p <= 2^kTau
 
 // Waves whose rows attend at most this many keys add P's bf16 rounding
 // residual to the PV product (the lo pass below).  With more keys the
@@ -134,6 +138,20 @@ __device__ __forceinline__ float xhalf_max(float x) {
 __device__ __forceinline__ float xhalf_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Minimum over lanes 0..31 of a non-negative float, as a wave-uniform
+// (scalar) value; every lane active.  Non-negative floats order as their bit
+// patterns, so the 16-lane steps (DPP: quad swaps, half-row and row mirrors)
+// and the final pick between the two rows are unsigned minima.
+__device__ __forceinline__ float wave_min32_nonneg(float x) {
+  unsigned u = __float_as_uint(x);
+  u = min(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  u = min(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  u = min(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  u = min(u, (unsigned)__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, false));  // row_mirror
+  const unsigned a = __builtin_amdgcn_readlane(u, 0), b = __builtin_amdgcn_readlane(u, 16);
+  return __uint_as_float(min(a, b));
 }
 
 // A operand of O^T += V^T P^T for output columns 32*db .. 32*db+31 and keys
@@ -407,10 +425,11 @@ struct Bf16Cfg {
   static constexpr int NTEN = JVP ? 4 : 2;  // tensors streamed per key tile
   static constexpr int STAGE = (JVP ? 2 : 1) * (TILE_K + TILE_V);  // bytes of one pipeline stage
   // Stage layout: K, V, then tK, tV, stage after stage.  When two stages
-  // pass the 16-bit offset of the LDS reads (the JVP with 256-wide queries
-  // and keys) both stages' K-side tiles come first and both stages' V-side
-  // tiles after them, and the V-side reads take that region's start as their
-  // base: VSPLIT.  KSTR / VSTR: bytes from one stage's K-side / V-side tiles
+  // pass the 16-bit offset of the LDS reads (256-wide queries and keys: the
+  // plain forward on 64-key tiles and the JVP on 32-key tiles; the biased
+  // 256-wide instances keep 32-key tiles and fit) both stages' K-side tiles
+  // come first and both stages' V-side tiles after them, and the V-side
+  // reads take that region's start as their base: VSPLIT.  KSTR / VSTR: bytes from one stage's K-side / V-side tiles
   // to the next stage's; VBASE: start of the V-side region; OFF_*: a tile's
   // offset from its side's stage start.
   static constexpr bool VSPLIT = !SPLIT && 2 * STAGE > 65536;
@@ -431,6 +450,10 @@ struct Bf16Cfg {
   static constexpr int CPR_K = DQK / 8, CPR_V = DVL / 8;  // 16-byte chunks per row (in LDS)
   static constexpr int CPR_VS = DV / 8;                   // of those, chunks that hold data
   static constexpr int WAVES_PER_EU = WIDE ? 1 : 2;
+  // The plain 4-wave forward at head dims up to 64 fits 128 registers (four
+  // waves per SIMD) with no room for a per-row lag of the running max: its
+  // waves share one lag in a scalar register.
+  static constexpr bool WAVE_LAG = !JVP && NW == 4 && DQK <= 64;
   static_assert(BN % 32 == 0, "unsupported tile");
   // 256-wide queries and keys: the plain forward with 256-wide values, or
   // the JVP with 128-wide values (a 256-wide JVP runs as two such halves)
@@ -647,10 +670,19 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     // scale of the scores into the exp2 domain at the softmax (1 once an
     // additive bias has been applied)
     const float cs = BIAS == kAddBias ? 1.f : a.c;
+    // the running max lags (see the header); the biased kernels and the fp16
+    // JVP keep it exact
+    constexpr bool LAGGED = BIAS == kNoBias && !(F16 && JVP);
+    // fp16 JVP: H = p * (scale tS), the tangent scores scaled before the
+    // product as the JVP pages order it, so H stays within fp16's range
+    constexpr bool HS = F16 && JVP;
 
     float m_run = -INFINITY;  // running max, exp2 domain (scores times c)
     float l_run = 0.f;        // this lane's partial row sum (its 16 of every 32 keys)
-    float r_run = 0.f;        // JVP: partial rowsum of p * (tQ K^T + Q tK^T)
+    float r_run = 0.f;        // JVP: partial rowsum of p * (tQ K^T + Q tK^T) (HS: times scale)
+    // how far a tile's max may pass m_run without a rescale (see the header;
+    // with C::WAVE_LAG one value for the wave, the smallest of its rows')
+    float lag = 0.f;
     // lane-dependent LDS offsets of the K fragments (per head-dim step) and of
     // the V^T fragments (per output column block); tile, block and stage
     // positions are added as immediates.  The swizzle depends on the row mod 16,
@@ -706,8 +738,9 @@ attn_fwd_bf16_kernel(FwdArgs a) {
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
         mx = xhalf_max(mx);
         const float m_new = mx * cs;
-        const bool upd = m_new > m_run + (BIAS != kNoBias ? kTauBias : kTau);
-        if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+        const bool upd = m_new > m_run + lag;
+        const bool rescaled = __builtin_amdgcn_ballot_w64(upd) != 0;  // wave-uniform
+        if (rescaled) {
           const float m_next = upd ? m_new : m_run;
           const float alpha = m_next == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_next);
 #pragma unroll
@@ -755,7 +788,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
           l_run += p;
           pf[b][r >> 3][r & 7] = to16<F16>(p);
           if constexpr (JVP) {
-            const float hv = p * ts[b][r];
+            const float hv = HS ? p * (ts[b][r] * a.sm_scale) : p * ts[b][r];
             r_run += hv;
             hf[b][r >> 3][r & 7] = to16<F16>(hv);
           }
@@ -772,6 +805,16 @@ attn_fwd_bf16_kernel(FwdArgs a) {
                 });
               }
             });
+        // the row's lag, log2(l) - 1 clamped to [0, kTau] (l = 0, no key yet,
+        // gives 0), from l_run as it stands after this tile's terms: after a
+        // rescale, and on tiles 0, 1, 3, 7, ... (l grows about linearly with
+        // the keys seen, so its log2 by about one per doubling)
+        if constexpr (LAGGED) {
+          if (rescaled || (j & (j + 1)) == 0) {
+            const float g = fminf(kTau, fmaxf(0.f, __log2f(xhalf_sum(l_run)) - 1.f));
+            lag = C::WAVE_LAG ? wave_min32_nonneg(g) : g;  // lanes l and l ^ 32 share a row
+          }
+        }
       }
 
       __syncthreads();
@@ -860,7 +903,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       const bool empty = !(l_tot > 0.f);
       const float inv = empty ? 0.f : 1.f / l_tot;
       const float lse = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
-      const float r_tot = JVP ? xhalf_sum(r_run) * a.sm_scale : 0.f;
+      const float r_tot = JVP ? xhalf_sum(r_run) * (HS ? 1.f : a.sm_scale) : 0.f;
       if (my_row < t.Lstore) {
         bf16* orow = (bf16*)a.o + t.o_off + my_row * a.o_sn;
         bf16* torow = JVP ? (bf16*)a.to + t.o_off + my_row * a.o_sn : nullptr;
@@ -877,7 +920,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
               const float o = acc[db][4 * g + e] * inv;
               ov[e] = to16<F16>(o);
               if constexpr (JVP)
-                tov[e] = to16<F16>((accA[db][4 * g + e] + a.sm_scale * accB[db][4 * g + e] - r_tot * o) * inv);
+                tov[e] = to16<F16>((accA[db][4 * g + e] + (HS ? 1.f : a.sm_scale) * accB[db][4 * g + e] - r_tot * o) * inv);
             }
             *(bf16x4*)(orow + d) = ov;
             if constexpr (JVP) *(bf16x4*)(torow + d) = tov;

@@ -40,8 +40,10 @@
  *   by default D^-0.5).
  * - Sizes: Nq, Nkv, total_len and num_seqs + 1 at most 2^31 - 1, and
  *   B * H at most 2^31 - 1 (the device indexes rows, tiles and (batch, head)
- *   pairs with 32-bit integers); larger extents are ATTN_ERR_INVALID, and the
- *   workspace-size functions return 0 for extents they cannot serve.
+ *   pairs with 32-bit integers); every launch grid within 2^31 - 1 blocks (for
+ *   the backward: B * H * Nq, or H * total_len, at most 8 (2^31 - 1) rows);
+ *   larger extents are ATTN_ERR_INVALID, and the workspace-size functions
+ *   return 0 for extents they cannot serve.
  * - A query row with no key to attend (Nkv == 0, or a jagged row beyond
  *   max_seq_len inside its sequence) gets O = 0, tO = 0 and LSE = -inf.
  * - All argument checks happen on the host before anything is enqueued; a

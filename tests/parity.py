@@ -48,8 +48,11 @@ def bf16_floor(ref):
     return float((r.bfloat16().double() - torch.from_numpy(np.ascontiguousarray(ref))).abs().max()) if r.numel() else 0.0
 
 
-def assert_close(dtype, o, lse, o_ref, lse_ref, to=None, to_ref=None, label=""):
-    tol = TOL[dtype]
+def assert_close(dtype, o, lse, o_ref, lse_ref, to=None, to_ref=None, label="", v_std=1.0):
+    """The bounds above for N(0, 1) values; with values of spread v_std, O
+    and its absolute error scale by v_std, and so does the O bound."""
+    tol = dict(TOL[dtype])
+    tol["o"] *= v_std
     eo = max_err(o, o_ref)
     el = lse_err(lse, lse_ref)
     msg = f"{label}: max|dO|={eo:.3e} (tol {tol['o']:.0e}), max|dLSE|={el:.3e} (tol {tol['lse']:.0e})"
@@ -63,3 +66,19 @@ def assert_close(dtype, o, lse, o_ref, lse_ref, to=None, to_ref=None, label=""):
         ok = ok and et <= tol["to"]
     print(msg, flush=True)
     assert ok, msg
+
+
+# Peaked rows (one key carries most of a row's weight): O tracks single
+# values of V, so storing O in bf16 alone costs up to half an ulp of |O|
+# (7.8e-3 for |O| in [2, 4)).  Beyond that storage floor the kernel's own
+# error comes from P's 16-bit rounding; with the dominant term taken at the
+# exact running max (p = 1, no rounding) it stays far below this margin.
+PEAKED_MARGIN = 2e-3
+
+
+def assert_within_floor(o, o_ref, label="", margin=PEAKED_MARGIN):
+    """max|O - O_ref| <= (bf16 storage floor of O_ref) + margin."""
+    eo, fl = max_err(o, o_ref), bf16_floor(o_ref)
+    msg = f"{label}: max|dO|={eo:.3e}, bf16 floor={fl:.3e}, excess={eo - fl:.2e} (margin {margin:.0e})"
+    print(msg, flush=True)
+    assert eo <= fl + margin, msg

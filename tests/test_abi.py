@@ -199,6 +199,20 @@ def test_bwd_validation(lib):
     assert zero == OK
 
 
+def test_bwd_grid_bounds(lib):
+    """The backward's prep kernel takes 8 rows per block at head dim 256: B H
+    Nq = 2^34 rows would need 2^31 blocks, one past an int grid.  Rejected
+    on the host, before anything is enqueued (the pointers are never used)."""
+    B, H, N, D = 1, 1 << 20, 1 << 14, 256
+    st = dense_strides(B, H, N, D)
+    need = lib.attn_bwd_workspace_bytes(B, H, N)
+    assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st,
+                        B, H, N, N, D, 0.0625, 0, P, need, None) == INVALID
+    sj = Strides3(N * D, D, 1)
+    assert lib.jagged_attn_bwd(BF16, P, sj, P, sj, P, sj, P, sj, P, sj, P, P, sj, P, sj, P, sj,
+                               P, 1, H, N, D, N, 0.0625, 0, P, 1 << 40, None) == INVALID
+
+
 def test_jagged_bwd_validation(lib):
     H, T, D, S = 2, 100, 64, 3
     st = Strides3(T * D, D, 1)

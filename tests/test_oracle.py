@@ -363,3 +363,42 @@ def test_value_head_dim_differs(Dqk, Dv, causal):
         return torch.softmax(s, dim=-1) @ c
     _, rto = torch.func.jvp(f, (t(q), t(k), t(v)), (t(tq), t(tk), t(tv)))
     np.testing.assert_allclose(to, rto.numpy(), rtol=0, atol=1e-12)
+
+
+def _decode16(bits, exp_bits, man_bits):
+    """IEEE-style binary16 layouts decoded from their definition: sign bit,
+    exp_bits of biased exponent, man_bits of fraction; exponent 0 is
+    subnormal (fraction * 2^(1 - bias - man_bits)), all ones is inf / NaN."""
+    b = bits.astype(np.int64)
+    sign = np.where((b >> (exp_bits + man_bits)) & 1, -1.0, 1.0)
+    e = (b >> man_bits) & ((1 << exp_bits) - 1)
+    f = (b & ((1 << man_bits) - 1)).astype(np.float64)
+    bias = (1 << (exp_bits - 1)) - 1
+    top = (1 << exp_bits) - 1
+    normal = np.ldexp(f + (1 << man_bits), (e - bias - man_bits).astype(np.int64))
+    sub = np.ldexp(f, np.full(e.shape, 1 - bias - man_bits, np.int64))
+    val = np.where(e == 0, sub, normal)
+    val = np.where(e == top, np.where(f == 0, np.inf, np.nan), val)
+    return sign * val
+
+
+@pytest.mark.parametrize("dtype,exp_bits,man_bits", [(torch.bfloat16, 8, 7), (torch.float16, 5, 10)])
+def test_as_f64_widens_16bit_tensors_exactly(dtype, exp_bits, man_bits):
+    """The widening every GPU parity test feeds through the oracle: all 65536
+    bit patterns of the format (zeros, subnormals, the largest finite values,
+    infinities, NaNs) as a CPU tensor become exactly the decoded value."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    x = torch.from_numpy(bits.view(np.int16).copy()).view(dtype)
+    got = oracle.as_f64(x)
+    want = _decode16(bits, exp_bits, man_bits)
+    assert got.dtype == np.float64 and got.shape == want.shape
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))  # -0.0 stays -0.0
+    # spot values of the format's range
+    tiny = 2.0 ** (2 - (1 << (exp_bits - 1)) - man_bits)  # smallest subnormal
+    assert got[1] == tiny and got[0x8001] == -tiny
+    top = (1 << exp_bits) - 2
+    largest = (2.0 - 2.0 ** -man_bits) * 2.0 ** (top - ((1 << (exp_bits - 1)) - 1))
+    assert got[(top << man_bits) | ((1 << man_bits) - 1)] == largest

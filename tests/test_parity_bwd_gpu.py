@@ -21,7 +21,7 @@ import torch
 import oracle
 import attention_forward_online_attn_amd as attn
 from attention_forward_online_attn_amd import workloads as wl
-from parity import host64
+from parity import assert_close, host64
 
 pytestmark = pytest.mark.gpu
 
@@ -117,10 +117,10 @@ def test_bwd_strided_layouts(gpu_lib):
 
 
 def test_bwd_unscaled_logits(gpu_lib):
-    """sm_scale = 1 with inputs scaled so the logits stay N(0, 1)-like."""
+    """sm_scale = 1 on the N(0, 1) inputs as drawn: raw q.k logits of std 8
+    (the SLL jagged page applies no scale), nearly one-hot rows."""
     B, H, N, D = 1, 2, 256, 64
     q, k, v = wl.dense_inputs(B, H, N, N, D, "bf16", 9)
-    q = (q.float() / 8).bfloat16()
     do = wl.grad_output(q.shape, "bf16", 9)
     qc, kc, vc, doc = (t.cuda() for t in (q, k, v, do))
     o, lse = attn.fwd(qc, kc, vc, causal=True, sm_scale=1.0)
@@ -153,8 +153,13 @@ def test_bwd_full_size_sampled_heads(gpu_lib, causal):
     qc, kc, vc, doc = (t.cuda() for t in (q, k, v, do))
     o, lse = attn.fwd(qc, kc, vc, causal=causal)
     dq, dk, dv = (g.cpu() for g in attn.bwd(qc, kc, vc, o, doc, lse, causal=causal))
-    del qc, kc, vc, doc, o, lse
+    o, lse = host64(o), host64(lse)
+    del qc, kc, vc, doc
     for b, h in ((0, 0), (3, 31), (1, 17)):
         sl = (slice(b, b + 1), slice(h, h + 1))
+        # the forward those gradients start from, on the same whole slice
+        ro, rl = oracle.attention(q[sl], k[sl], v[sl], oracle.scale_as_passed(D ** -0.5), causal)
+        assert_close(torch.bfloat16, o[sl], lse[sl], ro, rl,
+                     label=f"fwd [4,32,4096,128] causal={causal} slice (b={b}, h={h})")
         ref = oracle.attention_bwd(q[sl], k[sl], v[sl], do[sl], oracle.scale_as_passed(D ** -0.5), causal)
         check_grads((dq[sl], dk[sl], dv[sl]), ref, f"bwd [4,32,4096,128] causal={causal} slice (b={b}, h={h})")

@@ -2,7 +2,9 @@
 of each dtype: the forward (dense, causal, jagged, biased; bf16, fp16,
 fp32), the JVP (bf16, fp16; two launches over the halves of the value
 columns) and the backward (dense, jagged, biased; bf16, fp16).  The
-256-wide kernels use 32-key tiles and one wave per SIMD."""
+256-wide kernels run one wave per SIMD; the plain forward streams 64-key
+tiles through the split K-side / V-side LDS layout, the JVP and the biased
+instances 32-key tiles."""
 
 import pytest
 

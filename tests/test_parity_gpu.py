@@ -14,7 +14,7 @@ import torch
 import oracle
 import attention_forward_online_attn_amd as attn
 from attention_forward_online_attn_amd import workloads as wl
-from parity import assert_close, host64
+from parity import assert_close, assert_within_floor, host64
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,10 @@ def jvp_case(B, H, Nq, Nkv, D, dtype, causal, scale=None, seed=0, zero=None, lab
     ro, rto, rl = oracle.attention_jvp(*ts, oracle.scale_as_passed(scale), causal)
     assert_close(DT[dtype], host64(o), host64(lse), ro, rl, host64(to), rto,
                  label=label or f"jvp {B,H,Nq,Nkv,D} {dtype} causal={causal} zero={zero}")
+
+
+# (batch, head) slices of the [4, 32, 4096, 128] workload compared whole
+WHOLE_SLICES = ((0, 0), (3, 31), (1, 17))
 
 
 def sampled_rows(B, H, N, n_rows, tile=128, seed=0):
@@ -80,6 +84,13 @@ def test_long_d128_sampled(gpu_lib, causal, dtype):
     assert_close(DT[dtype], go, gl, ro, rl,
                  label=f"long {dtype} [4,32,4096,128] causal={causal}, {len(rows)} sampled rows")
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    # whole (batch, head) slices: every one of the 4096 rows, all 32 query
+    # tiles of the slice (heads are independent, so the oracle takes a slice)
+    for b, h in WHOLE_SLICES:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        so, sls = oracle.attention(q[sl], k[sl], v[sl], oracle.scale_as_passed(w.sm_scale), causal)
+        assert_close(DT[dtype], oc[sl], lc[sl], so, sls,
+                     label=f"long {dtype} [4,32,4096,128] causal={causal}, whole slice (b={b}, h={h})")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -93,6 +104,11 @@ def test_jvp_d64_sampled(gpu_lib, causal):
     pick = lambda a: np.stack([a[b, h, i] for b, h, i in rows])
     assert_close(BF16, pick(oc), np.array([lc[b, h, i] for b, h, i in rows]), ro, rl, pick(toc), rto,
                  label=f"jvp bf16 [4,16,2048,64] causal={causal}, {len(rows)} sampled rows")
+    for b, h in ((0, 0), (3, 15), (2, 7)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        so, sto, sls = oracle.attention_jvp(*(t[sl] for t in ts), oracle.scale_as_passed(w.sm_scale), causal)
+        assert_close(BF16, oc[sl], lc[sl], so, sls, toc[sl], sto,
+                     label=f"jvp bf16 [4,16,2048,64] causal={causal}, whole slice (b={b}, h={h})")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -150,16 +166,38 @@ def test_no_keys_gives_empty_rows(gpu_lib, dtype):
 @pytest.mark.parametrize("scale", [1.0, 0.0, 0.02])
 @pytest.mark.parametrize("causal", [False, True])
 def test_other_scales(gpu_lib, scale, causal):
-    """Scales other than D^-0.5.  For sm_scale = 1 the queries are scaled by
-    1/8 so that the logits keep the workloads' spread (std 1, not 8): with
-    std-8 logits the softmax is nearly one-hot and bf16 rounding of |O| ~ 4
-    alone reaches the O tolerance."""
+    """Scales other than D^-0.5 on the N(0, 1) inputs as drawn.  sm_scale = 1
+    gives raw q.k logits of std 8 (the SLL jagged page applies no scale): the
+    softmax is nearly one-hot, O follows single values of V, and O must stay
+    within its bf16 storage floor plus a small margin.  The seeds draw no
+    |O| >= 4, whose storage alone would cost 1.6e-2 (both floors are 7.8e-3)."""
     q, k, v = wl.dense_inputs(1, 2, 300, 300, 64, "bf16", 11 + causal)
-    if scale == 1.0:
-        q = (q.float() * 0.125).bfloat16()
     o, lse = attn.fwd(*cuda(q, k, v), causal=causal, sm_scale=scale)
     ro, rl = oracle.attention(q, k, v, oracle.scale_as_passed(scale), causal)
     assert_close(BF16, host64(o), host64(lse), ro, rl, label=f"sm_scale={scale} causal={causal}")
+    if scale == 1.0:
+        assert_within_floor(host64(o), ro, label=f"raw logits causal={causal}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("jvp", [False, True])
+def test_peaked_rows_long(gpu_lib, D, jvp):
+    """Raw logits (sm_scale = 1) over 2048 keys: dominant keys turn up in late
+    tiles, after the running max has settled, which is where a running max
+    that lags the row max would round the dominant term of P.  Seed 9 draws
+    storage floors of 7.8e-3 at both head dims (other seeds draw |O| >= 4,
+    whose bf16 storage alone costs up to 1.6e-2)."""
+    B, H, N = 1, 2, 2048
+    ts = wl.dense_inputs(B, H, N, N, D, "bf16", 9, tangents=jvp)
+    if jvp:
+        o, to, lse = attn.fwd_jvp(*cuda(*ts), sm_scale=1.0)
+        ro, rto, rl = oracle.attention_jvp(*ts, 1.0, False)
+        assert_close(BF16, host64(o), host64(lse), ro, rl, host64(to), rto, label=f"raw logits D={D} jvp")
+    else:
+        o, lse = attn.fwd(*cuda(*ts), sm_scale=1.0)
+        ro, rl = oracle.attention(*ts, 1.0, False)
+        assert_close(BF16, host64(o), host64(lse), ro, rl, label=f"raw logits D={D}")
+    assert_within_floor(host64(o), ro, label=f"raw logits D={D} jvp={jvp}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -237,14 +275,15 @@ def test_jagged_equal_lengths_match_dense(gpu_lib):
 
 
 def test_jagged_unscaled_logits(gpu_lib):
-    """sm_scale = 1 reproduces the SLL page's raw q.k logits (inputs scaled
-    down so that the softmax is not one-hot)."""
+    """sm_scale = 1 reproduces the SLL page's raw q.k logits on the N(0, 1)
+    inputs as drawn (std-8 logits, nearly one-hot rows); seed 5 draws a
+    storage floor of 7.8e-3."""
     lengths = torch.tensor([37, 250, 1])
     q, k, v, off = wl.jagged_inputs(lengths, 2, 64, "bf16", 5)
-    q = (q.float() * 0.125).bfloat16()
     o, lse = attn.jagged_fwd(*cuda(q, k, v, off), max_seq_len=512, sm_scale=1.0)
     ro, rl = oracle.jagged_attention(q, k, v, off.numpy(), 512, 1.0)
     assert_close(BF16, host64(o), host64(lse), ro, rl, label="jagged sm_scale=1")
+    assert_within_floor(host64(o), ro, label="jagged raw logits")
 
 
 def test_jagged_repeatable_and_workspace_independent(gpu_lib):
@@ -401,6 +440,23 @@ def test_fp16_cross_attention_and_tails(gpu_lib):
 def test_fp16_jvp(gpu_lib, causal):
     jvp_case(2, 3, 400, 400, 64, "fp16", causal, seed=45)
     jvp_case(1, 2, 200, 200, 128, "fp16", causal, seed=46)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_jvp_large_inputs(gpu_lib, D, causal):
+    """fp16 JVP on N(0, 3^2) primals and tangents: unscaled tangent scores
+    reach about 1e3 and, times a running-max-relative p that may exceed 1,
+    would pass fp16's 65504 in H.  The fp16 JVP keeps the exact running max
+    (p <= 1) and forms H = p (scale tS) as the JVP pages do, so tO stays
+    finite and within the fp16 bounds."""
+    ts = wl.dense_inputs(1, 2, 1024, 1024, D, "fp16", 60 + D, tangents=True, std=3.0)
+    scale = D ** -0.5
+    o, to, lse = attn.fwd_jvp(*cuda(*ts), causal=causal, sm_scale=scale)
+    assert torch.isfinite(to).all() and torch.isfinite(o).all()
+    ro, rto, rl = oracle.attention_jvp(*ts, oracle.scale_as_passed(scale), causal)
+    assert_close(FP16, host64(o), host64(lse), ro, rl, host64(to), rto,
+                 label=f"fp16 jvp std 3 D={D} causal={causal}", v_std=3.0)
 
 
 def test_fp16_jagged(gpu_lib):
