@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     jagged_bwd,
     jagged_bwd_workspace_bytes,
     jagged_fwd,
+    jagged_fwd_noalloc,
     jagged_workspace_bytes,
     library_path,
     load_library,

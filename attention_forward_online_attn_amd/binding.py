@@ -72,6 +72,9 @@ def load_library():
     lib.jagged_attn_fwd.argtypes = [i32, vp, S3, vp, S3, vp, S3, vp, S3, vp, vp,
                                     i64, i64, i64, i64, i64, f32, i32, vp, ctypes.c_size_t, vp]
     lib.jagged_attn_fwd.restype = i32
+    lib.jagged_attn_fwd_noalloc.argtypes = [i32, vp, S3, vp, S3, vp, S3, vp, S3, vp, vp,
+                                            i64, i64, i64, i64, i64, f32, i32, vp]
+    lib.jagged_attn_fwd_noalloc.restype = i32
     lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd.argtypes = [i32, vp, S4, vp, S4, vp, S4, vp, S4, vp, S4, vp, vp, S4, vp, S4, vp, S4,
@@ -236,6 +239,34 @@ def jagged_fwd(q, k, v, offsets, max_seq_len, causal=False, sm_scale=None, works
                                _ptr(o), _s3(o), _ptr(lse), _ptr(offsets), S, H, T, D,
                                int(max_seq_len), float(sm_scale), int(bool(causal)),
                                _ptr(workspace), workspace.numel(), _stream(q)))
+    return o, lse
+
+
+def jagged_fwd_noalloc(q, k, v, offsets, max_seq_len, causal=False, sm_scale=None, out=None):
+    """jagged_fwd without a workspace: the library keeps the tile plan in a
+    static device array (calls on one GPU must not overlap).  With
+    out=(o, lse) -- [H, total_len, D] of q's dtype and contiguous fp32
+    [H, total_len] -- nothing at all is allocated."""
+    lib = load_library()
+    _same(q, k, v)
+    if offsets.dtype != torch.int64 or offsets.device != q.device or offsets.dim() != 1 or not offsets.is_contiguous():
+        raise AttnError("offsets must be a contiguous 1-D int64 tensor on the same device")
+    H, T, D = q.shape
+    S = offsets.numel() - 1
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if out is None:
+        o = torch.empty((H, T, D), dtype=q.dtype, device=q.device)
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _same(q, o)
+        if o.shape != (H, T, D) or lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+                or lse.device != q.device:
+            raise AttnError("out must be (o [H, total_len, D], lse contiguous fp32 [H, total_len])")
+    _check(lib.jagged_attn_fwd_noalloc(_dtype_code(q), _ptr(q), _s3(q), _ptr(k), _s3(k), _ptr(v), _s3(v),
+                                       _ptr(o), _s3(o), _ptr(lse), _ptr(offsets), S, H, T, D,
+                                       int(max_seq_len), float(sm_scale), int(bool(causal)), _stream(q)))
     return o, lse
 
 

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "attn_common.h"
@@ -273,11 +274,45 @@ size_t jagged_attn_workspace_bytes(int64_t num_seqs, int64_t total_len) {
   return (size_t)(16 + 8 * cap);
 }
 
-int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, const void* k, attn_strides3 k_strides,
-                    const void* v, attn_strides3 v_strides, void* o, attn_strides3 o_strides, float* lse,
-                    const int64_t* offsets, int64_t num_seqs, int64_t H, int64_t total_len, int64_t D,
-                    int64_t max_seq_len, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+}  // extern "C"
+
+// Static scratch of jagged_attn_fwd_noalloc: the tile plan of a call lives
+// here instead of in a caller's workspace.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device array: every host use goes through
+// the device address from scratch_address().
+static __device__ __align__(256) int32_t scratch[ATTN_NOALLOC_SCRATCH_BYTES / 4];
+
+namespace attn {
+namespace {
+
+// This device's address of `scratch`: hipGetSymbolAddress once per device,
+// with that device current (the caller's), then cached.
+int scratch_address(void** out) {
+  static std::atomic<void*> addr[64];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ERR_HIP;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ATTN_ERR_HIP;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ATTN_OK;
+}
+
+// jagged_attn_fwd and jagged_attn_fwd_noalloc: with `noalloc` the plan goes
+// to this device's static scratch (workspace and workspace_bytes unused).
+int jagged_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, const void* k, attn_strides3 k_strides,
+               const void* v, attn_strides3 v_strides, void* o, attn_strides3 o_strides, float* lse,
+               const int64_t* offsets, int64_t num_seqs, int64_t H, int64_t total_len, int64_t D,
+               int64_t max_seq_len, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
+               bool noalloc, void* stream) {
   int rc = check_common((int)dtype, D, sm_scale, true, true);
   if (rc) return rc;
   if (num_seqs < 0 || H < 0 || total_len < 0 || max_seq_len < 1) return ATTN_ERR_INVALID;
@@ -295,9 +330,14 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   const KernelChoice kc = choose((int)dtype, (int)D, false, false, kNoBias, (int)D);
   const int BM = kc.BM;
   const int64_t cap = plan_capacity(num_seqs, total_len, BM);
-  if (!workspace || workspace_bytes < (size_t)(16 + 8 * cap) || ((uintptr_t)workspace & 15u)) return ATTN_ERR_WORKSPACE;
   const int64_t grid = cap * H;
   if (grid > INT_MAX) return ATTN_ERR_INVALID;
+  if (noalloc) {  // the plan must fit the static scratch
+    if (16 + 8 * cap > (int64_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+    if ((rc = scratch_address(&workspace))) return rc;
+  } else if (!workspace || workspace_bytes < (size_t)(16 + 8 * cap) || ((uintptr_t)workspace & 15u)) {
+    return ATTN_ERR_WORKSPACE;
+  }
   const int mlen = (int)(max_seq_len < INT_MAX ? max_seq_len : INT_MAX);
 
   hipStream_t st = (hipStream_t)stream;
@@ -325,6 +365,29 @@ int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, co
   rc = launch(kc, (int)grid, st, a);
   if (rc) return rc;
   return finish(st);
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" {
+
+int jagged_attn_fwd(attn_dtype dtype, const void* q, attn_strides3 q_strides, const void* k, attn_strides3 k_strides,
+                    const void* v, attn_strides3 v_strides, void* o, attn_strides3 o_strides, float* lse,
+                    const int64_t* offsets, int64_t num_seqs, int64_t H, int64_t total_len, int64_t D,
+                    int64_t max_seq_len, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return attn::jagged_fwd(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, offsets, num_seqs, H,
+                          total_len, D, max_seq_len, sm_scale, causal, workspace, workspace_bytes, false, stream);
+}
+
+int jagged_attn_fwd_noalloc(attn_dtype dtype, const void* q, attn_strides3 q_strides, const void* k,
+                            attn_strides3 k_strides, const void* v, attn_strides3 v_strides, void* o,
+                            attn_strides3 o_strides, float* lse, const int64_t* offsets, int64_t num_seqs, int64_t H,
+                            int64_t total_len, int64_t D, int64_t max_seq_len, float sm_scale, int causal,
+                            void* stream) {
+  return attn::jagged_fwd(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, offsets, num_seqs, H,
+                          total_len, D, max_seq_len, sm_scale, causal, nullptr, 0, true, stream);
 }
 
 size_t jagged_attn_bwd_workspace_bytes(int64_t num_seqs, int64_t H, int64_t total_len) {
@@ -530,7 +593,9 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_INVALID: return "invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (dtype, head dim or alignment)";
     case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires Nq == Nkv";
-    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_WORKSPACE:
+      return "workspace missing or too small (jagged_attn_fwd_noalloc: the tile plan exceeds the static scratch, "
+             "ATTN_NOALLOC_SCRATCH_BYTES)";
     case ATTN_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }

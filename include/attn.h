@@ -49,7 +49,9 @@
  * - All argument checks happen on the host before anything is enqueued; a
  *   failed check enqueues nothing and returns a negative status.
  * - The library keeps no mutable global state beyond a per-process cache of
- *   kernel attributes, so concurrent calls on different streams are safe.
+ *   kernel attributes and device addresses, so concurrent calls on different
+ *   streams are safe -- except jagged_attn_fwd_noalloc, whose calls share one
+ *   static device array per GPU (see there).
  */
 #ifndef ATTN_MI355X_ATTN_H
 #define ATTN_MI355X_ATTN_H
@@ -70,7 +72,7 @@ enum {
   ATTN_ERR_INVALID = -1,      /* null pointer with work to do, negative or oversized size, bad stride, bad scale */
   ATTN_ERR_UNSUPPORTED = -2,  /* head dim not supported by the call, unknown dtype, misaligned pointer/stride */
   ATTN_ERR_CAUSAL_SHAPE = -3, /* causal with Nq != Nkv (the mask is top-left aligned) */
-  ATTN_ERR_WORKSPACE = -4,    /* jagged workspace missing or too small */
+  ATTN_ERR_WORKSPACE = -4,    /* workspace missing or too small; for jagged_attn_fwd_noalloc, a plan beyond its static scratch */
   ATTN_ERR_HIP = -5           /* the HIP runtime reported an error while enqueuing */
 };
 
@@ -225,6 +227,40 @@ ATTN_API int jagged_attn_fwd(attn_dtype dtype,
                     int64_t num_seqs, int64_t H, int64_t total_len, int64_t D,
                     int64_t max_seq_len, float sm_scale, int causal,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of the static device scratch behind jagged_attn_fwd_noalloc (one
+ * copy per GPU the library runs on, held until the process ends).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/*
+ * jagged_attn_fwd for callers that cannot allocate device memory (code under
+ * stream or graph capture, serving loops and harnesses that forbid
+ * allocation): the same arguments and results without a workspace.  The tile
+ * plan goes to a static device array of the library instead, so the call
+ * allocates nothing and calls no allocating routine.
+ *   Limit: the plan must fit ATTN_NOALLOC_SCRATCH_BYTES, i.e.
+ *   16 + 8 * floor((total_len + (BM - 1) * num_seqs) / BM) <= 2^20 bytes with
+ *   BM = 128 query rows per tile for bf16 and fp16, 64 for fp32: at most
+ *   131070 query tiles (total_len up to 16.7M rows in bf16 with few
+ *   sequences, or up to 131070 short sequences); larger inputs return
+ *   ATTN_ERR_WORKSPACE before anything is enqueued.
+ *   Every call on a GPU shares that GPU's array and leaves its plan there:
+ *   calls that overlap on one GPU (on different streams, or from different
+ *   threads) race and must be serialised by the caller; calls on different
+ *   GPUs do not interact.  Nothing in the array needs clearing between calls.
+ */
+ATTN_API int jagged_attn_fwd_noalloc(attn_dtype dtype,
+                    const void* q, attn_strides3 q_strides,
+                    const void* k, attn_strides3 k_strides,
+                    const void* v, attn_strides3 v_strides,
+                    void* o, attn_strides3 o_strides,
+                    float* lse,
+                    const int64_t* offsets,
+                    int64_t num_seqs, int64_t H, int64_t total_len, int64_t D,
+                    int64_t max_seq_len, float sm_scale, int causal,
+                    void* stream);
 
 /*
  * Bytes of device workspace attn_bwd needs (host function, no GPU access):

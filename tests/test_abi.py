@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(
         ["attn_fwd", "attn_fwd_bias", "attn_fwd_dv", "attn_fwd_jvp", "jagged_attn_workspace_bytes", "jagged_attn_fwd",
          "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_bias", "jagged_attn_bwd_workspace_bytes", "jagged_attn_bwd",
-         "attn_status_string"])
+         "attn_status_string", "jagged_attn_fwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -160,6 +160,27 @@ def test_jagged_validation(lib):
     assert call(D=48) == UNSUPPORTED
     assert lib.jagged_attn_fwd(BF16, 0, st, 0, st, 0, st, 0, st, 0, 0, 0, H, 0, D, 64,
                                0.125, 0, 0, 0, None) == OK
+
+
+def test_jagged_noalloc_validation(lib):
+    """The argument checks of jagged_attn_fwd, and the plan's bound: it must
+    fit the 2^20-byte static scratch (16 + 8 x query tiles), checked on the
+    host before any device call."""
+    H, D = 2, 64
+
+    def call(S, T, offsets=P, msl=64, D=D, q=P):
+        st = Strides3(T * D, D, 1)
+        return lib.jagged_attn_fwd_noalloc(BF16, q, st, P, st, P, st, P, st, P, offsets, S, H, T, D, msl, 0.125, 0, None)
+    assert call(3, 100, offsets=0) == INVALID
+    assert call(3, 100, msl=0) == INVALID
+    assert call(3, 100, q=0) == INVALID
+    assert call(3, 100, D=48) == UNSUPPORTED
+    assert call(0, 100) == OK and call(3, 0) == OK
+    # 131071 one-row sequences: 131071 tiles of 128 rows -> 16 + 8 * 131071 bytes, one tile too many
+    assert call(131071, 131071) == WORKSPACE
+    # one long sequence: (T + 127) / 128 tiles
+    assert call(1, 131071 * 128) == WORKSPACE
+    assert b"static scratch" in lib.attn_status_string(WORKSPACE)
 
 
 def test_binding_rejects_host_tensors(lib):
