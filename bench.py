@@ -15,11 +15,17 @@ then exactly K steps between two device synchronisations; per-launch HIP
 events on the launch stream give the kernel's average duration for the
 `roofline` object.  Each entry of `extra` also reports the median and minimum
 launch and a cold-cache median (a 512 MiB buffer is rewritten before every
-launch, outside the events, which evicts L2 and the Infinity Cache).  `cpu_baseline` times the fp64 CPU oracle on a bounded
-sample of the same workload (a few heads) on this host's cores.
+launch, outside the events, which evicts L2 and the Infinity Cache), each
+median over at least 50 launches.  `roofline` and `jvp_roofline` give the
+headline forward's and the JVP forward's kernel rate (average launch from the
+events) against the bf16 MFMA peak.  `cpu_baseline` and `cpu_baseline_jvp`
+time the fp64 CPU oracle on bounded samples of those two workloads (whole
+(batch, head) slices) on this host's cores; `cpu_oracle_configs` gives the
+oracle's seconds on the other workloads (fp32 tiny, causal D=64, jagged),
+with the GPU/CPU ratio.
 
 Profiling modes (for rocprofv3 runs): --only {fwd,fwd_causal,jvp,jvp_causal,
-causal_d64,jagged,bwd,bwd_causal,fwd_fp16,fwd_bias,fwd_mask,bwd_bias,jagged_bwd} runs just that workload K times; --copy-calibration runs a
+causal_d64,jagged,tiny_fp32,bwd,bwd_causal,fwd_fp16,fwd_bias,fwd_mask,bwd_bias,jagged_bwd} runs just that workload K times; --copy-calibration runs a
 plain device copy of known size (the scale for FETCH_SIZE / WRITE_SIZE).
 """
 
@@ -32,6 +38,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -133,6 +141,13 @@ def make_cases(torch, attn, wl, only=None):
                     8 * w4.B * w4.H * w4.N * w4.D * 2 + w4.B * w4.H * w4.N * 4,
                     f"{w4.name}: B={w4.B} H={w4.H} N={w4.N} D={w4.D} bf16 causal={causal} (O, tO, LSE)")
 
+    def tiny_case():  # the small fp32 correctness workload (launch-latency bound)
+        t = wl.WORKLOADS["tiny_fp32"]
+        q1, k1, v1 = (x.to(dev) for x in wl.dense_inputs(t.B, t.H, t.N, t.N, t.D, "fp32", 0))
+        return Case("tiny_fp32", lambda: attn.fwd(q1, k1, v1, causal=False, sm_scale=t.sm_scale),
+                    dense_flops(t.B, t.H, t.N, t.N, t.D, False), 4 * q1.numel() * 4 + t.B * t.H * t.N * 4,
+                    f"{t.name}: B={t.B} H={t.H} N={t.N} D={t.D} fp32 causal=False")
+
     def causal_d64_case():
         q2, k2, v2 = (t.to(dev) for t in wl.dense_inputs(w2.B, w2.H, w2.N, w2.N, w2.D, "bf16", 0))
         return Case("causal_d64", lambda: attn.fwd(q2, k2, v2, causal=True, sm_scale=w2.sm_scale),
@@ -185,6 +200,7 @@ def make_cases(torch, attn, wl, only=None):
         "fwd": lambda: fwd_case(False), "fwd_causal": lambda: fwd_case(True), "fwd_fp16": fp16_case,
         "fwd_bias": bias_case, "fwd_mask": mask_case, "jvp": lambda: jvp_case(False),
         "jvp_causal": lambda: jvp_case(True), "causal_d64": causal_d64_case, "jagged": jagged_case,
+        "tiny_fp32": tiny_case,
         "bwd": lambda: bwd_case(False), "bwd_causal": lambda: bwd_case(True), "bwd_bias": bwd_bias_case,
         "jagged_bwd": jagged_bwd_case,
     }
@@ -238,25 +254,8 @@ def load_traffic(kernel_hash):
     return rec.get("fwd_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s=15.0):
-    """The fp64 oracle on a bounded sample of the headline workload: whole
-    (batch, head) slices of the same seeded B=4, H=32, N=4096, D=128 inputs,
-    one after another until the time budget is spent (at most all 128)."""
-    import oracle
+def _host_info():
     from threadpoolctl import threadpool_info
-
-    w = wl.WORKLOADS["long_d128"]
-    q, k, v = wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "bf16", 0)
-    scale = oracle.scale_as_passed(w.sm_scale)
-    oracle.attention(q[:1, :1, :64], k[:1, :1, :64], v[:1, :1, :64], scale, False)  # warm the BLAS pool
-    heads, t0 = 0, time.perf_counter()
-    while heads < w.B * w.H and (heads == 0 or time.perf_counter() - t0 < budget_s):
-        b, h = divmod(heads, w.H)
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        oracle.attention(q[sl], k[sl], v[sl], scale, False)
-        heads += 1
-    dt = time.perf_counter() - t0
-    flops = dense_flops(1, heads, w.N, w.N, w.D, False)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     model = ""
     try:
@@ -264,10 +263,123 @@ def cpu_baseline(wl, budget_s=15.0):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "cpu_model": model, "host_logical_cpus": os.cpu_count(),
+    return int(threads), model
+
+
+def _slices_until(budget_s, n_total, run_one):
+    """Runs run_one(i) for i = 0, 1, ... until the budget is spent (at least
+    once, at most n_total times); returns (count, seconds)."""
+    n, t0 = 0, time.perf_counter()
+    while n < n_total and (n == 0 or time.perf_counter() - t0 < budget_s):
+        run_one(n)
+        n += 1
+    return n, time.perf_counter() - t0
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    """The fp64 oracle on a bounded sample of the headline workload: whole
+    (batch, head) slices of the same seeded B=4, H=32, N=4096, D=128 inputs,
+    one after another until the time budget is spent (at most all 128)."""
+    import oracle
+
+    w = wl.WORKLOADS["long_d128"]
+    q, k, v = wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "bf16", 0)
+    scale = oracle.scale_as_passed(w.sm_scale)
+    oracle.attention(q[:1, :1, :64], k[:1, :1, :64], v[:1, :1, :64], scale, False)  # warm the BLAS pool
+
+    def one(i):
+        b, h = divmod(i, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attention(q[sl], k[sl], v[sl], scale, False)
+    heads, dt = _slices_until(budget_s, w.B * w.H, one)
+    flops = dense_flops(1, heads, w.N, w.N, w.D, False)
+    threads, model = _host_info()
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "host_logical_cpus": os.cpu_count(), "seconds": round(dt, 3),
             "sample": f"{heads} of the 128 (batch, head) slices of the B=4 H=32 N=4096 D=128 non-causal "
                       f"forward in {dt:.1f} s (fp64 numpy oracle, BLAS threads = cores)"}
+
+
+def cpu_baseline_jvp(wl, budget_s=8.0):
+    """The oracle's closed-form JVP (O, tO, LSE) on whole (batch, head) slices
+    of the B=4, H=16, N=2048, D=64 JVP workload, the metric's second half."""
+    import oracle
+
+    w = wl.WORKLOADS["jvp_d64"]
+    ts = wl.dense_inputs(w.B, w.H, w.N, w.N, w.D, "bf16", 0, tangents=True)
+    scale = oracle.scale_as_passed(w.sm_scale)
+
+    def one(i):
+        b, h = divmod(i, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attention_jvp(*(t[sl] for t in ts), scale, False)
+    heads, dt = _slices_until(budget_s, w.B * w.H, one)
+    flops = dense_flops(1, heads, w.N, w.N, w.D, False, jvp=True)
+    threads, _ = _host_info()
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{heads} of the 64 (batch, head) slices of the B=4 H=16 N=2048 D=64 non-causal JVP "
+                      f"forward in {dt:.1f} s (fp64 numpy oracle, closed-form tangent)"}
+
+
+def cpu_oracle_configs(wl, gpu_ms, budget_s=4.0):
+    """Oracle seconds on the other workloads, with the GPU/CPU ratio against
+    the GPU median of the same workload: the tiny fp32 forward whole (median
+    of 5), the causal D=64 forward and the jagged forward on bounded samples
+    (whole (batch, head) slices; whole sequences of all 8 heads), each scaled
+    to the full workload by its flop share."""
+    import oracle
+
+    out = {}
+    t = wl.WORKLOADS["tiny_fp32"]
+    q, k, v = wl.dense_inputs(t.B, t.H, t.N, t.N, t.D, "fp32", 0)
+    sc = oracle.scale_as_passed(t.sm_scale)
+    ts = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, sc, False)
+        ts.append(time.perf_counter() - t0)
+    sec = median(ts)
+    f = dense_flops(t.B, t.H, t.N, t.N, t.D, False)
+    out["tiny_fp32"] = {"oracle_s": round(sec, 6), "oracle_gflops": round(f / sec / 1e9, 3),
+                        "sample": "whole workload, median of 5"}
+
+    c = wl.WORKLOADS["causal_d64"]
+    q, k, v = wl.dense_inputs(c.B, c.H, c.N, c.N, c.D, "bf16", 0)
+    sc = oracle.scale_as_passed(c.sm_scale)
+
+    def one(i):
+        b, h = divmod(i, c.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attention(q[sl], k[sl], v[sl], sc, True)
+    n, dt = _slices_until(budget_s, c.B * c.H, one)
+    sec = dt * (c.B * c.H) / n
+    out["causal_d64"] = {"oracle_s": round(sec, 4), "oracle_gflops": round(dense_flops(c.B, c.H, c.N, c.N, c.D, True)
+                                                                           / sec / 1e9, 3),
+                         "sample": f"{n} of {c.B * c.H} (batch, head) slices in {dt:.1f} s, scaled"}
+
+    j = wl.WORKLOADS["jagged_d128"]
+    lengths = wl.jagged_lengths(j.num_seqs, j.max_len, 0)
+    jq, jk, jv, off = wl.jagged_inputs(lengths, j.H, j.D, "bf16", 0)
+    offs = off.numpy()
+    sc = oracle.scale_as_passed(j.sm_scale)
+    L = lengths.numpy()
+
+    def one_seq(i):
+        sl = slice(int(offs[i]), int(offs[i + 1]))
+        oracle.jagged_attention(jq[:, sl], jk[:, sl], jv[:, sl], np.array([0, L[i]]), j.max_len, sc)
+    n, dt = _slices_until(budget_s, j.num_seqs, one_seq)
+    share = float(np.sum(L[:n].astype(np.float64) ** 2) / np.sum(L.astype(np.float64) ** 2))
+    sec = dt / share
+    out["jagged"] = {"oracle_s": round(sec, 4), "oracle_gflops": round(jagged_flops(L.tolist(), j.H, j.D)
+                                                                            / sec / 1e9, 3),
+                          "sample": f"{n} of {j.num_seqs} sequences (all 8 heads) in {dt:.1f} s, "
+                                    f"{100 * share:.1f}% of the flops, scaled"}
+    for name, ms in gpu_ms.items():
+        if name in out and ms:
+            out[name]["gpu_ms"] = round(ms, 5)
+            out[name]["gpu_over_cpu"] = round(out[name]["oracle_s"] / (ms * 1e-3), 1)
+    return out
 
 
 def copy_calibration(torch, steps):
@@ -320,9 +432,10 @@ def main():
     value = head.flops / (ms_per_step * 1e-3) / 1e12
     achieved = head.flops / (avg * 1e-3) / 1e12
     # cold caches: a 512 MiB buffer (more than 8 x 4 MB L2 + 256 MB MALL) is
-    # rewritten before every launch, outside the timed events
+    # rewritten before every launch, outside the timed events; medians over at
+    # least 50 launches
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
-    n_cold = max(5, args.steps // 2)
+    n_cold = max(50, args.steps // 2)
 
     def summary(c, durs_w, durs_c):
         mw, mc = median(durs_w), median(durs_c)
@@ -335,13 +448,17 @@ def main():
                 "cold_tflops": round(c.flops / (mc * 1e-3) / 1e12, 2)}
 
     extra = {"fwd": summary(head, durs, time_launches(torch, head, n_cold, 2, flush)[0])}
-    for name in ("fwd_causal", "fwd_fp16", "fwd_bias", "fwd_mask", "jvp", "jvp_causal", "causal_d64", "jagged", "bwd",
-                 "bwd_causal", "bwd_bias", "jagged_bwd"):
+    warm = {}
+    for name in ("fwd_causal", "fwd_fp16", "fwd_bias", "fwd_mask", "jvp", "jvp_causal", "causal_d64", "jagged",
+                 "tiny_fp32", "bwd", "bwd_causal", "bwd_bias", "jagged_bwd"):
         c = cases[name]
-        dw, _ = time_launches(torch, c, max(5, args.steps // 2), 10)
+        dw, _ = time_launches(torch, c, max(50, args.steps // 2), 10)
         dc, _ = time_launches(torch, c, n_cold, 2, flush)
         extra[name] = summary(c, dw, dc)
+        warm[name] = dw
     del flush
+    jvp_avg = sum(warm["jvp"]) / len(warm["jvp"])
+    jvp_achieved = cases["jvp"].flops / (jvp_avg * 1e-3) / 1e12
     props = torch.cuda.get_device_properties(0)
     device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
               "compute_units": props.multi_processor_count}
@@ -367,11 +484,23 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic, "kernel": "attn_fwd_bf16_kernel<128,64,false,4,false,0,0>",
-                     "avg_launch_ms": round(avg, 4), "min_launch_ms": round(mn, 4)},
+                     "avg_launch_ms": round(avg, 4), "min_launch_ms": round(mn, 4),
+                     "cold_median_ms": extra["fwd"]["cold_median_ms"]},
+        "jvp_roofline": {"bound": "mfma", "achieved": round(jvp_achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(jvp_achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "kernel": "attn_fwd_bf16_kernel<64,32,true,4,false,0,0>",
+                         "avg_launch_ms": round(jvp_avg, 4), "min_launch_ms": round(min(warm["jvp"]), 4),
+                         "cold_median_ms": extra["jvp"]["cold_median_ms"],
+                         "flops_per_launch": cases["jvp"].flops},
         "extra": extra,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline_jvp"] = cpu_baseline_jvp(wl)
+        out["cpu_baseline_jvp"]["gpu_over_cpu"] = round(jvp_achieved / out["cpu_baseline_jvp"]["value"], 1)
+        out["cpu_baseline"]["gpu_over_cpu"] = round(achieved / out["cpu_baseline"]["value"], 1)
+        out["cpu_oracle_configs"] = cpu_oracle_configs(
+            wl, {n: extra[n]["median_ms"] for n in ("tiny_fp32", "causal_d64", "jagged")})
     print(json.dumps(out), flush=True)
 
 
