@@ -34,10 +34,9 @@
 //   p <= l / 2, i.e. at most a third of the row's final weight.  A row that
 //   one key dominates therefore has that key's p = exp2(0) = 1, exact in the
 //   16-bit P, as with the exact running max; spread rows, whose l grows fast,
-//   reach the full lag kTau after a tile or two.  The biased kernels and the
-//   fp16 JVP keep the exact running max (lag 0): the first because a bias
-//   makes rows peaked by construction, the second so that |p| <= 1 keeps the
-//   fp16 H = p * scale * tS within the range of the page's own formulation.
+//   reach the full lag kTau after a tile or two.  The fp16 JVP keeps the
+//   exact running max (lag 0), so that |p| <= 1 keeps the fp16
+//   H = p * scale * tS within the range of the page's own formulation.
 // * Per key tile: the next tile is copied straight from global memory into
 //   the other LDS stage (global_load_lds_dwordx4, no staging registers); the
 //   copies stay in flight through the tile's two MFMA sections (scores, then
@@ -385,8 +384,10 @@ __device__ __forceinline__ void bias_chunks(const char* brow, int kb, bool full,
 }
 
 // Applies the chunks to the scores: additive bias -> s c + bias log2(e) (the
-// exp2 domain, after which the softmax scale is 1); mask -> -inf where 0.
-template <int BIAS, bool F16, int NB>
+// exp2 domain, after which the softmax scale is 1), or with LN the logits
+// s sm_scale + bias themselves (natural-log units: one FMA per score, the
+// softmax then scales by log2(e)); mask -> -inf where 0.
+template <int BIAS, bool F16, int NB, bool LN = false>
 __device__ __forceinline__ void apply_bias(f32x16 (&s)[NB], const unsigned (&src)[2 * NB][bias_dwords<BIAS>()],
                                            float c) {
 #pragma unroll
@@ -396,7 +397,8 @@ __device__ __forceinline__ void apply_bias(f32x16 (&s)[NB], const unsigned (&src
       if constexpr (BIAS == kAddBias) {
         const unsigned w = src[2 * b + (r >> 3)][(r & 7) >> 1];
         const unsigned short h = (unsigned short)((r & 1) ? (w >> 16) : (w & 0xffffu));
-        s[b][r] = __builtin_fmaf(s[b][r], c, from16<F16>(__builtin_bit_cast(bf16, h)) * kLog2e);
+        const float bv = from16<F16>(__builtin_bit_cast(bf16, h));
+        s[b][r] = LN ? __builtin_fmaf(s[b][r], c, bv) : __builtin_fmaf(s[b][r], c, bv * kLog2e);
       } else {
         const unsigned w = src[2 * b + (r >> 3)][(r & 7) >> 2];
         if (((w >> (8 * (r & 3))) & 0xffu) == 0u) s[b][r] = -INFINITY;
@@ -653,8 +655,8 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     // c is accumulator registers 8 (c % 2) .. 8 (c % 2) + 7 of s[c / 2].  The
     // chunks of tile j + 1 are loaded into register slot (j + 1) % 2 at the start
     // of tile j, ahead of that tile's K/V fetch, so the barrier that ends tile j
-    // has also completed them.  With an additive bias the scores are moved to
-    // the exp2 domain once (s c + bias log2 e) and the scale below becomes 1.
+    // has also completed them.  With an additive bias the scores become the
+    // logits s sm_scale + bias, which the softmax takes to the exp2 domain.
     constexpr int BCH = 2 * NB;                      // chunks per lane per tile
     constexpr int BEL = BIAS == kAddBias ? 2 : 1;    // bytes per element
     unsigned bsl[BIAS ? 2 : 1][BIAS ? BCH : 1][bias_dwords<BIAS>()];
@@ -667,12 +669,14 @@ attn_fwd_bf16_kernel(FwdArgs a) {
       if constexpr (BIAS != kNoBias)
         bias_chunks<BIAS, BCH>(brow, j * BN + 8 * h32, j * BN + BN <= t.Lkv, t.Lkv, bsl[decltype(slot_tag)::value]);
     };
-    // scale of the scores into the exp2 domain at the softmax (1 once an
-    // additive bias has been applied)
-    const float cs = BIAS == kAddBias ? 1.f : a.c;
-    // the running max lags (see the header); the biased kernels and the fp16
-    // JVP keep it exact
-    constexpr bool LAGGED = BIAS == kNoBias && !(F16 && JVP);
+    // scale of the scores into the exp2 domain at the softmax (log2(e) once
+    // an additive bias has made them logits s sm_scale + bias)
+    const float cs = BIAS == kAddBias ? kLog2e : a.c;
+    // the scale taken with an additive bias (sm_scale 0 as the smallest
+    // normal, so that the -inf of masked keys stays -inf rather than 0 * inf)
+    const float bscale = a.sm_scale != 0.f ? a.sm_scale : 1.17549435e-38f;
+    // the running max lags (see the header); the fp16 JVP keeps it exact
+    constexpr bool LAGGED = !(F16 && JVP);
     // fp16 JVP: H = p * (scale tS), the tangent scores scaled before the
     // product as the JVP pages order it, so H stays within fp16's range
     constexpr bool HS = F16 && JVP;
@@ -728,7 +732,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
               if (key >= my_lim) s[b][r] = -INFINITY;
             }
         }
-        if constexpr (BIAS != kNoBias) apply_bias<BIAS, F16, NB>(s, bsl[S], a.c);
+        if constexpr (BIAS != kNoBias) apply_bias<BIAS, F16, NB, true>(s, bsl[S], bscale);
 
         // online softmax: tile row max (in-lane, then the other half-wave)
         float mx = s[0][0];
