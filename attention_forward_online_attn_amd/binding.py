@@ -41,6 +41,11 @@ class Strides3(ctypes.Structure):
 
 
 def library_path() -> str:
+    """The in-tree libattn_mi355x.so, or the build that ATTN_LIBRARY names
+    (another build of the same C ABI, such as the host-sanitizer build)."""
+    override = os.environ.get("ATTN_LIBRARY")
+    if override:
+        return override
     return os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
 
 
