@@ -48,7 +48,7 @@ bool stride_ok(int64_t stride, int64_t extent, int64_t vec) {
 }
 
 // d16: head dim 16 is allowed (the forward, JVP and backward); d256: head
-// dim 256 is allowed (the forward, the 16-bit JVP and the backward).
+// dim 256 is allowed (the forward, the JVP and the backward).
 int check_common(int dtype, int64_t D, float sm_scale, bool d16 = false, bool d256 = false) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP32 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale) || sm_scale < 0.f) return ATTN_ERR_INVALID;
@@ -105,7 +105,10 @@ bool use_split(int dtype, int D, bool jvp, bool dense_causal, int64_t grid) {
 // Forward kernel for a dtype, head dims and variant (instance tables in the
 // inst_*.hip translation units).
 KernelChoice choose(int dtype, int D, bool jvp, bool split, int bias_kind, int Dv) {
-  if (D == 256) return bias_kind != kNoBias ? fwd_d256_bias(dtype, bias_kind) : fwd_d256(dtype, jvp);
+  if (D == 256) {
+    if (bias_kind != kNoBias) return fwd_d256_bias(dtype, bias_kind);
+    return Dv == 256 && !jvp ? fwd_d256(dtype) : fwd_d256_dv(dtype, Dv, jvp);
+  }
   if (bias_kind != kNoBias) return fwd_bias(dtype, bias_kind, D);
   if (dtype == ATTN_FP32) return fwd_f32(D, Dv, jvp);
   if (Dv != D || D == 16) return dtype == ATTN_BF16 ? fwd_mixed_bf16(D, Dv, jvp) : fwd_mixed_fp16(D, Dv, jvp);
@@ -132,13 +135,12 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
           attn_strides4 sq, attn_strides4 sk, attn_strides4 sv, void* o, void* to, attn_strides4 so, float* lse,
           float* tlse, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t D, float sm_scale, int causal,
           void* stream, bool jvp, const BiasOperand& bias = BiasOperand(), int64_t Dv = 0) {
-  // head dim 256: equal value dim; the JVP only on the 16-bit kernels
-  const bool d256 = (Dv == 0 || Dv == D) && !(jvp && dtype == ATTN_FP32);
-  int rc = check_common(dtype, D, sm_scale, true, d256);
+  // query/key and value head dims: any of 16, 32, 64, 128, 256 (a 16-wide
+  // value tile is laid out 32 wide in LDS)
+  int rc = check_common(dtype, D, sm_scale, true, true);
   if (rc) return rc;
   if (Dv == 0) Dv = D;
-  const bool v16 = Dv == 16;  // a 16-wide value tile (laid out 32 wide in LDS)
-  if (Dv != 32 && Dv != 64 && Dv != 128 && !(Dv == 256 && D == 256) && !v16)
+  if (Dv != 16 && Dv != 32 && Dv != 64 && Dv != 128 && Dv != 256)
     return Dv < 0 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED;
   if (B < 0 || H < 0 || Nq < 0 || Nkv < 0) return ATTN_ERR_INVALID;
   if (causal && Nq != Nkv) return ATTN_ERR_CAUSAL_SHAPE;
@@ -167,14 +169,31 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   const int64_t n_qtiles = (Nq + 127) / 128;  // every bf16 instance uses 128-row q-tiles
   const bool split =
       bias_kind == kNoBias && Dv == D && D != 256 && D != 16 && use_split(dtype, (int)D, jvp, causal != 0, B * H * n_qtiles);
-  // The 16-bit JVP with 128 value columns (any query/key dim) or at
-  // D = Dv = 256 runs as two launches over the halves of the value columns:
-  // three value accumulators over 128 columns hold a wave to one per SIMD
-  // (at 256 they spill), over 64 columns two waves share a SIMD.  Each
-  // launch recomputes the scores, yet the pair ran 1.2x to 1.5x faster at
-  // Dv = 128, with identical bits (every column sees the same products).
-  const bool halves = jvp && dtype != ATTN_FP32 && bias_kind == kNoBias && (Dv == 128 || (D == 256 && Dv == 256));
-  const KernelChoice kc = choose(dtype, (int)D, jvp, split, bias_kind, (int)(halves ? Dv / 2 : Dv));
+  // Value columns per launch (the launches cover consecutive slices of V,
+  // tV, O and tO; each recomputes the scores, and every output column sees
+  // the same products as in one launch, so the bits do not change):
+  // * the 16-bit JVP with 128 value columns (query/key dims below 256) runs
+  //   as two 64-wide halves: three accumulators over 128 columns hold a wave
+  //   to one per SIMD, over 64 two waves share a SIMD; the halves ran 1.2x
+  //   to 1.5x faster than one launch;
+  // * 256 value columns with 256-wide queries and keys: the JVP in 128-wide
+  //   halves (three 256-wide accumulators would spill);
+  // * 256 value columns with narrower queries and keys: 128-wide halves,
+  //   the 16-bit JVP 64-wide quarters, on the value-dim instances of those
+  //   widths.
+  int64_t vs = Dv;
+  if (bias_kind == kNoBias) {
+    const bool jvp16 = jvp && dtype != ATTN_FP32;
+    if (D == 256) {
+      if (Dv == 256 && jvp) vs = 128;
+    } else if (Dv == 256) {
+      vs = jvp16 ? 64 : 128;
+    } else if (Dv == 128 && jvp16) {
+      vs = 64;
+    }
+  }
+  const int64_t n_slices = Dv / vs;
+  const KernelChoice kc = choose(dtype, (int)D, jvp, split, bias_kind, (int)vs);
   const int BM = kc.BM;
   const int64_t n_qtiles_k = (Nq + BM - 1) / BM;
   const int64_t grid = B * H * (split ? (n_qtiles_k + 1) / 2 : n_qtiles_k);
@@ -204,12 +223,12 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   (void)hipGetLastError();  // clear a stale error so that finish() reports only ours
   rc = launch(kc, (int)grid, st, a);
   if (rc) return rc;
-  if (halves) {  // the second half of the value columns; both launches write the same LSE and tLSE
-    const int64_t half = Dv / 2 * 2;  // bytes of Dv / 2 16-bit elements
-    a.v = v ? (const char*)v + half : nullptr;  // no keys: V is never read
-    a.tv = tv ? (const char*)tv + half : nullptr;
-    a.o = (char*)o + half;
-    a.to = (char*)to + half;
+  for (int64_t sl = 1; sl < n_slices; ++sl) {  // the other value slices; every launch writes the same LSE and tLSE
+    const int64_t off = sl * vs * (dtype == ATTN_FP32 ? 4 : 2);  // bytes to slice sl's first column
+    a.v = v ? (const char*)v + off : nullptr;  // no keys: V is never read
+    a.tv = tv ? (const char*)tv + off : nullptr;
+    a.o = (char*)o + off;
+    a.to = to ? (char*)to + off : nullptr;
     rc = launch(kc, (int)grid, st, a);
     if (rc) return rc;
   }

@@ -61,7 +61,8 @@ KernelChoice fwd_f32(int D, int Dv, bool jvp);                  // inst_fwd_f32.
 KernelChoice fwd_bias(int dtype, int kind, int D);              // inst_fwd_bias.hip
 KernelChoice fwd_mixed_bf16(int D, int Dv, bool jvp);           // inst_fwd_mixed_bf16.hip
 KernelChoice fwd_mixed_fp16(int D, int Dv, bool jvp);           // inst_fwd_mixed_fp16.hip
-KernelChoice fwd_d256(int dtype, bool jvp);                     // inst_fwd_d256.hip (forward, 16-bit JVP)
+KernelChoice fwd_d256(int dtype);                               // inst_fwd_d256.hip (values 256 wide)
+KernelChoice fwd_d256_dv(int dtype, int Dv, bool jvp);          // inst_fwd_d256.hip (values 16 to 128 wide)
 KernelChoice fwd_d256_bias(int dtype, int kind);                // inst_fwd_d256.hip (bias or mask)
 
 // Backward: enqueues the prep, dQ and dK/dV kernels (inst_bwd.hip).  Dense:

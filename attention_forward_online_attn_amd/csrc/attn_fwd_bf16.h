@@ -457,9 +457,9 @@ struct Bf16Cfg {
   // waves share one lag in a scalar register.
   static constexpr bool WAVE_LAG = !JVP && NW == 4 && DQK <= 64;
   static_assert(BN % 32 == 0, "unsupported tile");
-  // 256-wide queries and keys: the plain forward with 256-wide values, or
-  // the JVP with 128-wide values (a 256-wide JVP runs as two such halves)
-  static_assert(DQK == 16 || DQK == 32 || DQK == 64 || DQK == 128 || (DQK == 256 && DV == (JVP ? 128 : 256)),
+  // 256-wide queries and keys: values up to 128 wide, or 256 wide for the
+  // plain forward (a JVP with 256-wide values runs as two 128-wide halves)
+  static_assert(DQK == 16 || DQK == 32 || DQK == 64 || DQK == 128 || (DQK == 256 && (DV <= 128 || (!JVP && DV == 256))),
                 "unsupported head dim");
   static_assert(!VSPLIT || (2 * KSTR <= 65536 && 2 * VSTR <= 65536), "each side's two stages within 16-bit offsets");
   static_assert(DV == 16 || DV == 32 || DV == 64 || DV == 128 || DV == 256, "unsupported head dim");

@@ -6,17 +6,29 @@
 // with a bias or mask the 64-key instance would spill, so it keeps 32.  The
 // 16-bit JVP takes 128 value columns per launch (the caller runs it once per
 // half): its three accumulators over 256 columns would not fit beside the Q
-// and tQ fragments.
+// and tQ fragments.  Narrower value head dims (16 to 128; JVP page:
+// _attention.forward takes d_v != d_qk) have instances of their own: the
+// 16-bit ones on 64-key tiles (JVP: 32), one wave per SIMD for the 256-wide
+// Q fragments, and the fp32 ones, whose JVP also carries 128-wide halves of
+// 256-wide values.
 #include "../../include/attn.h"
 #include "attn_instances.h"
 
 namespace attn {
-KernelChoice fwd_d256(int dtype, bool jvp) {
-  if (jvp) return dtype == ATTN_FP16 ? r32<256, 32, true, 4, true, kNoBias, 128>()
-                                     : r32<256, 32, true, 4, false, kNoBias, 128>();
+KernelChoice fwd_d256(int dtype) {
   if (dtype == ATTN_BF16) return r32<256, 64, false, 4, false>();
   if (dtype == ATTN_FP16) return r32<256, 64, false, 4, true>();
   return f32k<256, false>();
+}
+
+KernelChoice fwd_d256_dv(int dtype, int Dv, bool jvp) {
+  return by_dim_qk(Dv, [&](auto dv) {
+    constexpr int V = decltype(dv)::value;
+    if (dtype == ATTN_FP32) return jvp ? f32k<256, true, kNoBias, V>() : f32k<256, false, kNoBias, V>();
+    if (jvp)
+      return dtype == ATTN_FP16 ? r32<256, 32, true, 4, true, kNoBias, V>() : r32<256, 32, true, 4, false, kNoBias, V>();
+    return dtype == ATTN_FP16 ? r32<256, 64, false, 4, true, kNoBias, V>() : r32<256, 64, false, 4, false, kNoBias, V>();
+  });
 }
 
 namespace {

@@ -28,11 +28,9 @@
  *   satisfy this.  Anything else is ATTN_ERR_UNSUPPORTED.
  * - Tangent tensors (JVP) share the strides of their primals, and tO shares
  *   the strides of O (as the JVP page's wrapper requires).
- * - Supported head dims: 16, 32, 64 and 128 everywhere (the forward, plain,
- *   biased or jagged, either side of attn_fwd_dv, the JVP and the backward);
- *   256 everywhere except the fp32 JVP and unequal value dims (attn_fwd,
- *   attn_fwd_bias, jagged_attn_fwd, attn_fwd_jvp in bf16 and fp16,
- *   attn_fwd_dv with Dqk = Dv = 256, and the three backward calls).  dtype ATTN_BF16 (ATTN_FP16) computes
+ * - Supported head dims: 16, 32, 64, 128 and 256 everywhere (the forward,
+ *   plain, biased or jagged, either side of attn_fwd_dv, the JVP and the
+ *   backward).  dtype ATTN_BF16 (ATTN_FP16) computes
  *   the products on bf16 (fp16) MFMA with fp32 accumulation and rounds O/tO to
  *   the input format (RNE); ATTN_FP32 computes everything in fp32.  LSE is
  *   always fp32.
@@ -178,8 +176,10 @@ ATTN_API int attn_fwd_jvp(attn_dtype dtype,
  *   o, to [B, H, Nq, Dv]    lse, tlse [B, H, Nq]
  * tq == NULL: the plain forward of attn_fwd (tk, tv, to and tlse must be
  * NULL too); otherwise the fused JVP of attn_fwd_jvp (tlse optional).
- * Dqk and Dv each in {16, 32, 64, 128}, or both 256 on the plain forward;
- * with Dqk == Dv this is exactly attn_fwd / attn_fwd_jvp.  sm_scale is the caller's (the page's default is
+ * Dqk and Dv each in {16, 32, 64, 128, 256}; with Dqk == Dv this is
+ * exactly attn_fwd / attn_fwd_jvp.  Some wide combinations run as several
+ * launches over slices of the value columns, each recomputing the scores
+ * (the same bits as one launch).  sm_scale is the caller's (the page's default is
  * Dqk^-0.5).  Other arguments, checks and errors as attn_fwd_jvp.
  */
 ATTN_API int attn_fwd_dv(attn_dtype dtype,

@@ -299,15 +299,13 @@ def test_bwd_bias_validation(lib):
 
 
 def test_d256_paths(lib):
-    """Head dim 256 runs the forward (biased or not), the 16-bit JVP and the
-    backward; the fp32 JVP and unequal value dims at 256 are not built."""
+    """Head dim 256 runs the forward (biased or not), the JVP (bf16, fp16
+    and fp32) and the backward."""
     B, H, N, D = 0, 2, 128, 256  # B = 0: nothing is enqueued when the call is accepted
     st = dense_strides(1, H, N, D)
     assert call_fwd(lib, D=256, B=0) == OK
-    for dt in (BF16, FP16):
+    for dt in (BF16, FP16, FP32):
         assert lib.attn_fwd_jvp(dt, P, P, P, P, P, P, st, st, st, P, P, st, P, None, 0, H, N, N, D, 0.1, 0, None) == OK
-    assert lib.attn_fwd_jvp(FP32, P, P, P, P, P, P, st, st, st, P, P, st, P, None, 1, H, N, N, D, 0.1, 0, None) \
-        == UNSUPPORTED
     full = Strides4(H * N * N, N * N, N, 1)
     assert lib.attn_fwd_bias(BF16, P, st, P, st, P, st, P, st, P, P, 1, full, 0, H, N, N, D, 0.1, 0, None) == OK
     need = lib.attn_bwd_workspace_bytes(1, H, N)
@@ -315,7 +313,28 @@ def test_d256_paths(lib):
                         P, need, None) == OK
     assert lib.attn_bwd(BF16, P, st, P, st, P, st, P, st, P, st, P, P, st, P, st, P, st, 1, H, N, N, 512, 0.1, 0,
                         P, need, None) == UNSUPPORTED
-    assert lib.attn_fwd_dv(BF16, P, P, P, 0, 0, 0, st, st, st, P, 0, st, P, 0, 1, H, N, N, 256, 128, 0.1, 0, None) \
+    assert lib.attn_fwd_dv(BF16, P, P, P, 0, 0, 0, st, st, st, P, 0, st, P, 0, 0, H, N, N, 256, 128, 0.1, 0, None) == OK
+
+
+def test_value_head_dims(lib):
+    """Every pair of query/key and value head dims in {16, 32, 64, 128, 256}
+    is accepted, plain and JVP, in every dtype (B = 0: nothing enqueued);
+    other value widths are not head dims."""
+    H, N = 2, 64
+    dims = (16, 32, 64, 128, 256)
+    for dt in (BF16, FP16, FP32):
+        for dq in dims:
+            for dv in dims:
+                sq, sv = dense_strides(1, H, N, dq), dense_strides(1, H, N, dv)
+                for jvp in (0, 1):
+                    t = P if jvp else 0
+                    rc = lib.attn_fwd_dv(dt, P, P, P, t, t, t, sq, sq, sv, P, t, sv, P, 0, 0, H, N, N, dq, dv, 0.1, 0,
+                                         None)
+                    assert rc == OK, (dt, dq, dv, jvp, rc)
+    sq, sv = dense_strides(1, H, N, 64), dense_strides(1, H, N, 48)
+    assert lib.attn_fwd_dv(BF16, P, P, P, 0, 0, 0, sq, sq, sv, P, 0, sv, P, 0, 0, H, N, N, 64, 48, 0.1, 0, None) \
+        == UNSUPPORTED
+    assert lib.attn_fwd_dv(BF16, P, P, P, 0, 0, 0, sq, sq, sv, P, 0, sv, P, 0, 0, H, N, N, 512, 64, 0.1, 0, None) \
         == UNSUPPORTED
 
 

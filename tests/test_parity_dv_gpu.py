@@ -1,9 +1,11 @@
 """GPU parity of the forward and JVP whose value head dim differs from the
 query/key one (attn_fwd_dv through the C ABI; JVP page: _attention.forward
 and _test_jvp_ca) against the fp64 oracle, for every pair of distinct head
-dims in {32, 64, 128} and a query/key dim of 16 with every value dim, bf16,
-fp16 and fp32, causal and not, including the
-JVP page's own cross-attention shapes (Nq != Nkv, Nkv < one key tile)."""
+dims in {32, 64, 128}, a query/key dim of 16 with every value dim, and a
+head dim of 256 on either side with every other dim (the single launches
+of the 256-wide instances and the launches over value-column slices), bf16,
+fp16 and fp32, causal and not, including the JVP page's own
+cross-attention shapes (Nq != Nkv, Nkv < one key tile)."""
 
 import pytest
 import torch
@@ -47,6 +49,24 @@ def test_dv_forward(gpu_lib, Dqk, Dv, dtype):
 def test_dv_jvp(gpu_lib, Dqk, Dv, dtype):
     dv_case(2, 2, 300, 300, Dqk, Dv, dtype, False, True, seed=102)
     dv_case(1, 2, 130, 130, Dqk, Dv, dtype, True, True, seed=103)
+
+
+PAIRS_256 = [(256, 16), (256, 32), (256, 64), (256, 128), (16, 256), (32, 256), (64, 256), (128, 256)]
+
+
+@pytest.mark.parametrize("Dqk,Dv", PAIRS_256)
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_dv_256_forward(gpu_lib, Dqk, Dv, dtype):
+    dv_case(2, 2, 300, 300, Dqk, Dv, dtype, False, False, seed=110)
+    dv_case(1, 2, 130, 130, Dqk, Dv, dtype, True, False, seed=111)
+    dv_case(1, 1, 77, 333, Dqk, Dv, dtype, False, False, seed=112)
+
+
+@pytest.mark.parametrize("Dqk,Dv", PAIRS_256 + [(256, 256)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_dv_256_jvp(gpu_lib, Dqk, Dv, dtype):
+    dv_case(2, 2, 200, 200, Dqk, Dv, dtype, False, True, seed=113)
+    dv_case(1, 2, 130, 130, Dqk, Dv, dtype, True, True, seed=114)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
