@@ -580,10 +580,16 @@ attn_fwd_bf16_kernel(FwdArgs a) {
           // the uniform part of the address stays an SGPR pair (saddr form:
           // scalar base + 32-bit lane offset); with several instructions per
           // tensor the compiler would otherwise fold it into per-lane 64-bit
-          // addresses held across the loop
+          // addresses held across the loop.  Likewise the lane offset: an
+          // opaque copy at each use keeps its zero-extension next to the load
+          // (hoisted out of the key loop, it would turn every copy into a
+          // 64-bit vector add and a 64-bit address: 28 more vector
+          // instructions per pass over the unrolled loop at D = 128, 1-3%)
           const char* b = src[x] + i * step_b[vs];
           if constexpr (NIM > 1) asm("" : "+s"(b));
-          __builtin_amdgcn_global_load_lds((const void*)(b + (vs ? dv0[i % NPH_V] : dk0[i % NPH_K])),
+          uint32_t lo = vs ? dv0[i % NPH_V] : dk0[i % NPH_K];
+          asm("" : "+v"(lo));
+          __builtin_amdgcn_global_load_lds((const void*)(b + lo),
                                            (__attribute__((address_space(3))) void*)(base + (NWD * i + wd) * 1024 + toff[x]),
                                            16, 0, 0);
         }
