@@ -568,7 +568,9 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     const int toff[4] = {stage * KSTR, VBASE + stage * VSTR + OFF_V, stage * KSTR + OFF_TK,
                          VBASE + stage * VSTR + OFF_TV};
     const int64_t step_b[2] = {(int64_t)RSTEP_K * a.k_sn * 2, (int64_t)RSTEP_V * a.v_sn * 2};
-    if (k0 + BN <= t.Lkv) {
+    // a whole tile of keys: in 32 bits (j BN < Lkv <= INT_MAX), a scalar
+    // compare rather than a 64-bit one on the vector ALU
+    if (j * BN <= t.Lkv - BN) {
 #pragma unroll
       for (int i = 0; i < NIM; ++i)
 #pragma unroll
