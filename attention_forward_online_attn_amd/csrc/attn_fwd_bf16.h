@@ -748,17 +748,22 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         }
         if constexpr (BIAS != kNoBias) apply_bias<BIAS, F16, NB, true>(s, bsl[S], bscale);
 
-        // online softmax: tile row max (in-lane, then the other half-wave)
+        // online softmax: the max over this lane's keys of the tile.  A row
+        // moves its running max when its tile max (the larger of its two
+        // lanes' maxima) passes m_run + lag, i.e. when one of its lanes'
+        // maxima does: the wave tests its lanes' own maxima, and only a wave
+        // that rescales takes the other half-wave's.  The IEEE maximum (a NaN
+        // score propagates) pairs up as one v_maximum3 per two scores with no
+        // quieting of its inputs, which fmaxf's NaN rule needs.
         float mx = s[0][0];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-        mx = xhalf_max(mx);
-        const float m_new = mx * cs;
-        const bool upd = m_new > m_run + lag;
-        const bool rescaled = __builtin_amdgcn_ballot_w64(upd) != 0;  // wave-uniform
+          for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, s[b][r]);
+        const bool rescaled = __builtin_amdgcn_ballot_w64(mx * cs > m_run + lag) != 0;  // wave-uniform
         if (rescaled) {
+          const float m_new = xhalf_max(mx) * cs;
+          const bool upd = m_new > m_run + lag;
           const float m_next = upd ? m_new : m_run;
           const float alpha = m_next == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_next);
 #pragma unroll
