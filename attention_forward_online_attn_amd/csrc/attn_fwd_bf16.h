@@ -738,13 +738,15 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         // mask keys past this row's limit (ragged tail, causal diagonal,
         // jagged truncation) -- only on tiles that reach some row's limit
         if ((jt + 1) * BN > wave_min) {
+          // key 32 b + 16 (r / 8) + (r % 8) of the lane's block offset
+          // jt BN + 8 h32 against the row's limit: one compare with an inline
+          // constant per score
+          const int lim = my_lim - (jt * BN + 8 * h32);
 #pragma unroll
           for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = jt * BN + 32 * b + 16 * (r >> 3) + 8 * h32 + (r & 7);
-              if (key >= my_lim) s[b][r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+              if (32 * b + 16 * (r >> 3) + (r & 7) >= lim) s[b][r] = -INFINITY;
         }
         if constexpr (BIAS != kNoBias) apply_bias<BIAS, F16, NB, true>(s, bsl[S], bscale);
 
