@@ -37,6 +37,22 @@ COMPILE_FLAGS = [
 ]
 # one-step build of a single source (used by tools that compile one file)
 FLAGS = [*COMPILE_FLAGS, "-shared"]
+# Per-file additions.  The backward units hold the one-wave dK/dV kernel
+# (D = 128), whose accumulators, K and V fragments fill both halves of the
+# register file: by default the compiler puts every MFMA result of such a
+# kernel in AGPRs, and the scores and dP that the vector ALU reads next are
+# then copied to VGPRs element by element (64 to 192 moves per step).  The
+# VGPR form keeps MFMA results in VGPRs, while the K and V fragments are
+# pinned to AGPRs in the kernel itself (MFMA B operands may be AGPRs).
+FILE_FLAGS = {
+    "inst_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "inst_bwd_bias.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
+def compile_flags(src: str) -> list[str]:
+    """hipcc flags for one translation unit."""
+    return [*COMPILE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), [])]
 
 
 def _noise(stderr: str):
@@ -52,7 +68,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     with tempfile.TemporaryDirectory(prefix="attn_build_") as tmpdir:
         def compile_one(src):
             obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
-            cmd = [HIPCC, *COMPILE_FLAGS, "-c", src, "-o", obj]
+            cmd = [HIPCC, *compile_flags(src), "-c", src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             return obj, subprocess.run(cmd, capture_output=True, text=True)

@@ -29,7 +29,7 @@ ASAN_HOST = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer"
 
 
 def _flags(src):
-    flags = list(_build.COMPILE_FLAGS)
+    flags = _build.compile_flags(src)
     if src == HOST_SRC:
         flags = [f for f in flags if f != "-O3"] + ["-O0", "-g", *ASAN_HOST]
     return flags

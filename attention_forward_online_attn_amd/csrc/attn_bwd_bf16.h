@@ -409,6 +409,7 @@ struct BwdDkdvCfg {
   // tensor so that every fragment read's offset fits the 16-bit immediate
   static constexpr int OFF_DO = 2 * TILE, OFF_ROWS = 4 * TILE, ROWS = NBQ * 256;
   static constexpr int LDS = 4 * TILE + 2 * ROWS;
+  static constexpr bool AGPR_KV = D == 128;  // K and V fragments pinned to AGPRs (below)
 };
 
 // PART: kDkdvBoth computes dK and dV; at D = 256, where K, V and both
@@ -461,6 +462,20 @@ __global__ void __launch_bounds__(256, (BwdDkdvCfg<D, BIAS>::WAVES_PER_EU)) attn
     } else {  // padding columns of a 16-wide head
       kf[kk] = bf16x8{};
       vf[kk] = bf16x8{};
+    }
+  }
+  // One wave per SIMD: the K and V fragments are pinned to the AGPR half of
+  // the register file and feed the MFMAs from there as B operands, which
+  // leaves the VGPR half to the accumulators and to the products the vector
+  // ALU reads (this unit is built with MFMA results in VGPRs; with the
+  // results in AGPRs every score and dP element was copied over first).
+  if constexpr (C::AGPR_KV) {
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) {
+      u32x4 ku = __builtin_bit_cast(u32x4, kf[kk]), vu = __builtin_bit_cast(u32x4, vf[kk]);
+      asm volatile("" : "+a"(ku), "+a"(vu));
+      kf[kk] = __builtin_bit_cast(bf16x8, ku);
+      vf[kk] = __builtin_bit_cast(bf16x8, vu);
     }
   }
 
