@@ -345,7 +345,7 @@ __global__ void __launch_bounds__(256, (BwdDqCfg<D, BN>::WAVES_PER_EU)) attn_bwd
   };
 
   auto fetch = [&](int j, int stage) {
-    if (bwd_dma_tile_ok<DL, BN, NW>() && (j + 1) * BN <= t.Lkv && bwd_stride_ok(a.k_sn) && bwd_stride_ok(a.v_sn)) {
+    if (bwd_dma_tile_ok<DL, BN, NW>() && j * BN <= t.Lkv - BN && bwd_stride_ok(a.k_sn) && bwd_stride_ok(a.v_sn)) {
       if constexpr (bwd_dma_tile_ok<DL, BN, NW>()) {
         bwd_dma_tile<DL, BN, NW, D>(K, a.k_sn, j * BN, smem + stage * STAGE, wave, lane);
         bwd_dma_tile<DL, BN, NW, D>(V, a.v_sn, j * BN, smem + stage * STAGE + TILE, wave, lane);
@@ -368,7 +368,7 @@ __global__ void __launch_bounds__(256, (BwdDqCfg<D, BN>::WAVES_PER_EU)) attn_bwd
       f32x16 s[NB], dp[NB];
       scores_section<DL, NB, false, S * STAGE, 0, F16>(kaddr, qf, dummy_t, s, dummy_ts);          // S^T = K Q^T
       scores_section<DL, NB, false, S * STAGE + TILE, 0, F16>(kaddr, df, dummy_t, dp, dummy_ts);  // dP^T = V dO^T
-      if ((j + 1) * BN > wave_min) {  // keys past this row's limit: P = 0
+      if (j * BN > wave_min - BN) {  // keys past this row's limit: P = 0
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb)
 #pragma unroll

@@ -737,7 +737,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
 
         // mask keys past this row's limit (ragged tail, causal diagonal,
         // jagged truncation) -- only on tiles that reach some row's limit
-        if ((jt + 1) * BN > wave_min) {
+        if (jt * BN > wave_min - BN) {
           // key 32 b + 16 (r / 8) + (r % 8) of the lane's block offset
           // jt BN + 8 h32 against the row's limit: one compare with an inline
           // constant per score
