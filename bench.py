@@ -405,8 +405,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (each (batch, head) is "
-              "independent; see the sharding notes in DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (each (batch, head) is "
+              "independent, so work would shard by head across GPUs). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
