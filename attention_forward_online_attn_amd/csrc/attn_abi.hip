@@ -176,8 +176,11 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   //   as two 64-wide halves: three accumulators over 128 columns hold a wave
   //   to one per SIMD, over 64 two waves share a SIMD; the halves ran 1.2x
   //   to 1.5x faster than one launch;
-  // * 256 value columns with 256-wide queries and keys: the JVP in 128-wide
-  //   halves (three 256-wide accumulators would spill);
+  // * 256-wide queries and keys: the 16-bit JVP in 64-wide slices of 128 or
+  //   256 value columns (the one-wave (256, 128) instance spilled about 580
+  //   bytes per lane inside its key loop; the 64-wide slices ran 2.2x
+  //   faster), the fp32 JVP with 256 value columns in 128-wide halves
+  //   (three 256-wide accumulators would spill);
   // * 256 value columns with narrower queries and keys: 128-wide halves,
   //   the 16-bit JVP 64-wide quarters, on the value-dim instances of those
   //   widths.
@@ -185,7 +188,8 @@ int dense(int dtype, const void* q, const void* k, const void* v, const void* tq
   if (bias_kind == kNoBias) {
     const bool jvp16 = jvp && dtype != ATTN_FP32;
     if (D == 256) {
-      if (Dv == 256 && jvp) vs = 128;
+      if (jvp16 && Dv >= 128) vs = 64;
+      else if (Dv == 256 && jvp) vs = 128;
     } else if (Dv == 256) {
       vs = jvp16 ? 64 : 128;
     } else if (Dv == 128 && jvp16) {

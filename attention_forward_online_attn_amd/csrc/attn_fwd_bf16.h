@@ -224,7 +224,7 @@ __device__ __forceinline__ void lds_wait(bf16x8 (&f)[F]) {
 // that order: the MFMA pipe sees back-to-back work while at most FD reads are
 // in flight, and the register footprint stays fixed (left alone, the
 // scheduler hoists every read of a section to its top and spills).
-constexpr int kFragDist = 4;
+constexpr int kFragDist = 4;  // FD of every instance but the JVP ones at the register limit
 // Raised wave priority while a wave streams MFMAs: when two waves share a
 // SIMD the one feeding the matrix core is issued first.
 constexpr int kMfmaPrio = 1;
@@ -245,11 +245,11 @@ __device__ __forceinline__ bf16x8 k_frag_async(uint32_t addr) {
 // head-dim step kk in block 0 of a tile at byte 0.  The reads are inline
 // assembly for the same reason as the V^T reads (they would otherwise be
 // re-addressed every tile), with the same explicit waits.
-template <int D, int NB, bool JVP, int KOFF, int TKOFF, bool F16 = false>
+template <int D, int NB, bool JVP, int KOFF, int TKOFF, bool F16 = false, int FD = kFragDist>
 __device__ __forceinline__ void scores_section(const uint32_t (&kaddr)[D / 16], const bf16x8 (&qf)[D / 16],
                                                const bf16x8 (&tqf)[JVP ? D / 16 : 1], f32x16 (&s)[NB],
                                                f32x16 (&ts)[JVP ? NB : 1]) {
-  constexpr int KD = D / 16, N = NB * KD, R = kFragDist + 1, F = JVP ? 2 : 1;
+  constexpr int KD = D / 16, N = NB * KD, R = FD + 1, F = JVP ? 2 : 1;
   bf16x8 ring[R][F];
   auto issue = [&](auto i_tag) {
     constexpr int i = decltype(i_tag)::value;
@@ -265,11 +265,11 @@ __device__ __forceinline__ void scores_section(const uint32_t (&kaddr)[D / 16], 
     if constexpr (JVP) ts[b] = f32x16{};
   }
   __builtin_amdgcn_s_setprio(kMfmaPrio);
-  static_for<kFragDist>(issue);
+  static_for<FD>(issue);
   static_for<N>([&](auto i_tag) {
     constexpr int i = decltype(i_tag)::value;
-    issue(std::integral_constant<int, i + kFragDist>{});
-    constexpr int later = F * ((N - 1 - i) < kFragDist ? (N - 1 - i) : kFragDist);
+    issue(std::integral_constant<int, i + FD>{});
+    constexpr int later = F * ((N - 1 - i) < FD ? (N - 1 - i) : FD);
     lds_wait<(later < 15 ? later : 15), F>(ring[i % R]);
     constexpr int b = i / KD, kk = i % KD;
     const bf16x8* f = ring[i % R];
@@ -289,12 +289,12 @@ __device__ __forceinline__ void scores_section(const uint32_t (&kaddr)[D / 16], 
 // placed after the MFMAs of step i) runs on the vector ALU while the matrix
 // core works through chunk c.  V^T (tV^T) sits at byte VOFF (TVOFF) of LDS;
 // lds_base is the LDS address of byte 0 and vlo/vhi the lane's offsets.
-template <int D, int NB, bool JVP, int VOFF, int TVOFF, bool F16 = false, class Inter>
+template <int D, int NB, bool JVP, int VOFF, int TVOFF, bool F16 = false, int FD = kFragDist, class Inter>
 __device__ __forceinline__ void pv_section(uint32_t lds_base, const int (&vlo)[D / 32], const int (&vhi)[D / 32],
                                            const bf16x8 (&pf)[NB][2], const bf16x8 (&hf)[JVP ? NB : 1][2],
                                            f32x16 (&acc)[D / 32], f32x16 (&accA)[JVP ? D / 32 : 1],
                                            f32x16 (&accB)[JVP ? D / 32 : 1], Inter&& inter) {
-  constexpr int DB = D / 32, KC = 2 * NB, N = DB * KC, R = kFragDist + 1, F = JVP ? 2 : 1;
+  constexpr int DB = D / 32, KC = 2 * NB, N = DB * KC, R = FD + 1, F = JVP ? 2 : 1;
   constexpr int RPF = 2 * F;  // LDS reads per issued step
   bf16x8 ring[R][F];
   auto issue = [&](auto i_tag) {
@@ -307,12 +307,12 @@ __device__ __forceinline__ void pv_section(uint32_t lds_base, const int (&vlo)[D
     }
   };
   __builtin_amdgcn_s_setprio(kMfmaPrio);
-  static_for<kFragDist>(issue);
+  static_for<FD>(issue);
   static_for<N>([&](auto i_tag) {
     constexpr int i = decltype(i_tag)::value;
-    issue(std::integral_constant<int, i + kFragDist>{});
-    // reads issued after step i's own: those of steps i+1 .. min(i+kFragDist, N-1)
-    constexpr int later = RPF * ((N - 1 - i) < kFragDist ? (N - 1 - i) : kFragDist);
+    issue(std::integral_constant<int, i + FD>{});
+    // reads issued after step i's own: those of steps i+1 .. min(i+FD, N-1)
+    constexpr int later = RPF * ((N - 1 - i) < FD ? (N - 1 - i) : FD);
     lds_wait<(later < 15 ? later : 15), F>(ring[i % R]);
     constexpr int db = i % DB, c = i / DB;
     const bf16x8* f = ring[i % R];
@@ -486,6 +486,13 @@ attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int NWD = SPLIT ? 4 : NW;              // waves that fill one tile (a group's)
   static_assert(!SPLIT || BIAS == kNoBias, "no score operand with key-split workgroups");
   constexpr int NB = BN / 32;    // 32-key blocks per tile
+  // LDS read-ahead of the MFMA sections: one step for the JVP instances that
+  // sit at 256 VGPRs (128-wide queries and keys over 64 value columns, and
+  // the key-split JVP at 64): with the full read-ahead their fragment rings
+  // spilled, and the reloads inside the score section waited on every
+  // outstanding load, the next tile's copies included (D = 128 JVP +10.6%,
+  // causal JVP at 64 +3.3% without them)
+  constexpr int FDIST = JVP && ((DQK == 128 && DV == 64) || (DQK == 64 && NW_ == 8)) ? 1 : kFragDist;
   constexpr int KD = DQK / 16;   // MFMA steps over the query/key head dim
   constexpr int DB = DVL / 32;   // 32-column output blocks
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
@@ -733,7 +740,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         // S^T = K Q^T (and the tangent scores tQ K^T + Q tK^T)
         f32x16 s[NB];
         f32x16 ts[JVP ? NB : 1];
-        scores_section<DQK, NB, JVP, S * KSTR, S * KSTR + OFF_TK, F16>(kaddr, qf, tqf, s, ts);
+        scores_section<DQK, NB, JVP, S * KSTR, S * KSTR + OFF_TK, F16, FDIST>(kaddr, qf, tqf, s, ts);
 
         // mask keys past this row's limit (ragged tail, causal diagonal,
         // jagged truncation) -- only on tiles that reach some row's limit
@@ -821,7 +828,7 @@ attn_fwd_bf16_kernel(FwdArgs a) {
         constexpr int EPS = 8 / DB;  // elements of the next chunk per PV step
         static_for<8>(soft);
         // O^T += V^T P^T (JVP: accB += V^T H^T, accA += tV^T P^T)
-        pv_section<DVL, NB, JVP, S * VSTR + OFF_V, S * VSTR + OFF_TV, F16>(
+        pv_section<DVL, NB, JVP, S * VSTR + OFF_V, S * VSTR + OFF_TV, F16, FDIST>(
             lds_g + VBASE, vlo, vhi, pf, hf, acc, accA, accB, [&](auto i_tag) {
               constexpr int i = decltype(i_tag)::value, c = i / DB;
               if constexpr (c + 1 < 2 * NB) {
