@@ -448,7 +448,7 @@ struct Bf16Cfg {
   static constexpr int OFF_TV = VSPLIT ? TILE_V : 2 * TILE_K + TILE_V;
   // one wave per SIMD: 128-wide JVP accumulators (three of 64 registers) or
   // 256-wide queries and keys; the JVP with 128-wide queries and keys and at
-  // most 64 value columns keeps two (at 64 with a 72-byte spill, still faster)
+  // most 64 value columns keeps two (at 64 with a one-step read-ahead, FDIST)
   static constexpr bool WIDE = (JVP && DV == 128) || DQK == 256;
   // floats per lane handed from group 1 to group 0 at the merge: m, l (r),
   // the O accumulator (and accA, accB)
@@ -464,7 +464,7 @@ struct Bf16Cfg {
   static constexpr bool WAVE_LAG = !JVP && NW == 4 && DQK <= 64;
   static_assert(BN % 32 == 0, "unsupported tile");
   // 256-wide queries and keys: values up to 128 wide, or 256 wide for the
-  // plain forward (a JVP with 256-wide values runs as two 128-wide halves)
+  // plain forward (the JVP is launched on 64-wide value slices)
   static_assert(DQK == 16 || DQK == 32 || DQK == 64 || DQK == 128 || (DQK == 256 && (DV <= 128 || (!JVP && DV == 256))),
                 "unsupported head dim");
   static_assert(!VSPLIT || (2 * KSTR <= 65536 && 2 * VSTR <= 65536), "each side's two stages within 16-bit offsets");

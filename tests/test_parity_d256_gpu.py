@@ -1,6 +1,6 @@
 """GPU parity at head dim 256 against the fp64 oracle, with the tolerances
 of each dtype: the forward (dense, causal, jagged, biased; bf16, fp16,
-fp32), the JVP (bf16, fp16; two launches over the halves of the value
+fp32), the JVP (bf16, fp16; launches over 64-wide slices of the value
 columns) and the backward (dense, jagged, biased; bf16, fp16).  The
 256-wide kernels run one wave per SIMD; the plain forward streams 64-key
 tiles through the split K-side / V-side LDS layout, the JVP and the biased
