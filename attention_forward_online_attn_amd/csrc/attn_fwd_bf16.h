@@ -566,6 +566,14 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     dch_v[ph] = (lane % CPR_V) ^ swz_f<DVL>(drow_v + RSTEP_V * ph);
     dv0[ph] = (uint32_t)((drow_v * a.v_sn + dch_v[ph] * 8) * 2);
   }
+  // Head dims 128 and 256: the lane offsets pass through an opaque
+  // statement in place once per tile (no copy per use), and the whole-tile
+  // branch ends in an empty volatile statement, so that its last copy is not
+  // merged with the ragged branch's into one copy with a 64-bit vector
+  // address: three fewer vector instructions per tile.  At narrower head
+  // dims both cost registers (the D = 64 forward would drop from four waves
+  // per SIMD to three), and the per-use copy stays.
+  constexpr bool OFFS_INPLACE = DQK >= 128;
   auto dma_tile = [&](int j, int stage) {
     const int64_t k0 = (int64_t)j * BN;
     const char* src[4] = {(const char*)K + k0 * a.k_sn * 2, (const char*)V + k0 * a.v_sn * 2,
@@ -575,6 +583,12 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     const int toff[4] = {stage * KSTR, VBASE + stage * VSTR + OFF_V, stage * KSTR + OFF_TK,
                          VBASE + stage * VSTR + OFF_TV};
     const int64_t step_b[2] = {(int64_t)RSTEP_K * a.k_sn * 2, (int64_t)RSTEP_V * a.v_sn * 2};
+    if constexpr (OFFS_INPLACE) {
+#pragma unroll
+      for (int ph = 0; ph < NPH_K; ++ph) asm("" : "+v"(dk0[ph]));
+#pragma unroll
+      for (int ph = 0; ph < NPH_V; ++ph) asm("" : "+v"(dv0[ph]));
+    }
     // a whole tile of keys: in 32 bits (j BN < Lkv <= INT_MAX), a scalar
     // compare rather than a 64-bit one on the vector ALU
     if (j * BN <= t.Lkv - BN) {
@@ -590,18 +604,20 @@ attn_fwd_bf16_kernel(FwdArgs a) {
           // scalar base + 32-bit lane offset); with several instructions per
           // tensor the compiler would otherwise fold it into per-lane 64-bit
           // addresses held across the loop.  Likewise the lane offset: an
-          // opaque copy at each use keeps its zero-extension next to the load
+          // opaque copy at each use (OFFS_INPLACE: the opaque statement per
+          // tile above) keeps its zero-extension next to the load
           // (hoisted out of the key loop, it would turn every copy into a
           // 64-bit vector add and a 64-bit address: 28 more vector
           // instructions per pass over the unrolled loop at D = 128, 1-3%)
           const char* b = src[x] + i * step_b[vs];
           if constexpr (NIM > 1) asm("" : "+s"(b));
           uint32_t lo = vs ? dv0[i % NPH_V] : dk0[i % NPH_K];
-          asm("" : "+v"(lo));
+          if constexpr (!OFFS_INPLACE) asm("" : "+v"(lo));
           __builtin_amdgcn_global_load_lds((const void*)(b + lo),
                                            (__attribute__((address_space(3))) void*)(base + (NWD * i + wd) * 1024 + toff[x]),
                                            16, 0, 0);
         }
+      if constexpr (OFFS_INPLACE) asm volatile("");
     } else {  // ragged last tile: rows past the keys re-read the last key (masked)
       const int last = t.Lkv - 1 - (int)k0;
 #pragma unroll
