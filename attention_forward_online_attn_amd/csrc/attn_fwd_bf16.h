@@ -566,15 +566,15 @@ attn_fwd_bf16_kernel(FwdArgs a) {
     dch_v[ph] = (lane % CPR_V) ^ swz_f<DVL>(drow_v + RSTEP_V * ph);
     dv0[ph] = (uint32_t)((drow_v * a.v_sn + dch_v[ph] * 8) * 2);
   }
-  // Head dims 128 and 256, and the plain key-split workgroups: the lane
-  // offsets pass through an opaque statement in place once per tile (no copy
-  // per use), and the whole-tile branch ends in an empty volatile statement,
-  // so that its last copy is not merged with the ragged branch's into one
-  // copy with a 64-bit vector address: three fewer vector instructions per
-  // tile.  Elsewhere both cost registers (the 4-wave D = 64 forward would
-  // drop from four waves per SIMD to three, the key-split D = 64 JVP would
-  // spill more), and the per-use copy stays.
-  constexpr bool OFFS_INPLACE = DQK >= 128 || (NW_ == 8 && !JVP);
+  // Head dims 128 and 256, the plain key-split workgroups and the 4-wave
+  // JVP: the lane offsets pass through an opaque statement in place once per
+  // tile (no copy per use), and the whole-tile branch ends in an empty
+  // volatile statement, so that its last copy is not merged with the ragged
+  // branch's into one copy with a 64-bit vector address: three fewer vector
+  // instructions per tile.  Elsewhere both cost registers (the 4-wave plain
+  // D = 64 forward would drop from four waves per SIMD to three, the
+  // key-split D = 64 JVP would spill more), and the per-use copy stays.
+  constexpr bool OFFS_INPLACE = DQK >= 128 || (NW_ == 8 && !JVP) || (NW_ == 4 && JVP);
   auto dma_tile = [&](int j, int stage) {
     const int64_t k0 = (int64_t)j * BN;
     const char* src[4] = {(const char*)K + k0 * a.k_sn * 2, (const char*)V + k0 * a.v_sn * 2,
